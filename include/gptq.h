@@ -1,0 +1,163 @@
+/*
+ * gptq.h - C ABI of the MI355X (gfx950) GPTQ per-layer quantization solve.
+ *
+ * The solve follows the GPTQ description of "GPTQ 实战" chapter 5 (CSDN),
+ * section 5.1.8 (quantize one column, spread its error over the columns not
+ * yet quantized with the Cholesky factor of the inverse Hessian, lazy batches
+ * of 128 columns) and the BaseQuantizeConfig fields of the AutoGPTQ examples
+ * walkthrough, section 1.4 (bits, group_size, damp_percent, desc_act,
+ * static_groups, sym).  A layer is solved by four calls:
+ *
+ *   gptq_hessian_accumulate   S += X^T X over token chunks      (any number)
+ *   gptq_prepare_hinv         H = 2 S / N, damping, act-order, inverse factor U
+ *   gptq_quantize_layer       column sweep -> codes, scales, zeros, g_idx
+ *   gptq_pack                 codes -> int32 qweight
+ *
+ * Conventions shared by every call
+ *   - All array pointers are DEVICE pointers on the current HIP device; the
+ *     caller owns every buffer (inputs, outputs, workspaces).  The library
+ *     allocates no device memory.
+ *   - Matrices are row-major.  W is [d_out, d_in] (nn.Linear layout), X is
+ *     [n_tokens, d_in] with row stride ldx elements.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Every call only enqueues work on it and returns; results are valid once
+ *     the stream has reached that point.
+ *   - Arguments are checked on the host before anything is enqueued; a bad
+ *     argument returns GPTQ_ERR_INVALID_ARG and enqueues nothing.  A failed
+ *     kernel launch returns GPTQ_ERR_HIP.
+ *   - Workspaces: query the size with the matching *_workspace_size call and
+ *     pass at least that many bytes, 256-byte aligned.  Their contents on
+ *     entry do not matter and are undefined on exit.  Concurrent calls must
+ *     not share a workspace.
+ */
+#ifndef GPTQ_H
+#define GPTQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  GPTQ_OK = 0,
+  GPTQ_ERR_INVALID_ARG = 1,  /* rejected on the host, nothing enqueued */
+  GPTQ_ERR_NOT_SPD = 2,      /* reserved for host wrappers reading info_dev */
+  GPTQ_ERR_HIP = 3,          /* a HIP runtime call or kernel launch failed */
+  GPTQ_ERR_WORKSPACE = 4     /* workspace missing, too small or misaligned */
+} gptq_status;
+
+typedef enum { GPTQ_F32 = 0, GPTQ_BF16 = 1 } gptq_dtype;
+
+/*
+ * Quantization parameters, named after BaseQuantizeConfig (AutoGPTQ examples
+ * walkthrough, section 1.4; OLMo AutoGPTQ quick-start, section 三):
+ *   bits          2, 3, 4 or 8
+ *   group_size    -1 (one group per output row) or > 0 input columns per group
+ *   damp_percent  in (0, 1): H += damp_percent * mean(diag H) * I
+ *   desc_act      nonzero: sweep columns by descending diag(H) (act-order)
+ *   static_groups nonzero: every group's scale/zero comes from the original
+ *                 weights before the sweep; zero: a group's parameters are
+ *                 taken from the current (compensated) weights when the sweep
+ *                 reaches the group's first column
+ *   sym           nonzero: symmetric range [-max|w|, max|w|], zero = 2^(bits-1)
+ *   block_size    lazy-batch width; must be 128 (chapter 5, section 5.1.8)
+ */
+typedef struct {
+  int32_t bits;
+  int32_t group_size;
+  float damp_percent;
+  int32_t desc_act;
+  int32_t static_groups;
+  int32_t sym;
+  int32_t block_size;
+} gptq_config;
+
+/* Host-only check of the rules above plus the solve's own constraint that a
+ * group either divides the 128-column block or is a multiple of it (so the
+ * lazy batches reproduce the plain column-by-column sweep).  Returns GPTQ_OK or
+ * GPTQ_ERR_INVALID_ARG. */
+gptq_status gptq_config_validate(const gptq_config* cfg);
+
+/* Human-readable name of a status code (static storage). */
+const char* gptq_status_string(gptq_status status);
+
+/*
+ * S += X^T X  (chapter 5, section 5.1.7: the layer Hessian is X X^T up to a
+ * constant, estimated from calibration activations).
+ *   S        [d_in, d_in] fp32, full symmetric storage, read-modify-write;
+ *            zero it before the first chunk of a layer.
+ *   X        [n_tokens, ldx] bf16 (GPTQ_BF16) or fp32 (GPTQ_F32); the first
+ *            d_in entries of each row are used.  Needs 16-byte alignment and
+ *            ldx a multiple of 8 (bf16) or 4 (fp32).
+ *   n_tokens >= 0; 0 leaves S unchanged.
+ * Products are formed exactly (bf16) or in fp32 and summed in fp32.  The sum
+ * is deterministic: a fixed token split and a fixed reduction order.
+ */
+size_t gptq_hessian_workspace_size(int64_t d_in, int64_t n_tokens, gptq_dtype xt);
+gptq_status gptq_hessian_accumulate(float* S, int64_t d_in, const void* X, gptq_dtype xt,
+                                    int64_t n_tokens, int64_t ldx, void* ws, size_t ws_bytes,
+                                    void* stream);
+
+/*
+ * From the accumulated S of n_total tokens:
+ *   H = (2 / n_total) S                  written back into S_to_H (kept for checks)
+ *   lambda = damp_percent * mean(diag H), H_d = H + lambda I
+ *                                        (chapter 5, section 5.1.8, damping)
+ *   perm: desc_act ? stable sort of columns by descending diag(H) (ties: lower
+ *         index first) : identity.  perm[i] = original column swept at position i.
+ *   U = upper-triangular factor with (H_d[perm][:, perm])^-1 = U^T U
+ *       (chapter 5, section 5.1.8: "Cholesky(inverse(H))"), [d_in, d_in] fp32,
+ *       zeros below the diagonal.
+ *   info_dev (device int32): 0 on success; k > 0 when the damped Hessian is
+ *       not positive definite, k-1 being the first sweep position at which a
+ *       pivot failed (U is then undefined).  Read it after synchronising.
+ * n_total must be > 0.
+ */
+size_t gptq_prepare_workspace_size(int64_t d_in);
+gptq_status gptq_prepare_hinv(float* S_to_H, int64_t d_in, int64_t n_total, const gptq_config* cfg,
+                              float* U, int32_t* perm, int32_t* info_dev, void* ws,
+                              size_t ws_bytes, void* stream);
+
+/*
+ * The GPTQ column sweep (chapter 5, section 5.1.8, the implementation-level
+ * pseudocode), in sweep order perm, over lazy blocks of 128 columns:
+ *   per column i: q = clamp(rint(w / s) + z, 0, 2^bits - 1), w_hat = s (q - z),
+ *   err = (w - w_hat) / U[i, i], later columns of the block -= err * U[i, :];
+ *   after each block the remaining columns -= Err_block @ U[block, rest].
+ *   W        [d_out, d_in] fp32 or bf16 (not modified)
+ *   U, perm  from gptq_prepare_hinv
+ *   codes    [d_out, d_in] uint8, ORIGINAL column order
+ *   scales   [n_groups, d_out] fp32, zeros [n_groups, d_out] int32, with
+ *            n_groups = ceil(d_in / group_size), or 1 for group_size -1
+ *   g_idx    [d_in] int32: group of each original column
+ *   Q_or_null        optional [d_out, d_in] fp32 dequantized weights, original order
+ *   row_loss_or_null optional [d_out] fp32: sum of err^2 over the row, which
+ *                    equals (w - w_hat) H_d (w - w_hat)^T
+ * Requires d_in % (32 / bits) == 0 (d_in % 32 == 0 for 3 bits).
+ */
+size_t gptq_workspace_size(int64_t d_out, int64_t d_in, const gptq_config* cfg);
+gptq_status gptq_quantize_layer(const void* W, gptq_dtype wt, int64_t d_out, int64_t d_in,
+                                const float* U, const int32_t* perm, const gptq_config* cfg,
+                                uint8_t* codes, float* scales, int32_t* zeros, int32_t* g_idx,
+                                float* Q_or_null, float* row_loss_or_null, void* ws,
+                                size_t ws_bytes, void* stream);
+
+/*
+ * qweight[w, n] holds bits [32 w, 32 w + 32) of output row n's code stream,
+ * in which code (n, j) occupies bits [bits * j, bits * j + bits) (least
+ * significant first; 3-bit codes straddle words).  qweight is
+ * [d_in * bits / 32, d_out] int32 (the AutoGPTQ examples walkthrough names
+ * the packed tensor qweight; the practitioner blog, section 3.3, gives the
+ * density: 128 4-bit codes fill 64 bytes).  Codes must lie in [0, 2^bits).
+ * Requires d_in % (32 / bits) == 0 (d_in % 32 == 0 for 3 bits).
+ */
+gptq_status gptq_pack(const uint8_t* codes, int64_t d_out, int64_t d_in, int32_t bits,
+                      int32_t* qweight, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GPTQ_H */

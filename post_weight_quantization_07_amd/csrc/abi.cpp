@@ -1,0 +1,130 @@
+// C ABI of the GPTQ layer solve: argument checks, workspace sizing and the
+// launch sequence of each call.  Declarations and contracts: include/gptq.h.
+#include "../../include/gptq.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "gptq_internal.h"
+
+namespace {
+
+constexpr int kBlock = 128;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned256(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 255u) == 0; }
+
+int device_cus() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) return 256;
+  return cus;
+}
+
+gptq_status from_hip(hipError_t e) { return e == hipSuccess ? GPTQ_OK : GPTQ_ERR_HIP; }
+
+bool bits_ok(int32_t b) { return b == 2 || b == 3 || b == 4 || b == 8; }
+
+// d_in % (32 / bits) == 0, and d_in % 32 == 0 for 3 bits: whole words per row
+bool packable(int64_t d_in, int32_t bits) {
+  if (!bits_ok(bits) || d_in <= 0) return false;
+  const int64_t m = (bits == 3) ? 32 : 32 / bits;
+  return d_in % m == 0;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* gptq_status_string(gptq_status s) {
+  switch (s) {
+    case GPTQ_OK: return "ok";
+    case GPTQ_ERR_INVALID_ARG: return "invalid argument";
+    case GPTQ_ERR_NOT_SPD: return "damped Hessian is not positive definite";
+    case GPTQ_ERR_HIP: return "HIP runtime error";
+    case GPTQ_ERR_WORKSPACE: return "workspace missing, too small or misaligned";
+  }
+  return "unknown status";
+}
+
+gptq_status gptq_config_validate(const gptq_config* c) {
+  if (!c) return GPTQ_ERR_INVALID_ARG;
+  if (!bits_ok(c->bits)) return GPTQ_ERR_INVALID_ARG;
+  if (!(c->group_size == -1 || c->group_size > 0)) return GPTQ_ERR_INVALID_ARG;
+  if (!(c->damp_percent > 0.0f && c->damp_percent < 1.0f)) return GPTQ_ERR_INVALID_ARG;
+  if (c->block_size != kBlock) return GPTQ_ERR_INVALID_ARG;
+  if (c->group_size > 0 && !(kBlock % c->group_size == 0 || c->group_size % kBlock == 0))
+    return GPTQ_ERR_INVALID_ARG;
+  return GPTQ_OK;
+}
+
+size_t gptq_hessian_workspace_size(int64_t d_in, int64_t n_tokens, gptq_dtype xt) {
+  if (d_in <= 0 || n_tokens < 0 || (xt != GPTQ_F32 && xt != GPTQ_BF16)) return 0;
+  return gptq::hessian_plan(d_in, n_tokens, xt == GPTQ_BF16, device_cus()).ws_bytes;
+}
+
+gptq_status gptq_hessian_accumulate(float* S, int64_t d_in, const void* X, gptq_dtype xt, int64_t n_tokens,
+                                    int64_t ldx, void* ws, size_t ws_bytes, void* stream) {
+  if (!S || d_in <= 0 || n_tokens < 0 || (xt != GPTQ_F32 && xt != GPTQ_BF16)) return GPTQ_ERR_INVALID_ARG;
+  if (n_tokens == 0) return GPTQ_OK;
+  const bool bf16 = (xt == GPTQ_BF16);
+  const int64_t vec = bf16 ? 8 : 4;
+  if (!X || d_in % vec != 0 || ldx < d_in || ldx % vec != 0 || !aligned16(X) || !aligned16(S))
+    return GPTQ_ERR_INVALID_ARG;
+  if (ldx > (int64_t{1} << 24)) return GPTQ_ERR_INVALID_ARG;  // 32-bit in-stage offsets
+  const gptq::HessPlan plan = gptq::hessian_plan(d_in, n_tokens, bf16, device_cus());
+  if (!ws || ws_bytes < plan.ws_bytes || !aligned256(ws)) return GPTQ_ERR_WORKSPACE;
+  return from_hip(gptq::hessian_launch(plan, S, d_in, X, bf16, n_tokens, ldx, ws,
+                                       static_cast<hipStream_t>(stream)));
+}
+
+size_t gptq_prepare_workspace_size(int64_t d_in) {
+  if (d_in <= 0) return 0;
+  return gptq::prepare_layout(d_in).ws_bytes;
+}
+
+gptq_status gptq_prepare_hinv(float* S_to_H, int64_t d_in, int64_t n_total, const gptq_config* cfg, float* U,
+                              int32_t* perm, int32_t* info_dev, void* ws, size_t ws_bytes, void* stream) {
+  if (!S_to_H || !U || !perm || !info_dev || d_in <= 0 || n_total <= 0) return GPTQ_ERR_INVALID_ARG;
+  if (gptq_config_validate(cfg) != GPTQ_OK) return GPTQ_ERR_INVALID_ARG;
+  if (d_in % 4 != 0 || !aligned16(S_to_H) || !aligned16(U)) return GPTQ_ERR_INVALID_ARG;
+  const gptq::PrepLayout lay = gptq::prepare_layout(d_in);
+  if (!ws || ws_bytes < lay.ws_bytes || !aligned256(ws)) return GPTQ_ERR_WORKSPACE;
+  return from_hip(gptq::prepare_launch(S_to_H, d_in, n_total, cfg->damp_percent, cfg->desc_act != 0, U, perm,
+                                       info_dev, ws, static_cast<hipStream_t>(stream)));
+}
+
+size_t gptq_workspace_size(int64_t d_out, int64_t d_in, const gptq_config* cfg) {
+  (void)cfg;
+  if (d_out <= 0 || d_in <= 0) return 0;
+  return gptq::quant_layout(d_out, d_in).ws_bytes;
+}
+
+gptq_status gptq_quantize_layer(const void* W, gptq_dtype wt, int64_t d_out, int64_t d_in, const float* U,
+                                const int32_t* perm, const gptq_config* cfg, uint8_t* codes, float* scales,
+                                int32_t* zeros, int32_t* g_idx, float* Q_or_null, float* row_loss_or_null,
+                                void* ws, size_t ws_bytes, void* stream) {
+  if (gptq_config_validate(cfg) != GPTQ_OK) return GPTQ_ERR_INVALID_ARG;
+  if (!W || !U || !codes || !scales || !zeros || !g_idx || d_out <= 0 || d_in <= 0) return GPTQ_ERR_INVALID_ARG;
+  if (wt != GPTQ_F32 && wt != GPTQ_BF16) return GPTQ_ERR_INVALID_ARG;
+  if (cfg->desc_act && !perm) return GPTQ_ERR_INVALID_ARG;
+  if (!packable(d_in, cfg->bits)) return GPTQ_ERR_INVALID_ARG;
+  if (!aligned16(U) || !aligned16(codes) || (Q_or_null && !aligned16(Q_or_null))) return GPTQ_ERR_INVALID_ARG;
+  const gptq::QuantLayout lay = gptq::quant_layout(d_out, d_in);
+  if (!ws || ws_bytes < lay.ws_bytes || !aligned256(ws)) return GPTQ_ERR_WORKSPACE;
+  return from_hip(gptq::quantize_launch(W, wt == GPTQ_BF16, d_out, d_in, U, perm, cfg->bits, cfg->group_size,
+                                        cfg->sym != 0, cfg->static_groups != 0, codes, scales, zeros, g_idx,
+                                        Q_or_null, row_loss_or_null, ws, static_cast<hipStream_t>(stream),
+                                        cfg->desc_act == 0));
+}
+
+gptq_status gptq_pack(const uint8_t* codes, int64_t d_out, int64_t d_in, int32_t bits, int32_t* qweight,
+                      void* stream) {
+  if (!codes || !qweight || d_out <= 0) return GPTQ_ERR_INVALID_ARG;
+  if (!packable(d_in, bits)) return GPTQ_ERR_INVALID_ARG;
+  return from_hip(gptq::pack_launch(codes, d_out, d_in, bits, qweight, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

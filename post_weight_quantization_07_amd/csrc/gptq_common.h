@@ -1,0 +1,49 @@
+// Shared device helpers of the gfx950 GPTQ kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#define GPTQ_DEV __device__ __forceinline__
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
+typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4_t;
+
+namespace gptq {
+
+constexpr int kWave = 64;
+
+GPTQ_DEV int lane_id() { return static_cast<int>(threadIdx.x) & (kWave - 1); }
+
+// bf16 bit pattern -> fp32 (exact)
+GPTQ_DEV float bf16_to_f32(uint16_t b) { return __uint_as_float(static_cast<uint32_t>(b) << 16); }
+
+// Broadcast the value of lane `src` of every 16-lane DPP row to the whole row.
+template <int src>
+GPTQ_DEV float row_bcast(float v) {
+  static_assert(src >= 0 && src < 16, "row lane");
+  return __builtin_amdgcn_update_dpp(0.0f, v, 0x150 + src, 0xf, 0xf, false);
+}
+
+// Reductions over one 16-lane row with DPP (quad_perm, row_half_mirror, row_mirror).
+GPTQ_DEV float row_max16(float v) {
+  v = fmaxf(v, __builtin_amdgcn_update_dpp(0.0f, v, 0xB1, 0xf, 0xf, false));  // quad_perm [1,0,3,2]
+  v = fmaxf(v, __builtin_amdgcn_update_dpp(0.0f, v, 0x4E, 0xf, 0xf, false));  // quad_perm [2,3,0,1]
+  v = fmaxf(v, __builtin_amdgcn_update_dpp(0.0f, v, 0x141, 0xf, 0xf, false)); // row_half_mirror
+  v = fmaxf(v, __builtin_amdgcn_update_dpp(0.0f, v, 0x140, 0xf, 0xf, false)); // row_mirror
+  return v;
+}
+GPTQ_DEV float row_min16(float v) {
+  v = fminf(v, __builtin_amdgcn_update_dpp(0.0f, v, 0xB1, 0xf, 0xf, false));
+  v = fminf(v, __builtin_amdgcn_update_dpp(0.0f, v, 0x4E, 0xf, 0xf, false));
+  v = fminf(v, __builtin_amdgcn_update_dpp(0.0f, v, 0x141, 0xf, 0xf, false));
+  v = fminf(v, __builtin_amdgcn_update_dpp(0.0f, v, 0x140, 0xf, 0xf, false));
+  return v;
+}
+
+// Agent-scope acquire/release fences around the split-reduction tickets.
+GPTQ_DEV void fence_release() { __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent"); }
+GPTQ_DEV void fence_acquire() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
+
+}  // namespace gptq

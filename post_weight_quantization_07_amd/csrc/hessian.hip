@@ -1,0 +1,399 @@
+// S += X^T X on gfx950 matrix cores.
+//
+// GPTQ 实战 ch.5, section 5.1.7: the layer Hessian is X X^T (up to a constant)
+// estimated from calibration activations.  X arrives token-major
+// ([tokens, d_in]), so the contraction runs over the strided token axis.
+//
+// Work split: the d_in x d_in output is cut into tiles of the upper triangle
+// (diagonal tiles computed whole); the token axis is cut into n_split equal
+// slices so a launch has enough workgroups for 256 CUs.  Each workgroup owns
+// one (tile, slice) pair and writes its fp32 partial tile; the last workgroup
+// of a tile to finish (a ticket counter) sums the partials in slice order and
+// adds the result to S and to its mirror tile.  The sum order is fixed, so
+// the result does not depend on scheduling.
+//
+// bf16 path: 256x256 tile, 4 waves of 128x128, v_mfma_f32_16x16x32_bf16.
+//   Each thread loads an 8-token x 8-channel block (eight 16-byte loads) and
+//   transposes it in registers with v_perm_b32, so LDS holds every channel's
+//   tokens contiguously: MFMA operands are single ds_read_b128.  LDS rows are
+//   128 bytes (64 tokens); the 16-byte chunk index is XOR-swizzled with the
+//   row index so both the transposing stores and the operand loads are free
+//   of bank conflicts.  Double-buffered: 2 x (32 KB + 32 KB).
+// fp32 path: 128x128 tile, 4 waves of 64x64, v_mfma_f32_16x16x4_f32, LDS
+//   holds [token][channel] rows padded to 144 floats.
+#include "gptq_common.h"
+#include "gptq_internal.h"
+
+#include <algorithm>
+
+namespace gptq {
+namespace {
+
+constexpr int kThreads = 256;
+
+struct HessParams {
+  const void* X;
+  int64_t ldx;
+  int64_t n_tokens;
+  int32_t d_in;
+  int32_t nt;
+  int32_t n_tiles;
+  int32_t n_split;
+  int64_t split_len;
+  float* partial;
+  int32_t* tickets;
+  float* S;
+};
+
+GPTQ_DEV void tile_coords(int t, int nt, int& I, int& J) {
+  int i = 0;
+  while (t >= nt - i) {
+    t -= nt - i;
+    ++i;
+  }
+  I = i;
+  J = i + t;
+}
+
+// ----------------------------------------------------------------------------
+// Split-slice epilogue shared by both paths.  Accumulators are NI x NJ MFMA
+// 16x16 tiles per wave; element (i, j, r) of a lane sits at tile row
+// rbase + 16 i + 4 (lane >> 4) + r and tile column cbase + 16 j + (lane & 15).
+// ----------------------------------------------------------------------------
+template <int TILE>
+GPTQ_DEV void add_frag_to_S(const HessParams& p, int I, int J, int row0, int col, const f32x4_t& v) {
+  // v[r] belongs to tile element (row0 + r, col)
+  const int d = p.d_in;
+  const int gc = J * TILE + col;
+  if (gc >= d) return;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int gr = I * TILE + row0 + r;
+    if (gr < d) {
+      p.S[static_cast<int64_t>(gr) * d + gc] += v[r];
+      if (I != J) p.S[static_cast<int64_t>(gc) * d + gr] += v[r];
+    }
+  }
+}
+
+template <int NI, int NJ, int TILE>
+GPTQ_DEV void finish_tile(const HessParams& p, int t, int split, int I, int J, int rbase, int cbase,
+                          const f32x4_t (&acc)[NI][NJ]) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int rsub = 4 * (lane >> 4), csub = lane & 15;
+  if (p.n_split == 1) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+        add_frag_to_S<TILE>(p, I, J, rbase + 16 * i + rsub, cbase + 16 * j + csub, acc[i][j]);
+    return;
+  }
+  constexpr int64_t kElems = static_cast<int64_t>(TILE) * TILE;
+  // partials are stored in register order: [wave][i][j][lane][4]
+  const int wave = tid >> 6;
+  float* mine = p.partial + (static_cast<int64_t>(t) * p.n_split + split) * kElems;
+#pragma unroll
+  for (int i = 0; i < NI; ++i)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+      *reinterpret_cast<f32x4_t*>(mine + ((((wave * NI + i) * NJ + j) * 64 + lane) << 2)) = acc[i][j];
+  fence_release();
+  __syncthreads();
+  __shared__ int s_last;
+  if (tid == 0) {
+    const int old = atomicAdd(&p.tickets[t], 1);
+    s_last = (old == p.n_split - 1);
+  }
+  __syncthreads();
+  if (!s_last) return;
+  fence_acquire();
+  // the last slice to arrive sums all slices in slice order, fragment by fragment
+  const float* base = p.partial + static_cast<int64_t>(t) * p.n_split * kElems;
+  for (int f = 0; f < NI * NJ; ++f) {
+    const int i = f / NJ, j = f % NJ;
+    const int64_t off = static_cast<int64_t>(((wave * NI + i) * NJ + j) * 64 + lane) << 2;
+    f32x4_t sum = {0.f, 0.f, 0.f, 0.f};
+    for (int k = 0; k < p.n_split; ++k) sum += *reinterpret_cast<const f32x4_t*>(base + k * kElems + off);
+    add_frag_to_S<TILE>(p, I, J, rbase + 16 * i + rsub, cbase + 16 * j + csub, sum);
+  }
+}
+
+// ============================================================ bf16 path ====
+constexpr int kBTile = 256;
+constexpr int kBStage = 64;              // tokens per stage = 128 bytes per LDS row
+constexpr int kBOpBytes = kBTile * 128;  // one operand stage: 32 KB
+
+// Loads tokens [row0, row0 + 8) of one 8-channel group.  Xs points at the
+// stage's first token (uniform), so per-lane offsets stay 32-bit.  d_in is a
+// multiple of 8: a channel group is either wholly inside or outside.
+GPTQ_DEV void load_block_bf16(const uint16_t* __restrict__ Xs, int ldx, int row0, int rows_left,
+                              int col, int d_in, u32x4_t (&r)[8]) {
+  const bool col_ok = col < d_in;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int row = row0 + j;
+    u32x4_t v = {0u, 0u, 0u, 0u};
+    if (col_ok && row < rows_left) v = *reinterpret_cast<const u32x4_t*>(Xs + (row * ldx + col));
+    r[j] = v;
+  }
+}
+
+// r[j] holds tokens (8 tg + j) x channels (8 cg .. 8 cg + 7); write each channel's
+// 8 tokens as one 16-byte chunk of LDS row (8 cg + c), chunk tg swizzled by c.
+GPTQ_DEV void store_block_bf16(uint8_t* lds, int cg, int tg, const u32x4_t (&r)[8]) {
+#pragma unroll
+  for (int pch = 0; pch < 4; ++pch) {
+    u32x4_t lo, hi;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      lo[q] = __builtin_amdgcn_perm(r[2 * q + 1][pch], r[2 * q][pch], 0x05040100u);
+      hi[q] = __builtin_amdgcn_perm(r[2 * q + 1][pch], r[2 * q][pch], 0x07060302u);
+    }
+    const int m0 = 8 * cg + 2 * pch;
+    *reinterpret_cast<u32x4_t*>(lds + m0 * 128 + ((tg ^ (2 * pch)) << 4)) = lo;
+    *reinterpret_cast<u32x4_t*>(lds + (m0 + 1) * 128 + ((tg ^ (2 * pch + 1)) << 4)) = hi;
+  }
+}
+
+GPTQ_DEV void mfma_stage_bf16(const uint8_t* A, const uint8_t* B, int wm, int wn, int lane,
+                              f32x4_t (&acc)[8][8]) {
+  const int r16 = lane & 15;
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk) {
+    const int q = (lane >> 4) + 4 * kk;
+    const int chunk = (q ^ (lane & 7)) << 4;
+    bf16x8_t a[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      a[i] = *reinterpret_cast<const bf16x8_t*>(A + (wm * 128 + 16 * i + r16) * 128 + chunk);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const bf16x8_t b = *reinterpret_cast<const bf16x8_t*>(B + (wn * 128 + 16 * j + r16) * 128 + chunk);
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b, acc[i][j], 0, 0, 0);
+    }
+  }
+}
+
+__global__ __launch_bounds__(kThreads, 1) void hessian_bf16_kernel(HessParams p) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2][2][kBOpBytes];
+  const int t = blockIdx.x % p.n_tiles;
+  const int split = blockIdx.x / p.n_tiles;
+  int I, J;
+  tile_coords(t, p.nt, I, J);
+  const bool diag = (I == J);
+  const int64_t k0 = static_cast<int64_t>(split) * p.split_len;
+  const int64_t k1 = min(p.n_tokens, k0 + p.split_len);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int tg = lane & 7, cg = (lane >> 3) + 8 * wave;
+  const int colA = I * kBTile + 8 * cg, colB = J * kBTile + 8 * cg;
+  const uint16_t* X = static_cast<const uint16_t*>(p.X);
+
+  f32x4_t acc[8][8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  const int nstage = (k1 > k0) ? static_cast<int>((k1 - k0 + kBStage - 1) / kBStage) : 0;
+  const int ldx = static_cast<int>(p.ldx);
+  u32x4_t ra[8], rb[8];
+  if (nstage > 0) {
+    const uint16_t* Xs = X + k0 * p.ldx;
+    const int left = static_cast<int>(min<int64_t>(k1 - k0, kBStage));
+    load_block_bf16(Xs, ldx, 8 * tg, left, colA, p.d_in, ra);
+    if (!diag) load_block_bf16(Xs, ldx, 8 * tg, left, colB, p.d_in, rb);
+    store_block_bf16(lds[0][0], cg, tg, ra);
+    if (!diag) store_block_bf16(lds[0][1], cg, tg, rb);
+  }
+  __syncthreads();
+  for (int s = 0; s < nstage; ++s) {
+    const int cur = s & 1;
+    const bool more = (s + 1) < nstage;
+    if (more) {
+      const int64_t t0 = k0 + static_cast<int64_t>(s + 1) * kBStage;
+      const uint16_t* Xs = X + t0 * p.ldx;
+      const int left = static_cast<int>(min<int64_t>(k1 - t0, kBStage));
+      load_block_bf16(Xs, ldx, 8 * tg, left, colA, p.d_in, ra);
+      if (!diag) load_block_bf16(Xs, ldx, 8 * tg, left, colB, p.d_in, rb);
+    }
+    mfma_stage_bf16(lds[cur][0], diag ? lds[cur][0] : lds[cur][1], wm, wn, lane, acc);
+    if (more) {
+      store_block_bf16(lds[cur ^ 1][0], cg, tg, ra);
+      if (!diag) store_block_bf16(lds[cur ^ 1][1], cg, tg, rb);
+    }
+    __syncthreads();
+  }
+  finish_tile<8, 8, kBTile>(p, t, split, I, J, wm * 128, wn * 128, acc);
+}
+
+// ============================================================ fp32 path ====
+constexpr int kFTile = 128;
+constexpr int kFStage = 32;    // tokens per stage
+constexpr int kFPitch = 144;   // floats per LDS row (128 + 16 pad)
+
+// d_in is a multiple of 4, so a 4-channel group is either wholly inside or outside.
+GPTQ_DEV void load_stage_f32(const float* __restrict__ X, int64_t ldx, int64_t row0, int64_t row_end,
+                             int col0, int d_in, int tid, f32x4_t (&r)[4]) {
+  const int c = col0 + 4 * (tid & 31);
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int64_t row = row0 + (tid >> 5) + 8 * u;
+    f32x4_t v = {0.f, 0.f, 0.f, 0.f};
+    if (c < d_in && row < row_end) v = *reinterpret_cast<const f32x4_t*>(X + row * ldx + c);
+    r[u] = v;
+  }
+}
+
+GPTQ_DEV void store_stage_f32(float* lds, int tid, const f32x4_t (&r)[4]) {
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+    *reinterpret_cast<f32x4_t*>(lds + ((tid >> 5) + 8 * u) * kFPitch + 4 * (tid & 31)) = r[u];
+}
+
+__global__ __launch_bounds__(kThreads, 2) void hessian_f32_kernel(HessParams p) {
+  __shared__ __attribute__((aligned(16))) float lds[2][2][kFStage * kFPitch];
+  const int t = blockIdx.x % p.n_tiles;
+  const int split = blockIdx.x / p.n_tiles;
+  int I, J;
+  tile_coords(t, p.nt, I, J);
+  const bool diag = (I == J);
+  const int64_t k0 = static_cast<int64_t>(split) * p.split_len;
+  const int64_t k1 = min(p.n_tokens, k0 + p.split_len);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const float* X = static_cast<const float*>(p.X);
+
+  f32x4_t acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  const int nstage = (k1 > k0) ? static_cast<int>((k1 - k0 + kFStage - 1) / kFStage) : 0;
+  f32x4_t ra[4], rb[4];
+  if (nstage > 0) {
+    load_stage_f32(X, p.ldx, k0, k1, I * kFTile, p.d_in, tid, ra);
+    if (!diag) load_stage_f32(X, p.ldx, k0, k1, J * kFTile, p.d_in, tid, rb);
+    store_stage_f32(lds[0][0], tid, ra);
+    if (!diag) store_stage_f32(lds[0][1], tid, rb);
+  }
+  __syncthreads();
+  for (int s = 0; s < nstage; ++s) {
+    const int cur = s & 1;
+    const bool more = (s + 1) < nstage;
+    if (more) {
+      const int64_t row0 = k0 + static_cast<int64_t>(s + 1) * kFStage;
+      load_stage_f32(X, p.ldx, row0, k1, I * kFTile, p.d_in, tid, ra);
+      if (!diag) load_stage_f32(X, p.ldx, row0, k1, J * kFTile, p.d_in, tid, rb);
+    }
+    const float* A = lds[cur][0];
+    const float* B = diag ? lds[cur][0] : lds[cur][1];
+#pragma unroll
+    for (int k4 = 0; k4 < kFStage / 4; ++k4) {
+      const int kr = 4 * k4 + (lane >> 4);
+      float a[4], b[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] = A[kr * kFPitch + wm * 64 + 16 * i + (lane & 15)];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) b[j] = B[kr * kFPitch + wn * 64 + 16 * j + (lane & 15)];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i], b[j], acc[i][j], 0, 0, 0);
+    }
+    if (more) {
+      store_stage_f32(lds[cur ^ 1][0], tid, ra);
+      if (!diag) store_stage_f32(lds[cur ^ 1][1], tid, rb);
+    }
+    __syncthreads();
+  }
+  finish_tile<4, 4, kFTile>(p, t, split, I, J, wm * 64, wn * 64, acc);
+}
+
+__global__ void fill_i32_kernel(int32_t* p, int64_t n, int32_t v) {
+  for (int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; i < n;
+       i += static_cast<int64_t>(gridDim.x) * blockDim.x)
+    p[i] = v;
+}
+
+}  // namespace
+
+hipError_t fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  const int64_t blocks = std::min<int64_t>((n + 255) / 256, 4096);
+  fill_i32_kernel<<<static_cast<int>(blocks), 256, 0, stream>>>(p, n, v);
+  return hipGetLastError();
+}
+
+HessPlan hessian_plan(int64_t d_in, int64_t n_tokens, bool bf16, int n_cu) {
+  HessPlan pl{};
+  pl.tile = bf16 ? kBTile : kFTile;
+  pl.stage_tokens = bf16 ? kBStage : kFStage;
+  pl.nt = static_cast<int>((d_in + pl.tile - 1) / pl.tile);
+  pl.n_tiles = pl.nt * (pl.nt + 1) / 2;
+  const int per_cu = bf16 ? 1 : 2;  // resident workgroups per CU (LDS bound)
+  const int64_t slots = static_cast<int64_t>(n_cu > 0 ? n_cu : 256) * per_cu;
+  const int64_t stages = (n_tokens + pl.stage_tokens - 1) / pl.stage_tokens;
+  // choose the slice count that fills whole waves of workgroups, with a mild
+  // preference for fewer slices (each slice costs a partial tile in HBM)
+  int best = 1;
+  double best_score = -1e30;
+  const int max_split = static_cast<int>(std::min<int64_t>(64, std::max<int64_t>(1, stages / 4)));
+  for (int s = 1; s <= max_split; ++s) {
+    const int64_t blocks = static_cast<int64_t>(pl.n_tiles) * s;
+    const int64_t waves = (blocks + slots - 1) / slots;
+    const double eff = static_cast<double>(blocks) / static_cast<double>(waves * slots);
+    const double score = eff - 0.002 * s;
+    if (score > best_score + 1e-12) {
+      best_score = score;
+      best = s;
+    }
+  }
+  pl.n_split = best;
+  const int64_t per = (stages + best - 1) / best;
+  pl.split_len = per * pl.stage_tokens;
+  if (pl.split_len <= 0) pl.split_len = pl.stage_tokens;
+  pl.n_split = static_cast<int>(std::max<int64_t>(1, (n_tokens + pl.split_len - 1) / pl.split_len));
+  const size_t tile_bytes = static_cast<size_t>(pl.tile) * pl.tile * sizeof(float);
+  pl.partial_bytes = pl.n_split > 1 ? static_cast<size_t>(pl.n_tiles) * pl.n_split * tile_bytes : 0;
+  pl.ticket_bytes = static_cast<size_t>(pl.n_tiles) * sizeof(int32_t);
+  auto up = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
+  pl.ws_bytes = up(pl.partial_bytes) + up(pl.ticket_bytes);
+  return pl;
+}
+
+hipError_t hessian_launch(const HessPlan& pl, float* S, int64_t d_in, const void* X, bool bf16,
+                          int64_t n_tokens, int64_t ldx, void* ws, hipStream_t stream) {
+  if (n_tokens <= 0 || d_in <= 0) return hipSuccess;
+  auto up = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
+  HessParams p{};
+  p.X = X;
+  p.ldx = ldx;
+  p.n_tokens = n_tokens;
+  p.d_in = static_cast<int32_t>(d_in);
+  p.nt = pl.nt;
+  p.n_tiles = pl.n_tiles;
+  p.n_split = pl.n_split;
+  p.split_len = pl.split_len;
+  p.partial = static_cast<float*>(ws);
+  p.tickets = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + up(pl.partial_bytes));
+  p.S = S;
+  if (pl.n_split > 1) {
+    hipError_t e = fill_i32(p.tickets, pl.n_tiles, 0, stream);
+    if (e != hipSuccess) return e;
+  }
+  const int blocks = pl.n_tiles * pl.n_split;
+  if (bf16)
+    hessian_bf16_kernel<<<blocks, kThreads, 0, stream>>>(p);
+  else
+    hessian_f32_kernel<<<blocks, kThreads, 0, stream>>>(p);
+  return hipGetLastError();
+}
+
+}  // namespace gptq

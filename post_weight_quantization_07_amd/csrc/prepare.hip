@@ -1,0 +1,321 @@
+// Hessian finalisation, damping, act-order and the inverse factor U.
+//
+// GPTQ 实战 ch.5, section 5.1.8: damp H by lambda * mean(diag H) * I, then
+// take "Cholesky(inverse(H))" once; its rows are the compensation
+// coefficients of the column sweep.  desc_act (AutoGPTQ examples walkthrough,
+// section 1.4) orders the columns by descending diag(H).
+//
+// Route on the GPU.  With J the index reversal, H_p = U^-1 U^-T for the
+// upper-triangular U with H_p^-1 = U^T U, hence J U^-1 J is the lower Cholesky
+// factor of J H_p J.  So
+//     U = J * chol_lower(J H_p J)^-1 * J,
+// one Cholesky and one triangular inverse, no explicit inverse of H.  The
+// reversal and the act-order permutation are folded into one gather.
+//
+//   finalize   H = (2/N) S in place, diag(H) saved
+//   lambda     lambda = damp * mean(diag H)              (one workgroup, fixed order)
+//   order      perm by rank of -diag(H), ties by index   (stable sort by counting)
+//   gather     Hr[a][b] = H[p(a)][p(b)] + lambda d_ab, p(a) = perm[n-1-a], lower part
+//   panels     right-looking blocked Cholesky of Hr, 64-column panels:
+//                panel kernel: factor the 64x64 diagonal block (one wave, rows in
+//                registers), then solve the panel rows below against it;
+//                trailing update Hr[k+64:, k+64:] -= P P^T on MFMA (lower tiles)
+//   diag inv   invert every 64x64 diagonal block of the factor in place
+//   trtri      recursive doubling: for neighbouring inverted blocks A^-1, C^-1
+//              and the factor block L21 below A, M21 = -C^-1 (L21 A^-1)
+//   reverse    U[i][j] = M[n-1-i][n-1-j] for j >= i, 0 below the diagonal
+#include "gptq_common.h"
+#include "gptq_internal.h"
+
+#include <algorithm>
+
+namespace gptq {
+namespace {
+
+constexpr int kNB = kPanel;  // 64
+
+__global__ void finalize_kernel(float* S, int64_t n, float scale, float* diag) {
+  const int64_t total = n * n;
+  for (int64_t e = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; e < total;
+       e += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    const float v = S[e] * scale;
+    S[e] = v;
+    const int64_t r = e / n;
+    if (r * n + r == e) diag[r] = v;
+  }
+}
+
+// lambda = damp * mean(diag): fixed-order tree over 1024 threads.
+__global__ __launch_bounds__(1024) void lambda_kernel(const float* diag, int64_t n, float damp,
+                                                      float* lambda_out, int32_t* info) {
+  __shared__ double part[1024];
+  double s = 0.0;
+  for (int64_t i = threadIdx.x; i < n; i += 1024) s += static_cast<double>(diag[i]);
+  part[threadIdx.x] = s;
+  __syncthreads();
+  for (int w = 512; w > 0; w >>= 1) {
+    if (threadIdx.x < w) part[threadIdx.x] += part[threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    lambda_out[0] = damp * static_cast<float>(part[0] / static_cast<double>(n));
+    info[0] = 0;
+  }
+}
+
+// perm[rank(i)] = i with rank(i) = #{j : d_j > d_i} + #{j < i : d_j == d_i}.
+__global__ __launch_bounds__(256) void order_kernel(const float* diag, int64_t n, int desc_act,
+                                                    int32_t* perm) {
+  __shared__ float tile[1024];
+  const int64_t i = blockIdx.x * 256 + threadIdx.x;
+  if (!desc_act) {
+    if (i < n) perm[i] = static_cast<int32_t>(i);
+    return;
+  }
+  const float di = (i < n) ? diag[i] : 0.f;
+  int64_t rank = 0;
+  for (int64_t base = 0; base < n; base += 1024) {
+    __syncthreads();
+    for (int t = threadIdx.x; t < 1024; t += 256) tile[t] = (base + t < n) ? diag[base + t] : 0.f;
+    __syncthreads();
+    const int lim = static_cast<int>(std::min<int64_t>(1024, n - base));
+    for (int t = 0; t < lim; ++t) {
+      const float dj = tile[t];
+      rank += (dj > di) || (dj == di && base + t < i);
+    }
+  }
+  if (i < n) perm[rank] = static_cast<int32_t>(i);
+}
+
+// Hr[a][b] = H[p(a)][p(b)] (+ lambda on the diagonal) for b <= a, 0 above.
+__global__ void gather_kernel(const float* H, int64_t n, const int32_t* perm, const float* lambda,
+                              float* Hr) {
+  const float lam = lambda[0];
+  const int64_t total = n * n;
+  for (int64_t e = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; e < total;
+       e += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    const int64_t a = e / n, b = e - a * n;
+    float v = 0.f;
+    if (b <= a) {
+      const int64_t pa = perm[n - 1 - a], pb = perm[n - 1 - b];
+      v = H[pa * n + pb];
+      if (a == b) v += lam;
+    }
+    Hr[e] = v;
+  }
+}
+
+// Lower Cholesky of the 64x64 block held in L (LDS, pitch 65), by wave 0:
+// lane r keeps row r in registers; column j is published through LDS.
+// Returns through `fail` the first failing local pivot (or -1).
+GPTQ_DEV void factor_block_wave(float (*L)[68], float* col, int lane, int& fail) {
+  float v[kNB];
+#pragma unroll
+  for (int c = 0; c < kNB; ++c) v[c] = L[lane][c];
+  fail = -1;
+#pragma unroll
+  for (int j = 0; j < kNB; ++j) {
+    const float piv = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v[j]), j));
+    if (!(piv > 0.f) && fail < 0) fail = j;
+    const float d = sqrtf(piv);
+    const float inv = 1.0f / d;
+    v[j] = (lane == j) ? d : ((lane > j) ? v[j] * inv : v[j]);
+    col[lane] = v[j];
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int c = j + 1; c < kNB; ++c) v[c] = fmaf(-v[j], col[c], v[c]);
+    __builtin_amdgcn_wave_barrier();
+  }
+#pragma unroll
+  for (int c = 0; c < kNB; ++c) L[lane][c] = (c <= lane) ? v[c] : 0.f;
+}
+
+// One launch per panel k: every workgroup factors the diagonal block (the same
+// arithmetic, so the same result), workgroup 0 stores it, and each thread
+// solves one panel row x against it: x L^T = p (forward substitution).
+__global__ __launch_bounds__(256) void panel_kernel(float* Hr, int64_t n, int64_t k, int32_t* info) {
+  __shared__ __attribute__((aligned(16))) float L[kNB][68];
+  __shared__ float col[kNB];
+  __shared__ float dinv[kNB];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nb = static_cast<int>(std::min<int64_t>(kNB, n - k));
+  for (int e = tid; e < kNB * kNB; e += 256) {
+    const int r = e >> 6, c = e & 63;
+    float v = (r == c) ? 1.f : 0.f;
+    if (r < nb && c <= r) v = Hr[(k + r) * n + k + c];
+    L[r][c] = v;
+  }
+  __syncthreads();
+  if (wave == 0) {
+    int fail;
+    factor_block_wave(L, col, lane, fail);
+    if (lane == 0 && blockIdx.x == 0 && fail >= 0 && fail < nb)
+      atomicCAS(info, 0, static_cast<int32_t>(n - (k + fail)));
+  }
+  __syncthreads();
+  if (tid < kNB) dinv[tid] = 1.0f / L[tid][tid];
+  if (blockIdx.x == 0) {
+    for (int e = tid; e < nb * nb; e += 256) {
+      const int r = e / nb, c = e - r * nb;
+      Hr[(k + r) * n + k + c] = L[r][c];
+    }
+  }
+  __syncthreads();
+  const int64_t row = k + kNB + static_cast<int64_t>(blockIdx.x) * 256 + tid;
+  if (nb < kNB || row >= n) return;
+  float x[kNB];
+  const float* src = Hr + row * n + k;
+#pragma unroll
+  for (int q = 0; q < kNB / 4; ++q) {
+    const f32x4_t t = *reinterpret_cast<const f32x4_t*>(src + 4 * q);
+    x[4 * q] = t[0];
+    x[4 * q + 1] = t[1];
+    x[4 * q + 2] = t[2];
+    x[4 * q + 3] = t[3];
+  }
+#pragma unroll
+  for (int c = 0; c < kNB; ++c) {
+    float s = x[c];
+#pragma unroll
+    for (int t = 0; t < c; ++t) s = fmaf(-x[t], L[c][t], s);
+    x[c] = s * dinv[c];
+  }
+  float* dst = Hr + row * n + k;
+#pragma unroll
+  for (int q = 0; q < kNB / 4; ++q)
+    *reinterpret_cast<f32x4_t*>(dst + 4 * q) = f32x4_t{x[4 * q], x[4 * q + 1], x[4 * q + 2], x[4 * q + 3]};
+}
+
+// Invert every 64x64 diagonal block of the lower factor in place.  Wave 0,
+// lane c computes column c of the inverse by forward substitution.
+__global__ __launch_bounds__(256) void diag_inverse_kernel(float* Hr, int64_t n) {
+  __shared__ __attribute__((aligned(16))) float L[kNB][68];
+  const int64_t k = static_cast<int64_t>(blockIdx.x) * kNB;
+  const int nb = static_cast<int>(std::min<int64_t>(kNB, n - k));
+  const int tid = threadIdx.x, lane = tid & 63;
+  for (int e = tid; e < kNB * kNB; e += 256) {
+    const int r = e >> 6, c = e & 63;
+    float v = (r == c) ? 1.f : 0.f;
+    if (r < nb && c <= r) v = Hr[(k + r) * n + k + c];
+    L[r][c] = v;
+  }
+  __syncthreads();
+  if (tid >= 64) return;
+  float m[kNB];
+#pragma unroll
+  for (int i = 0; i < kNB; ++i) {
+    float s = (i == lane) ? 1.f : 0.f;
+#pragma unroll
+    for (int t = 0; t < i; ++t) s = fmaf(-L[i][t], m[t], s);
+    m[i] = (i >= lane) ? s / L[i][i] : 0.f;
+  }
+  for (int i = 0; i < nb; ++i)
+    if (lane < nb) Hr[(k + i) * n + k + lane] = m[i];
+}
+
+__global__ void reverse_kernel(const float* M, int64_t n, float* U) {
+  const int64_t total = n * n;
+  for (int64_t e = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; e < total;
+       e += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    const int64_t i = e / n, j = e - i * n;
+    U[e] = (j >= i) ? M[(n - 1 - i) * n + (n - 1 - j)] : 0.f;
+  }
+}
+
+int grid_for(int64_t total) {
+  return static_cast<int>(std::max<int64_t>(1, std::min<int64_t>((total + 255) / 256, 8192)));
+}
+
+}  // namespace
+
+PrepLayout prepare_layout(int64_t d) {
+  auto up = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
+  PrepLayout L{};
+  size_t off = 0;
+  L.off_hr = off;
+  off += up(static_cast<size_t>(d) * d * sizeof(float));
+  L.off_t = off;  // trtri scratch: at most d*d/4 floats
+  off += up(static_cast<size_t>(d) * d / 4 * sizeof(float) + 64 * 64 * sizeof(float));
+  L.off_diag = off;
+  off += up(static_cast<size_t>(d) * sizeof(float));
+  L.off_lambda = off;
+  off += 256;
+  L.ws_bytes = off;
+  return L;
+}
+
+#define GPTQ_TRY(x)                          \
+  do {                                       \
+    hipError_t e_ = (x);                     \
+    if (e_ != hipSuccess) return e_;         \
+  } while (0)
+
+hipError_t prepare_launch(float* S, int64_t n, int64_t n_total, float damp, bool desc_act, float* U,
+                          int32_t* perm, int32_t* info, void* ws, hipStream_t st) {
+  const PrepLayout lay = prepare_layout(n);
+  char* w = static_cast<char*>(ws);
+  float* Hr = reinterpret_cast<float*>(w + lay.off_hr);
+  float* T = reinterpret_cast<float*>(w + lay.off_t);
+  float* diag = reinterpret_cast<float*>(w + lay.off_diag);
+  float* lam = reinterpret_cast<float*>(w + lay.off_lambda);
+  const int64_t nn = n * n;
+
+  finalize_kernel<<<grid_for(nn), 256, 0, st>>>(S, n, static_cast<float>(2.0 / static_cast<double>(n_total)), diag);
+  GPTQ_TRY(hipGetLastError());
+  lambda_kernel<<<1, 1024, 0, st>>>(diag, n, damp, lam, info);
+  GPTQ_TRY(hipGetLastError());
+  order_kernel<<<static_cast<int>((n + 255) / 256), 256, 0, st>>>(diag, n, desc_act ? 1 : 0, perm);
+  GPTQ_TRY(hipGetLastError());
+  gather_kernel<<<grid_for(nn), 256, 0, st>>>(S, n, perm, lam, Hr);
+  GPTQ_TRY(hipGetLastError());
+
+  // blocked right-looking Cholesky of Hr
+  for (int64_t k = 0; k < n; k += kNB) {
+    const int64_t below = std::max<int64_t>(0, n - k - kNB);
+    const int blocks = static_cast<int>(std::max<int64_t>(1, (below + 255) / 256));
+    panel_kernel<<<blocks, 256, 0, st>>>(Hr, n, k, info);
+    GPTQ_TRY(hipGetLastError());
+    if (below > 0) {
+      const float* P = Hr + (k + kNB) * n + k;
+      GPTQ_TRY(gemm_f32(below, below, kNB, -1.f, P, n, 0, P, n, 0, true, 1.f, Hr + (k + kNB) * (n + 1), n,
+                        0, 1, true, false, st));
+    }
+  }
+  // triangular inverse: diagonal blocks, then recursive doubling
+  const int64_t nblk = (n + kNB - 1) / kNB;
+  diag_inverse_kernel<<<static_cast<int>(nblk), 256, 0, st>>>(Hr, n);
+  GPTQ_TRY(hipGetLastError());
+  for (int64_t h = 1; h < nblk; h *= 2) {
+    const int64_t w_el = h * kNB;           // width of A (elements)
+    const int64_t groups_full = n / (2 * w_el);
+    // full groups: A and C both h blocks wide
+    if (groups_full > 0) {
+      const int64_t gs = 2 * w_el * (n + 1);  // stride between groups in Hr
+      const float* L21 = Hr + w_el * n;        // rows [w_el, 2 w_el), cols [0, w_el)
+      const float* Ainv = Hr;
+      const float* Cinv = Hr + w_el * (n + 1);
+      GPTQ_TRY(gemm_f32(w_el, w_el, w_el, 1.f, L21, n, gs, Ainv, n, gs, false, 0.f, T, w_el, w_el * w_el,
+                        static_cast<int>(groups_full), false, false, st));
+      GPTQ_TRY(gemm_f32(w_el, w_el, w_el, -1.f, Cinv, n, gs, T, w_el, w_el * w_el, false, 0.f,
+                        Hr + w_el * n, n, gs, static_cast<int>(groups_full), false, false, st));
+    }
+    // ragged last group: A is h blocks wide, C is what remains (< h blocks)
+    const int64_t a0 = groups_full * 2 * w_el;
+    const int64_t c0 = a0 + w_el;
+    if (c0 < n) {
+      const int64_t cw = n - c0;
+      const float* L21 = Hr + c0 * n + a0;
+      const float* Ainv = Hr + a0 * (n + 1);
+      const float* Cinv = Hr + c0 * (n + 1);
+      GPTQ_TRY(gemm_f32(cw, w_el, w_el, 1.f, L21, n, 0, Ainv, n, 0, false, 0.f, T, w_el, 0, 1, false, false, st));
+      GPTQ_TRY(gemm_f32(cw, w_el, cw, -1.f, Cinv, n, 0, T, w_el, 0, false, 0.f, Hr + c0 * n + a0, n, 0, 1, false,
+                        false, st));
+    }
+  }
+  reverse_kernel<<<grid_for(nn), 256, 0, st>>>(Hr, n, U);
+  return hipGetLastError();
+}
+
+}  // namespace gptq

@@ -1,0 +1,392 @@
+// The GPTQ column sweep over lazy 128-column blocks.
+//
+// GPTQ 实战 ch.5, section 5.1.8 (the implementation-level pseudocode and the
+// OBS closed form): each column is rounded to its group's grid, its error is
+// normalised by the factor's diagonal U[i][i] and subtracted, scaled by row i
+// of U, from the not-yet-quantized columns of the block; after the block one
+// matrix product applies the block's errors to every later column.  Groups
+// (skill card, 分组量化; ch.5 section 5.1.10) carry one scale and zero point
+// per output row; sym / static_groups follow BaseQuantizeConfig (AutoGPTQ
+// examples walkthrough, section 1.4).
+//
+// Rows are independent given U, so the sweep is parallel over output rows and
+// sequential over the block's 128 columns.  Layout: 16 lanes (one DPP row) per
+// output row, lane t owning block columns 8t .. 8t+7 in registers.  At step i
+// every lane quantizes its own copy of register i%8, the owner lane's error is
+// broadcast to its row with DPP row_newbcast, and every lane applies the
+// rank-1 update to its 8 columns with U[i][8t .. 8t+7] read from LDS (zeros
+// left of the diagonal make the update uniform).  Group ranges reduce over the
+// 16-lane row with DPP mirrors.
+#include "gptq_common.h"
+#include "gptq_internal.h"
+
+#include <algorithm>
+
+namespace gptq {
+namespace {
+
+constexpr int kB = 128;         // lazy-batch width
+constexpr int kRowsPerWG = 16;  // 256 threads / 16 lanes
+
+struct SweepParams {
+  float* Wp;            // [d_out, d_in] fp32 working copy, sweep order
+  const float* U;       // [d_in, d_in]
+  const int32_t* perm;  // sweep position -> original column
+  uint8_t* codes;       // [d_out, d_in] original order
+  float* Q;             // optional [d_out, d_in] original order
+  float* scales;        // [n_groups, d_out]
+  int32_t* zeros;       // [n_groups, d_out]
+  float* row_loss;      // optional [d_out]
+  float* Err;           // [d_out, 128]
+  int64_t d_out, d_in;
+  int64_t j0;           // first sweep column of the block
+  int ncols;            // columns in this block
+  int bits;
+  float maxq;
+  int group;            // group size, or 0 for one group per row
+  int sym;
+  int preset;           // 1: scales/zeros of every column are already in the outputs
+  int identity;         // perm is the identity
+};
+
+GPTQ_DEV void group_params(float lo, float hi, const SweepParams& p, float& scale, float& zero) {
+  lo = fminf(lo, 0.f);
+  hi = fmaxf(hi, 0.f);
+  if (p.sym) {
+    const float a = fmaxf(-lo, hi);
+    lo = -a;
+    hi = a;
+  }
+  if (hi == lo) {
+    lo = -1.f;
+    hi = 1.f;
+  }
+  scale = (hi - lo) / p.maxq;
+  zero = p.sym ? static_cast<float>(1 << (p.bits - 1)) : rintf(-lo / scale);
+}
+
+template <int I>
+GPTQ_DEV void sweep_step(const SweepParams& p, const float (*Ub)[kB], const float* dinv, int t,
+                         float (&v)[8], float (&sc)[8], float (&zr)[8], float (&qc)[8], float (&qv)[8],
+                         float (&er)[8], float& loss, int64_t row) {
+  constexpr int r = I & 7, owner = I >> 3;
+  // this step's row of U is issued first; its latency hides behind the rounding
+  const f32x4_t u0 = *reinterpret_cast<const f32x4_t*>(&Ub[I][8 * t]);
+  const f32x4_t u1 = *reinterpret_cast<const f32x4_t*>(&Ub[I][8 * t + 4]);
+  // dynamic groups that start inside the block: range over the group's current values
+  if (!p.preset && p.group > 0 && p.group <= kB && (I % p.group) == 0 && I < p.ncols) {
+    float lo = 0.f, hi = 0.f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int c = 8 * t + k;
+      const bool in = (c >= I) && (c < I + p.group) && (c < p.ncols);
+      lo = in ? fminf(lo, v[k]) : lo;
+      hi = in ? fmaxf(hi, v[k]) : hi;
+    }
+    lo = row_min16(lo);
+    hi = row_max16(hi);
+    float s, z;
+    group_params(lo, hi, p, s, z);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int c = 8 * t + k;
+      const bool in = (c >= I) && (c < I + p.group);
+      sc[k] = in ? s : sc[k];
+      zr[k] = in ? z : zr[k];
+    }
+    if (t == owner && row < p.d_out) {
+      const int64_t g = (p.j0 + I) / p.group;
+      p.scales[g * p.d_out + row] = s;
+      p.zeros[g * p.d_out + row] = static_cast<int32_t>(z);
+    }
+  }
+  const float w = v[r];
+  const float s = sc[r], z = zr[r];
+  const float q = fminf(fmaxf(rintf(w / s) + z, 0.f), p.maxq);
+  const float what = s * (q - z);
+  const float err = (w - what) * dinv[I];
+  const float eb = row_bcast<owner>(err);
+  qc[r] = (t == owner) ? q : qc[r];
+  qv[r] = (t == owner) ? what : qv[r];
+  er[r] = (t == owner) ? eb : er[r];
+  // materialise the selects here: left alone, the compiler sinks them to the
+  // end of the block and keeps every step's code alive until then
+  asm volatile("" : "+v"(qc[r]), "+v"(qv[r]), "+v"(er[r]));
+  loss = fmaf(eb, eb, loss);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    v[k] = fmaf(-eb, u0[k], v[k]);
+    v[k + 4] = fmaf(-eb, u1[k], v[k + 4]);
+  }
+  // keep each step a scheduling region of its own (bounded register pressure)
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+template <int... Is>
+GPTQ_DEV void sweep_all(const SweepParams& p, const float (*Ub)[kB], const float* dinv, int t, float (&v)[8],
+                        float (&sc)[8], float (&zr)[8], float (&qc)[8], float (&qv)[8], float (&er)[8],
+                        float& loss, int64_t row, std::integer_sequence<int, Is...>) {
+  (sweep_step<Is>(p, Ub, dinv, t, v, sc, zr, qc, qv, er, loss, row), ...);
+}
+
+__global__ __launch_bounds__(256) void sweep_kernel(SweepParams p) {
+  __shared__ __attribute__((aligned(16))) float Ub[kB][kB];
+  __shared__ float dinv[kB];
+  const int tid = threadIdx.x;
+  const int t = tid & 15;
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * kRowsPerWG + (tid >> 4);
+  const bool row_ok = row < p.d_out;
+
+  // diagonal block of U (zeros outside the block's columns)
+  for (int e = tid; e < kB * kB / 4; e += 256) {
+    const int i = e / (kB / 4), c4 = 4 * (e % (kB / 4));
+    f32x4_t u = {0.f, 0.f, 0.f, 0.f};
+    if (i < p.ncols && c4 < p.ncols)
+      u = *reinterpret_cast<const f32x4_t*>(p.U + (p.j0 + i) * p.d_in + p.j0 + c4);
+    *reinterpret_cast<f32x4_t*>(&Ub[i][c4]) = u;
+  }
+  __syncthreads();
+  if (tid < kB) dinv[tid] = (tid < p.ncols) ? 1.0f / Ub[tid][tid] : 0.f;
+
+  float v[8], sc[8], zr[8], qc[8], qv[8], er[8];
+  const int c0 = 8 * t;
+  {
+    const float* src = p.Wp + row * p.d_in + p.j0 + c0;
+    f32x4_t a = {0.f, 0.f, 0.f, 0.f}, b = {0.f, 0.f, 0.f, 0.f};
+    if (row_ok && c0 < p.ncols) a = *reinterpret_cast<const f32x4_t*>(src);
+    if (row_ok && c0 + 4 < p.ncols) b = *reinterpret_cast<const f32x4_t*>(src + 4);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      v[k] = a[k];
+      v[k + 4] = b[k];
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    sc[k] = 1.f;
+    zr[k] = 0.f;
+    qc[k] = 0.f;
+    qv[k] = 0.f;
+    er[k] = 0.f;
+  }
+  // parameters fixed before this block: static groups, one group per row, or a
+  // dynamic group wider than the block that started in an earlier block
+  const bool wide_group_running = !p.preset && p.group > kB && (p.j0 % p.group) != 0;
+  if ((p.preset || wide_group_running) && row_ok) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int64_t j = p.j0 + c0 + k;
+      if (c0 + k < p.ncols) {
+        int64_t g = 0;
+        if (p.group > 0) g = (p.preset && !p.identity) ? p.perm[j] / p.group : j / p.group;
+        sc[k] = p.scales[g * p.d_out + row];
+        zr[k] = static_cast<float>(p.zeros[g * p.d_out + row]);
+      }
+    }
+  }
+  // a dynamic group wider than the block starts here: range over W[row, j0 : j0+group)
+  if (!p.preset && p.group > kB && (p.j0 % p.group) == 0) {
+    float lo = 0.f, hi = 0.f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      lo = fminf(lo, v[k]);
+      hi = fmaxf(hi, v[k]);
+    }
+    if (row_ok) {
+      const int64_t end = std::min<int64_t>(p.j0 + p.group, p.d_in);
+      for (int64_t c = p.j0 + kB + t; c < end; c += 16) {
+        const float x = p.Wp[row * p.d_in + c];
+        lo = fminf(lo, x);
+        hi = fmaxf(hi, x);
+      }
+    }
+    lo = row_min16(lo);
+    hi = row_max16(hi);
+    float s, z;
+    group_params(lo, hi, p, s, z);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      sc[k] = s;
+      zr[k] = z;
+    }
+    if (t == 0 && row_ok) {
+      const int64_t g = p.j0 / p.group;
+      p.scales[g * p.d_out + row] = s;
+      p.zeros[g * p.d_out + row] = static_cast<int32_t>(z);
+    }
+  }
+  __syncthreads();
+
+  float loss = 0.f;
+  sweep_all(p, Ub, dinv, t, v, sc, zr, qc, qv, er, loss, row, std::make_integer_sequence<int, kB>{});
+
+  if (!row_ok) return;
+  // normalised errors of the block, for the trailing update
+  float* e = p.Err + row * kB + c0;
+  *reinterpret_cast<f32x4_t*>(e) = f32x4_t{er[0], er[1], er[2], er[3]};
+  *reinterpret_cast<f32x4_t*>(e + 4) = f32x4_t{er[4], er[5], er[6], er[7]};
+  // codes and dequantized weights, written in original column order
+  if (p.identity && c0 + 8 <= p.ncols) {
+    const int64_t base = row * p.d_in + p.j0 + c0;
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      lo |= static_cast<uint32_t>(qc[k]) << (8 * k);
+      hi |= static_cast<uint32_t>(qc[k + 4]) << (8 * k);
+    }
+    *reinterpret_cast<uint2*>(p.codes + base) = make_uint2(lo, hi);
+    if (p.Q) {
+      *reinterpret_cast<f32x4_t*>(p.Q + base) = f32x4_t{qv[0], qv[1], qv[2], qv[3]};
+      *reinterpret_cast<f32x4_t*>(p.Q + base + 4) = f32x4_t{qv[4], qv[5], qv[6], qv[7]};
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      if (c0 + k < p.ncols) {
+        const int64_t j = p.j0 + c0 + k;
+        const int64_t oc = p.identity ? j : p.perm[j];
+        p.codes[row * p.d_in + oc] = static_cast<uint8_t>(qc[k]);
+        if (p.Q) p.Q[row * p.d_in + oc] = qv[k];
+      }
+    }
+  }
+  if (p.row_loss && t == 0) p.row_loss[row] = (p.j0 == 0 ? 0.f : p.row_loss[row]) + loss;
+}
+
+// Wp[r][i] = W[r][perm[i]] in fp32.
+__global__ void gather_w_kernel(const void* W, int w_bf16, int64_t d_out, int64_t d_in, const int32_t* perm,
+                                int identity, float* Wp) {
+  const int64_t total = d_out * d_in;
+  for (int64_t e = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; e < total;
+       e += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    const int64_t r = e / d_in, i = e - r * d_in;
+    const int64_t c = identity ? i : perm[i];
+    const int64_t src = r * d_in + c;
+    Wp[e] = w_bf16 ? bf16_to_f32(static_cast<const uint16_t*>(W)[src]) : static_cast<const float*>(W)[src];
+  }
+}
+
+// Group parameters from the original weights: static groups (original column
+// groups) or one group per row.  One wave per (group, row).
+__global__ __launch_bounds__(256) void static_params_kernel(const void* W, int w_bf16, int64_t d_out,
+                                                            int64_t d_in, int group, int n_groups, int bits,
+                                                            int sym, float* scales, int32_t* zeros) {
+  const int lane = threadIdx.x & 63;
+  const int64_t wave = (blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x) >> 6;
+  const int64_t nwaves = (static_cast<int64_t>(gridDim.x) * blockDim.x) >> 6;
+  const int64_t pairs = static_cast<int64_t>(n_groups) * d_out;
+  for (int64_t pr = wave; pr < pairs; pr += nwaves) {
+    const int64_t g = pr / d_out, row = pr - g * d_out;
+    const int64_t c_begin = (group > 0) ? g * group : 0;
+    const int64_t c_end = (group > 0) ? std::min<int64_t>(d_in, c_begin + group) : d_in;
+    float lo = 0.f, hi = 0.f;
+    for (int64_t c = c_begin + lane; c < c_end; c += 64) {
+      const int64_t src = row * d_in + c;
+      const float x = w_bf16 ? bf16_to_f32(static_cast<const uint16_t*>(W)[src]) : static_cast<const float*>(W)[src];
+      lo = fminf(lo, x);
+      hi = fmaxf(hi, x);
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      lo = fminf(lo, __shfl_xor(lo, off));
+      hi = fmaxf(hi, __shfl_xor(hi, off));
+    }
+    if (lane == 0) {
+      SweepParams p{};
+      p.sym = sym;
+      p.bits = bits;
+      p.maxq = static_cast<float>((1 << bits) - 1);
+      float s, z;
+      group_params(lo, hi, p, s, z);
+      scales[g * d_out + row] = s;
+      zeros[g * d_out + row] = static_cast<int32_t>(z);
+    }
+  }
+}
+
+__global__ void g_idx_kernel(int64_t d_in, int group, int by_position, const int32_t* perm, int32_t* g_idx) {
+  for (int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; i < d_in;
+       i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    if (group <= 0)
+      g_idx[i] = 0;
+    else if (by_position)
+      g_idx[perm[i]] = static_cast<int32_t>(i / group);  // dynamic groups follow the sweep order
+    else
+      g_idx[i] = static_cast<int32_t>(i / group);
+  }
+}
+
+int grid_for(int64_t total) {
+  return static_cast<int>(std::max<int64_t>(1, std::min<int64_t>((total + 255) / 256, 8192)));
+}
+
+}  // namespace
+
+QuantLayout quant_layout(int64_t d_out, int64_t d_in) {
+  auto up = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
+  QuantLayout L{};
+  L.off_wp = 0;
+  L.off_err = up(static_cast<size_t>(d_out) * d_in * sizeof(float));
+  L.ws_bytes = L.off_err + up(static_cast<size_t>(d_out) * kB * sizeof(float));
+  return L;
+}
+
+hipError_t quantize_launch(const void* W, bool w_bf16, int64_t d_out, int64_t d_in, const float* U,
+                           const int32_t* perm, int bits, int group_size, bool sym, bool static_groups,
+                           uint8_t* codes, float* scales, int32_t* zeros, int32_t* g_idx, float* Q,
+                           float* row_loss, void* ws, hipStream_t st, bool identity) {
+  const QuantLayout lay = quant_layout(d_out, d_in);
+  float* Wp = reinterpret_cast<float*>(static_cast<char*>(ws) + lay.off_wp);
+  float* Err = reinterpret_cast<float*>(static_cast<char*>(ws) + lay.off_err);
+  const int group = group_size > 0 ? group_size : 0;
+  const int n_groups = group > 0 ? static_cast<int>((d_in + group - 1) / group) : 1;
+  const bool preset = static_groups || group == 0;
+
+  gather_w_kernel<<<grid_for(d_out * d_in), 256, 0, st>>>(W, w_bf16 ? 1 : 0, d_out, d_in, perm, identity ? 1 : 0, Wp);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (preset) {
+    const int64_t pairs = static_cast<int64_t>(n_groups) * d_out;
+    const int blocks = static_cast<int>(std::max<int64_t>(1, std::min<int64_t>((pairs + 3) / 4, 16384)));
+    static_params_kernel<<<blocks, 256, 0, st>>>(W, w_bf16 ? 1 : 0, d_out, d_in, group, n_groups, bits, sym ? 1 : 0,
+                                                 scales, zeros);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  g_idx_kernel<<<grid_for(d_in), 256, 0, st>>>(d_in, group, (!preset && !identity) ? 1 : 0, perm, g_idx);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+
+  SweepParams p{};
+  p.Wp = Wp;
+  p.U = U;
+  p.perm = perm;
+  p.codes = codes;
+  p.Q = Q;
+  p.scales = scales;
+  p.zeros = zeros;
+  p.row_loss = row_loss;
+  p.Err = Err;
+  p.d_out = d_out;
+  p.d_in = d_in;
+  p.bits = bits;
+  p.maxq = static_cast<float>((1 << bits) - 1);
+  p.group = group;
+  p.sym = sym ? 1 : 0;
+  p.preset = preset ? 1 : 0;
+  p.identity = identity ? 1 : 0;
+  const int blocks = static_cast<int>((d_out + kRowsPerWG - 1) / kRowsPerWG);
+  for (int64_t j0 = 0; j0 < d_in; j0 += kB) {
+    p.j0 = j0;
+    p.ncols = static_cast<int>(std::min<int64_t>(kB, d_in - j0));
+    sweep_kernel<<<blocks, 256, 0, st>>>(p);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const int64_t rest = d_in - j0 - kB;
+    if (rest > 0) {
+      e = gemm_f32(d_out, rest, kB, -1.f, Err, kB, 0, U + j0 * d_in + j0 + kB, d_in, 0, false, 1.f,
+                   Wp + j0 + kB, d_in, 0, 1, false, false, st);
+      if (e != hipSuccess) return e;
+    }
+  }
+  return hipSuccess;
+}
+
+}  // namespace gptq
