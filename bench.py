@@ -1,0 +1,258 @@
+#!/usr/bin/env python3
+"""Benchmark of the GPTQ per-layer solve on one MI355X.
+
+One step = one whole layer solve of the Llama-2-7B-shaped q_proj layer:
+W 4096 x 4096 bf16, N = 262144 calibration tokens (128 x 2048) of bf16
+activations, 4-bit, group 128, symmetric, no act-order, damp 0.01:
+
+    S = 0; S += X^T X (all N tokens, one call); H, damping, U; column sweep
+    over 32 lazy blocks; pack.
+
+Inputs are synthetic (seeded generators with the layer's distributions) and
+resident in HBM before timing starts.  Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "GPTQ layer-solve ms & weight cols/s (4096×4096, N=262144); MFMA % peak"
+PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "hessian_bf16_4096x4096_N262144_counters.md")
+HESSIAN_SRC = os.path.join(ROOT, "post_weight_quantization_07_amd", "csrc", "hessian.hip")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calib-mib", type=int, default=0,
+                    help="launch one device copy of this many MiB first (HBM counter calibration)")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=16384)
+    ap.add_argument("--cpu-sample-rows", type=int, default=128)
+    return ap.parse_args()
+
+
+def source_hash() -> str:
+    with open(HESSIAN_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def recorded_traffic():
+    """HBM bytes per launch of the Hessian kernel from the committed counter
+    summary, or None when it is missing or was taken on other kernel source."""
+    if not os.path.exists(COUNTERS_FILE):
+        return None
+    txt = open(COUNTERS_FILE).read()
+    m = re.search(r"traffic_json:\s*(\{.*\})", txt)
+    if not m:
+        return None
+    rec = json.loads(m.group(1))
+    if rec.get("source_sha256") != source_hash():
+        return None
+    return rec
+
+
+def cpu_baseline(layer, W_host, args):
+    """The oracle, untuned, on a bounded sample of the same workload."""
+    import numpy as np
+
+    import oracle as O
+    import synth
+    try:
+        from threadpoolctl import threadpool_info
+        blas = [(i.get("internal_api"), i.get("num_threads")) for i in threadpool_info() if i.get("user_api") == "blas"]
+    except Exception:  # pragma: no cover
+        blas = []
+    threads = max([t for _, t in blas if t] or [os.cpu_count() or 1])
+    n_s = min(args.cpu_sample_tokens, layer.n_tokens)
+    rows = min(args.cpu_sample_rows, layer.d_out)
+    sig = synth.channel_sigma(layer)
+    chunks = [synth.activation_chunk(layer, c, sig) for c in range((n_s + synth.CHUNK_TOKENS - 1) // synth.CHUNK_TOKENS)]
+    t0 = time.perf_counter()
+    S, n = O.hessian_sum(chunks)
+    t_h = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    H = O.finalize_hessian(S, n)
+    prep = O.prepare(H, layer.damp_percent, layer.desc_act)
+    t_p = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    sw = O.quantize_layer(W_host, prep.U, prep.perm, layer.bits, layer.group_size, layer.sym, layer.static_groups,
+                          rows=np.arange(rows))
+    t_q = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    O.pack(sw.codes, layer.bits)
+    t_k = time.perf_counter() - t0
+    total = t_h * (layer.n_tokens / n) + t_p + (t_q + t_k) * (layer.d_out / rows)
+    return {
+        "value": layer.d_in / total,
+        "unit": "weight cols/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": (f"X^T X on {n} of {layer.n_tokens} tokens (scaled x{layer.n_tokens / n:g}); full {layer.d_in}x"
+                   f"{layer.d_in} damping+order+inverse+Cholesky; sweep and pack on {rows} of {layer.d_out} rows "
+                   f"(scaled x{layer.d_out / rows:g}); numpy fp64, BLAS {blas}"),
+        "est_total_s": total,
+        "measured_s": t_h + t_p + t_q + t_k,
+        "stages_s": {"hessian": t_h, "prepare": t_p, "quantize": t_q, "pack": t_k},
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the layer solve is measured on a single "
+              "MI355X; multi-GPU sharding is described, not run.", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import post_weight_quantization_07_amd as G
+    import synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    layer = synth.config_layers(3)[0]
+    d_out, d_in, N = layer.d_out, layer.d_in, layer.n_tokens
+    cfg = G.QuantizeConfig(**layer.quant_kwargs())
+    t_setup = time.perf_counter()
+
+    # ---- inputs resident in HBM -------------------------------------------
+    W_host = synth.weight(layer)
+    W = torch.from_numpy(synth.bf16_bits(W_host).view(np.int16)).to(dev).view(torch.bfloat16)
+    X = torch.empty((N, d_in), dtype=torch.bfloat16, device=dev)
+    row = 0
+    for bits in synth.activation_chunks_threaded(layer, workers=min(16, os.cpu_count() or 1), as_bf16_bits=True):
+        X[row:row + bits.shape[0]].copy_(torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16))
+        row += bits.shape[0]
+    assert row == N
+
+    # ---- outputs and workspaces (allocated once) --------------------------
+    S = torch.empty((d_in, d_in), dtype=torch.float32, device=dev)
+    U = torch.empty((d_in, d_in), dtype=torch.float32, device=dev)
+    perm = torch.empty(d_in, dtype=torch.int32, device=dev)
+    info = torch.empty(1, dtype=torch.int32, device=dev)
+    ws_h = torch.empty(max(256, G.gptq_hessian_workspace_size(d_in, N, torch.bfloat16)), dtype=torch.uint8, device=dev)
+    ws_p = torch.empty(max(256, G.gptq_prepare_workspace_size(d_in)), dtype=torch.uint8, device=dev)
+    ws_q = torch.empty(max(256, G.gptq_workspace_size(d_out, d_in, cfg)), dtype=torch.uint8, device=dev)
+    ng = cfg.n_groups(d_in)
+    out = {"codes": torch.empty((d_out, d_in), dtype=torch.uint8, device=dev),
+           "scales": torch.empty((ng, d_out), dtype=torch.float32, device=dev),
+           "zeros": torch.empty((ng, d_out), dtype=torch.int32, device=dev),
+           "g_idx": torch.empty(d_in, dtype=torch.int32, device=dev),
+           "row_loss": torch.empty(d_out, dtype=torch.float32, device=dev)}
+    qweight = torch.empty((d_in * cfg.bits // 32, d_out), dtype=torch.int32, device=dev)
+
+    if args.copy_calib_mib > 0:
+        nbytes = args.copy_calib_mib << 20
+        a = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+    stage_ms = {"hessian": [], "prepare": [], "quantize": [], "pack": []}
+
+    def step(record: bool):
+        S.zero_()
+        if record:
+            ev[0].record()
+        G.gptq_hessian_accumulate(S, X, ws=ws_h)
+        if record:
+            ev[1].record()
+        G.gptq_prepare_hinv(S, N, cfg, U=U, perm=perm, info=info, ws=ws_p, check=False)
+        if record:
+            ev[2].record()
+        G.gptq_quantize_layer(W, U, perm, cfg, want_q=False, want_loss=True, out=out, ws=ws_q)
+        if record:
+            ev[3].record()
+        G.gptq_pack(out["codes"], cfg.bits, qweight=qweight)
+        if record:
+            ev[4].record()
+
+    torch.cuda.synchronize()
+    t_setup = time.perf_counter() - t_setup
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    if int(info.item()) != 0:
+        raise RuntimeError(f"prepare reported a failed pivot: info={int(info.item())}")
+
+    # ---- timed region: exactly K steps ------------------------------------
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(False)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+
+    # ---- per-stage launch durations (HIP events on the launch stream) -----
+    for _ in range(args.steps):
+        step(True)
+        torch.cuda.synchronize()
+        stage_ms["hessian"].append(ev[0].elapsed_time(ev[1]))
+        stage_ms["prepare"].append(ev[1].elapsed_time(ev[2]))
+        stage_ms["quantize"].append(ev[2].elapsed_time(ev[3]))
+        stage_ms["pack"].append(ev[3].elapsed_time(ev[4]))
+    st = {k: float(np.mean(v)) for k, v in stage_ms.items()}
+    codes_max = int(out["codes"].max().item())
+    assert 0 <= codes_max <= (1 << cfg.bits) - 1
+
+    f_h = float(N) * d_in * (d_in + 1)                    # algorithmic flops of X^T X (unique entries)
+    f_inv = 2.0 / 3.0 * d_in ** 3
+    f_upd = float(d_out) * d_in * (d_in - 1)
+    achieved = f_h / (st["hessian"] * 1e-3) / 1e12
+    rec = recorded_traffic()
+    roofline = {"kernel": "hessian_bf16_kernel (S += X^T X)", "bound": "mfma", "achieved": achieved,
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
+                "traffic": (rec["bytes_per_launch"] if rec else None),
+                "algorithmic_flops_per_launch": f_h, "launch_ms": st["hessian"]}
+
+    result = {
+        "metric": METRIC,
+        "value": d_in / (ms_per_step * 1e-3),
+        "unit": "weight cols/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "gptq_layer_solve", "layer": "q_proj (Llama-2-7B shape)", "d_out": d_out,
+                   "d_in": d_in, "n_tokens": N, "x_dtype": "bf16", "w_dtype": "bf16", "bits": cfg.bits,
+                   "group_size": cfg.group_size, "sym": cfg.sym, "desc_act": cfg.desc_act,
+                   "static_groups": cfg.static_groups, "damp_percent": cfg.damp_percent, "block_size": 128},
+        "stages_ms": st,
+        "stage_tflops": {"hessian": achieved, "prepare_inverse": f_inv / (st["prepare"] * 1e-3) / 1e12,
+                         "quantize_update": f_upd / (st["quantize"] * 1e-3) / 1e12},
+        "roofline": roofline,
+        "setup_s": t_setup,
+    }
+    if not args.no_cpu_baseline:
+        cb = cpu_baseline(layer, W_host, args)
+        result["cpu_baseline"] = {k: cb[k] for k in ("value", "unit", "cores", "kind", "sample")}
+        result["cpu_baseline"]["est_total_s"] = cb["est_total_s"]
+        result["cpu_baseline"]["measured_s"] = cb["measured_s"]
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -12,13 +12,14 @@
 // adds the result to S and to its mirror tile.  The sum order is fixed, so
 // the result does not depend on scheduling.
 //
-// bf16 path: 256x256 tile, 4 waves of 128x128, v_mfma_f32_16x16x32_bf16.
+// bf16 path: 256x256 tile, 4 waves of 128x128, v_mfma_f32_32x32x16_bf16.
 //   Each thread loads an 8-token x 8-channel block (eight 16-byte loads) and
 //   transposes it in registers with v_perm_b32, so LDS holds every channel's
-//   tokens contiguously: MFMA operands are single ds_read_b128.  LDS rows are
-//   128 bytes (64 tokens); the 16-byte chunk index is XOR-swizzled with the
-//   row index so both the transposing stores and the operand loads are free
-//   of bank conflicts.  Double-buffered: 2 x (32 KB + 32 KB).
+//   tokens contiguously: MFMA operands are single ds_read_b128.  A wave's
+//   load instruction reads two token rows, 512 contiguous bytes each.  LDS
+//   rows are 128 bytes (64 tokens); the 16-byte chunk index is XOR-swizzled
+//   with the row index so both the transposing stores and the operand loads
+//   are free of bank conflicts.  Double-buffered: 2 x (32 KB + 32 KB).
 // fp32 path: 128x128 tile, 4 waves of 64x64, v_mfma_f32_16x16x4_f32, LDS
 //   holds [token][channel] rows padded to 144 floats.
 #include "gptq_common.h"
@@ -28,6 +29,8 @@
 
 namespace gptq {
 namespace {
+
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
 
 constexpr int kThreads = 256;
 
@@ -45,14 +48,57 @@ struct HessParams {
   float* S;
 };
 
-GPTQ_DEV void tile_coords(int t, int nt, int& I, int& J) {
-  int i = 0;
-  while (t >= nt - i) {
-    t -= nt - i;
-    ++i;
+// Tiles of the upper triangle in "super-tile" order: 4x4 blocks of tiles
+// row-major over the block-upper triangle, tiles row-major inside a block.
+// Consecutive tiles then share few row and column blocks of X.
+GPTQ_DEV void tile_coords(int pos, int nt, int& I, int& J) {
+  const int ns = (nt + 3) >> 2;
+  for (int si = 0; si < ns; ++si) {
+    const int ri = min(4, nt - 4 * si);
+    for (int sj = si; sj < ns; ++sj) {
+      const int cj = min(4, nt - 4 * sj);
+      const int cnt = (si == sj) ? ri * (ri + 1) / 2 : ri * cj;
+      if (pos >= cnt) {
+        pos -= cnt;
+        continue;
+      }
+      if (si == sj) {
+        int i = 0;
+        while (pos >= ri - i) {
+          pos -= ri - i;
+          ++i;
+        }
+        I = 4 * si + i;
+        J = 4 * si + i + pos;
+      } else {
+        I = 4 * si + pos / cj;
+        J = 4 * sj + pos % cj;
+      }
+      return;
+    }
   }
-  I = i;
-  J = i + t;
+  I = J = 0;
+}
+
+// Work item of workgroup b.  Workgroups are dispatched round-robin over the
+// 8 XCDs (b % 8), each with its own L2.  The item list (tile groups in
+// super-tile order, every group swept over all token slices, slice-major
+// inside the group) is cut into 8 contiguous pieces, one per XCD, so the ~32
+// workgroups resident on one XCD work on a compact group of tiles and the
+// same token slice, and share X through that XCD's L2.
+GPTQ_DEV void work_item(int b, int n_tiles, int n_split, int& tile_pos, int& split) {
+  constexpr int kXcd = 8;
+  const int B = n_tiles * n_split;
+  const int x = b % kXcd, l = b / kXcd;
+  const int base = B / kXcd, rem = B % kXcd;
+  const int q = x * base + min(x, rem) + l;
+  int g = 0;
+  while (g + 1 < kXcd && q >= n_split * (((g + 1) * n_tiles) / kXcd)) ++g;
+  const int g0 = (g * n_tiles) / kXcd, g1 = ((g + 1) * n_tiles) / kXcd;
+  const int local = q - n_split * g0;
+  const int gsize = g1 - g0;
+  split = local / gsize;
+  tile_pos = g0 + local % gsize;
 }
 
 // ----------------------------------------------------------------------------
@@ -76,34 +122,24 @@ GPTQ_DEV void add_frag_to_S(const HessParams& p, int I, int J, int row0, int col
   }
 }
 
-template <int NI, int NJ, int TILE>
-GPTQ_DEV void finish_tile(const HessParams& p, int t, int split, int I, int J, int rbase, int cbase,
-                          const f32x4_t (&acc)[NI][NJ]) {
+// Split-slice epilogue.  The caller has stored its accumulators to its
+// partial tile in register order (lane-fastest f32x4 fragments).  The
+// accumulators only ever leave through memory stores (which read AGPRs
+// directly): arithmetic on them would make the register allocator keep part
+// of them in VGPRs across the main loop and shuffle them every stage.
+// coord(f, row0, col): tile row of fragment f's first element and its column
+// (the 4 elements are 4 consecutive rows).
+template <int NF, int TILE, typename Coord>
+GPTQ_DEV void finish_tile(const HessParams& p, int t, int I, int J, Coord coord) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int rsub = 4 * (lane >> 4), csub = lane & 15;
-  if (p.n_split == 1) {
-#pragma unroll
-    for (int i = 0; i < NI; ++i)
-#pragma unroll
-      for (int j = 0; j < NJ; ++j)
-        add_frag_to_S<TILE>(p, I, J, rbase + 16 * i + rsub, cbase + 16 * j + csub, acc[i][j]);
-    return;
-  }
-  constexpr int64_t kElems = static_cast<int64_t>(TILE) * TILE;
-  // partials are stored in register order: [wave][i][j][lane][4]
   const int wave = tid >> 6;
-  float* mine = p.partial + (static_cast<int64_t>(t) * p.n_split + split) * kElems;
-#pragma unroll
-  for (int i = 0; i < NI; ++i)
-#pragma unroll
-    for (int j = 0; j < NJ; ++j)
-      *reinterpret_cast<f32x4_t*>(mine + ((((wave * NI + i) * NJ + j) * 64 + lane) << 2)) = acc[i][j];
+  constexpr int64_t kElems = static_cast<int64_t>(TILE) * TILE;
   fence_release();
   __syncthreads();
   __shared__ int s_last;
   if (tid == 0) {
-    const int old = atomicAdd(&p.tickets[t], 1);
+    const int old = (p.n_split == 1) ? 0 : atomicAdd(&p.tickets[t], 1);
     s_last = (old == p.n_split - 1);
   }
   __syncthreads();
@@ -111,13 +147,18 @@ GPTQ_DEV void finish_tile(const HessParams& p, int t, int split, int I, int J, i
   fence_acquire();
   // the last slice to arrive sums all slices in slice order, fragment by fragment
   const float* base = p.partial + static_cast<int64_t>(t) * p.n_split * kElems;
-  for (int f = 0; f < NI * NJ; ++f) {
-    const int i = f / NJ, j = f % NJ;
-    const int64_t off = static_cast<int64_t>(((wave * NI + i) * NJ + j) * 64 + lane) << 2;
+  for (int f = 0; f < NF; ++f) {
+    const int64_t off = static_cast<int64_t>((wave * NF + f) * 64 + lane) << 2;
     f32x4_t sum = {0.f, 0.f, 0.f, 0.f};
     for (int k = 0; k < p.n_split; ++k) sum += *reinterpret_cast<const f32x4_t*>(base + k * kElems + off);
-    add_frag_to_S<TILE>(p, I, J, rbase + 16 * i + rsub, cbase + 16 * j + csub, sum);
+    int row0, col;
+    coord(f, row0, col);
+    add_frag_to_S<TILE>(p, I, J, row0, col, sum);
   }
+}
+
+GPTQ_DEV float* partial_tile(const HessParams& p, int t, int split, int64_t elems) {
+  return p.partial + (static_cast<int64_t>(t) * p.n_split + split) * elems;
 }
 
 // ============================================================ bf16 path ====
@@ -125,23 +166,35 @@ constexpr int kBTile = 256;
 constexpr int kBStage = 64;              // tokens per stage = 128 bytes per LDS row
 constexpr int kBOpBytes = kBTile * 128;  // one operand stage: 32 KB
 
-// Loads tokens [row0, row0 + 8) of one 8-channel group.  Xs points at the
-// stage's first token (uniform), so per-lane offsets stay 32-bit.  d_in is a
-// multiple of 8: a channel group is either wholly inside or outside.
-GPTQ_DEV void load_block_bf16(const uint16_t* __restrict__ Xs, int ldx, int row0, int rows_left,
-                              int col, int d_in, u32x4_t (&r)[8]) {
-  const bool col_ok = col < d_in;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int row = row0 + j;
-    u32x4_t v = {0u, 0u, 0u, 0u};
-    if (col_ok && row < rows_left) v = *reinterpret_cast<const u32x4_t*>(Xs + (row * ldx + col));
-    r[j] = v;
-  }
+// Buffer resource over one stage of X: `rows` token rows starting at Xs.  Reads
+// past the end (tokens beyond the slice) return zeros in hardware.
+GPTQ_DEV __amdgpu_buffer_rsrc_t stage_rsrc(const uint16_t* Xs, int rows, int ldx) {
+  // every field is workgroup-uniform; say so, or the compiler builds a waterfall loop
+  const uint64_t a = reinterpret_cast<uint64_t>(Xs);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a >> 32));
+  const int n = __builtin_amdgcn_readfirstlane(rows * ldx * 2);
+  void* base = reinterpret_cast<void*>((static_cast<uint64_t>(hi) << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(base, static_cast<short>(0), n, 0x00020000);
 }
 
+// Loads tokens [8 tg, 8 tg + 8) of the stage for one 8-channel group: the lane
+// offset is 32-bit, the row step is a scalar offset.  A channel group beyond
+// d_in (d_in is a multiple of 8) gets an out-of-range offset and reads zeros.
+GPTQ_DEV void load_block_bf16(__amdgpu_buffer_rsrc_t rs, int ldx, int tg, int col, int d_in, u32x4_t (&r)[8]) {
+  const uint32_t voff = (col < d_in) ? static_cast<uint32_t>((8 * tg * ldx + col) * 2) : 0x80000000u;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) r[j] = __builtin_amdgcn_raw_buffer_load_b128(rs, voff, j * ldx * 2, 0);
+}
+
+// LDS row m (one channel, 64 tokens = eight 16-byte chunks): logical chunk q is
+// stored at q ^ (m & 7) ^ ((m >> 3) & 7).  Both the transposing stores (eight
+// rows 8 apart per instruction) and the operand loads (consecutive rows) then
+// touch eight distinct bank groups.
+GPTQ_DEV int swz(int m, int q) { return q ^ (m & 7) ^ ((m >> 3) & 7); }
+
 // r[j] holds tokens (8 tg + j) x channels (8 cg .. 8 cg + 7); write each channel's
-// 8 tokens as one 16-byte chunk of LDS row (8 cg + c), chunk tg swizzled by c.
+// 8 tokens as one 16-byte chunk (logical chunk tg) of LDS row 8 cg + c.
 GPTQ_DEV void store_block_bf16(uint8_t* lds, int cg, int tg, const u32x4_t (&r)[8]) {
 #pragma unroll
   for (int pch = 0; pch < 4; ++pch) {
@@ -152,83 +205,110 @@ GPTQ_DEV void store_block_bf16(uint8_t* lds, int cg, int tg, const u32x4_t (&r)[
       hi[q] = __builtin_amdgcn_perm(r[2 * q + 1][pch], r[2 * q][pch], 0x07060302u);
     }
     const int m0 = 8 * cg + 2 * pch;
-    *reinterpret_cast<u32x4_t*>(lds + m0 * 128 + ((tg ^ (2 * pch)) << 4)) = lo;
-    *reinterpret_cast<u32x4_t*>(lds + (m0 + 1) * 128 + ((tg ^ (2 * pch + 1)) << 4)) = hi;
+    *reinterpret_cast<u32x4_t*>(lds + m0 * 128 + (swz(m0, tg) << 4)) = lo;
+    *reinterpret_cast<u32x4_t*>(lds + (m0 + 1) * 128 + (swz(m0 + 1, tg) << 4)) = hi;
   }
 }
 
+// One 64-token stage on v_mfma_f32_32x32x16_bf16: the wave's 128x128 block is
+// 4x4 MFMA tiles; per 16 tokens each lane reads one 16-byte chunk (8 tokens of
+// one channel) per A and B tile.  32x32 tiles keep the loop free of
+// accumulator moves (the allocator handles 16 wide tuples well).
 GPTQ_DEV void mfma_stage_bf16(const uint8_t* A, const uint8_t* B, int wm, int wn, int lane,
-                              f32x4_t (&acc)[8][8]) {
-  const int r16 = lane & 15;
+                              f32x16_t (&acc)[4][4]) {
+  const int r32 = lane & 31;
 #pragma unroll
-  for (int kk = 0; kk < 2; ++kk) {
-    const int q = (lane >> 4) + 4 * kk;
-    const int chunk = (q ^ (lane & 7)) << 4;
-    bf16x8_t a[8];
+  for (int ks = 0; ks < 4; ++ks) {
+    const int q = (lane >> 5) + 2 * ks;
+    bf16x8_t a[4], b[4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      a[i] = *reinterpret_cast<const bf16x8_t*>(A + (wm * 128 + 16 * i + r16) * 128 + chunk);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const bf16x8_t b = *reinterpret_cast<const bf16x8_t*>(B + (wn * 128 + 16 * j + r16) * 128 + chunk);
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b, acc[i][j], 0, 0, 0);
+    for (int i = 0; i < 4; ++i) {
+      const int m = wm * 128 + 32 * i + r32;
+      a[i] = *reinterpret_cast<const bf16x8_t*>(A + m * 128 + (swz(m, q) << 4));
     }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int m = wn * 128 + 32 * j + r32;
+      b[j] = *reinterpret_cast<const bf16x8_t*>(B + m * 128 + (swz(m, q) << 4));
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
   }
 }
 
 __global__ __launch_bounds__(kThreads, 1) void hessian_bf16_kernel(HessParams p) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[2][2][kBOpBytes];
-  const int t = blockIdx.x % p.n_tiles;
-  const int split = blockIdx.x / p.n_tiles;
-  int I, J;
+  int t, split, I, J;
+  work_item(blockIdx.x, p.n_tiles, p.n_split, t, split);
   tile_coords(t, p.nt, I, J);
   const bool diag = (I == J);
   const int64_t k0 = static_cast<int64_t>(split) * p.split_len;
   const int64_t k1 = min(p.n_tokens, k0 + p.split_len);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  const int tg = lane & 7, cg = (lane >> 3) + 8 * wave;
+  // a load instruction covers two token rows, 512 contiguous bytes each
+  const int cg = lane & 31, tg = (lane >> 5) + 2 * wave;
   const int colA = I * kBTile + 8 * cg, colB = J * kBTile + 8 * cg;
   const uint16_t* X = static_cast<const uint16_t*>(p.X);
 
-  f32x4_t acc[8][8];
+  f32x16_t acc[4][4];
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
   const int nstage = (k1 > k0) ? static_cast<int>((k1 - k0 + kBStage - 1) / kBStage) : 0;
   const int ldx = static_cast<int>(p.ldx);
+  // diagonal tiles load the same channel block for both operands (an L2 hit):
+  // one code path keeps the loop free of branches, which lets the compiler
+  // keep the 256 accumulators in fixed AGPRs
   u32x4_t ra[8], rb[8];
+  auto load_stage = [&](int s) {
+    const int64_t t0 = k0 + static_cast<int64_t>(s) * kBStage;
+    const int left = static_cast<int>(min<int64_t>(k1 - t0, kBStage));
+    const __amdgpu_buffer_rsrc_t rs = stage_rsrc(X + t0 * p.ldx, left, ldx);
+    load_block_bf16(rs, ldx, tg, colA, p.d_in, ra);
+    load_block_bf16(rs, ldx, tg, colB, p.d_in, rb);
+  };
+  auto store_stage = [&](int buf) {
+    store_block_bf16(lds[buf][0], cg, tg, ra);
+    store_block_bf16(lds[buf][1], cg, tg, rb);
+  };
   if (nstage > 0) {
-    const uint16_t* Xs = X + k0 * p.ldx;
-    const int left = static_cast<int>(min<int64_t>(k1 - k0, kBStage));
-    load_block_bf16(Xs, ldx, 8 * tg, left, colA, p.d_in, ra);
-    if (!diag) load_block_bf16(Xs, ldx, 8 * tg, left, colB, p.d_in, rb);
-    store_block_bf16(lds[0][0], cg, tg, ra);
-    if (!diag) store_block_bf16(lds[0][1], cg, tg, rb);
+    load_stage(0);
+    store_stage(0);
   }
   __syncthreads();
-  for (int s = 0; s < nstage; ++s) {
+  for (int s = 0; s + 1 < nstage; ++s) {
     const int cur = s & 1;
-    const bool more = (s + 1) < nstage;
-    if (more) {
-      const int64_t t0 = k0 + static_cast<int64_t>(s + 1) * kBStage;
-      const uint16_t* Xs = X + t0 * p.ldx;
-      const int left = static_cast<int>(min<int64_t>(k1 - t0, kBStage));
-      load_block_bf16(Xs, ldx, 8 * tg, left, colA, p.d_in, ra);
-      if (!diag) load_block_bf16(Xs, ldx, 8 * tg, left, colB, p.d_in, rb);
-    }
-    mfma_stage_bf16(lds[cur][0], diag ? lds[cur][0] : lds[cur][1], wm, wn, lane, acc);
-    if (more) {
-      store_block_bf16(lds[cur ^ 1][0], cg, tg, ra);
-      if (!diag) store_block_bf16(lds[cur ^ 1][1], cg, tg, rb);
-    }
+    load_stage(s + 1);
+    mfma_stage_bf16(lds[cur][0], lds[cur][1], wm, wn, lane, acc);
+    store_stage(cur ^ 1);
     __syncthreads();
   }
-  finish_tile<8, 8, kBTile>(p, t, split, I, J, wm * 128, wn * 128, acc);
+  if (nstage > 0) mfma_stage_bf16(lds[(nstage - 1) & 1][0], lds[(nstage - 1) & 1][1], wm, wn, lane, acc);
+  (void)diag;
+  // 32x32 accumulator layout: element r of lane l is tile row
+  // 8 (r / 4) + 4 (l / 32) + r % 4, column l % 32; stored as 4 fragments of 4 rows
+  float* mine = partial_tile(p, t, split, static_cast<int64_t>(kBTile) * kBTile);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        *reinterpret_cast<f32x4_t*>(mine + (((wave * 64 + (i * 4 + j) * 4 + e) * 64 + lane) << 2)) =
+            f32x4_t{acc[i][j][4 * e], acc[i][j][4 * e + 1], acc[i][j][4 * e + 2], acc[i][j][4 * e + 3]};
+  finish_tile<64, kBTile>(p, t, I, J, [&](int f, int& row0, int& col) {
+    const int i = f >> 4, j = (f >> 2) & 3, e = f & 3;
+    row0 = wm * 128 + 32 * i + 8 * e + 4 * (lane >> 5);
+    col = wn * 128 + 32 * j + (lane & 31);
+  });
 }
 
 // ============================================================ fp32 path ====
@@ -257,9 +337,8 @@ GPTQ_DEV void store_stage_f32(float* lds, int tid, const f32x4_t (&r)[4]) {
 
 __global__ __launch_bounds__(kThreads, 2) void hessian_f32_kernel(HessParams p) {
   __shared__ __attribute__((aligned(16))) float lds[2][2][kFStage * kFPitch];
-  const int t = blockIdx.x % p.n_tiles;
-  const int split = blockIdx.x / p.n_tiles;
-  int I, J;
+  int t, split, I, J;
+  work_item(blockIdx.x, p.n_tiles, p.n_split, t, split);
   tile_coords(t, p.nt, I, J);
   const bool diag = (I == J);
   const int64_t k0 = static_cast<int64_t>(split) * p.split_len;
@@ -313,7 +392,17 @@ __global__ __launch_bounds__(kThreads, 2) void hessian_f32_kernel(HessParams p) 
     }
     __syncthreads();
   }
-  finish_tile<4, 4, kFTile>(p, t, split, I, J, wm * 64, wn * 64, acc);
+  float* mine = partial_tile(p, t, split, static_cast<int64_t>(kFTile) * kFTile);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      *reinterpret_cast<f32x4_t*>(mine + (((wave * 16 + i * 4 + j) * 64 + lane) << 2)) = acc[i][j];
+  finish_tile<16, kFTile>(p, t, I, J, [&](int f, int& row0, int& col) {
+    const int i = f >> 2, j = f & 3;
+    row0 = wm * 64 + 16 * i + 4 * (lane >> 4);
+    col = wn * 64 + 16 * j + (lane & 15);
+  });
 }
 
 __global__ void fill_i32_kernel(int32_t* p, int64_t n, int32_t v) {
@@ -361,7 +450,7 @@ HessPlan hessian_plan(int64_t d_in, int64_t n_tokens, bool bf16, int n_cu) {
   if (pl.split_len <= 0) pl.split_len = pl.stage_tokens;
   pl.n_split = static_cast<int>(std::max<int64_t>(1, (n_tokens + pl.split_len - 1) / pl.split_len));
   const size_t tile_bytes = static_cast<size_t>(pl.tile) * pl.tile * sizeof(float);
-  pl.partial_bytes = pl.n_split > 1 ? static_cast<size_t>(pl.n_tiles) * pl.n_split * tile_bytes : 0;
+  pl.partial_bytes = static_cast<size_t>(pl.n_tiles) * pl.n_split * tile_bytes;
   pl.ticket_bytes = static_cast<size_t>(pl.n_tiles) * sizeof(int32_t);
   auto up = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
   pl.ws_bytes = up(pl.partial_bytes) + up(pl.ticket_bytes);

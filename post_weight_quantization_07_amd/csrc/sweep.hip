@@ -47,6 +47,7 @@ struct SweepParams {
   int sym;
   int preset;           // 1: scales/zeros of every column are already in the outputs
   int identity;         // perm is the identity
+  uint64_t gstart[2];   // bit i: block column i starts a dynamic group (group <= 128)
 };
 
 GPTQ_DEV void group_params(float lo, float hi, const SweepParams& p, float& scale, float& zero) {
@@ -66,7 +67,7 @@ GPTQ_DEV void group_params(float lo, float hi, const SweepParams& p, float& scal
 }
 
 template <int I>
-GPTQ_DEV void sweep_step(const SweepParams& p, const float (*Ub)[kB], const float* dinv, int t,
+GPTQ_DEV void sweep_step(const SweepParams& p, const float (*Ub)[kB], const float (&dv)[8], int t,
                          float (&v)[8], float (&sc)[8], float (&zr)[8], float (&qc)[8], float (&qv)[8],
                          float (&er)[8], float& loss, int64_t row) {
   constexpr int r = I & 7, owner = I >> 3;
@@ -74,7 +75,7 @@ GPTQ_DEV void sweep_step(const SweepParams& p, const float (*Ub)[kB], const floa
   const f32x4_t u0 = *reinterpret_cast<const f32x4_t*>(&Ub[I][8 * t]);
   const f32x4_t u1 = *reinterpret_cast<const f32x4_t*>(&Ub[I][8 * t + 4]);
   // dynamic groups that start inside the block: range over the group's current values
-  if (!p.preset && p.group > 0 && p.group <= kB && (I % p.group) == 0 && I < p.ncols) {
+  if ((p.gstart[I >> 6] >> (I & 63)) & 1ull) {
     float lo = 0.f, hi = 0.f;
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
@@ -104,7 +105,7 @@ GPTQ_DEV void sweep_step(const SweepParams& p, const float (*Ub)[kB], const floa
   const float s = sc[r], z = zr[r];
   const float q = fminf(fmaxf(rintf(w / s) + z, 0.f), p.maxq);
   const float what = s * (q - z);
-  const float err = (w - what) * dinv[I];
+  const float err = (w - what) * dv[r];
   const float eb = row_bcast<owner>(err);
   qc[r] = (t == owner) ? q : qc[r];
   qv[r] = (t == owner) ? what : qv[r];
@@ -123,15 +124,14 @@ GPTQ_DEV void sweep_step(const SweepParams& p, const float (*Ub)[kB], const floa
 }
 
 template <int... Is>
-GPTQ_DEV void sweep_all(const SweepParams& p, const float (*Ub)[kB], const float* dinv, int t, float (&v)[8],
+GPTQ_DEV void sweep_all(const SweepParams& p, const float (*Ub)[kB], const float (&dv)[8], int t, float (&v)[8],
                         float (&sc)[8], float (&zr)[8], float (&qc)[8], float (&qv)[8], float (&er)[8],
                         float& loss, int64_t row, std::integer_sequence<int, Is...>) {
-  (sweep_step<Is>(p, Ub, dinv, t, v, sc, zr, qc, qv, er, loss, row), ...);
+  (sweep_step<Is>(p, Ub, dv, t, v, sc, zr, qc, qv, er, loss, row), ...);
 }
 
 __global__ __launch_bounds__(256) void sweep_kernel(SweepParams p) {
   __shared__ __attribute__((aligned(16))) float Ub[kB][kB];
-  __shared__ float dinv[kB];
   const int tid = threadIdx.x;
   const int t = tid & 15;
   const int64_t row = static_cast<int64_t>(blockIdx.x) * kRowsPerWG + (tid >> 4);
@@ -146,10 +146,12 @@ __global__ __launch_bounds__(256) void sweep_kernel(SweepParams p) {
     *reinterpret_cast<f32x4_t*>(&Ub[i][c4]) = u;
   }
   __syncthreads();
-  if (tid < kB) dinv[tid] = (tid < p.ncols) ? 1.0f / Ub[tid][tid] : 0.f;
 
-  float v[8], sc[8], zr[8], qc[8], qv[8], er[8];
+  float v[8], sc[8], zr[8], qc[8], qv[8], er[8], dv[8];
   const int c0 = 8 * t;
+  // 1 / U[i][i] of this lane's own columns (only the owner of a column uses it)
+#pragma unroll
+  for (int k = 0; k < 8; ++k) dv[k] = (c0 + k < p.ncols) ? 1.0f / Ub[c0 + k][c0 + k] : 0.f;
   {
     const float* src = p.Wp + row * p.d_in + p.j0 + c0;
     f32x4_t a = {0.f, 0.f, 0.f, 0.f}, b = {0.f, 0.f, 0.f, 0.f};
@@ -218,7 +220,7 @@ __global__ __launch_bounds__(256) void sweep_kernel(SweepParams p) {
   __syncthreads();
 
   float loss = 0.f;
-  sweep_all(p, Ub, dinv, t, v, sc, zr, qc, qv, er, loss, row, std::make_integer_sequence<int, kB>{});
+  sweep_all(p, Ub, dv, t, v, sc, zr, qc, qv, er, loss, row, std::make_integer_sequence<int, kB>{});
 
   if (!row_ok) return;
   // normalised errors of the block, for the trailing update
@@ -377,6 +379,9 @@ hipError_t quantize_launch(const void* W, bool w_bf16, int64_t d_out, int64_t d_
   for (int64_t j0 = 0; j0 < d_in; j0 += kB) {
     p.j0 = j0;
     p.ncols = static_cast<int>(std::min<int64_t>(kB, d_in - j0));
+    p.gstart[0] = p.gstart[1] = 0;
+    if (!preset && group <= kB)
+      for (int i = 0; i < p.ncols; i += group) p.gstart[i >> 6] |= 1ull << (i & 63);
     sweep_kernel<<<blocks, 256, 0, st>>>(p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const int64_t rest = d_in - j0 - kB;

@@ -144,6 +144,29 @@ def activation_chunks(layer: Layer) -> Iterator[np.ndarray]:
         yield activation_chunk(layer, c, sigma, mix)
 
 
+def activation_chunks_threaded(layer: Layer, workers: int = 8, as_bf16_bits: bool = False):
+    """Same chunks as activation_chunks, produced by a thread pool, in order.
+    With as_bf16_bits the chunks come as uint16 bf16 bit patterns."""
+    import concurrent.futures as cf
+    sigma = channel_sigma(layer)
+    mix = _mixing(layer)
+
+    def make(c):
+        x = activation_chunk(layer, c, sigma, mix)
+        return bf16_bits(x) if as_bf16_bits else x
+
+    with cf.ThreadPoolExecutor(max(1, workers)) as ex:
+        futs = [ex.submit(make, c) for c in range(min(layer.n_chunks(), 2 * workers))]
+        nxt = len(futs)
+        for c in range(layer.n_chunks()):
+            x = futs[c].result()
+            futs[c] = None
+            if nxt < layer.n_chunks():
+                futs.append(ex.submit(make, nxt))
+                nxt += 1
+            yield x
+
+
 def activations(layer: Layer) -> np.ndarray:
     """All of X [N, d_in] (fp32 values); small layers only."""
     return np.concatenate(list(activation_chunks(layer)), axis=0)

@@ -199,10 +199,10 @@ def test_quantize_stagewise(G, case):
         assert clean.mean() >= 0.9
         np.testing.assert_allclose(sc[:, clean], ref.scales[:, clean], rtol=1e-4, atol=0)
         assert np.mean(zr[:, clean] == ref.zeros[:, clean]) >= 0.999
-    # dequantized weights where codes agree; row losses
+    # dequantized weights on rows without a code flip; row losses
     Q = out["Q"].cpu().numpy()
-    same = codes == ref.codes
-    np.testing.assert_allclose(Q[same], ref.Q[same], rtol=1e-6, atol=1e-7)
+    clean = ~np.any(codes != ref.codes, axis=1)
+    np.testing.assert_allclose(Q[clean], ref.Q[clean], rtol=1e-6, atol=1e-7)
     rl = out["row_loss"].cpu().numpy()
     np.testing.assert_allclose(rl, ref.row_loss, rtol=2e-2, atol=1e-9 * ref.row_loss.max())
     # pack of the GPU's codes: bit-exact
