@@ -266,32 +266,51 @@ __global__ __launch_bounds__(kThreads, 1) void hessian_bf16_kernel(HessParams p)
   const int ldx = static_cast<int>(p.ldx);
   // diagonal tiles load the same channel block for both operands (an L2 hit):
   // one code path keeps the loop free of branches, which lets the compiler
-  // keep the 256 accumulators in fixed AGPRs
-  u32x4_t ra[8], rb[8];
-  auto load_stage = [&](int s) {
+  // keep the 256 accumulators in fixed AGPRs.  Global loads run two stages
+  // ahead of the MFMAs (two register sets), so about two stages of load
+  // latency are hidden behind matrix work.
+  u32x4_t ra0[8], rb0[8], ra1[8], rb1[8];
+  auto load_stage = [&](int s, u32x4_t (&ra)[8], u32x4_t (&rb)[8]) {
     const int64_t t0 = k0 + static_cast<int64_t>(s) * kBStage;
     const int left = static_cast<int>(min<int64_t>(k1 - t0, kBStage));
     const __amdgpu_buffer_rsrc_t rs = stage_rsrc(X + t0 * p.ldx, left, ldx);
     load_block_bf16(rs, ldx, tg, colA, p.d_in, ra);
     load_block_bf16(rs, ldx, tg, colB, p.d_in, rb);
   };
-  auto store_stage = [&](int buf) {
+  auto store_stage = [&](int buf, const u32x4_t (&ra)[8], const u32x4_t (&rb)[8]) {
     store_block_bf16(lds[buf][0], cg, tg, ra);
     store_block_bf16(lds[buf][1], cg, tg, rb);
   };
-  if (nstage > 0) {
-    load_stage(0);
-    store_stage(0);
-  }
+  // stage s lives in LDS buffer s & 1 and, before that, in register set s & 1
+  if (nstage > 0) load_stage(0, ra0, rb0);
+  if (nstage > 1) load_stage(1, ra1, rb1);
+  if (nstage > 0) store_stage(0, ra0, rb0);
   __syncthreads();
-  for (int s = 0; s + 1 < nstage; ++s) {
-    const int cur = s & 1;
-    load_stage(s + 1);
-    mfma_stage_bf16(lds[cur][0], lds[cur][1], wm, wn, lane, acc);
-    store_stage(cur ^ 1);
+  int s = 0;
+  for (; s + 3 < nstage; s += 2) {
+    load_stage(s + 2, ra0, rb0);
+    mfma_stage_bf16(lds[0][0], lds[0][1], wm, wn, lane, acc);
+    store_stage(1, ra1, rb1);
+    __syncthreads();
+    load_stage(s + 3, ra1, rb1);
+    mfma_stage_bf16(lds[1][0], lds[1][1], wm, wn, lane, acc);
+    store_stage(0, ra0, rb0);
     __syncthreads();
   }
-  if (nstage > 0) mfma_stage_bf16(lds[(nstage - 1) & 1][0], lds[(nstage - 1) & 1][1], wm, wn, lane, acc);
+  // tail: at most three stages left, s even; stage s is in LDS 0, s + 1 in set 1
+  for (; s < nstage; ++s) {
+    const int cur = s & 1;
+    if (s + 2 < nstage) {
+      if (cur == 0) load_stage(s + 2, ra0, rb0);
+      else load_stage(s + 2, ra1, rb1);
+    }
+    mfma_stage_bf16(lds[cur][0], lds[cur][1], wm, wn, lane, acc);
+    if (s + 1 < nstage) {
+      if (cur == 0) store_stage(1, ra1, rb1);
+      else store_stage(0, ra0, rb0);
+    }
+    __syncthreads();
+  }
   (void)diag;
   // 32x32 accumulator layout: element r of lane l is tile row
   // 8 (r / 4) + 4 (l / 32) + r % 4, column l % 32; stored as 4 fragments of 4 rows

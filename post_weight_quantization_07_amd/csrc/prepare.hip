@@ -105,7 +105,7 @@ __global__ void gather_kernel(const float* H, int64_t n, const int32_t* perm, co
   }
 }
 
-// Lower Cholesky of the 64x64 block held in L (LDS, pitch 65), by wave 0:
+// Lower Cholesky of the 64x64 block held in L (LDS, pitch 68), by wave 0:
 // lane r keeps row r in registers; column j is published through LDS.
 // Returns through `fail` the first failing local pivot (or -1).
 GPTQ_DEV void factor_block_wave(float (*L)[68], float* col, int lane, int& fail) {
@@ -117,8 +117,10 @@ GPTQ_DEV void factor_block_wave(float (*L)[68], float* col, int lane, int& fail)
   for (int j = 0; j < kNB; ++j) {
     const float piv = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v[j]), j));
     if (!(piv > 0.f) && fail < 0) fail = j;
-    const float d = sqrtf(piv);
-    const float inv = 1.0f / d;
+    // hardware square root and reciprocal (about 1 ulp): the pivot chain is the
+    // latency-critical path of the factorization
+    const float d = __builtin_amdgcn_sqrtf(piv);
+    const float inv = __builtin_amdgcn_rcpf(d);
     v[j] = (lane == j) ? d : ((lane > j) ? v[j] * inv : v[j]);
     col[lane] = v[j];
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -132,11 +134,45 @@ GPTQ_DEV void factor_block_wave(float (*L)[68], float* col, int lane, int& fail)
   for (int c = 0; c < kNB; ++c) L[lane][c] = (c <= lane) ? v[c] : 0.f;
 }
 
-// One launch per panel k: every workgroup factors the diagonal block (the same
-// arithmetic, so the same result), workgroup 0 stores it, and each thread
-// solves one panel row x against it: x L^T = p (forward substitution).
+// One launch per panel k: every workgroup factors the 64x64 diagonal block
+// (the same arithmetic, so the same result), workgroup 0 stores it, and the
+// workgroup then solves 64 panel rows x L^T = p against it.  Each row is
+// solved by a quad of lanes, lane q holding columns q, q+4, ..., q+60:
+// right-looking substitution (once x_c is known, every later column of the row
+// is updated at once) keeps the dependent chain at 64 steps, and x_c reaches
+// the other three lanes of the quad through a DPP quad broadcast.
+constexpr int kPanelRows = 64;
+
+template <int Q>
+GPTQ_DEV float quad_bcast(float v) {
+  constexpr int sel = Q | (Q << 2) | (Q << 4) | (Q << 6);
+  return __builtin_amdgcn_update_dpp(0.0f, v, sel, 0xf, 0xf, false);
+}
+
+template <int C>
+GPTQ_DEV void solve_step(float (&sv)[16], float (&xv)[16], const float (*LTq)[4][16], const float* dinv, int q) {
+  constexpr int owner = C & 3, u = C >> 2;
+  const float xc = quad_bcast<owner>(sv[u] * dinv[C]);
+  xv[u] = (q == owner) ? xc : xv[u];
+  // column C of L for this lane's columns 4 k + q (zeros above the diagonal)
+  const f32x4_t* lt = reinterpret_cast<const f32x4_t*>(&LTq[C][q][0]);
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const f32x4_t l4 = lt[w];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) sv[4 * w + e] = fmaf(-xc, l4[e], sv[4 * w + e]);
+  }
+}
+
+template <int... Cs>
+GPTQ_DEV void solve_all(float (&sv)[16], float (&xv)[16], const float (*LTq)[4][16], const float* dinv, int q,
+                        std::integer_sequence<int, Cs...>) {
+  (solve_step<Cs>(sv, xv, LTq, dinv, q), ...);
+}
+
 __global__ __launch_bounds__(256) void panel_kernel(float* Hr, int64_t n, int64_t k, int32_t* info) {
   __shared__ __attribute__((aligned(16))) float L[kNB][68];
+  __shared__ __attribute__((aligned(16))) float LTq[kNB][4][16];  // LTq[c][q][u] = L[4u+q][c]
   __shared__ float col[kNB];
   __shared__ float dinv[kNB];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -155,7 +191,11 @@ __global__ __launch_bounds__(256) void panel_kernel(float* Hr, int64_t n, int64_
       atomicCAS(info, 0, static_cast<int32_t>(n - (k + fail)));
   }
   __syncthreads();
-  if (tid < kNB) dinv[tid] = 1.0f / L[tid][tid];
+  if (tid < kNB) dinv[tid] = __builtin_amdgcn_rcpf(L[tid][tid]);
+  for (int e = tid; e < kNB * kNB; e += 256) {
+    const int c = e >> 6, r = e & 63;
+    LTq[c][r & 3][r >> 2] = L[r][c];
+  }
   if (blockIdx.x == 0) {
     for (int e = tid; e < nb * nb; e += 256) {
       const int r = e / nb, c = e - r * nb;
@@ -163,29 +203,20 @@ __global__ __launch_bounds__(256) void panel_kernel(float* Hr, int64_t n, int64_
     }
   }
   __syncthreads();
-  const int64_t row = k + kNB + static_cast<int64_t>(blockIdx.x) * 256 + tid;
+  const int q = tid & 3;
+  const int64_t row = k + kNB + static_cast<int64_t>(blockIdx.x) * kPanelRows + (tid >> 2);
   if (nb < kNB || row >= n) return;
-  float x[kNB];
+  float sv[16], xv[16];
   const float* src = Hr + row * n + k;
 #pragma unroll
-  for (int q = 0; q < kNB / 4; ++q) {
-    const f32x4_t t = *reinterpret_cast<const f32x4_t*>(src + 4 * q);
-    x[4 * q] = t[0];
-    x[4 * q + 1] = t[1];
-    x[4 * q + 2] = t[2];
-    x[4 * q + 3] = t[3];
+  for (int u = 0; u < 16; ++u) {
+    sv[u] = src[4 * u + q];
+    xv[u] = 0.f;
   }
-#pragma unroll
-  for (int c = 0; c < kNB; ++c) {
-    float s = x[c];
-#pragma unroll
-    for (int t = 0; t < c; ++t) s = fmaf(-x[t], L[c][t], s);
-    x[c] = s * dinv[c];
-  }
+  solve_all(sv, xv, LTq, dinv, q, std::make_integer_sequence<int, kNB>{});
   float* dst = Hr + row * n + k;
 #pragma unroll
-  for (int q = 0; q < kNB / 4; ++q)
-    *reinterpret_cast<f32x4_t*>(dst + 4 * q) = f32x4_t{x[4 * q], x[4 * q + 1], x[4 * q + 2], x[4 * q + 3]};
+  for (int u = 0; u < 16; ++u) dst[4 * u + q] = xv[u];
 }
 
 // Invert every 64x64 diagonal block of the lower factor in place.  Wave 0,
@@ -209,7 +240,7 @@ __global__ __launch_bounds__(256) void diag_inverse_kernel(float* Hr, int64_t n)
     float s = (i == lane) ? 1.f : 0.f;
 #pragma unroll
     for (int t = 0; t < i; ++t) s = fmaf(-L[i][t], m[t], s);
-    m[i] = (i >= lane) ? s / L[i][i] : 0.f;
+    m[i] = (i >= lane) ? s * __builtin_amdgcn_rcpf(L[i][i]) : 0.f;
   }
   for (int i = 0; i < nb; ++i)
     if (lane < nb) Hr[(k + i) * n + k + lane] = m[i];
@@ -274,7 +305,7 @@ hipError_t prepare_launch(float* S, int64_t n, int64_t n_total, float damp, bool
   // blocked right-looking Cholesky of Hr
   for (int64_t k = 0; k < n; k += kNB) {
     const int64_t below = std::max<int64_t>(0, n - k - kNB);
-    const int blocks = static_cast<int>(std::max<int64_t>(1, (below + 255) / 256));
+    const int blocks = static_cast<int>(std::max<int64_t>(1, (below + kPanelRows - 1) / kPanelRows));
     panel_kernel<<<blocks, 256, 0, st>>>(Hr, n, k, info);
     GPTQ_TRY(hipGetLastError());
     if (below > 0) {

@@ -47,7 +47,6 @@ struct SweepParams {
   int sym;
   int preset;           // 1: scales/zeros of every column are already in the outputs
   int identity;         // perm is the identity
-  uint64_t gstart[2];   // bit i: block column i starts a dynamic group (group <= 128)
 };
 
 GPTQ_DEV void group_params(float lo, float hi, const SweepParams& p, float& scale, float& zero) {
@@ -66,7 +65,11 @@ GPTQ_DEV void group_params(float lo, float hi, const SweepParams& p, float& scal
   zero = p.sym ? static_cast<float>(1 << (p.bits - 1)) : rintf(-lo / scale);
 }
 
-template <int I>
+// GS > 0: dynamic groups of GS columns start inside the block (GS divides
+// 128), so the range code is emitted only at steps I % GS == 0; GS == 0: every
+// column's parameters are known before the block.  Keeping the code of the
+// 128 unrolled steps small matters: it has to stay in the instruction cache.
+template <int GS, int I>
 GPTQ_DEV void sweep_step(const SweepParams& p, const float (*Ub)[kB], const float (&dv)[8], int t,
                          float (&v)[8], float (&sc)[8], float (&zr)[8], float (&qc)[8], float (&qv)[8],
                          float (&er)[8], float& loss, int64_t row) {
@@ -75,30 +78,34 @@ GPTQ_DEV void sweep_step(const SweepParams& p, const float (*Ub)[kB], const floa
   const f32x4_t u0 = *reinterpret_cast<const f32x4_t*>(&Ub[I][8 * t]);
   const f32x4_t u1 = *reinterpret_cast<const f32x4_t*>(&Ub[I][8 * t + 4]);
   // dynamic groups that start inside the block: range over the group's current values
-  if ((p.gstart[I >> 6] >> (I & 63)) & 1ull) {
-    float lo = 0.f, hi = 0.f;
+  if constexpr (GS > 0 && (I % GS) == 0) {
+    if (I < p.ncols) {
+      float lo = 0.f, hi = 0.f;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const int c = 8 * t + k;
-      const bool in = (c >= I) && (c < I + p.group) && (c < p.ncols);
-      lo = in ? fminf(lo, v[k]) : lo;
-      hi = in ? fmaxf(hi, v[k]) : hi;
-    }
-    lo = row_min16(lo);
-    hi = row_max16(hi);
-    float s, z;
-    group_params(lo, hi, p, s, z);
+      for (int k = 0; k < 8; ++k) {
+        const int c = 8 * t + k;
+        const bool in = (c >= I) && (c < I + GS) && (c < p.ncols);
+        lo = in ? fminf(lo, v[k]) : lo;
+        hi = in ? fmaxf(hi, v[k]) : hi;
+      }
+      if constexpr (GS > 8) {  // the group spans several lanes of the row
+        lo = row_min16(lo);
+        hi = row_max16(hi);
+      }
+      float s, z;
+      group_params(lo, hi, p, s, z);
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const int c = 8 * t + k;
-      const bool in = (c >= I) && (c < I + p.group);
-      sc[k] = in ? s : sc[k];
-      zr[k] = in ? z : zr[k];
-    }
-    if (t == owner && row < p.d_out) {
-      const int64_t g = (p.j0 + I) / p.group;
-      p.scales[g * p.d_out + row] = s;
-      p.zeros[g * p.d_out + row] = static_cast<int32_t>(z);
+      for (int k = 0; k < 8; ++k) {
+        const int c = 8 * t + k;
+        const bool in = (c >= I) && (c < I + GS);
+        sc[k] = in ? s : sc[k];
+        zr[k] = in ? z : zr[k];
+      }
+      if (t == owner && row < p.d_out) {
+        const int64_t g = p.j0 / GS + I / GS;
+        p.scales[g * p.d_out + row] = s;
+        p.zeros[g * p.d_out + row] = static_cast<int32_t>(z);
+      }
     }
   }
   const float w = v[r];
@@ -123,13 +130,14 @@ GPTQ_DEV void sweep_step(const SweepParams& p, const float (*Ub)[kB], const floa
   __builtin_amdgcn_sched_barrier(0);
 }
 
-template <int... Is>
+template <int GS, int... Is>
 GPTQ_DEV void sweep_all(const SweepParams& p, const float (*Ub)[kB], const float (&dv)[8], int t, float (&v)[8],
                         float (&sc)[8], float (&zr)[8], float (&qc)[8], float (&qv)[8], float (&er)[8],
                         float& loss, int64_t row, std::integer_sequence<int, Is...>) {
-  (sweep_step<Is>(p, Ub, dv, t, v, sc, zr, qc, qv, er, loss, row), ...);
+  (sweep_step<GS, Is>(p, Ub, dv, t, v, sc, zr, qc, qv, er, loss, row), ...);
 }
 
+template <int GS>
 __global__ __launch_bounds__(256) void sweep_kernel(SweepParams p) {
   __shared__ __attribute__((aligned(16))) float Ub[kB][kB];
   const int tid = threadIdx.x;
@@ -220,7 +228,7 @@ __global__ __launch_bounds__(256) void sweep_kernel(SweepParams p) {
   __syncthreads();
 
   float loss = 0.f;
-  sweep_all(p, Ub, dv, t, v, sc, zr, qc, qv, er, loss, row, std::make_integer_sequence<int, kB>{});
+  sweep_all<GS>(p, Ub, dv, t, v, sc, zr, qc, qv, er, loss, row, std::make_integer_sequence<int, kB>{});
 
   if (!row_ok) return;
   // normalised errors of the block, for the trailing update
@@ -379,10 +387,19 @@ hipError_t quantize_launch(const void* W, bool w_bf16, int64_t d_out, int64_t d_
   for (int64_t j0 = 0; j0 < d_in; j0 += kB) {
     p.j0 = j0;
     p.ncols = static_cast<int>(std::min<int64_t>(kB, d_in - j0));
-    p.gstart[0] = p.gstart[1] = 0;
-    if (!preset && group <= kB)
-      for (int i = 0; i < p.ncols; i += group) p.gstart[i >> 6] |= 1ull << (i & 63);
-    sweep_kernel<<<blocks, 256, 0, st>>>(p);
+    const int gs = (!preset && group <= kB) ? group : 0;
+    switch (gs) {
+      case 0: sweep_kernel<0><<<blocks, 256, 0, st>>>(p); break;
+      case 1: sweep_kernel<1><<<blocks, 256, 0, st>>>(p); break;
+      case 2: sweep_kernel<2><<<blocks, 256, 0, st>>>(p); break;
+      case 4: sweep_kernel<4><<<blocks, 256, 0, st>>>(p); break;
+      case 8: sweep_kernel<8><<<blocks, 256, 0, st>>>(p); break;
+      case 16: sweep_kernel<16><<<blocks, 256, 0, st>>>(p); break;
+      case 32: sweep_kernel<32><<<blocks, 256, 0, st>>>(p); break;
+      case 64: sweep_kernel<64><<<blocks, 256, 0, st>>>(p); break;
+      case 128: sweep_kernel<128><<<blocks, 256, 0, st>>>(p); break;
+      default: return hipErrorInvalidValue;  // the ABI admits only groups dividing 128 here
+    }
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const int64_t rest = d_in - j0 - kB;
     if (rest > 0) {

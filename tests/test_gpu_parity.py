@@ -202,7 +202,9 @@ def test_quantize_stagewise(G, case):
     # dequantized weights on rows without a code flip; row losses
     Q = out["Q"].cpu().numpy()
     clean = ~np.any(codes != ref.codes, axis=1)
-    np.testing.assert_allclose(Q[clean], ref.Q[clean], rtol=1e-6, atol=1e-7)
+    # Q = scale * (q - z): exact-input scales for static / whole-row groups,
+    # compensated-input scales (rtol 1e-4 above) for dynamic groups
+    np.testing.assert_allclose(Q[clean], ref.Q[clean], rtol=1e-6 if exact else 1e-4, atol=1e-7)
     rl = out["row_loss"].cpu().numpy()
     np.testing.assert_allclose(rl, ref.row_loss, rtol=2e-2, atol=1e-9 * ref.row_loss.max())
     # pack of the GPU's codes: bit-exact
