@@ -330,6 +330,168 @@ __global__ __launch_bounds__(kThreads, 1) void hessian_bf16_kernel(HessParams p)
   });
 }
 
+// ======================================================= bf16 DMA path ====
+// Same tiling and epilogue as hessian_bf16_kernel, but X moves from HBM to LDS
+// with buffer_load ... lds (no VGPRs, no register transposition) through a
+// ring of four 32-token stages (three in flight while one is consumed), and
+// the MFMA operands come out of the token-major LDS tile through
+// ds_read_b64_tr_b16.  In a 16-lane group, if lane s points at token
+// t0 + (s >> 2), channels m0 + 4 (s & 3) .. +3, lane i receives tokens
+// t0 .. t0 + 3 of channel m0 + i: two such reads make one 8-token operand.
+// LDS rows (tokens) are 512 bytes; the 16-byte chunk index is XOR-swizzled
+// with 2 (row & 3) so the eight chunks one read touches fall in distinct banks.
+constexpr int kDStage = 32;               // tokens per stage
+constexpr int kDOpBytes = kDStage * 512;  // one operand stage: 16 KB
+
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4_t;
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+#define GPTQ_VMCNT(n) (((n) & 15) | (((n) >> 4) << 14) | 0x0F70)
+
+GPTQ_DEV void dma_operand(__amdgpu_buffer_rsrc_t rs, uint8_t* buf, int ldx, int col0, int d_in, int wave_u,
+                          int lane) {
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int q = 4 * wave_u + u;               // 1 KB piece: token rows 2q, 2q + 1
+    const int row = 2 * q + (lane >> 5);
+    const int c = (lane & 31) ^ (2 * (row & 3));  // logical chunk held at this lane's slot
+    const int col = col0 + 8 * c;
+    const uint32_t voff = (col < d_in) ? static_cast<uint32_t>((row * ldx + col) * 2) : 0x80000000u;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(buf + q * 1024), 16, voff, 0, 0, 0);
+  }
+}
+
+GPTQ_DEV bf16x8_t tr_operand(const uint8_t* buf, uint32_t lane_off, int imm) {
+  typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+  uint8_t* b = const_cast<uint8_t*>(buf) + lane_off + imm;
+  const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)b);
+  const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(b + 4 * 512));
+  typedef __attribute__((__vector_size__(8 * sizeof(short)))) short s16x8_t;
+  const s16x8_t v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8_t, v);
+}
+
+// lane offsets of the transposed reads for even / odd 32-channel tiles of a wave block
+struct TrLane {
+  uint32_t off[2];
+};
+GPTQ_DEV TrLane tr_lane(int lane, int wblock) {
+  const int g = lane >> 4, s = lane & 15;
+  const int base_row = 8 * (g >> 1) + (s >> 2);
+  const int f = 2 * (s >> 2);
+  const int cl = 2 * (g & 1) + ((s & 3) >> 1);
+  TrLane t;
+#pragma unroll
+  for (int par = 0; par < 2; ++par)
+    t.off[par] = static_cast<uint32_t>(base_row * 512 + (s & 1) * 8 + 16 * ((4 * par + cl) ^ f) + 256 * wblock);
+  return t;
+}
+
+GPTQ_DEV void mfma_stage_tr(const uint8_t* A, const uint8_t* B, const TrLane& la, const TrLane& lb,
+                            f32x16_t (&acc)[4][4]) {
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    bf16x8_t a[4], b[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) a[i] = tr_operand(A, la.off[i & 1], ks * 16 * 512 + (i >> 1) * 128);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) b[j] = tr_operand(B, lb.off[j & 1], ks * 16 * 512 + (j >> 1) * 128);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+  }
+}
+
+__global__ __launch_bounds__(kThreads, 1) void hessian_bf16_dma_kernel(HessParams p) {
+  __shared__ __attribute__((aligned(1024))) uint8_t sA0[kDOpBytes], sB0[kDOpBytes], sA1[kDOpBytes], sB1[kDOpBytes],
+      sA2[kDOpBytes], sB2[kDOpBytes], sA3[kDOpBytes], sB3[kDOpBytes];
+  int t, split, I, J;
+  work_item(blockIdx.x, p.n_tiles, p.n_split, t, split);
+  tile_coords(t, p.nt, I, J);
+  const int64_t k0 = static_cast<int64_t>(split) * p.split_len;
+  const int64_t k1 = min(p.n_tokens, k0 + p.split_len);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int colA = I * kBTile, colB = J * kBTile;
+  const int ldx = static_cast<int>(p.ldx);
+  const uint16_t* X = static_cast<const uint16_t*>(p.X);
+  const TrLane la = tr_lane(lane, wm), lb = tr_lane(lane, wn);
+
+  f32x16_t acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+  const int nstage = (k1 > k0) ? static_cast<int>((k1 - k0 + kDStage - 1) / kDStage) : 0;
+  auto issue = [&](int s, uint8_t* bA, uint8_t* bB) {
+    const int64_t t0 = k0 + static_cast<int64_t>(s) * kDStage;
+    const int left = static_cast<int>(min<int64_t>(k1 - t0, kDStage));
+    const __amdgpu_buffer_rsrc_t rs = stage_rsrc(X + t0 * p.ldx, left, ldx);
+    dma_operand(rs, bA, ldx, colA, p.d_in, wave, lane);
+    dma_operand(rs, bB, ldx, colB, p.d_in, wave, lane);
+  };
+  auto bufA = [&](int r) { return r == 0 ? sA0 : r == 1 ? sA1 : r == 2 ? sA2 : sA3; };
+  auto bufB = [&](int r) { return r == 0 ? sB0 : r == 1 ? sB1 : r == 2 ? sB2 : sB3; };
+  int s = 0;
+  if (nstage > 6) {
+    // steady state: stage s + r lives in ring buffer r and every wait leaves
+    // the two stages issued after it in flight.  All issues here are
+    // unconditional, which keeps the compiler's own wait tracking exact.
+    issue(0, sA0, sB0);
+    issue(1, sA1, sB1);
+    issue(2, sA2, sB2);
+    for (; s + 6 < nstage; s += 4) {
+      __builtin_amdgcn_s_waitcnt(GPTQ_VMCNT(16));
+      __builtin_amdgcn_s_barrier();
+      issue(s + 3, sA3, sB3);
+      mfma_stage_tr(sA0, sB0, la, lb, acc);
+      __builtin_amdgcn_s_waitcnt(GPTQ_VMCNT(16));
+      __builtin_amdgcn_s_barrier();
+      issue(s + 4, sA0, sB0);
+      mfma_stage_tr(sA1, sB1, la, lb, acc);
+      __builtin_amdgcn_s_waitcnt(GPTQ_VMCNT(16));
+      __builtin_amdgcn_s_barrier();
+      issue(s + 5, sA1, sB1);
+      mfma_stage_tr(sA2, sB2, la, lb, acc);
+      __builtin_amdgcn_s_waitcnt(GPTQ_VMCNT(16));
+      __builtin_amdgcn_s_barrier();
+      issue(s + 6, sA2, sB2);
+      mfma_stage_tr(sA3, sB3, la, lb, acc);
+    }
+  } else {
+    for (int x = 0; x < nstage && x < 3; ++x) issue(x, bufA(x), bufB(x));
+  }
+  // tail (at most six stages): stage x in buffer x % 4, stages up to s + 2
+  // already issued; full waits.  A buffer is refilled only after the barrier
+  // that follows everyone's last read of it.
+  for (int x = s; x < nstage; ++x) {
+    __builtin_amdgcn_s_waitcnt(GPTQ_VMCNT(0));
+    __builtin_amdgcn_s_barrier();
+    if (x + 3 < nstage) issue(x + 3, bufA((x + 3) & 3), bufB((x + 3) & 3));
+    mfma_stage_tr(bufA(x & 3), bufB(x & 3), la, lb, acc);
+  }
+  float* mine = partial_tile(p, t, split, static_cast<int64_t>(kBTile) * kBTile);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        *reinterpret_cast<f32x4_t*>(mine + (((wave * 64 + (i * 4 + j) * 4 + e) * 64 + lane) << 2)) =
+            f32x4_t{acc[i][j][4 * e], acc[i][j][4 * e + 1], acc[i][j][4 * e + 2], acc[i][j][4 * e + 3]};
+  finish_tile<64, kBTile>(p, t, I, J, [&](int f, int& row0, int& col) {
+    const int i = f >> 4, j = (f >> 2) & 3, e = f & 3;
+    row0 = wm * 128 + 32 * i + 8 * e + 4 * (lane >> 5);
+    col = wn * 128 + 32 * j + (lane & 31);
+  });
+}
+
 // ============================================================ fp32 path ====
 constexpr int kFTile = 128;
 constexpr int kFStage = 32;    // tokens per stage
@@ -498,7 +660,7 @@ hipError_t hessian_launch(const HessPlan& pl, float* S, int64_t d_in, const void
   }
   const int blocks = pl.n_tiles * pl.n_split;
   if (bf16)
-    hessian_bf16_kernel<<<blocks, kThreads, 0, stream>>>(p);
+    hessian_bf16_dma_kernel<<<blocks, kThreads, 0, stream>>>(p);
   else
     hessian_f32_kernel<<<blocks, kThreads, 0, stream>>>(p);
   return hipGetLastError();
