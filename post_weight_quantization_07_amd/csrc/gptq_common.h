@@ -42,8 +42,4 @@ GPTQ_DEV float row_min16(float v) {
   return v;
 }
 
-// Agent-scope acquire/release fences around the split-reduction tickets.
-GPTQ_DEV void fence_release() { __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent"); }
-GPTQ_DEV void fence_acquire() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
-
 }  // namespace gptq

@@ -16,7 +16,6 @@ struct HessPlan {
   int n_split;       // token slices
   int64_t split_len; // tokens per slice (multiple of stage_tokens)
   size_t partial_bytes;
-  size_t ticket_bytes;
   size_t ws_bytes;
 };
 HessPlan hessian_plan(int64_t d_in, int64_t n_tokens, bool bf16, int n_cu);
@@ -56,8 +55,5 @@ hipError_t quantize_launch(const void* W, bool w_bf16, int64_t d_out, int64_t d_
 // ------------------------------------------------------------------- pack --
 hipError_t pack_launch(const uint8_t* codes, int64_t d_out, int64_t d_in, int bits, int32_t* qweight,
                        hipStream_t stream);
-
-// ------------------------------------------------------------------ utils --
-hipError_t fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t stream);
 
 }  // namespace gptq

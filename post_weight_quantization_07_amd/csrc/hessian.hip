@@ -7,19 +7,15 @@
 // Work split: the d_in x d_in output is cut into tiles of the upper triangle
 // (diagonal tiles computed whole); the token axis is cut into n_split equal
 // slices so a launch has enough workgroups for 256 CUs.  Each workgroup owns
-// one (tile, slice) pair and writes its fp32 partial tile; the last workgroup
-// of a tile to finish (a ticket counter) sums the partials in slice order and
-// adds the result to S and to its mirror tile.  The sum order is fixed, so
-// the result does not depend on scheduling.
+// one (tile, slice) pair and stores its fp32 partial tile.  A second, wide
+// kernel sums the partials of every tile in slice order and adds the result
+// to S and to its mirror.  The sum order is fixed, so the result does not
+// depend on scheduling.
 //
 // bf16 path: 256x256 tile, 4 waves of 128x128, v_mfma_f32_32x32x16_bf16.
-//   Each thread loads an 8-token x 8-channel block (eight 16-byte loads) and
-//   transposes it in registers with v_perm_b32, so LDS holds every channel's
-//   tokens contiguously: MFMA operands are single ds_read_b128.  A wave's
-//   load instruction reads two token rows, 512 contiguous bytes each.  LDS
-//   rows are 128 bytes (64 tokens); the 16-byte chunk index is XOR-swizzled
-//   with the row index so both the transposing stores and the operand loads
-//   are free of bank conflicts.  Double-buffered: 2 x (32 KB + 32 KB).
+//   X moves to LDS with buffer_load ... lds (no VGPRs, no register
+//   transposition) through a ring of eight 16-token stages, and the MFMA
+//   operands come out of the token-major LDS tile through ds_read_b64_tr_b16.
 // fp32 path: 128x128 tile, 4 waves of 64x64, v_mfma_f32_16x16x4_f32, LDS
 //   holds [token][channel] rows padded to 144 floats.
 #include "gptq_common.h"
@@ -31,6 +27,8 @@ namespace gptq {
 namespace {
 
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4_t;
+typedef __attribute__((address_space(3))) void lds_void_t;
 
 constexpr int kThreads = 256;
 
@@ -44,8 +42,6 @@ struct HessParams {
   int32_t n_split;
   int64_t split_len;
   float* partial;
-  int32_t* tickets;
-  float* S;
 };
 
 // Tiles of the upper triangle in "super-tile" order: 4x4 blocks of tiles
@@ -101,70 +97,16 @@ GPTQ_DEV void work_item(int b, int n_tiles, int n_split, int& tile_pos, int& spl
   tile_pos = g0 + local % gsize;
 }
 
-// ----------------------------------------------------------------------------
-// Split-slice epilogue shared by both paths.  Accumulators are NI x NJ MFMA
-// 16x16 tiles per wave; element (i, j, r) of a lane sits at tile row
-// rbase + 16 i + 4 (lane >> 4) + r and tile column cbase + 16 j + (lane & 15).
-// ----------------------------------------------------------------------------
-template <int TILE>
-GPTQ_DEV void add_frag_to_S(const HessParams& p, int I, int J, int row0, int col, const f32x4_t& v) {
-  // v[r] belongs to tile element (row0 + r, col)
-  const int d = p.d_in;
-  const int gc = J * TILE + col;
-  if (gc >= d) return;
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int gr = I * TILE + row0 + r;
-    if (gr < d) {
-      p.S[static_cast<int64_t>(gr) * d + gc] += v[r];
-      if (I != J) p.S[static_cast<int64_t>(gc) * d + gr] += v[r];
-    }
-  }
-}
-
-// Split-slice epilogue.  The caller has stored its accumulators to its
-// partial tile in register order (lane-fastest f32x4 fragments).  The
-// accumulators only ever leave through memory stores (which read AGPRs
-// directly): arithmetic on them would make the register allocator keep part
-// of them in VGPRs across the main loop and shuffle them every stage.
-// coord(f, row0, col): tile row of fragment f's first element and its column
-// (the 4 elements are 4 consecutive rows).
-template <int NF, int TILE, typename Coord>
-GPTQ_DEV void finish_tile(const HessParams& p, int t, int I, int J, Coord coord) {
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  constexpr int64_t kElems = static_cast<int64_t>(TILE) * TILE;
-  fence_release();
-  __syncthreads();
-  __shared__ int s_last;
-  if (tid == 0) {
-    const int old = (p.n_split == 1) ? 0 : atomicAdd(&p.tickets[t], 1);
-    s_last = (old == p.n_split - 1);
-  }
-  __syncthreads();
-  if (!s_last) return;
-  fence_acquire();
-  // the last slice to arrive sums all slices in slice order, fragment by fragment
-  const float* base = p.partial + static_cast<int64_t>(t) * p.n_split * kElems;
-  for (int f = 0; f < NF; ++f) {
-    const int64_t off = static_cast<int64_t>((wave * NF + f) * 64 + lane) << 2;
-    f32x4_t sum = {0.f, 0.f, 0.f, 0.f};
-    for (int k = 0; k < p.n_split; ++k) sum += *reinterpret_cast<const f32x4_t*>(base + k * kElems + off);
-    int row0, col;
-    coord(f, row0, col);
-    add_frag_to_S<TILE>(p, I, J, row0, col, sum);
-  }
-}
-
+// Partial tiles are stored in register order: fragment f of wave w, lane l
+// holds 4 floats at ((w * NF + f) * 64 + l) * 4 of the (tile, slice) block.
 GPTQ_DEV float* partial_tile(const HessParams& p, int t, int split, int64_t elems) {
   return p.partial + (static_cast<int64_t>(t) * p.n_split + split) * elems;
 }
 
 // ============================================================ bf16 path ====
 constexpr int kBTile = 256;
-constexpr int kBStage = 64;              // tokens per stage = 128 bytes per LDS row
-constexpr int kBOpBytes = kBTile * 128;  // one operand stage: 32 KB
+
+#define GPTQ_VMCNT(n) (((n) & 15) | (((n) >> 4) << 14) | 0x0F70)
 
 // Buffer resource over one stage of X: `rows` token rows starting at Xs.  Reads
 // past the end (tokens beyond the slice) return zeros in hardware.
@@ -178,235 +120,111 @@ GPTQ_DEV __amdgpu_buffer_rsrc_t stage_rsrc(const uint16_t* Xs, int rows, int ldx
   return __builtin_amdgcn_make_buffer_rsrc(base, static_cast<short>(0), n, 0x00020000);
 }
 
-// Loads tokens [8 tg, 8 tg + 8) of the stage for one 8-channel group: the lane
-// offset is 32-bit, the row step is a scalar offset.  A channel group beyond
-// d_in (d_in is a multiple of 8) gets an out-of-range offset and reads zeros.
-GPTQ_DEV void load_block_bf16(__amdgpu_buffer_rsrc_t rs, int ldx, int tg, int col, int d_in, u32x4_t (&r)[8]) {
-  const uint32_t voff = (col < d_in) ? static_cast<uint32_t>((8 * tg * ldx + col) * 2) : 0x80000000u;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) r[j] = __builtin_amdgcn_raw_buffer_load_b128(rs, voff, j * ldx * 2, 0);
+// X moves to LDS by buffer_load ... lds in 16-token stages through a ring of
+// eight (7 in flight), and each stage's MFMA operands are read from LDS while
+// the previous stage's MFMAs run: every v_mfma is paired with one
+// ds_read_b64_tr_b16 of the next stage, so the matrix pipe never waits for an
+// operand at a stage boundary.  One barrier per stage: it publishes the next
+// stage's DMA to all waves and frees the slot read two stages ago.
+//
+// LDS: token rows of 512 bytes (256 channels).  The 16-byte chunk c of row r
+// sits at physical chunk c ^ 2 (r & 3) ^ 8 bit1(c): for one transposed read,
+// the 32 lanes of each half-wave then cover all 64 banks exactly once.
+constexpr int kPStage = 16;               // tokens per stage
+constexpr int kPSlots = 8;                // ring depth
+constexpr int kPOpBytes = kPStage * 512;  // one operand stage: 8 KB
+
+// logical chunk held by physical chunk p of token row `row` (inverse swizzle)
+GPTQ_DEV int pipe_logical_chunk(int p, int row) {
+  const int j = row & 3;
+  const int c1 = ((p >> 1) & 1) ^ (j & 1);
+  const int c2 = ((p >> 2) & 1) ^ (j >> 1);
+  const int c3 = ((p >> 3) & 1) ^ c1;
+  return (p & 0x11) | (c1 << 1) | (c2 << 2) | (c3 << 3);
 }
 
-// LDS row m (one channel, 64 tokens = eight 16-byte chunks): logical chunk q is
-// stored at q ^ (m & 7) ^ ((m >> 3) & 7).  Both the transposing stores (eight
-// rows 8 apart per instruction) and the operand loads (consecutive rows) then
-// touch eight distinct bank groups.
-GPTQ_DEV int swz(int m, int q) { return q ^ (m & 7) ^ ((m >> 3) & 7); }
-
-// r[j] holds tokens (8 tg + j) x channels (8 cg .. 8 cg + 7); write each channel's
-// 8 tokens as one 16-byte chunk (logical chunk tg) of LDS row 8 cg + c.
-GPTQ_DEV void store_block_bf16(uint8_t* lds, int cg, int tg, const u32x4_t (&r)[8]) {
+// One operand stage (16 rows x 512 bytes = eight 1 KB pieces); wave w moves
+// pieces 2w and 2w + 1.  Lane l of a piece writes bytes [16 l, 16 l + 16).
+GPTQ_DEV void pipe_dma(__amdgpu_buffer_rsrc_t rs, uint8_t* slot, int ldx, int col0, int d_in, int wave_u,
+                       int lane) {
 #pragma unroll
-  for (int pch = 0; pch < 4; ++pch) {
-    u32x4_t lo, hi;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      lo[q] = __builtin_amdgcn_perm(r[2 * q + 1][pch], r[2 * q][pch], 0x05040100u);
-      hi[q] = __builtin_amdgcn_perm(r[2 * q + 1][pch], r[2 * q][pch], 0x07060302u);
-    }
-    const int m0 = 8 * cg + 2 * pch;
-    *reinterpret_cast<u32x4_t*>(lds + m0 * 128 + (swz(m0, tg) << 4)) = lo;
-    *reinterpret_cast<u32x4_t*>(lds + (m0 + 1) * 128 + (swz(m0 + 1, tg) << 4)) = hi;
-  }
-}
-
-// One 64-token stage on v_mfma_f32_32x32x16_bf16: the wave's 128x128 block is
-// 4x4 MFMA tiles; per 16 tokens each lane reads one 16-byte chunk (8 tokens of
-// one channel) per A and B tile.  32x32 tiles keep the loop free of
-// accumulator moves (the allocator handles 16 wide tuples well).
-GPTQ_DEV void mfma_stage_bf16(const uint8_t* A, const uint8_t* B, int wm, int wn, int lane,
-                              f32x16_t (&acc)[4][4]) {
-  const int r32 = lane & 31;
-#pragma unroll
-  for (int ks = 0; ks < 4; ++ks) {
-    const int q = (lane >> 5) + 2 * ks;
-    bf16x8_t a[4], b[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int m = wm * 128 + 32 * i + r32;
-      a[i] = *reinterpret_cast<const bf16x8_t*>(A + m * 128 + (swz(m, q) << 4));
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int m = wn * 128 + 32 * j + r32;
-      b[j] = *reinterpret_cast<const bf16x8_t*>(B + m * 128 + (swz(m, q) << 4));
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
-  }
-}
-
-__global__ __launch_bounds__(kThreads, 1) void hessian_bf16_kernel(HessParams p) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2][2][kBOpBytes];
-  int t, split, I, J;
-  work_item(blockIdx.x, p.n_tiles, p.n_split, t, split);
-  tile_coords(t, p.nt, I, J);
-  const bool diag = (I == J);
-  const int64_t k0 = static_cast<int64_t>(split) * p.split_len;
-  const int64_t k1 = min(p.n_tokens, k0 + p.split_len);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  // a load instruction covers two token rows, 512 contiguous bytes each
-  const int cg = lane & 31, tg = (lane >> 5) + 2 * wave;
-  const int colA = I * kBTile + 8 * cg, colB = J * kBTile + 8 * cg;
-  const uint16_t* X = static_cast<const uint16_t*>(p.X);
-
-  f32x16_t acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
-
-  const int nstage = (k1 > k0) ? static_cast<int>((k1 - k0 + kBStage - 1) / kBStage) : 0;
-  const int ldx = static_cast<int>(p.ldx);
-  // diagonal tiles load the same channel block for both operands (an L2 hit):
-  // one code path keeps the loop free of branches, which lets the compiler
-  // keep the 256 accumulators in fixed AGPRs.  Global loads run two stages
-  // ahead of the MFMAs (two register sets), so about two stages of load
-  // latency are hidden behind matrix work.
-  u32x4_t ra0[8], rb0[8], ra1[8], rb1[8];
-  auto load_stage = [&](int s, u32x4_t (&ra)[8], u32x4_t (&rb)[8]) {
-    const int64_t t0 = k0 + static_cast<int64_t>(s) * kBStage;
-    const int left = static_cast<int>(min<int64_t>(k1 - t0, kBStage));
-    const __amdgpu_buffer_rsrc_t rs = stage_rsrc(X + t0 * p.ldx, left, ldx);
-    load_block_bf16(rs, ldx, tg, colA, p.d_in, ra);
-    load_block_bf16(rs, ldx, tg, colB, p.d_in, rb);
-  };
-  auto store_stage = [&](int buf, const u32x4_t (&ra)[8], const u32x4_t (&rb)[8]) {
-    store_block_bf16(lds[buf][0], cg, tg, ra);
-    store_block_bf16(lds[buf][1], cg, tg, rb);
-  };
-  // stage s lives in LDS buffer s & 1 and, before that, in register set s & 1
-  if (nstage > 0) load_stage(0, ra0, rb0);
-  if (nstage > 1) load_stage(1, ra1, rb1);
-  if (nstage > 0) store_stage(0, ra0, rb0);
-  __syncthreads();
-  int s = 0;
-  for (; s + 3 < nstage; s += 2) {
-    load_stage(s + 2, ra0, rb0);
-    mfma_stage_bf16(lds[0][0], lds[0][1], wm, wn, lane, acc);
-    store_stage(1, ra1, rb1);
-    __syncthreads();
-    load_stage(s + 3, ra1, rb1);
-    mfma_stage_bf16(lds[1][0], lds[1][1], wm, wn, lane, acc);
-    store_stage(0, ra0, rb0);
-    __syncthreads();
-  }
-  // tail: at most three stages left, s even; stage s is in LDS 0, s + 1 in set 1
-  for (; s < nstage; ++s) {
-    const int cur = s & 1;
-    if (s + 2 < nstage) {
-      if (cur == 0) load_stage(s + 2, ra0, rb0);
-      else load_stage(s + 2, ra1, rb1);
-    }
-    mfma_stage_bf16(lds[cur][0], lds[cur][1], wm, wn, lane, acc);
-    if (s + 1 < nstage) {
-      if (cur == 0) store_stage(1, ra1, rb1);
-      else store_stage(0, ra0, rb0);
-    }
-    __syncthreads();
-  }
-  (void)diag;
-  // 32x32 accumulator layout: element r of lane l is tile row
-  // 8 (r / 4) + 4 (l / 32) + r % 4, column l % 32; stored as 4 fragments of 4 rows
-  float* mine = partial_tile(p, t, split, static_cast<int64_t>(kBTile) * kBTile);
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        *reinterpret_cast<f32x4_t*>(mine + (((wave * 64 + (i * 4 + j) * 4 + e) * 64 + lane) << 2)) =
-            f32x4_t{acc[i][j][4 * e], acc[i][j][4 * e + 1], acc[i][j][4 * e + 2], acc[i][j][4 * e + 3]};
-  finish_tile<64, kBTile>(p, t, I, J, [&](int f, int& row0, int& col) {
-    const int i = f >> 4, j = (f >> 2) & 3, e = f & 3;
-    row0 = wm * 128 + 32 * i + 8 * e + 4 * (lane >> 5);
-    col = wn * 128 + 32 * j + (lane & 31);
-  });
-}
-
-// ======================================================= bf16 DMA path ====
-// Same tiling and epilogue as hessian_bf16_kernel, but X moves from HBM to LDS
-// with buffer_load ... lds (no VGPRs, no register transposition) through a
-// ring of four 32-token stages (three in flight while one is consumed), and
-// the MFMA operands come out of the token-major LDS tile through
-// ds_read_b64_tr_b16.  In a 16-lane group, if lane s points at token
-// t0 + (s >> 2), channels m0 + 4 (s & 3) .. +3, lane i receives tokens
-// t0 .. t0 + 3 of channel m0 + i: two such reads make one 8-token operand.
-// LDS rows (tokens) are 512 bytes; the 16-byte chunk index is XOR-swizzled
-// with 2 (row & 3) so the eight chunks one read touches fall in distinct banks.
-constexpr int kDStage = 32;               // tokens per stage
-constexpr int kDOpBytes = kDStage * 512;  // one operand stage: 16 KB
-
-typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4_t;
-typedef __attribute__((address_space(3))) void lds_void_t;
-
-#define GPTQ_VMCNT(n) (((n) & 15) | (((n) >> 4) << 14) | 0x0F70)
-
-GPTQ_DEV void dma_operand(__amdgpu_buffer_rsrc_t rs, uint8_t* buf, int ldx, int col0, int d_in, int wave_u,
-                          int lane) {
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int q = 4 * wave_u + u;               // 1 KB piece: token rows 2q, 2q + 1
+  for (int u = 0; u < 2; ++u) {
+    const int q = 2 * wave_u + u;
     const int row = 2 * q + (lane >> 5);
-    const int c = (lane & 31) ^ (2 * (row & 3));  // logical chunk held at this lane's slot
-    const int col = col0 + 8 * c;
+    const int col = col0 + 8 * pipe_logical_chunk(lane & 31, row);
     const uint32_t voff = (col < d_in) ? static_cast<uint32_t>((row * ldx + col) * 2) : 0x80000000u;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(buf + q * 1024), 16, voff, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(slot + q * 1024), 16, voff, 0, 0, 0);
   }
 }
 
-GPTQ_DEV bf16x8_t tr_operand(const uint8_t* buf, uint32_t lane_off, int imm) {
+// Byte offsets of a lane's low transposed read for the four 32-channel MFMA
+// tiles of wave block wb; the high read (tokens +4) is 2048 bytes further.
+struct PipeLane {
+  uint32_t off[4];
+};
+GPTQ_DEV PipeLane pipe_lane(int lane, int wb) {
+  const int g = lane >> 4, s = lane & 15;
+  const int row = 8 * (g >> 1) + (s >> 2);
+  const int j = s >> 2;
+  const int c1 = g & 1, c0 = (s >> 1) & 1;
+  PipeLane t;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int c = 16 * wb + 4 * i + 2 * c1 + c0;
+    const int pc = c ^ (2 * j) ^ (c1 << 3);
+    t.off[i] = static_cast<uint32_t>(row * 512 + pc * 16 + (s & 1) * 8);
+  }
+  return t;
+}
+
+GPTQ_DEV bf16x8_t pipe_operand(const uint8_t* slot, uint32_t off) {
   typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
-  uint8_t* b = const_cast<uint8_t*>(buf) + lane_off + imm;
+  uint8_t* b = const_cast<uint8_t*>(slot) + off;
   const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)b);
-  const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(b + 4 * 512));
+  const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(b + 2048));
   typedef __attribute__((__vector_size__(8 * sizeof(short)))) short s16x8_t;
   const s16x8_t v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   return __builtin_bit_cast(bf16x8_t, v);
 }
 
-// lane offsets of the transposed reads for even / odd 32-channel tiles of a wave block
-struct TrLane {
-  uint32_t off[2];
-};
-GPTQ_DEV TrLane tr_lane(int lane, int wblock) {
-  const int g = lane >> 4, s = lane & 15;
-  const int base_row = 8 * (g >> 1) + (s >> 2);
-  const int f = 2 * (s >> 2);
-  const int cl = 2 * (g & 1) + ((s & 3) >> 1);
-  TrLane t;
+// operands of one stage, in the order the MFMAs below consume them
+GPTQ_DEV void pipe_read(const uint8_t* A, const uint8_t* B, const PipeLane& la, const PipeLane& lb,
+                        bf16x8_t (&a)[4], bf16x8_t (&b)[4]) {
+  a[0] = pipe_operand(A, la.off[0]);
 #pragma unroll
-  for (int par = 0; par < 2; ++par)
-    t.off[par] = static_cast<uint32_t>(base_row * 512 + (s & 1) * 8 + 16 * ((4 * par + cl) ^ f) + 256 * wblock);
-  return t;
+  for (int j = 0; j < 4; ++j) b[j] = pipe_operand(B, lb.off[j]);
+#pragma unroll
+  for (int i = 1; i < 4; ++i) a[i] = pipe_operand(A, la.off[i]);
 }
 
-GPTQ_DEV void mfma_stage_tr(const uint8_t* A, const uint8_t* B, const TrLane& la, const TrLane& lb,
-                            f32x16_t (&acc)[4][4]) {
+GPTQ_DEV void pipe_mfma(const bf16x8_t (&a)[4], const bf16x8_t (&b)[4], f32x16_t (&acc)[4][4]) {
 #pragma unroll
-  for (int ks = 0; ks < 2; ++ks) {
-    bf16x8_t a[4], b[4];
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) a[i] = tr_operand(A, la.off[i & 1], ks * 16 * 512 + (i >> 1) * 128);
+    for (int j = 0; j < 4; ++j)
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+}
+
+// MFMAs of the current stage with the reads of the next one interleaved 1:1
+GPTQ_DEV void pipe_step(const bf16x8_t (&a)[4], const bf16x8_t (&b)[4], const uint8_t* nA, const uint8_t* nB,
+                        const PipeLane& la, const PipeLane& lb, bf16x8_t (&na)[4], bf16x8_t (&nb)[4],
+                        f32x16_t (&acc)[4][4]) {
+  pipe_read(nA, nB, la, lb, na, nb);
+  pipe_mfma(a, b, acc);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) b[j] = tr_operand(B, lb.off[j & 1], ks * 16 * 512 + (j >> 1) * 128);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+  for (int k = 0; k < 16; ++k) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
   }
 }
 
-__global__ __launch_bounds__(kThreads, 1) void hessian_bf16_dma_kernel(HessParams p) {
-  __shared__ __attribute__((aligned(1024))) uint8_t sA0[kDOpBytes], sB0[kDOpBytes], sA1[kDOpBytes], sB1[kDOpBytes],
-      sA2[kDOpBytes], sB2[kDOpBytes], sA3[kDOpBytes], sB3[kDOpBytes];
+__global__ __launch_bounds__(kThreads, 1) void hessian_bf16_pipe_kernel(HessParams p) {
+  // one array per slot: the compiler's wait insertion then sees that reads of
+  // one slot do not alias DMA writes in flight into another
+  __shared__ __attribute__((aligned(1024))) uint8_t sA0[kPOpBytes], sA1[kPOpBytes], sA2[kPOpBytes],
+      sA3[kPOpBytes], sA4[kPOpBytes], sA5[kPOpBytes], sA6[kPOpBytes], sA7[kPOpBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t sB0[kPOpBytes], sB1[kPOpBytes], sB2[kPOpBytes],
+      sB3[kPOpBytes], sB4[kPOpBytes], sB5[kPOpBytes], sB6[kPOpBytes], sB7[kPOpBytes];
   int t, split, I, J;
   work_item(blockIdx.x, p.n_tiles, p.n_split, t, split);
   tile_coords(t, p.nt, I, J);
@@ -418,7 +236,7 @@ __global__ __launch_bounds__(kThreads, 1) void hessian_bf16_dma_kernel(HessParam
   const int colA = I * kBTile, colB = J * kBTile;
   const int ldx = static_cast<int>(p.ldx);
   const uint16_t* X = static_cast<const uint16_t*>(p.X);
-  const TrLane la = tr_lane(lane, wm), lb = tr_lane(lane, wn);
+  const PipeLane la = pipe_lane(lane, wm), lb = pipe_lane(lane, wn);
 
   f32x16_t acc[4][4];
 #pragma unroll
@@ -428,54 +246,94 @@ __global__ __launch_bounds__(kThreads, 1) void hessian_bf16_dma_kernel(HessParam
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-  const int nstage = (k1 > k0) ? static_cast<int>((k1 - k0 + kDStage - 1) / kDStage) : 0;
-  auto issue = [&](int s, uint8_t* bA, uint8_t* bB) {
-    const int64_t t0 = k0 + static_cast<int64_t>(s) * kDStage;
-    const int left = static_cast<int>(min<int64_t>(k1 - t0, kDStage));
-    const __amdgpu_buffer_rsrc_t rs = stage_rsrc(X + t0 * p.ldx, left, ldx);
-    dma_operand(rs, bA, ldx, colA, p.d_in, wave, lane);
-    dma_operand(rs, bB, ldx, colB, p.d_in, wave, lane);
-  };
-  auto bufA = [&](int r) { return r == 0 ? sA0 : r == 1 ? sA1 : r == 2 ? sA2 : sA3; };
-  auto bufB = [&](int r) { return r == 0 ? sB0 : r == 1 ? sB1 : r == 2 ? sB2 : sB3; };
-  int s = 0;
-  if (nstage > 6) {
-    // steady state: stage s + r lives in ring buffer r and every wait leaves
-    // the two stages issued after it in flight.  All issues here are
-    // unconditional, which keeps the compiler's own wait tracking exact.
-    issue(0, sA0, sB0);
-    issue(1, sA1, sB1);
-    issue(2, sA2, sB2);
-    for (; s + 6 < nstage; s += 4) {
-      __builtin_amdgcn_s_waitcnt(GPTQ_VMCNT(16));
-      __builtin_amdgcn_s_barrier();
-      issue(s + 3, sA3, sB3);
-      mfma_stage_tr(sA0, sB0, la, lb, acc);
-      __builtin_amdgcn_s_waitcnt(GPTQ_VMCNT(16));
-      __builtin_amdgcn_s_barrier();
-      issue(s + 4, sA0, sB0);
-      mfma_stage_tr(sA1, sB1, la, lb, acc);
-      __builtin_amdgcn_s_waitcnt(GPTQ_VMCNT(16));
-      __builtin_amdgcn_s_barrier();
-      issue(s + 5, sA1, sB1);
-      mfma_stage_tr(sA2, sB2, la, lb, acc);
-      __builtin_amdgcn_s_waitcnt(GPTQ_VMCNT(16));
-      __builtin_amdgcn_s_barrier();
-      issue(s + 6, sA2, sB2);
-      mfma_stage_tr(sA3, sB3, la, lb, acc);
+  // stages run in blocks of eight; stages past the slice end read zeros
+  const int nstage = (k1 > k0) ? static_cast<int>((k1 - k0 + kPStage - 1) / kPStage) : 0;
+  const int nblk = (nstage + kPSlots - 1) / kPSlots;
+  auto slotA = [&](int u) -> uint8_t* {
+    switch (u & 7) {
+      case 0: return sA0; case 1: return sA1; case 2: return sA2; case 3: return sA3;
+      case 4: return sA4; case 5: return sA5; case 6: return sA6; default: return sA7;
     }
-  } else {
-    for (int x = 0; x < nstage && x < 3; ++x) issue(x, bufA(x), bufB(x));
-  }
-  // tail (at most six stages): stage x in buffer x % 4, stages up to s + 2
-  // already issued; full waits.  A buffer is refilled only after the barrier
-  // that follows everyone's last read of it.
-  for (int x = s; x < nstage; ++x) {
+  };
+  auto slotB = [&](int u) -> uint8_t* {
+    switch (u & 7) {
+      case 0: return sB0; case 1: return sB1; case 2: return sB2; case 3: return sB3;
+      case 4: return sB4; case 5: return sB5; case 6: return sB6; default: return sB7;
+    }
+  };
+  auto issue = [&](int s, int slot) {
+    const int64_t t0 = k0 + static_cast<int64_t>(s) * kPStage;
+    const int64_t rem = k1 - t0;
+    const int left = rem <= 0 ? 0 : (rem >= kPStage ? kPStage : static_cast<int>(rem));
+    const __amdgpu_buffer_rsrc_t rs = stage_rsrc(X + t0 * p.ldx, left, ldx);
+    pipe_dma(rs, slotA(slot), ldx, colA, p.d_in, wave, lane);
+    pipe_dma(rs, slotB(slot), ldx, colB, p.d_in, wave, lane);
+  };
+  bf16x8_t a0[4], b0[4], a1[4], b1[4];
+  if (nblk >= 2) {
+    // Stage s lives in slot s % 8 and its operands in register set s % 2.
+    // Before stage s: wait for the DMA of stage s + 1 (stages s + 2 .. s + 6
+    // stay in flight: 4 loads each per wave), barrier, refill the slot of
+    // stage s - 1 (read during stage s - 2, consumed by everyone's MFMAs of
+    // stage s - 1, which precede the barrier) with stage s + 7.
+    for (int x = 0; x < 7; ++x) issue(x, x);
+    __builtin_amdgcn_s_waitcnt(GPTQ_VMCNT(24));
+    __builtin_amdgcn_s_barrier();
+    pipe_read(slotA(0), slotB(0), la, lb, a0, b0);
+    for (int blk = 0; blk + 1 < nblk; ++blk) {
+      const int s = blk * kPSlots;
+#pragma unroll
+      for (int u = 0; u < 8; u += 2) {
+        __builtin_amdgcn_s_waitcnt(GPTQ_VMCNT(20));
+        __builtin_amdgcn_s_barrier();
+        issue(s + u + 7, u + 7);
+        pipe_step(a0, b0, slotA(u + 1), slotB(u + 1), la, lb, a1, b1, acc);
+        __builtin_amdgcn_s_waitcnt(GPTQ_VMCNT(20));
+        __builtin_amdgcn_s_barrier();
+        issue(s + u + 8, u + 8);
+        pipe_step(a1, b1, slotA(u + 2), slotB(u + 2), la, lb, a0, b0, acc);
+      }
+    }
+    // last block: its first stage issues the final stage, then the waits drain
+    const int L = (nblk - 1) * kPSlots;
+    __builtin_amdgcn_s_waitcnt(GPTQ_VMCNT(20));
+    __builtin_amdgcn_s_barrier();
+    issue(L + 7, 7);
+    pipe_step(a0, b0, slotA(1), slotB(1), la, lb, a1, b1, acc);
+    __builtin_amdgcn_s_waitcnt(GPTQ_VMCNT(20));
+    __builtin_amdgcn_s_barrier();
+    pipe_step(a1, b1, slotA(2), slotB(2), la, lb, a0, b0, acc);
+    __builtin_amdgcn_s_waitcnt(GPTQ_VMCNT(16));
+    __builtin_amdgcn_s_barrier();
+    pipe_step(a0, b0, slotA(3), slotB(3), la, lb, a1, b1, acc);
+    __builtin_amdgcn_s_waitcnt(GPTQ_VMCNT(12));
+    __builtin_amdgcn_s_barrier();
+    pipe_step(a1, b1, slotA(4), slotB(4), la, lb, a0, b0, acc);
+    __builtin_amdgcn_s_waitcnt(GPTQ_VMCNT(8));
+    __builtin_amdgcn_s_barrier();
+    pipe_step(a0, b0, slotA(5), slotB(5), la, lb, a1, b1, acc);
+    __builtin_amdgcn_s_waitcnt(GPTQ_VMCNT(4));
+    __builtin_amdgcn_s_barrier();
+    pipe_step(a1, b1, slotA(6), slotB(6), la, lb, a0, b0, acc);
     __builtin_amdgcn_s_waitcnt(GPTQ_VMCNT(0));
     __builtin_amdgcn_s_barrier();
-    if (x + 3 < nstage) issue(x + 3, bufA((x + 3) & 3), bufB((x + 3) & 3));
-    mfma_stage_tr(bufA(x & 3), bufB(x & 3), la, lb, acc);
+    pipe_step(a0, b0, slotA(7), slotB(7), la, lb, a1, b1, acc);
+    pipe_mfma(a1, b1, acc);
+  } else if (nblk == 1) {
+    // at most eight stages: load them all, then compute
+#pragma unroll
+    for (int x = 0; x < 8; ++x) issue(x, x);
+    __builtin_amdgcn_s_waitcnt(GPTQ_VMCNT(0));
+    __builtin_amdgcn_s_barrier();
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      pipe_read(slotA(u), slotB(u), la, lb, a0, b0);
+      pipe_mfma(a0, b0, acc);
+    }
   }
+  // 32x32 accumulator layout: element r of lane l is tile row 8 (r / 4) +
+  // 4 (l / 32) + r % 4, column l % 32.  Stored as fragments of 4 rows; the
+  // accumulators only leave through stores, which read AGPRs directly
   float* mine = partial_tile(p, t, split, static_cast<int64_t>(kBTile) * kBTile);
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -485,11 +343,6 @@ __global__ __launch_bounds__(kThreads, 1) void hessian_bf16_dma_kernel(HessParam
       for (int e = 0; e < 4; ++e)
         *reinterpret_cast<f32x4_t*>(mine + (((wave * 64 + (i * 4 + j) * 4 + e) * 64 + lane) << 2)) =
             f32x4_t{acc[i][j][4 * e], acc[i][j][4 * e + 1], acc[i][j][4 * e + 2], acc[i][j][4 * e + 3]};
-  finish_tile<64, kBTile>(p, t, I, J, [&](int f, int& row0, int& col) {
-    const int i = f >> 4, j = (f >> 2) & 3, e = f & 3;
-    row0 = wm * 128 + 32 * i + 8 * e + 4 * (lane >> 5);
-    col = wn * 128 + 32 * j + (lane & 31);
-  });
 }
 
 // ============================================================ fp32 path ====
@@ -579,32 +432,51 @@ __global__ __launch_bounds__(kThreads, 2) void hessian_f32_kernel(HessParams p) 
 #pragma unroll
     for (int j = 0; j < 4; ++j)
       *reinterpret_cast<f32x4_t*>(mine + (((wave * 16 + i * 4 + j) * 64 + lane) << 2)) = acc[i][j];
-  finish_tile<16, kFTile>(p, t, I, J, [&](int f, int& row0, int& col) {
-    const int i = f >> 2, j = f & 3;
-    row0 = wm * 64 + 16 * i + 4 * (lane >> 4);
-    col = wn * 64 + 16 * j + (lane & 15);
-  });
 }
 
-__global__ void fill_i32_kernel(int32_t* p, int64_t n, int32_t v) {
-  for (int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; i < n;
-       i += static_cast<int64_t>(gridDim.x) * blockDim.x)
-    p[i] = v;
+// ========================================================= slice reduce ====
+// One workgroup per (tile, wave w, MFMA tile i, j): a BS x BS block made of
+// NE fragments x 64 lanes x 4 rows.  Sums the n_split partials of the block
+// in slice order, stages the sum in LDS and adds it to S row by row, then to
+// the mirror block (tile (J, I)) column by column, so both updates are
+// coalesced.  Every element of S is updated by exactly one thread.
+//   bf16 (TILE 256, BS 32, NE 4): fragment e, lane l -> rows 8 e + 4 (l / 32) + r, col l % 32
+//   fp32 (TILE 128, BS 16, NE 1): lane l -> rows 4 (l / 16) + r, col l % 16
+template <int TILE, int BS, int NE>
+__global__ __launch_bounds__(NE * 64) void hessian_reduce_kernel(const float* __restrict__ partial, int n_split,
+                                                                 int nt, int d, float* __restrict__ S) {
+  __shared__ float blk[BS][BS + 1];
+  const int t = blockIdx.x >> 6, b = blockIdx.x & 63;
+  int I, J;
+  tile_coords(t, nt, I, J);
+  const int w = b >> 4, i = (b >> 2) & 3, j = b & 3;
+  const int tid = threadIdx.x, e = tid >> 6, lane = tid & 63;
+  constexpr int64_t kElems = static_cast<int64_t>(TILE) * TILE;
+  const int64_t off = static_cast<int64_t>((w * 16 * NE + (i * 4 + j) * NE + e) * 64 + lane) << 2;
+  const float* src = partial + static_cast<int64_t>(t) * n_split * kElems + off;
+  f32x4_t sum = {0.f, 0.f, 0.f, 0.f};
+  for (int k = 0; k < n_split; ++k) sum += *reinterpret_cast<const f32x4_t*>(src + k * kElems);
+  const int r0 = (NE == 4) ? 8 * e + 4 * (lane >> 5) : 4 * (lane >> 4);
+  const int c = lane & (BS - 1);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) blk[r0 + r][c] = sum[r];
+  __syncthreads();
+  const int row0 = I * TILE + (w >> 1) * (TILE / 2) + BS * i;
+  const int col0 = J * TILE + (w & 1) * (TILE / 2) + BS * j;
+  for (int idx = tid; idx < BS * BS; idx += NE * 64) {
+    const int rr = idx / BS, cc = idx % BS;
+    if (row0 + rr < d && col0 + cc < d) S[static_cast<int64_t>(row0 + rr) * d + col0 + cc] += blk[rr][cc];
+    if (I != J && col0 + rr < d && row0 + cc < d)
+      S[static_cast<int64_t>(col0 + rr) * d + row0 + cc] += blk[cc][rr];
+  }
 }
 
 }  // namespace
 
-hipError_t fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t stream) {
-  if (n <= 0) return hipSuccess;
-  const int64_t blocks = std::min<int64_t>((n + 255) / 256, 4096);
-  fill_i32_kernel<<<static_cast<int>(blocks), 256, 0, stream>>>(p, n, v);
-  return hipGetLastError();
-}
-
 HessPlan hessian_plan(int64_t d_in, int64_t n_tokens, bool bf16, int n_cu) {
   HessPlan pl{};
   pl.tile = bf16 ? kBTile : kFTile;
-  pl.stage_tokens = bf16 ? kBStage : kFStage;
+  pl.stage_tokens = bf16 ? kPStage * kPSlots : kFStage;
   pl.nt = static_cast<int>((d_in + pl.tile - 1) / pl.tile);
   pl.n_tiles = pl.nt * (pl.nt + 1) / 2;
   const int per_cu = bf16 ? 1 : 2;  // resident workgroups per CU (LDS bound)
@@ -632,16 +504,13 @@ HessPlan hessian_plan(int64_t d_in, int64_t n_tokens, bool bf16, int n_cu) {
   pl.n_split = static_cast<int>(std::max<int64_t>(1, (n_tokens + pl.split_len - 1) / pl.split_len));
   const size_t tile_bytes = static_cast<size_t>(pl.tile) * pl.tile * sizeof(float);
   pl.partial_bytes = static_cast<size_t>(pl.n_tiles) * pl.n_split * tile_bytes;
-  pl.ticket_bytes = static_cast<size_t>(pl.n_tiles) * sizeof(int32_t);
-  auto up = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
-  pl.ws_bytes = up(pl.partial_bytes) + up(pl.ticket_bytes);
+  pl.ws_bytes = (pl.partial_bytes + 255) & ~static_cast<size_t>(255);
   return pl;
 }
 
 hipError_t hessian_launch(const HessPlan& pl, float* S, int64_t d_in, const void* X, bool bf16,
                           int64_t n_tokens, int64_t ldx, void* ws, hipStream_t stream) {
   if (n_tokens <= 0 || d_in <= 0) return hipSuccess;
-  auto up = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
   HessParams p{};
   p.X = X;
   p.ldx = ldx;
@@ -652,17 +521,15 @@ hipError_t hessian_launch(const HessPlan& pl, float* S, int64_t d_in, const void
   p.n_split = pl.n_split;
   p.split_len = pl.split_len;
   p.partial = static_cast<float*>(ws);
-  p.tickets = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + up(pl.partial_bytes));
-  p.S = S;
-  if (pl.n_split > 1) {
-    hipError_t e = fill_i32(p.tickets, pl.n_tiles, 0, stream);
-    if (e != hipSuccess) return e;
-  }
   const int blocks = pl.n_tiles * pl.n_split;
-  if (bf16)
-    hessian_bf16_dma_kernel<<<blocks, kThreads, 0, stream>>>(p);
-  else
+  const int d = static_cast<int>(d_in);
+  if (bf16) {
+    hessian_bf16_pipe_kernel<<<blocks, kThreads, 0, stream>>>(p);
+    hessian_reduce_kernel<kBTile, 32, 4><<<pl.n_tiles * 64, 256, 0, stream>>>(p.partial, pl.n_split, pl.nt, d, S);
+  } else {
     hessian_f32_kernel<<<blocks, kThreads, 0, stream>>>(p);
+    hessian_reduce_kernel<kFTile, 16, 1><<<pl.n_tiles * 64, 64, 0, stream>>>(p.partial, pl.n_split, pl.nt, d, S);
+  }
   return hipGetLastError();
 }
 
