@@ -5,18 +5,25 @@
 // Cholesky trailing update, the triangular inverse and the GPTQ lazy-batch
 // update W[:, j+B:] -= Err * U[j:j+B, j+B:] (GPTQ 实战 ch.5, section 5.1.8).
 //
-// 64x64 or 128x128 output tile per 256-thread workgroup (2x2 waves), k-stage
-// of 16.  LDS holds both operands k-major ([k][m] and [k][n]); stages are
-// double-buffered with the next stage's global loads in registers.
+// 64x64 or 128x128 output tile per 256-thread workgroup (2x2 waves), 32-k
+// stages moved HBM -> LDS by buffer_load ... lds through a ring of three (two
+// in flight).
 // Requirements (checked by the callers): K, N, lda, ldb, ldc multiples of 4 and
-// 16-byte aligned base pointers; M arbitrary.
+// 16-byte aligned base pointers; M arbitrary.  `tri` marks a lower-triangular
+// operand (B, or A) whose zero part a tile's K range skips: the triangular
+// inverse multiplies by inverted diagonal blocks.
 #include "gptq_common.h"
 #include "gptq_internal.h"
 
 namespace gptq {
 namespace {
 
-constexpr int kBK = 16;
+constexpr int kBK = 32;  // k per stage
+constexpr int kSlots = 3;
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+#define GPTQ_VMCNT(n) (((n) & 15) | (((n) >> 4) << 14) | 0x0F70)
 
 struct GemmParams {
   int64_t M, N, K;
@@ -28,126 +35,281 @@ struct GemmParams {
   float* C;
   int64_t ldc, sC;
   int lower_tiles;
+  int tri;  // 0: dense; 1: B lower-triangular (k >= n0); 2: A lower-triangular (k < m0 + T)
+  int tiles_m, tiles_n, tiles;  // tile grid; tiles per batch entry
+  int batch;
 };
 
-// BM x BN output tile, 2x2 waves of (BM/2) x (BN/2), MFMA 16x16x4.  LDS rows
-// hold BM (or BN) floats plus 16 of padding, so the four k-rows one operand
-// load touches fall in distinct bank groups.
-template <bool TRANS_B, int BM, int BN>
-__global__ __launch_bounds__(256, 2) void gemm_f32_kernel(GemmParams p) {
-  constexpr int PA = BM + 16, PB = BN + 16;
-  constexpr int NI = BM / 32, NJ = BN / 32;       // 16x16 tiles per wave
-  constexpr int LA = BM * kBK / 4 / 256;           // float4 loads per thread (A)
-  constexpr int LB = BN * kBK / 4 / 256;           // float4 loads per thread (B)
-  __shared__ __attribute__((aligned(16))) float As[2][kBK * PA];
-  __shared__ __attribute__((aligned(16))) float Bs[2][kBK * PB];
-  const int64_t m0 = static_cast<int64_t>(blockIdx.y) * BM;
-  const int64_t n0 = static_cast<int64_t>(blockIdx.x) * BN;
-  if (m0 >= p.M) return;
-  if (p.lower_tiles && n0 > m0 + BM - 1) return;
-  const float* A = p.A + blockIdx.z * p.sA;
-  const float* B = p.B + blockIdx.z * p.sB;
-  float* C = p.C + blockIdx.z * p.sC;
+// Tile of workgroup b.  Workgroups go round-robin to the 8 XCDs (b % 8), each
+// with its own L2: the tile list is cut into 8 contiguous ranges, one per XCD.
+// Dense tiles are listed in groups of 8 tile rows, column by column inside a
+// group, so the tiles an XCD runs at once share rows of A and columns of B.
+// Lower-tile problems list the tiles (i >= j) row by row.  Triangular
+// operands make tiles unequal: they are listed heaviest first.
+GPTQ_DEV bool gemm_tile(const GemmParams& p, int b, int& z, int& tm, int& tn) {
+  constexpr int kXcd = 8;
+  const int G = p.tiles * p.batch;
+  const int x = b % kXcd, l = b / kXcd;
+  const int base = G / kXcd, rem = G % kXcd;
+  const int q = x * base + min(x, rem) + l;
+  if (l >= base + (x < rem ? 1 : 0)) return false;
+  z = q / p.tiles;
+  const int t = q - z * p.tiles;
+  if (p.lower_tiles) {
+    int i = static_cast<int>((__builtin_sqrtf(8.f * t + 1.f) - 1.f) * 0.5f);
+    while (i * (i + 1) / 2 > t) --i;
+    while ((i + 1) * (i + 2) / 2 <= t) ++i;
+    tm = i;
+    tn = t - i * (i + 1) / 2;
+  } else if (p.tri == 2) {
+    // A lower-triangular: the work of a tile grows with its row, so list
+    // groups of 8 tile columns (one per XCD range) with the heaviest rows first
+    const int g = t / (8 * p.tiles_m);
+    const int cols = min(8, p.tiles_n - 8 * g);
+    const int idx = t - g * 8 * p.tiles_m;
+    tm = p.tiles_m - 1 - idx / cols;
+    tn = 8 * g + idx % cols;
+  } else {
+    // (with B lower-triangular the work falls with the column: heaviest first)
+    const int g = t / (8 * p.tiles_n);
+    const int rows = min(8, p.tiles_m - 8 * g);
+    const int idx = t - g * 8 * p.tiles_n;
+    tn = idx / rows;
+    tm = 8 * g + idx % rows;
+  }
+  return true;
+}
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+// Buffer resource over `bytes` bytes at `base`; reads past the end return
+// zeros in hardware.  Every field is workgroup-uniform.
+GPTQ_DEV __amdgpu_buffer_rsrc_t gemm_rsrc(const float* base, int64_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a >> 32));
+  const int64_t cl = bytes < 0 ? 0 : (bytes > 0x7FFFFFF0LL ? 0x7FFFFFF0LL : bytes);
+  const int n = __builtin_amdgcn_readfirstlane(static_cast<int>(cl));
+  void* b = reinterpret_cast<void*>((static_cast<uint64_t>(hi) << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(b, static_cast<short>(0), n, 0x00020000);
+}
+
+// k-major operand stage (rows of A, or of B given as [N, K]): T rows x 32 k,
+// 128-byte LDS rows; physical 16-byte chunk p of row r holds logical chunk
+// p ^ ((r >> 1) & 7), which makes the MFMA operand reads (16 rows x 4 k per
+// instruction) cover all 64 banks.  1 KB pieces of 8 rows, T / 32 per wave;
+// chunks at or past ke read zeros.
+template <int T>
+GPTQ_DEV void dma_kmajor(__amdgpu_buffer_rsrc_t rs, uint8_t* slot, int64_t ld, int64_t k0, int64_t ke, int wave,
+                         int lane) {
+#pragma unroll
+  for (int u = 0; u < T / 32; ++u) {
+    const int q = (T / 32) * wave + u;
+    const int r = 8 * q + (lane >> 3);
+    const int c = (lane & 7) ^ ((r >> 1) & 7);
+    const int64_t k = k0 + 4 * c;
+    const uint32_t voff = (k < ke) ? static_cast<uint32_t>((r * ld + k) * 4) : 0x80000000u;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(slot + q * 1024), 16, voff, 0, 0, 0);
+  }
+}
+
+// row-major B stage ([K, N]): 32 k-rows x T n, 4T-byte LDS rows; physical
+// chunk p of k-row r holds logical chunk p ^ (4 (r & 3)).  rs starts at k-row
+// k0 of the stage and column 0; columns at or past N read zeros.
+template <int T>
+GPTQ_DEV void dma_nmajor(__amdgpu_buffer_rsrc_t rs, uint8_t* slot, int64_t ld, int64_t n0, int64_t N, int wave,
+                         int lane) {
+  constexpr int kRowsPerPiece = 1024 / (4 * T);  // 4 (T = 64) or 2 (T = 128)
+  constexpr int kChunks = T / 4;                 // 16-byte chunks per row
+#pragma unroll
+  for (int u = 0; u < T / 32; ++u) {
+    const int q = (T / 32) * wave + u;
+    const int r = kRowsPerPiece * q + lane / kChunks;
+    const int c = (lane % kChunks) ^ (4 * (r & 3));
+    const int64_t n = n0 + 4 * c;
+    const uint32_t voff = (n < N) ? static_cast<uint32_t>((r * ld + n) * 4) : 0x80000000u;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(slot + q * 1024), 16, voff, 0, 0, 0);
+  }
+}
+
+GPTQ_DEV float lds_f32(const uint8_t* base, uint32_t off) {
+  return *reinterpret_cast<const float*>(base + off);
+}
+
+// T x T output tile (T = 64 or 128), 2x2 waves of (T/2) x (T/2) on
+// v_mfma_f32_16x16x4_f32.  The operands stream through a ring of three 32-k
+// stages (two in flight), one LDS array per slot so the compiler's wait
+// insertion sees no false aliasing.
+template <bool TRANS_B, int T>
+__global__ __launch_bounds__(256, T == 64 ? 3 : 1) void gemm_f32_kernel(GemmParams p) {
+  constexpr int kOp = T * kBK * 4;  // one operand stage
+  constexpr int NB = T / 32;        // 16x16 blocks per wave and dimension
+  __shared__ __attribute__((aligned(1024))) uint8_t sa0[kOp], sa1[kOp], sa2[kOp];
+  __shared__ __attribute__((aligned(1024))) uint8_t sb0[kOp], sb1[kOp], sb2[kOp];
+  int z, tm, tn;
+  if (!gemm_tile(p, blockIdx.x, z, tm, tn)) return;
+  const int64_t m0 = static_cast<int64_t>(tm) * T;
+  const int64_t n0 = static_cast<int64_t>(tn) * T;
+  const float* A = p.A + z * p.sA;
+  const float* B = p.B + z * p.sB;
+  float* C = p.C + z * p.sC;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
 
-  f32x4_t acc[NI][NJ];
-#pragma unroll
-  for (int i = 0; i < NI; ++i)
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  // K range of this tile: a lower-triangular operand is zero outside it
+  int64_t kb = 0, ke = p.K;
+  if (p.tri == 1) kb = n0;
+  if (p.tri == 2) ke = min(p.K, m0 + T);
+  const int nstage = (ke > kb) ? static_cast<int>((ke - kb + kBK - 1) / kBK) : 0;
 
-  // k-major sources (A, transposed B): float4 along k, row = tid % R, k-quad by tid / R
-  auto load_kmajor = [&](const float* src, int64_t ld, int64_t rows, int64_t r0, int64_t k0, int R, int u) {
-    const int r = tid % R, kq = tid / R + (256 / R) * u;
-    const int64_t gr = r0 + r, gk = k0 + 4 * kq;
-    f32x4_t v = {0.f, 0.f, 0.f, 0.f};
-    if (gr < rows && gk < p.K) v = *reinterpret_cast<const f32x4_t*>(src + gr * ld + gk);
-    return v;
-  };
-  auto store_kmajor = [&](float* dst, int pitch, int R, int u, const f32x4_t& v) {
-    const int r = tid % R, kq = tid / R + (256 / R) * u;
+  // C rows of this wave's block as float4 (row-contiguous), read between the
+  // first two stages so the latency overlaps the K loop.  A load instruction
+  // covers kCRows rows; lane l takes row l / (T / 8), columns 4 (l % (T / 8)).
+  constexpr int kC4 = T / 8;            // float4 per block row
+  constexpr int kCRows = 64 / kC4;      // rows per instruction
+  constexpr int kCLoads = (T / 2) / kCRows;
+  f32x4_t cpre[kCLoads];
+  const bool use_c = p.beta != 0.f;
+  auto load_c = [&]() {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) dst[(4 * kq + e) * pitch + r] = v[e];
-  };
-  // row-major B [K, N]: float4 along n
-  auto load_b_rows = [&](int64_t k0, int u) {
-    constexpr int Q = BN / 4;
-    const int nq = tid % Q, kr = tid / Q + (256 / Q) * u;
-    const int64_t gk = k0 + kr, gn = n0 + 4 * nq;
-    f32x4_t v = {0.f, 0.f, 0.f, 0.f};
-    if (gk < p.K && gn < p.N) v = *reinterpret_cast<const f32x4_t*>(B + gk * p.ldb + gn);
-    return v;
-  };
-  auto store_b_rows = [&](float* dst, int u, const f32x4_t& v) {
-    constexpr int Q = BN / 4;
-    const int nq = tid % Q, kr = tid / Q + (256 / Q) * u;
-    *reinterpret_cast<f32x4_t*>(dst + kr * PB + 4 * nq) = v;
-  };
-
-  f32x4_t ra[LA], rb[LB];
-  auto load_stage = [&](int64_t k0) {
-#pragma unroll
-    for (int u = 0; u < LA; ++u) ra[u] = load_kmajor(A, p.lda, p.M, m0, k0, BM, u);
-#pragma unroll
-    for (int u = 0; u < LB; ++u) rb[u] = TRANS_B ? load_kmajor(B, p.ldb, p.N, n0, k0, BN, u) : load_b_rows(k0, u);
-  };
-  auto store_stage = [&](int buf) {
-#pragma unroll
-    for (int u = 0; u < LA; ++u) store_kmajor(As[buf], PA, BM, u, ra[u]);
-#pragma unroll
-    for (int u = 0; u < LB; ++u) {
-      if (TRANS_B)
-        store_kmajor(Bs[buf], PB, BN, u, rb[u]);
-      else
-        store_b_rows(Bs[buf], u, rb[u]);
+    for (int u = 0; u < kCLoads; ++u) {
+      const int64_t m = m0 + wm * (T / 2) + u * kCRows + lane / kC4;
+      const int64_t n = n0 + wn * (T / 2) + 4 * (lane % kC4);
+      cpre[u] = (m < p.M && n < p.N) ? *reinterpret_cast<const f32x4_t*>(C + m * p.ldc + n)
+                                     : f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
   };
 
-  const int nstage = static_cast<int>((p.K + kBK - 1) / kBK);
-  load_stage(0);
-  store_stage(0);
-  __syncthreads();
-  for (int s = 0; s < nstage; ++s) {
-    const int cur = s & 1;
-    const bool more = s + 1 < nstage;
-    if (more) load_stage(static_cast<int64_t>(s + 1) * kBK);
-    const float* as = As[cur];
-    const float* bs = Bs[cur];
+  f32x4_t acc[NB][NB];
 #pragma unroll
-    for (int kk = 0; kk < kBK; kk += 4) {
-      const int kr = kk + (lane >> 4);
-      float a[NI], b[NJ];
+  for (int i = 0; i < NB; ++i)
 #pragma unroll
-      for (int i = 0; i < NI; ++i) a[i] = as[kr * PA + wm * (BM / 2) + 16 * i + (lane & 15)];
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) b[j] = bs[kr * PB + wn * (BN / 2) + 16 * j + (lane & 15)];
-#pragma unroll
-      for (int i = 0; i < NI; ++i)
-#pragma unroll
-        for (int j = 0; j < NJ; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i], b[j], acc[i][j], 0, 0, 0);
+    for (int j = 0; j < NB; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  const __amdgpu_buffer_rsrc_t rsA = gemm_rsrc(A + m0 * p.lda, min<int64_t>(p.M - m0, T) * p.lda * 4);
+  const __amdgpu_buffer_rsrc_t rsBt =
+      gemm_rsrc(B + (TRANS_B ? n0 * p.ldb : 0), TRANS_B ? min<int64_t>(p.N - n0, T) * p.ldb * 4 : 0);
+  auto issue = [&](int s, uint8_t* da, uint8_t* db) {
+    const int64_t k0 = kb + static_cast<int64_t>(s) * kBK;
+    dma_kmajor<T>(rsA, da, p.lda, k0, ke, wave, lane);
+    if (TRANS_B) {
+      dma_kmajor<T>(rsBt, db, p.ldb, k0, ke, wave, lane);
+    } else {
+      const int64_t rows = min<int64_t>(ke - k0, kBK);
+      dma_nmajor<T>(gemm_rsrc(B + k0 * p.ldb, rows * p.ldb * 4), db, p.ldb, n0, p.N, wave, lane);
     }
-    if (more) store_stage(cur ^ 1);
-    __syncthreads();
+  };
+  constexpr int kLoadsPerStage = 2 * (T / 32);  // DMA instructions per wave per stage
+
+  // operand read offsets (bytes within a stage)
+  uint32_t abase[NB], asw[NB], bbase[NB], bsw[NB];
+#pragma unroll
+  for (int i = 0; i < NB; ++i) {
+    const int r = wm * (T / 2) + 16 * i + (lane & 15);
+    abase[i] = static_cast<uint32_t>(r * 128 + (lane >> 4) * 4);
+    asw[i] = static_cast<uint32_t>(((r >> 1) & 7) * 16);
   }
-  // epilogue: element (i, j, r) -> row 16 i + 4 (lane >> 4) + r, col 16 j + (lane & 15) of the wave block
 #pragma unroll
-  for (int i = 0; i < NI; ++i) {
+  for (int j = 0; j < NB; ++j) {
+    const int nn = wn * (T / 2) + 16 * j + (lane & 15);
+    const int kk = lane >> 4;
+    if (TRANS_B) {
+      bbase[j] = static_cast<uint32_t>(nn * 128 + kk * 4);
+      bsw[j] = static_cast<uint32_t>(((nn >> 1) & 7) * 16);
+    } else {
+      bbase[j] = static_cast<uint32_t>(kk * (4 * T) + (((nn >> 2) ^ (4 * kk)) * 16) + (nn & 3) * 4);
+      bsw[j] = 0;
+    }
+  }
+  auto compute = [&](const uint8_t* da, const uint8_t* db) {
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      const int64_t n = n0 + wn * (BN / 2) + 16 * j + (lane & 15);
-      if (n >= p.N) continue;
+    for (int h = 0; h < 2; ++h) {
+      // half a stage of operands first, then its MFMAs
+      float a[kBK / 8][NB], b[kBK / 8][NB];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int64_t m = m0 + wm * (BM / 2) + 16 * i + 4 * (lane >> 4) + r;
-        if (m < p.M) {
-          float* c = C + m * p.ldc + n;
-          const float v = p.alpha * acc[i][j][r];
-          *c = (p.beta == 0.f) ? v : v + p.beta * *c;
-        }
+      for (int tt = 0; tt < kBK / 8; ++tt) {
+        const int t = h * (kBK / 8) + tt;
+#pragma unroll
+        for (int i = 0; i < NB; ++i) a[tt][i] = lds_f32(da, abase[i] + ((16u * t) ^ asw[i]));
+#pragma unroll
+        for (int j = 0; j < NB; ++j)
+          b[tt][j] = TRANS_B ? lds_f32(db, bbase[j] + ((16u * t) ^ bsw[j]))
+                             : lds_f32(db, bbase[j] + static_cast<uint32_t>(16 * T) * t);
       }
+      __builtin_amdgcn_sched_barrier(0);  // keep these reads above the MFMAs
+#pragma unroll
+      for (int tt = 0; tt < kBK / 8; ++tt)
+#pragma unroll
+        for (int i = 0; i < NB; ++i)
+#pragma unroll
+          for (int j = 0; j < NB; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[tt][i], b[tt][j], acc[i][j], 0, 0, 0);
+    }
+  };
+  // Stage x lives in slot x % 3.  Before computing stage x: wait until its
+  // loads (and everything older) have landed, barrier (all waves' pieces are
+  // in; everyone is done with slot (x - 1) % 3), then refill that slot with
+  // stage x + 2.
+  auto step = [&](int x, const uint8_t* da, const uint8_t* db, uint8_t* na, uint8_t* nb) {
+    if (x >= nstage) return;
+    if (x == 0) {
+      // issue order: stage 0, C, stage 1
+      const bool s1 = nstage > 1;
+      if (use_c) {
+        if (s1) __builtin_amdgcn_s_waitcnt(GPTQ_VMCNT(kCLoads + kLoadsPerStage));
+        else __builtin_amdgcn_s_waitcnt(GPTQ_VMCNT(kCLoads));
+      } else {
+        if (s1) __builtin_amdgcn_s_waitcnt(GPTQ_VMCNT(kLoadsPerStage));
+        else __builtin_amdgcn_s_waitcnt(GPTQ_VMCNT(0));
+      }
+    } else if (x + 1 < nstage) {
+      __builtin_amdgcn_s_waitcnt(GPTQ_VMCNT(kLoadsPerStage));
+    } else {
+      __builtin_amdgcn_s_waitcnt(GPTQ_VMCNT(0));
+    }
+    __builtin_amdgcn_s_barrier();
+    if (x + 2 < nstage) issue(x + 2, na, nb);
+    compute(da, db);
+  };
+  if (nstage > 0) issue(0, sa0, sb0);
+  if (use_c) load_c();
+  if (nstage > 1) issue(1, sa1, sb1);
+  for (int s = 0; s < nstage; s += 3) {
+    step(s, sa0, sb0, sa2, sb2);
+    step(s + 1, sa1, sb1, sa0, sb0);
+    step(s + 2, sa2, sb2, sa1, sb1);
+  }
+  // epilogue: each wave stages its (T/2) x (T/2) block in its own LDS slot
+  // array (row-major; T = 128: 64-float rows, column bits 4-5 XOR-ed with
+  // row bits 2-3; T = 64: rows padded to 36 floats), then writes C as float4
+  // rows.  Accumulator element (i, j, e) is block row 16 i + 4 (lane >> 4) + e,
+  // column 16 j + (lane & 15).  Lower-tile problems never write above the
+  // 64-block diagonal.
+  constexpr int kP = (T == 128) ? 64 : 36;
+  auto xr = [&](int row) { return (T == 128) ? 16 * ((row >> 2) & 3) : 0; };
+  __syncthreads();  // every wave is done with the ring
+  float* stg = reinterpret_cast<float*>(wave == 0 ? sa0 : wave == 1 ? sa1 : wave == 2 ? sa2 : sb0);
+#pragma unroll
+  for (int i = 0; i < NB; ++i)
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int row = 16 * i + 4 * (lane >> 4) + e, col = 16 * j + (lane & 15);
+        stg[row * kP + (col ^ xr(row))] = acc[i][j][e];
+      }
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+#pragma unroll
+  for (int u = 0; u < kCLoads; ++u) {
+    const int row = u * kCRows + lane / kC4, c4 = lane % kC4;
+    const f32x4_t v = *reinterpret_cast<const f32x4_t*>(stg + row * kP + ((4 * c4) ^ xr(row)));
+    const int64_t m = m0 + wm * (T / 2) + row;
+    const int64_t n = n0 + wn * (T / 2) + 4 * c4;
+    const bool upper = p.lower_tiles && (m >> 6) < (n >> 6);
+    if (m < p.M && n < p.N && !upper) {
+      f32x4_t out = p.alpha * v;
+      if (use_c) out += p.beta * cpre[u];
+      *reinterpret_cast<f32x4_t*>(C + m * p.ldc + n) = out;
     }
   }
 }
@@ -156,26 +318,29 @@ __global__ __launch_bounds__(256, 2) void gemm_f32_kernel(GemmParams p) {
 
 hipError_t gemm_f32(int64_t M, int64_t N, int64_t K, float alpha, const float* A, int64_t lda,
                     int64_t sA, const float* B, int64_t ldb, int64_t sB, bool transB, float beta,
-                    float* C, int64_t ldc, int64_t sC, int batch, bool lower_tiles, bool /*wide_n*/,
+                    float* C, int64_t ldc, int64_t sC, int batch, bool lower_tiles, int tri,
                     hipStream_t stream) {
   if (M <= 0 || N <= 0 || batch <= 0) return hipSuccess;
-  GemmParams p{M, N, K, alpha, beta, A, lda, sA, B, ldb, sB, C, ldc, sC, lower_tiles ? 1 : 0};
-  // 64x64 tiles: measured faster than 128x128 on every shape this library
-  // issues (more resident workgroups hide the global-load latency better).
-  // Lower-tile problems need tiles aligned with their 64-column diagonal blocks.
-  const bool big = false;
-  if (big) {
-    dim3 grid(static_cast<unsigned>((N + 127) / 128), static_cast<unsigned>((M + 127) / 128), static_cast<unsigned>(batch));
-    if (transB)
-      gemm_f32_kernel<true, 128, 128><<<grid, 256, 0, stream>>>(p);
-    else
-      gemm_f32_kernel<false, 128, 128><<<grid, 256, 0, stream>>>(p);
+  GemmParams p{M, N, K, alpha, beta, A, lda, sA, B, ldb, sB, C, ldc, sC, lower_tiles ? 1 : 0, tri, 0, 0, 0, batch};
+  // 128x128 tiles halve the operand bytes per flop; used when they still give
+  // every CU a tile.  Lower-tile problems are square (the Cholesky update).
+  auto count = [&](int T) {
+    const int tm = static_cast<int>((M + T - 1) / T), tn = static_cast<int>((N + T - 1) / T);
+    return lower_tiles ? tm * (tm + 1) / 2 : tm * tn;
+  };
+  // triangular operands make tiles unequal: small tiles, heaviest first, balance them
+  const bool big = tri == 0 && static_cast<int64_t>(count(128)) * batch >= 256;
+  const int T = big ? 128 : 64;
+  p.tiles_m = static_cast<int>((M + T - 1) / T);
+  p.tiles_n = static_cast<int>((N + T - 1) / T);
+  p.tiles = count(T);
+  const unsigned blocks = static_cast<unsigned>(static_cast<int64_t>(p.tiles) * batch);
+  if (transB) {
+    if (big) gemm_f32_kernel<true, 128><<<blocks, 256, 0, stream>>>(p);
+    else gemm_f32_kernel<true, 64><<<blocks, 256, 0, stream>>>(p);
   } else {
-    dim3 grid(static_cast<unsigned>((N + 63) / 64), static_cast<unsigned>((M + 63) / 64), static_cast<unsigned>(batch));
-    if (transB)
-      gemm_f32_kernel<true, 64, 64><<<grid, 256, 0, stream>>>(p);
-    else
-      gemm_f32_kernel<false, 64, 64><<<grid, 256, 0, stream>>>(p);
+    if (big) gemm_f32_kernel<false, 128><<<blocks, 256, 0, stream>>>(p);
+    else gemm_f32_kernel<false, 64><<<blocks, 256, 0, stream>>>(p);
   }
   return hipGetLastError();
 }

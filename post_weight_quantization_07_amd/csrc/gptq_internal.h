@@ -36,10 +36,12 @@ hipError_t prepare_launch(float* S_to_H, int64_t d_in, int64_t n_total, float da
 // C[M,N] = alpha * op(A)[M,K] * op(B)[K,N] + beta * C, row-major fp32 on MFMA.
 // transB: B is given as [N, K] row-major.  lower_tiles: only compute tiles whose
 // first row >= first column (block-lower part; used by the Cholesky update).
+// tri: 0 dense; 1 B is lower-triangular (a tile skips k < its first column);
+// 2 A is lower-triangular (a tile skips k past its last row).
 // Batched over blockIdx.z with element strides sA, sB, sC.
 hipError_t gemm_f32(int64_t M, int64_t N, int64_t K, float alpha, const float* A, int64_t lda,
                     int64_t sA, const float* B, int64_t ldb, int64_t sB, bool transB, float beta,
-                    float* C, int64_t ldc, int64_t sC, int batch, bool lower_tiles, bool wide_n,
+                    float* C, int64_t ldc, int64_t sC, int batch, bool lower_tiles, int tri,
                     hipStream_t stream);
 
 // --------------------------------------------------------------- quantize --

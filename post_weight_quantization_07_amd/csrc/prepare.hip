@@ -105,33 +105,62 @@ __global__ void gather_kernel(const float* H, int64_t n, const int32_t* perm, co
   }
 }
 
-// Lower Cholesky of the 64x64 block held in L (LDS, pitch 68), by wave 0:
-// lane r keeps row r in registers; column j is published through LDS.
-// Returns through `fail` the first failing local pivot (or -1).
-GPTQ_DEV void factor_block_wave(float (*L)[68], float* col, int lane, int& fail) {
+// Lower Cholesky of the 64x64 block held in L (LDS, pitch 68), by one wave:
+// lane r keeps row r in registers.  Right-looking, pipelined by one step: at
+// step j column j is complete; the step's update of column j + 1 is applied at
+// once (the next pivot depends on it, and l[j+1] comes by readlane), and its
+// updates of columns j + 2 .. 63 are applied during step j + 1 from the
+// column published in LDS one step earlier, so the LDS round trip overlaps
+// the pivot chain.  Every lane scales its column-j entry by 1 / sqrt(pivot):
+// lanes above the pivot only ever touch their own upper-triangle entries,
+// which are discarded.  Writes the factor to L (zeros above the diagonal) and
+// its transpose to LTq (LTq[c][q][u] = L[4u+q][c], the layout of the panel
+// solve), and returns through `fail` the first local pivot that is not
+// positive (or -1).
+GPTQ_DEV void factor_block_wave(float (*L)[68], float (*LTq)[4][16], f32x4_t (*colbuf)[kNB / 4], int lane,
+                                int& fail) {
   float v[kNB];
 #pragma unroll
   for (int c = 0; c < kNB; ++c) v[c] = L[lane][c];
   fail = -1;
+  float lp = 0.f;
+  f32x4_t xp[kNB / 4], xn[kNB / 4];  // column of the previous / current step, read back from LDS
 #pragma unroll
   for (int j = 0; j < kNB; ++j) {
     const float piv = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v[j]), j));
     if (!(piv > 0.f) && fail < 0) fail = j;
     // hardware square root and reciprocal (about 1 ulp): the pivot chain is the
     // latency-critical path of the factorization
-    const float d = __builtin_amdgcn_sqrtf(piv);
-    const float inv = __builtin_amdgcn_rcpf(d);
-    v[j] = (lane == j) ? d : ((lane > j) ? v[j] * inv : v[j]);
-    col[lane] = v[j];
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const float inv = __builtin_amdgcn_rcpf(__builtin_amdgcn_sqrtf(piv));
+    const float l = v[j] * inv;
+    v[j] = l;
+    reinterpret_cast<float*>(colbuf[j & 1])[lane] = l;
+    // keep the publication above the reads of this buffer
+    asm volatile("" ::: "memory");
+    // read the column back now for the next step's update of columns j + 2 ..
 #pragma unroll
-    for (int c = j + 1; c < kNB; ++c) v[c] = fmaf(-v[j], col[c], v[c]);
-    __builtin_amdgcn_wave_barrier();
+    for (int q4 = (j + 2) >> 2; q4 < kNB / 4; ++q4) xn[q4] = colbuf[j & 1][q4];
+    if (j + 1 < kNB) {
+      const float lj1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, l), j + 1));
+      v[j + 1] = fmaf(-l, lj1, v[j + 1]);
+    }
+    if (j >= 1) {
+#pragma unroll
+      for (int q4 = (j + 1) >> 2; q4 < kNB / 4; ++q4)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (4 * q4 + e > j) v[4 * q4 + e] = fmaf(-lp, xp[q4][e], v[4 * q4 + e]);
+    }
+    lp = l;
+#pragma unroll
+    for (int q4 = 0; q4 < kNB / 4; ++q4) xp[q4] = xn[q4];
   }
 #pragma unroll
-  for (int c = 0; c < kNB; ++c) L[lane][c] = (c <= lane) ? v[c] : 0.f;
+  for (int c = 0; c < kNB; ++c) {
+    const float x = (c <= lane) ? v[c] : 0.f;
+    L[lane][c] = x;
+    LTq[c][lane & 3][lane >> 2] = x;
+  }
 }
 
 // One launch per panel k: every workgroup factors the 64x64 diagonal block
@@ -170,10 +199,10 @@ GPTQ_DEV void solve_all(float (&sv)[16], float (&xv)[16], const float (*LTq)[4][
   (solve_step<Cs>(sv, xv, LTq, dinv, q), ...);
 }
 
-__global__ __launch_bounds__(256) void panel_kernel(float* Hr, int64_t n, int64_t k, int32_t* info) {
+__global__ __launch_bounds__(256, 1) void panel_kernel(float* Hr, int64_t n, int64_t k, int32_t* info) {
   __shared__ __attribute__((aligned(16))) float L[kNB][68];
   __shared__ __attribute__((aligned(16))) float LTq[kNB][4][16];  // LTq[c][q][u] = L[4u+q][c]
-  __shared__ float col[kNB];
+  __shared__ f32x4_t colbuf[2][kNB / 4];
   __shared__ float dinv[kNB];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nb = static_cast<int>(std::min<int64_t>(kNB, n - k));
@@ -183,19 +212,26 @@ __global__ __launch_bounds__(256) void panel_kernel(float* Hr, int64_t n, int64_
     if (r < nb && c <= r) v = Hr[(k + r) * n + k + c];
     L[r][c] = v;
   }
+  // this thread's panel row (quad q holds columns q, q + 4, ..., q + 60):
+  // loaded now, so the load overlaps the factorization
+  const int q = tid & 3;
+  const int64_t row = k + kNB + static_cast<int64_t>(blockIdx.x) * kPanelRows + (tid >> 2);
+  const bool solve = (nb == kNB) && (row < n);
+  float sv[16], xv[16];
+#pragma unroll
+  for (int u = 0; u < 16; ++u) {
+    sv[u] = solve ? Hr[row * n + k + 4 * u + q] : 0.f;
+    xv[u] = 0.f;
+  }
   __syncthreads();
   if (wave == 0) {
     int fail;
-    factor_block_wave(L, col, lane, fail);
+    factor_block_wave(L, LTq, colbuf, lane, fail);
     if (lane == 0 && blockIdx.x == 0 && fail >= 0 && fail < nb)
       atomicCAS(info, 0, static_cast<int32_t>(n - (k + fail)));
   }
   __syncthreads();
   if (tid < kNB) dinv[tid] = __builtin_amdgcn_rcpf(L[tid][tid]);
-  for (int e = tid; e < kNB * kNB; e += 256) {
-    const int c = e >> 6, r = e & 63;
-    LTq[c][r & 3][r >> 2] = L[r][c];
-  }
   if (blockIdx.x == 0) {
     for (int e = tid; e < nb * nb; e += 256) {
       const int r = e / nb, c = e - r * nb;
@@ -203,16 +239,7 @@ __global__ __launch_bounds__(256) void panel_kernel(float* Hr, int64_t n, int64_
     }
   }
   __syncthreads();
-  const int q = tid & 3;
-  const int64_t row = k + kNB + static_cast<int64_t>(blockIdx.x) * kPanelRows + (tid >> 2);
-  if (nb < kNB || row >= n) return;
-  float sv[16], xv[16];
-  const float* src = Hr + row * n + k;
-#pragma unroll
-  for (int u = 0; u < 16; ++u) {
-    sv[u] = src[4 * u + q];
-    xv[u] = 0.f;
-  }
+  if (!solve) return;
   solve_all(sv, xv, LTq, dinv, q, std::make_integer_sequence<int, kNB>{});
   float* dst = Hr + row * n + k;
 #pragma unroll
@@ -311,7 +338,7 @@ hipError_t prepare_launch(float* S, int64_t n, int64_t n_total, float damp, bool
     if (below > 0) {
       const float* P = Hr + (k + kNB) * n + k;
       GPTQ_TRY(gemm_f32(below, below, kNB, -1.f, P, n, 0, P, n, 0, true, 1.f, Hr + (k + kNB) * (n + 1), n,
-                        0, 1, true, false, st));
+                        0, 1, true, 0, st));
     }
   }
   // triangular inverse: diagonal blocks, then recursive doubling
@@ -328,9 +355,9 @@ hipError_t prepare_launch(float* S, int64_t n, int64_t n_total, float damp, bool
       const float* Ainv = Hr;
       const float* Cinv = Hr + w_el * (n + 1);
       GPTQ_TRY(gemm_f32(w_el, w_el, w_el, 1.f, L21, n, gs, Ainv, n, gs, false, 0.f, T, w_el, w_el * w_el,
-                        static_cast<int>(groups_full), false, false, st));
+                        static_cast<int>(groups_full), false, 1, st));
       GPTQ_TRY(gemm_f32(w_el, w_el, w_el, -1.f, Cinv, n, gs, T, w_el, w_el * w_el, false, 0.f,
-                        Hr + w_el * n, n, gs, static_cast<int>(groups_full), false, false, st));
+                        Hr + w_el * n, n, gs, static_cast<int>(groups_full), false, 2, st));
     }
     // ragged last group: A is h blocks wide, C is what remains (< h blocks)
     const int64_t a0 = groups_full * 2 * w_el;
@@ -340,9 +367,9 @@ hipError_t prepare_launch(float* S, int64_t n, int64_t n_total, float damp, bool
       const float* L21 = Hr + c0 * n + a0;
       const float* Ainv = Hr + a0 * (n + 1);
       const float* Cinv = Hr + c0 * (n + 1);
-      GPTQ_TRY(gemm_f32(cw, w_el, w_el, 1.f, L21, n, 0, Ainv, n, 0, false, 0.f, T, w_el, 0, 1, false, false, st));
+      GPTQ_TRY(gemm_f32(cw, w_el, w_el, 1.f, L21, n, 0, Ainv, n, 0, false, 0.f, T, w_el, 0, 1, false, 1, st));
       GPTQ_TRY(gemm_f32(cw, w_el, cw, -1.f, Cinv, n, 0, T, w_el, 0, false, 0.f, Hr + c0 * n + a0, n, 0, 1, false,
-                        false, st));
+                        2, st));
     }
   }
   reverse_kernel<<<grid_for(nn), 256, 0, st>>>(Hr, n, U);

@@ -404,7 +404,7 @@ hipError_t quantize_launch(const void* W, bool w_bf16, int64_t d_out, int64_t d_
     const int64_t rest = d_in - j0 - kB;
     if (rest > 0) {
       e = gemm_f32(d_out, rest, kB, -1.f, Err, kB, 0, U + j0 * d_in + j0 + kB, d_in, 0, false, 1.f,
-                   Wp + j0 + kB, d_in, 0, 1, false, false, st);
+                   Wp + j0 + kB, d_in, 0, 1, false, 0, st);
       if (e != hipSuccess) return e;
     }
   }
