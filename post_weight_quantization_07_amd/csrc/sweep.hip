@@ -37,7 +37,8 @@ struct SweepParams {
   float* scales;        // [n_groups, d_out]
   int32_t* zeros;       // [n_groups, d_out]
   float* row_loss;      // optional [d_out]
-  float* Err;           // [d_out, 128]
+  float* Err;           // this block's normalised errors, rows of ld_err floats
+  int ld_err;
   int64_t d_out, d_in;
   int64_t j0;           // first sweep column of the block
   int ncols;            // columns in this block
@@ -232,7 +233,7 @@ __global__ __launch_bounds__(256) void sweep_kernel(SweepParams p) {
 
   if (!row_ok) return;
   // normalised errors of the block, for the trailing update
-  float* e = p.Err + row * kB + c0;
+  float* e = p.Err + row * p.ld_err + c0;
   *reinterpret_cast<f32x4_t*>(e) = f32x4_t{er[0], er[1], er[2], er[3]};
   *reinterpret_cast<f32x4_t*>(e + 4) = f32x4_t{er[4], er[5], er[6], er[7]};
   // codes and dequantized weights, written in original column order
@@ -337,7 +338,7 @@ QuantLayout quant_layout(int64_t d_out, int64_t d_in) {
   QuantLayout L{};
   L.off_wp = 0;
   L.off_err = up(static_cast<size_t>(d_out) * d_in * sizeof(float));
-  L.ws_bytes = L.off_err + up(static_cast<size_t>(d_out) * kB * sizeof(float));
+  L.ws_bytes = L.off_err + up(static_cast<size_t>(d_out) * 2 * kB * sizeof(float));
   return L;
 }
 
@@ -384,27 +385,47 @@ hipError_t quantize_launch(const void* W, bool w_bf16, int64_t d_out, int64_t d_
   p.preset = preset ? 1 : 0;
   p.identity = identity ? 1 : 0;
   const int blocks = static_cast<int>((d_out + kRowsPerWG - 1) / kRowsPerWG);
-  for (int64_t j0 = 0; j0 < d_in; j0 += kB) {
-    p.j0 = j0;
-    p.ncols = static_cast<int>(std::min<int64_t>(kB, d_in - j0));
-    const int gs = (!preset && group <= kB) ? group : 0;
-    switch (gs) {
-      case 0: sweep_kernel<0><<<blocks, 256, 0, st>>>(p); break;
-      case 1: sweep_kernel<1><<<blocks, 256, 0, st>>>(p); break;
-      case 2: sweep_kernel<2><<<blocks, 256, 0, st>>>(p); break;
-      case 4: sweep_kernel<4><<<blocks, 256, 0, st>>>(p); break;
-      case 8: sweep_kernel<8><<<blocks, 256, 0, st>>>(p); break;
-      case 16: sweep_kernel<16><<<blocks, 256, 0, st>>>(p); break;
-      case 32: sweep_kernel<32><<<blocks, 256, 0, st>>>(p); break;
-      case 64: sweep_kernel<64><<<blocks, 256, 0, st>>>(p); break;
-      case 128: sweep_kernel<128><<<blocks, 256, 0, st>>>(p); break;
-      default: return hipErrorInvalidValue;  // the ABI admits only groups dividing 128 here
+  // The trailing update runs once per pair of 128-column blocks (K = 256): the
+  // second block of a pair is first brought up to date with the first block's
+  // errors.  The result is the lazy-batch sweep's (the same products, summed
+  // in another order).  A dynamic group wider than a block reads columns past
+  // the block at its start, so pairs are used only when such groups start on
+  // pair boundaries.
+  const bool pair = preset || group <= kB || group % (2 * kB) == 0;
+  const int SB = pair ? 2 * kB : kB;
+  const int gs = (!preset && group <= kB) ? group : 0;
+  p.ld_err = SB;
+  for (int64_t j0 = 0; j0 < d_in; j0 += SB) {
+    for (int h = 0; h < SB / kB; ++h) {
+      const int64_t jb = j0 + static_cast<int64_t>(h) * kB;
+      if (jb >= d_in) break;
+      const int ncols = static_cast<int>(std::min<int64_t>(kB, d_in - jb));
+      if (h > 0) {
+        e = gemm_f32(d_out, ncols, h * kB, -1.f, Err, SB, 0, U + j0 * d_in + jb, d_in, 0, false, 1.f, Wp + jb, d_in,
+                     0, 1, false, 0, st);
+        if (e != hipSuccess) return e;
+      }
+      p.j0 = jb;
+      p.ncols = ncols;
+      p.Err = Err + h * kB;
+      switch (gs) {
+        case 0: sweep_kernel<0><<<blocks, 256, 0, st>>>(p); break;
+        case 1: sweep_kernel<1><<<blocks, 256, 0, st>>>(p); break;
+        case 2: sweep_kernel<2><<<blocks, 256, 0, st>>>(p); break;
+        case 4: sweep_kernel<4><<<blocks, 256, 0, st>>>(p); break;
+        case 8: sweep_kernel<8><<<blocks, 256, 0, st>>>(p); break;
+        case 16: sweep_kernel<16><<<blocks, 256, 0, st>>>(p); break;
+        case 32: sweep_kernel<32><<<blocks, 256, 0, st>>>(p); break;
+        case 64: sweep_kernel<64><<<blocks, 256, 0, st>>>(p); break;
+        case 128: sweep_kernel<128><<<blocks, 256, 0, st>>>(p); break;
+        default: return hipErrorInvalidValue;  // the ABI admits only groups dividing 128 here
+      }
+      if ((e = hipGetLastError()) != hipSuccess) return e;
     }
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    const int64_t rest = d_in - j0 - kB;
+    const int64_t rest = d_in - j0 - SB;
     if (rest > 0) {
-      e = gemm_f32(d_out, rest, kB, -1.f, Err, kB, 0, U + j0 * d_in + j0 + kB, d_in, 0, false, 1.f,
-                   Wp + j0 + kB, d_in, 0, 1, false, 0, st);
+      e = gemm_f32(d_out, rest, SB, -1.f, Err, SB, 0, U + j0 * d_in + j0 + SB, d_in, 0, false, 1.f, Wp + j0 + SB, d_in,
+                   0, 1, false, 0, st);
       if (e != hipSuccess) return e;
     }
   }

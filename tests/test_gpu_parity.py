@@ -150,6 +150,7 @@ SWEEP_CASES = [  # d_out, d_in, bits, G, sym, desc_act, static, w dtype
     (40, 256, 4, -1, False, True, False, "f32"),
     (33, 768, 4, 256, True, False, False, "f32"),     # dynamic group wider than the block
     (33, 768, 4, 256, True, True, True, "f32"),
+    (33, 768, 4, 384, True, False, False, "f32"),     # wide groups starting inside a block pair
     (24, 192, 4, 8, False, False, False, "f32"),      # group narrower than a lane's 8 columns
     (1, 128, 4, 128, True, False, False, "f32"),
 ]
