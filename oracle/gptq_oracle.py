@@ -195,6 +195,7 @@ class SweepResult:
     g_idx: np.ndarray      # int64 [d_in], original column -> group
     err: np.ndarray        # fp64  [d_out, d_in], normalised errors, sweep order
     row_loss: np.ndarray   # fp64  [d_out], sum of err^2 per row
+    ties: int = 0          # decisions taken from `follow` at float ties
 
 
 def _n_groups(d_in: int, group_size: int) -> int:
@@ -230,7 +231,8 @@ def _group_plan(d_in: int, perm: np.ndarray, group_size: int, static_groups: boo
 
 def quantize_layer(W: np.ndarray, U: np.ndarray, perm: np.ndarray, bits: int, group_size: int,
                    sym: bool, static_groups: bool, blocksize: Optional[int] = 128,
-                   rows: Optional[Sequence[int]] = None) -> SweepResult:
+                   rows: Optional[Sequence[int]] = None, follow: Optional[np.ndarray] = None,
+                   tie_tol: float = 0.0) -> SweepResult:
     """GPTQ column sweep.
 
     blocksize=None runs the plain form: after column i is quantized its
@@ -242,7 +244,15 @@ def quantize_layer(W: np.ndarray, U: np.ndarray, perm: np.ndarray, bits: int, gr
     exactly in real arithmetic when group_size divides the block or the block
     divides group_size.
 
-    rows selects a subset of output rows (rows are independent given U)."""
+    rows selects a subset of output rows (rows are independent given U).
+
+    follow (test use): codes [rows, d_in] in original column order produced by
+    another implementation.  Where that code and this sweep's differ by one
+    and this sweep's pre-rounding value w/s + z lies within tie_tol (in
+    quantization steps) of the rounding boundary between them, both codes are
+    correct up to rounding of the running weights; the sweep then takes the
+    followed code and continues from it (counted in `ties`).  Every other
+    decision is this sweep's own."""
     W = np.asarray(W, dtype=np.float64)
     if rows is not None:
         W = W[np.asarray(rows)]
@@ -265,6 +275,8 @@ def quantize_layer(W: np.ndarray, U: np.ndarray, perm: np.ndarray, bits: int, gr
         scales, zeros = _static_params(W, bits, G, sym)
 
     Wp = W[:, perm].copy()
+    follow_p = None if follow is None else np.asarray(follow, dtype=np.int64)[:, perm]
+    n_ties = [0]
     codes_p = np.zeros((d_out, d_in), dtype=np.int64)
     Q_p = np.zeros((d_out, d_in), dtype=np.float64)
     Err = np.zeros((d_out, d_in), dtype=np.float64)
@@ -274,6 +286,14 @@ def quantize_layer(W: np.ndarray, U: np.ndarray, perm: np.ndarray, bits: int, gr
         g = gpos[i]
         w = cur[:, col]
         q, what = quantize_values(w, scales[g], zeros[g], bits)
+        if follow_p is not None:
+            f = follow_p[:, i]
+            v = (w.astype(np.float32) / scales[g] + zeros[g]).astype(np.float64)
+            tie = (np.abs(q - f) == 1) & (np.abs(v - (np.minimum(q, f) + 0.5)) <= tie_tol)
+            if np.any(tie):
+                q = np.where(tie, f, q)
+                what = scales[g].astype(np.float64) * (q.astype(np.float64) - zeros[g].astype(np.float64))
+                n_ties[0] += int(np.sum(tie))
         codes_p[:, i] = q
         Q_p[:, i] = what
         e = w - what
@@ -311,7 +331,7 @@ def quantize_layer(W: np.ndarray, U: np.ndarray, perm: np.ndarray, bits: int, gr
     codes[:, perm] = codes_p
     Q[:, perm] = Q_p
     return SweepResult(codes=codes, Q=Q, scales=scales, zeros=zeros.astype(np.int64), g_idx=g_idx,
-                       err=Err, row_loss=np.sum(Err * Err, axis=1))
+                       err=Err, row_loss=np.sum(Err * Err, axis=1), ties=n_ties[0])
 
 
 def naive_obq(W: np.ndarray, Hp: np.ndarray, perm: np.ndarray, bits: int, group_size: int,

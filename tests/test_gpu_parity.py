@@ -15,7 +15,7 @@ import torch
 
 import oracle as O
 import synth
-from gpu_helpers import banner, dev, host, rel_fro, to_dev
+from gpu_helpers import banner, dev, host, rel_fro, sweep_parity, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -177,11 +177,12 @@ def test_quantize_stagewise(G, case):
     torch.cuda.synchronize()
     U_h = U.cpu().numpy().astype(np.float64)
     perm_h = perm.cpu().numpy().astype(np.int64)
-    ref = O.quantize_layer(W.astype(np.float64), U_h, perm_h, bits, Gs, sym, static)
     codes = out["codes"].cpu().numpy().astype(np.int64)
-    mism = np.mean(codes != ref.codes)
-    print(f"  code mismatch {mism:.5%}")
-    assert mism <= 1e-3
+    # the oracle follows the GPU's decision only at float ties (both codes correct)
+    ref, mism, ties = sweep_parity(W, U_h, perm_h, dict(bits=bits, group_size=Gs, sym=sym, static_groups=static),
+                                   codes)
+    print(f"  code mismatch {mism:.5%} (float ties followed {ties:.5%})")
+    assert mism <= 1e-3 and ties <= 1e-3
     np.testing.assert_array_equal(out["g_idx"].cpu().numpy(), ref.g_idx)
     # scales/zeros: static / whole-row groups come from the original weights
     # (exact); dynamic groups from compensated values, which carry the fp32
@@ -193,9 +194,9 @@ def test_quantize_stagewise(G, case):
         np.testing.assert_array_equal(sc, ref.scales)
         np.testing.assert_array_equal(zr, ref.zeros)
     else:
-        # a near-tie code flip changes that row's later compensated values (and
-        # so its later group ranges); rows are independent, so compare the rows
-        # without a flip
+        # a code that still differs changes that row's later compensated values
+        # (and so its later group ranges); rows are independent, so compare the
+        # rows without one
         clean = ~np.any(codes != ref.codes, axis=1)
         assert clean.mean() >= 0.9
         np.testing.assert_allclose(sc[:, clean], ref.scales[:, clean], rtol=1e-4, atol=0)

@@ -426,3 +426,41 @@ def test_pack_density_and_group_count_from_pages():
     W = np.random.default_rng(0).standard_normal((gc["d_out"], gc["d_in"])).astype(np.float32) * 0.02
     s, z = O.gptq_oracle._static_params(W, 4, gc["group_size"], True)
     assert s.size == gc["groups"]
+
+
+# ------------------------------------------------ tie-following (test use) --
+
+def test_follow_takes_only_float_ties():
+    """An exact tie: 2-bit asym over a row [0, 3, 1.5] gives scale 1, zero 0,
+    and 1.5 sits on the boundary between codes 1 and 2 (rint picks 2).  A
+    followed code 1 there is taken; a followed code 3 is not (1.5 is a whole
+    step from the 2|3 boundary); U = I keeps the columns independent."""
+    W = np.array([[0.0, 3.0, 1.5]])
+    U = np.eye(3)
+    perm = np.arange(3)
+    kw = dict(bits=2, group_size=-1, sym=False, static_groups=False)
+    plain = O.quantize_layer(W, U, perm, **kw)
+    np.testing.assert_array_equal(plain.codes, [[0, 3, 2]])
+    tied = O.quantize_layer(W, U, perm, **kw, follow=np.array([[0, 3, 1]]), tie_tol=1e-6)
+    np.testing.assert_array_equal(tied.codes, [[0, 3, 1]])
+    assert tied.ties == 1
+    np.testing.assert_allclose(tied.Q, [[0.0, 3.0, 1.0]])
+    far = O.quantize_layer(W, U, perm, **kw, follow=np.array([[0, 3, 3]]), tie_tol=1e-6)
+    np.testing.assert_array_equal(far.codes, [[0, 3, 2]])
+    assert far.ties == 0
+
+
+def test_follow_own_codes_changes_nothing():
+    rng = np.random.default_rng(5)
+    W = rng.standard_normal((6, 64))
+    X = rng.standard_normal((300, 64)) @ rng.standard_normal((64, 64))
+    p = O.prepare(O.finalize_hessian(X.T @ X, 300), 0.01, True)
+    kw = dict(bits=3, group_size=16, sym=True, static_groups=False)
+    a = O.quantize_layer(W, p.U, p.perm, **kw)
+    b = O.quantize_layer(W, p.U, p.perm, **kw, follow=a.codes, tie_tol=2.0 ** -12)
+    assert b.ties == 0
+    np.testing.assert_array_equal(a.codes, b.codes)
+    np.testing.assert_array_equal(a.Q, b.Q)
+    # codes one level off everywhere are almost never float ties
+    c = O.quantize_layer(W, p.U, p.perm, **kw, follow=np.clip(a.codes + 1, 0, 7), tie_tol=2.0 ** -12)
+    assert c.ties <= 1
