@@ -72,12 +72,17 @@ GPTQ_DEV void group_params(float lo, float hi, const SweepParams& p, float& scal
 // 128 unrolled steps small matters: it has to stay in the instruction cache.
 template <int GS, int I>
 GPTQ_DEV void sweep_step(const SweepParams& p, const float (*Ub)[kB], const float (&dv)[8], int t,
-                         float (&v)[8], float (&sc)[8], float (&zr)[8], float (&qc)[8], float (&qv)[8],
-                         float (&er)[8], float& loss, int64_t row) {
+                         float (&v)[8], float (&sc)[8], float (&rc)[8], float (&zr)[8], float (&qc)[8],
+                         float (&qv)[8], float (&er)[8], float& loss, int64_t row, f32x4_t (&ua)[2],
+                         f32x4_t (&ub)[2]) {
   constexpr int r = I & 7, owner = I >> 3;
-  // this step's row of U is issued first; its latency hides behind the rounding
-  const f32x4_t u0 = *reinterpret_cast<const f32x4_t*>(&Ub[I][8 * t]);
-  const f32x4_t u1 = *reinterpret_cast<const f32x4_t*>(&Ub[I][8 * t + 4]);
+  // the next step's row of U is read now (two register sets), so its LDS
+  // latency hides behind this whole step
+  if constexpr (I + 1 < kB) {
+    ua[(I + 1) & 1] = *reinterpret_cast<const f32x4_t*>(&Ub[I + 1][8 * t]);
+    ub[(I + 1) & 1] = *reinterpret_cast<const f32x4_t*>(&Ub[I + 1][8 * t + 4]);
+  }
+  const f32x4_t u0 = ua[I & 1], u1 = ub[I & 1];
   // dynamic groups that start inside the block: range over the group's current values
   if constexpr (GS > 0 && (I % GS) == 0) {
     if (I < p.ncols) {
@@ -95,11 +100,13 @@ GPTQ_DEV void sweep_step(const SweepParams& p, const float (*Ub)[kB], const floa
       }
       float s, z;
       group_params(lo, hi, p, s, z);
+      const float y = 1.0f / s;
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
         const int c = 8 * t + k;
         const bool in = (c >= I) && (c < I + GS);
         sc[k] = in ? s : sc[k];
+        rc[k] = in ? y : rc[k];
         zr[k] = in ? z : zr[k];
       }
       if (t == owner && row < p.d_out) {
@@ -111,7 +118,14 @@ GPTQ_DEV void sweep_step(const SweepParams& p, const float (*Ub)[kB], const floa
   }
   const float w = v[r];
   const float s = sc[r], z = zr[r];
-  const float q = fminf(fmaxf(rintf(w / s) + z, 0.f), p.maxq);
+  // w / s correctly rounded from the correctly rounded reciprocal y = 1 / s:
+  // q0 = w y is within an ulp, the remainder w - s q0 is exact in one fma, and
+  // q0 + (w - s q0) y rounds to the quotient (Markstein's correction step).
+  // Three dependent operations instead of the division sequence.
+  const float y = rc[r];
+  const float q0 = w * y;
+  const float quot = fmaf(fmaf(-s, q0, w), y, q0);
+  const float q = fminf(fmaxf(rintf(quot) + z, 0.f), p.maxq);
   const float what = s * (q - z);
   const float err = (w - what) * dv[r];
   const float eb = row_bcast<owner>(err);
@@ -122,10 +136,13 @@ GPTQ_DEV void sweep_step(const SweepParams& p, const float (*Ub)[kB], const floa
   // end of the block and keeps every step's code alive until then
   asm volatile("" : "+v"(qc[r]), "+v"(qv[r]), "+v"(er[r]));
   loss = fmaf(eb, eb, loss);
+  // the next column first: the next step's decision waits on it
+  constexpr int rn = (I + 1) & 7;
+  v[rn] = fmaf(-eb, rn < 4 ? u0[rn & 3] : u1[rn & 3], v[rn]);
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    v[k] = fmaf(-eb, u0[k], v[k]);
-    v[k + 4] = fmaf(-eb, u1[k], v[k + 4]);
+    if (k != rn) v[k] = fmaf(-eb, u0[k], v[k]);
+    if (k + 4 != rn) v[k + 4] = fmaf(-eb, u1[k], v[k + 4]);
   }
   // keep each step a scheduling region of its own (bounded register pressure)
   __builtin_amdgcn_sched_barrier(0);
@@ -133,9 +150,12 @@ GPTQ_DEV void sweep_step(const SweepParams& p, const float (*Ub)[kB], const floa
 
 template <int GS, int... Is>
 GPTQ_DEV void sweep_all(const SweepParams& p, const float (*Ub)[kB], const float (&dv)[8], int t, float (&v)[8],
-                        float (&sc)[8], float (&zr)[8], float (&qc)[8], float (&qv)[8], float (&er)[8],
-                        float& loss, int64_t row, std::integer_sequence<int, Is...>) {
-  (sweep_step<GS, Is>(p, Ub, dv, t, v, sc, zr, qc, qv, er, loss, row), ...);
+                        float (&sc)[8], float (&rc)[8], float (&zr)[8], float (&qc)[8], float (&qv)[8],
+                        float (&er)[8], float& loss, int64_t row, std::integer_sequence<int, Is...>) {
+  f32x4_t ua[2], ub[2];
+  ua[0] = *reinterpret_cast<const f32x4_t*>(&Ub[0][8 * t]);
+  ub[0] = *reinterpret_cast<const f32x4_t*>(&Ub[0][8 * t + 4]);
+  (sweep_step<GS, Is>(p, Ub, dv, t, v, sc, rc, zr, qc, qv, er, loss, row, ua, ub), ...);
 }
 
 template <int GS>
@@ -156,7 +176,7 @@ __global__ __launch_bounds__(256) void sweep_kernel(SweepParams p) {
   }
   __syncthreads();
 
-  float v[8], sc[8], zr[8], qc[8], qv[8], er[8], dv[8];
+  float v[8], sc[8], rc[8], zr[8], qc[8], qv[8], er[8], dv[8];
   const int c0 = 8 * t;
   // 1 / U[i][i] of this lane's own columns (only the owner of a column uses it)
 #pragma unroll
@@ -175,6 +195,7 @@ __global__ __launch_bounds__(256) void sweep_kernel(SweepParams p) {
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
     sc[k] = 1.f;
+    rc[k] = 1.f;
     zr[k] = 0.f;
     qc[k] = 0.f;
     qv[k] = 0.f;
@@ -191,6 +212,7 @@ __global__ __launch_bounds__(256) void sweep_kernel(SweepParams p) {
         int64_t g = 0;
         if (p.group > 0) g = (p.preset && !p.identity) ? p.perm[j] / p.group : j / p.group;
         sc[k] = p.scales[g * p.d_out + row];
+        rc[k] = 1.0f / sc[k];
         zr[k] = static_cast<float>(p.zeros[g * p.d_out + row]);
       }
     }
@@ -215,9 +237,11 @@ __global__ __launch_bounds__(256) void sweep_kernel(SweepParams p) {
     hi = row_max16(hi);
     float s, z;
     group_params(lo, hi, p, s, z);
+    const float y = 1.0f / s;
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
       sc[k] = s;
+      rc[k] = y;
       zr[k] = z;
     }
     if (t == 0 && row_ok) {
@@ -229,7 +253,7 @@ __global__ __launch_bounds__(256) void sweep_kernel(SweepParams p) {
   __syncthreads();
 
   float loss = 0.f;
-  sweep_all<GS>(p, Ub, dv, t, v, sc, zr, qc, qv, er, loss, row, std::make_integer_sequence<int, kB>{});
+  sweep_all<GS>(p, Ub, dv, t, v, sc, rc, zr, qc, qv, er, loss, row, std::make_integer_sequence<int, kB>{});
 
   if (!row_ok) return;
   // normalised errors of the block, for the trailing update
