@@ -29,7 +29,7 @@ PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "hessian_bf16_4096x4096_N262144_counters.md")
 HESSIAN_SRC = os.path.join(ROOT, "post_weight_quantization_07_amd", "csrc", "hessian.hip")
-HESSIAN_KERNEL = "hessian_bf16_dma_kernel"
+HESSIAN_KERNEL = "hessian_bf16_pipe_kernel+hessian_reduce_kernel"
 
 
 def parse():
@@ -217,7 +217,7 @@ def main():
     f_upd = float(d_out) * d_in * (d_in - 1)
     achieved = f_h / (st["hessian"] * 1e-3) / 1e12
     rec = recorded_traffic()
-    roofline = {"kernel": HESSIAN_KERNEL + " (S += X^T X)", "bound": "mfma", "achieved": achieved,
+    roofline = {"kernel": "gptq_hessian_accumulate = " + HESSIAN_KERNEL + " (S += X^T X)", "bound": "mfma", "achieved": achieved,
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
                 "traffic": (rec["bytes_per_launch"] if rec else None),
                 "algorithmic_flops_per_launch": f_h, "launch_ms": st["hessian"]}
