@@ -105,61 +105,99 @@ __global__ void gather_kernel(const float* H, int64_t n, const int32_t* perm, co
   }
 }
 
-// Lower Cholesky of the 64x64 block held in L (LDS, pitch 68), by one wave:
-// lane r keeps row r in registers.  Right-looking, pipelined by one step: at
-// step j column j is complete; the step's update of column j + 1 is applied at
-// once (the next pivot depends on it, and l[j+1] comes by readlane), and its
-// updates of columns j + 2 .. 63 are applied during step j + 1 from the
-// column published in LDS one step earlier, so the LDS round trip overlaps
-// the pivot chain.  Every lane scales its column-j entry by 1 / sqrt(pivot):
-// lanes above the pivot only ever touch their own upper-triangle entries,
-// which are discarded.  Writes the factor to L (zeros above the diagonal) and
-// its transpose to LTq (LTq[c][q][u] = L[4u+q][c], the layout of the panel
-// solve), and returns through `fail` the first local pivot that is not
-// positive (or -1).
-GPTQ_DEV void factor_block_wave(float (*L)[68], float (*LTq)[4][16], f32x4_t (*colbuf)[kNB / 4], int lane,
-                                int& fail) {
-  float v[kNB];
+// Lower Cholesky of the 64x64 block held in L (LDS, pitch 68), blocked by 16
+// columns.  Sub-panel b (columns 16 b .. 16 b + 15, all rows) is factored by
+// one wave, lane r holding row r's 16 entries in registers; the rank-16 update
+// of the lower 16x16 blocks to its right then runs on MFMA, spread over the
+// workgroup's four waves.
+//
+// Sub-panel factor: right-looking, pipelined by one step: at step j column j
+// is complete; the step's update of column j + 1 is applied at once (the next
+// pivot depends on it, and l[j+1] comes by readlane), and its updates of the
+// sub-panel's later columns are applied during step j + 1 from the column
+// published in LDS one step earlier, so the LDS round trip overlaps the pivot
+// chain.  Every lane scales its column-j entry by 1 / sqrt(pivot): lanes above
+// the pivot only ever touch their own upper-triangle entries, which are
+// discarded (each sub-panel is written back with zeros above the diagonal,
+// also to LTq, the transposed layout of the row solve).  `fail` receives the
+// first pivot that is not positive.
+template <int b>
+GPTQ_DEV void factor_subpanel(float (*L)[68], float (*LTq)[4][16], f32x4_t (*colbuf)[kNB / 4], int lane,
+                              int& fail) {
+  constexpr int c0 = 16 * b;
+  float v[16];
 #pragma unroll
-  for (int c = 0; c < kNB; ++c) v[c] = L[lane][c];
-  fail = -1;
+  for (int c = 0; c < 16; ++c) v[c] = L[lane][c0 + c];
   float lp = 0.f;
-  f32x4_t xp[kNB / 4], xn[kNB / 4];  // column of the previous / current step, read back from LDS
+  f32x4_t xp[4], xn[4];  // published column of the previous / current step (sub-panel window)
 #pragma unroll
-  for (int j = 0; j < kNB; ++j) {
-    const float piv = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v[j]), j));
+  for (int jj = 0; jj < 16; ++jj) {
+    const int j = c0 + jj;
+    const float piv = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v[jj]), j));
     if (!(piv > 0.f) && fail < 0) fail = j;
     // hardware square root and reciprocal (about 1 ulp): the pivot chain is the
     // latency-critical path of the factorization
     const float inv = __builtin_amdgcn_rcpf(__builtin_amdgcn_sqrtf(piv));
-    const float l = v[j] * inv;
-    v[j] = l;
-    reinterpret_cast<float*>(colbuf[j & 1])[lane] = l;
+    const float l = v[jj] * inv;
+    v[jj] = l;
+    reinterpret_cast<float*>(colbuf[jj & 1])[lane] = l;
     // keep the publication above the reads of this buffer
     asm volatile("" ::: "memory");
     // read the column back now for the next step's update of columns j + 2 ..
 #pragma unroll
-    for (int q4 = (j + 2) >> 2; q4 < kNB / 4; ++q4) xn[q4] = colbuf[j & 1][q4];
-    if (j + 1 < kNB) {
+    for (int q = (jj + 2) >> 2; q < 4; ++q) xn[q] = colbuf[jj & 1][c0 / 4 + q];
+    if (jj + 1 < 16) {
       const float lj1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, l), j + 1));
-      v[j + 1] = fmaf(-l, lj1, v[j + 1]);
+      v[jj + 1] = fmaf(-l, lj1, v[jj + 1]);
     }
-    if (j >= 1) {
+    if (jj >= 1) {
 #pragma unroll
-      for (int q4 = (j + 1) >> 2; q4 < kNB / 4; ++q4)
+      for (int q = (jj + 1) >> 2; q < 4; ++q)
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          if (4 * q4 + e > j) v[4 * q4 + e] = fmaf(-lp, xp[q4][e], v[4 * q4 + e]);
+          if (4 * q + e > jj) v[4 * q + e] = fmaf(-lp, xp[q][e], v[4 * q + e]);
     }
     lp = l;
 #pragma unroll
-    for (int q4 = 0; q4 < kNB / 4; ++q4) xp[q4] = xn[q4];
+    for (int q = 0; q < 4; ++q) xp[q] = xn[q];
   }
+  // the sub-panel's columns are final: write them and their transpose for the
+  // row solve (LTq[c][q][u] = L[4u+q][c])
 #pragma unroll
-  for (int c = 0; c < kNB; ++c) {
-    const float x = (c <= lane) ? v[c] : 0.f;
-    L[lane][c] = x;
-    LTq[c][lane & 3][lane >> 2] = x;
+  for (int c = 0; c < 16; ++c) {
+    const float x = (c0 + c <= lane) ? v[c] : 0.f;
+    L[lane][c0 + c] = x;
+    LTq[c0 + c][lane & 3][lane >> 2] = x;
+  }
+}
+
+// Rank-16 update after sub-panel b: for the lower 16x16 blocks (I, J),
+// b < J <= I <= 3, L[I][J] -= P_I P_J^T with P_I = L[16 I .., 16 b ..].
+// v_mfma_f32_16x16x4_f32: lane l supplies A[l % 16][l / 16], B[l / 16][l % 16]
+// and holds D[4 (l / 16) + e][l % 16].  Block t goes to wave t % 4.
+template <int b>
+GPTQ_DEV void trailing_update(float (*L)[68], int wave, int lane) {
+  constexpr int n = 3 - b;  // trailing blocks per edge
+  const int m = lane & 15, kq = lane >> 4;
+  int t = 0;
+#pragma unroll
+  for (int i = 0; i < n; ++i) {
+#pragma unroll
+    for (int jb = 0; jb <= i; ++jb, ++t) {
+      if (t % 4 != wave) continue;
+      const int I = b + 1 + i, J = b + 1 + jb;
+      f32x4_t acc;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[e] = L[16 * I + 4 * kq + e][16 * J + m];
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) {
+        const float a = -L[16 * I + m][16 * b + 4 * tt + kq];
+        const float bb = L[16 * J + m][16 * b + 4 * tt + kq];
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a, bb, acc, 0, 0, 0);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) L[16 * I + 4 * kq + e][16 * J + m] = acc[e];
+    }
   }
 }
 
@@ -224,26 +262,41 @@ __global__ __launch_bounds__(256, 1) void panel_kernel(float* Hr, int64_t n, int
     xv[u] = 0.f;
   }
   __syncthreads();
+  int fail = -1;
+  if (wave == 0) factor_subpanel<0>(L, LTq, colbuf, lane, fail);
+  __syncthreads();
+  trailing_update<0>(L, wave, lane);
+  __syncthreads();
+  if (wave == 0) factor_subpanel<1>(L, LTq, colbuf, lane, fail);
+  __syncthreads();
+  trailing_update<1>(L, wave, lane);
+  __syncthreads();
+  if (wave == 0) factor_subpanel<2>(L, LTq, colbuf, lane, fail);
+  __syncthreads();
+  trailing_update<2>(L, wave, lane);
+  __syncthreads();
   if (wave == 0) {
-    int fail;
-    factor_block_wave(L, LTq, colbuf, lane, fail);
+    factor_subpanel<3>(L, LTq, colbuf, lane, fail);
     if (lane == 0 && blockIdx.x == 0 && fail >= 0 && fail < nb)
       atomicCAS(info, 0, static_cast<int32_t>(n - (k + fail)));
   }
   __syncthreads();
   if (tid < kNB) dinv[tid] = __builtin_amdgcn_rcpf(L[tid][tid]);
+  __syncthreads();
+  if (solve) {
+    solve_all(sv, xv, LTq, dinv, q, std::make_integer_sequence<int, kNB>{});
+    float* dst = Hr + row * n + k;
+#pragma unroll
+    for (int u = 0; u < 16; ++u) dst[4 * u + q] = xv[u];
+  }
+  // the factored diagonal block (L stays valid in LDS), after the solve so it
+  // does not hold up workgroup 0's rows
   if (blockIdx.x == 0) {
     for (int e = tid; e < nb * nb; e += 256) {
       const int r = e / nb, c = e - r * nb;
       Hr[(k + r) * n + k + c] = L[r][c];
     }
   }
-  __syncthreads();
-  if (!solve) return;
-  solve_all(sv, xv, LTq, dinv, q, std::make_integer_sequence<int, kNB>{});
-  float* dst = Hr + row * n + k;
-#pragma unroll
-  for (int u = 0; u < 16; ++u) dst[4 * u + q] = xv[u];
 }
 
 // Invert every 64x64 diagonal block of the lower factor in place.  Wave 0,
@@ -303,6 +356,7 @@ PrepLayout prepare_layout(int64_t d) {
   L.ws_bytes = off;
   return L;
 }
+
 
 #define GPTQ_TRY(x)                          \
   do {                                       \
