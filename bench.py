@@ -26,6 +26,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "GPTQ layer-solve ms & weight cols/s (4096×4096, N=262144); MFMA % peak"
 PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
+PEAK_FP32_TFLOPS = 157.3        # MI355X dense fp32 MFMA
 PEAK_HBM_GBS = 8000.0
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "hessian_bf16_4096x4096_N262144_counters.md")
 HESSIAN_SRC = os.path.join(ROOT, "post_weight_quantization_07_amd", "csrc", "hessian.hip")
@@ -42,6 +43,10 @@ def parse():
                     help="launch one device copy of this many MiB first (HBM counter calibration)")
     ap.add_argument("--cpu-sample-tokens", type=int, default=16384)
     ap.add_argument("--cpu-sample-rows", type=int, default=128)
+    ap.add_argument("--all-configs", metavar="PATH", default=None,
+                    help="instead of the one-line result: time every layer of the five configurations and write "
+                         "a markdown table to PATH")
+    ap.add_argument("--all-configs-steps", type=int, default=3)
     return ap.parse_args()
 
 
@@ -110,117 +115,200 @@ def cpu_baseline(layer, W_host, args):
     }
 
 
+def stage_metrics(layer, st):
+    """Algorithmic rates of the four stages and their fraction of the bound
+    that applies: MFMA peak (bf16 or fp32) for the contractions, HBM for the
+    sweep (approximated on the whole quantize stage) and the pack."""
+    d_out, d_in, N = layer.d_out, layer.d_in, layer.n_tokens
+    G = layer.group_size if layer.group_size > 0 else d_in
+    f_h = float(N) * d_in * (d_in + 1)
+    f_inv = 2.0 / 3.0 * d_in ** 3
+    f_upd = float(d_out) * d_in * (d_in - 1)
+    b_sweep = float(d_out) * d_in * (9 + 8.0 / G)
+    b_pack = float(d_out) * d_in * (1 + layer.bits / 8.0)
+    peak_h = PEAK_BF16_TFLOPS if layer.x_dtype == "bf16" else PEAK_FP32_TFLOPS
+
+    def rate(work, ms, scale):
+        return work / (ms * 1e-3) / scale
+    h = rate(f_h, st["hessian"], 1e12)
+    p_ = rate(f_inv, st["prepare"], 1e12)
+    q = rate(f_upd, st["quantize"], 1e12)
+    qb = rate(b_sweep, st["quantize"], 1e9)
+    k = rate(b_pack, st["pack"], 1e9)
+    return {
+        "hessian": {"ms": st["hessian"], "TFLOP/s": h, "peak": peak_h, "frac": h / peak_h, "flops": f_h},
+        "prepare": {"ms": st["prepare"], "TFLOP/s": p_, "peak": PEAK_FP32_TFLOPS, "frac": p_ / PEAK_FP32_TFLOPS,
+                    "flops": f_inv},
+        "quantize": {"ms": st["quantize"], "update TFLOP/s": q, "peak": PEAK_FP32_TFLOPS, "frac": q / PEAK_FP32_TFLOPS,
+                     "flops": f_upd, "sweep GB/s": qb, "sweep frac of HBM": qb / PEAK_HBM_GBS, "sweep bytes": b_sweep},
+        "pack": {"ms": st["pack"], "GB/s": k, "frac of HBM": k / PEAK_HBM_GBS, "bytes": b_pack},
+    }
+
+
+class LayerSolve:
+    """Inputs resident in HBM, outputs and workspaces allocated once; step()
+    runs one whole layer solve (zero S, accumulate all tokens in one call,
+    prepare, quantize, pack) on the current stream."""
+
+    def __init__(self, layer, copy_calib_mib=0):
+        import numpy as np
+        import torch
+
+        import post_weight_quantization_07_amd as G
+        import synth
+        self.G, self.layer, self.torch = G, layer, torch
+        dev = torch.device("cuda:0")
+        d_out, d_in, N = layer.d_out, layer.d_in, layer.n_tokens
+        self.cfg = cfg = G.QuantizeConfig(**layer.quant_kwargs())
+        self.W_host = synth.weight(layer)
+        if layer.w_dtype == "bf16":
+            self.W = torch.from_numpy(synth.bf16_bits(self.W_host).view(np.int16)).to(dev).view(torch.bfloat16)
+        else:
+            self.W = torch.from_numpy(self.W_host).to(dev)
+        bf16 = layer.x_dtype == "bf16"
+        self.X = torch.empty((N, d_in), dtype=torch.bfloat16 if bf16 else torch.float32, device=dev)
+        row = 0
+        for x in synth.activation_chunks_threaded(layer, workers=min(16, os.cpu_count() or 1), as_bf16_bits=bf16):
+            t = torch.from_numpy(x.view(np.int16)).view(torch.bfloat16) if bf16 else torch.from_numpy(x)
+            self.X[row:row + x.shape[0]].copy_(t)
+            row += x.shape[0]
+        assert row == N
+        self.S = torch.empty((d_in, d_in), dtype=torch.float32, device=dev)
+        self.U = torch.empty((d_in, d_in), dtype=torch.float32, device=dev)
+        self.perm = torch.empty(d_in, dtype=torch.int32, device=dev)
+        self.info = torch.empty(1, dtype=torch.int32, device=dev)
+        u8 = torch.uint8
+        self.ws_h = torch.empty(max(256, G.gptq_hessian_workspace_size(d_in, N, self.X.dtype)), dtype=u8, device=dev)
+        self.ws_p = torch.empty(max(256, G.gptq_prepare_workspace_size(d_in)), dtype=u8, device=dev)
+        self.ws_q = torch.empty(max(256, G.gptq_workspace_size(d_out, d_in, cfg)), dtype=u8, device=dev)
+        ng = cfg.n_groups(d_in)
+        self.out = {"codes": torch.empty((d_out, d_in), dtype=torch.uint8, device=dev),
+                    "scales": torch.empty((ng, d_out), dtype=torch.float32, device=dev),
+                    "zeros": torch.empty((ng, d_out), dtype=torch.int32, device=dev),
+                    "g_idx": torch.empty(d_in, dtype=torch.int32, device=dev),
+                    "row_loss": torch.empty(d_out, dtype=torch.float32, device=dev)}
+        self.qweight = torch.empty((d_in * cfg.bits // 32, d_out), dtype=torch.int32, device=dev)
+        if copy_calib_mib > 0:
+            a = torch.ones((copy_calib_mib << 20) // 4, dtype=torch.float32, device=dev)
+            b = torch.empty_like(a)
+            b.copy_(a)
+            torch.cuda.synchronize()
+            del a, b
+        self.ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+
+    def step(self, record=False):
+        G, ev, cfg = self.G, self.ev, self.cfg
+        self.S.zero_()
+        if record:
+            ev[0].record()
+        G.gptq_hessian_accumulate(self.S, self.X, ws=self.ws_h)
+        if record:
+            ev[1].record()
+        G.gptq_prepare_hinv(self.S, self.layer.n_tokens, cfg, U=self.U, perm=self.perm, info=self.info, ws=self.ws_p,
+                            check=False)
+        if record:
+            ev[2].record()
+        G.gptq_quantize_layer(self.W, self.U, self.perm, cfg, want_q=False, want_loss=True, out=self.out,
+                              ws=self.ws_q)
+        if record:
+            ev[3].record()
+        G.gptq_pack(self.out["codes"], cfg.bits, qweight=self.qweight)
+        if record:
+            ev[4].record()
+
+    def measure(self, steps, warmup):
+        """Wall ms per step over exactly `steps` steps (synchronised on both
+        sides), then the mean per-stage durations from HIP events."""
+        import numpy as np
+        torch = self.torch
+        for _ in range(warmup):
+            self.step()
+        torch.cuda.synchronize()
+        if int(self.info.item()) != 0:
+            raise RuntimeError(f"prepare reported a failed pivot: info={int(self.info.item())}")
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            self.step()
+        torch.cuda.synchronize()
+        ms_per_step = (time.perf_counter() - t0) * 1e3 / steps
+        stage_ms = {"hessian": [], "prepare": [], "quantize": [], "pack": []}
+        ev = self.ev
+        for _ in range(steps):
+            self.step(True)
+            torch.cuda.synchronize()
+            stage_ms["hessian"].append(ev[0].elapsed_time(ev[1]))
+            stage_ms["prepare"].append(ev[1].elapsed_time(ev[2]))
+            stage_ms["quantize"].append(ev[2].elapsed_time(ev[3]))
+            stage_ms["pack"].append(ev[3].elapsed_time(ev[4]))
+        codes_max = int(self.out["codes"].max().item())
+        assert 0 <= codes_max <= (1 << self.cfg.bits) - 1
+        return ms_per_step, {k: float(np.mean(v)) for k, v in stage_ms.items()}
+
+
+def all_configs(args):
+    """Every layer of the five configurations: ms per solve, weight columns/s
+    and each stage's rate with its fraction of the bound; a markdown table."""
+    import torch
+
+    import synth
+    lines = ["| cfg | layer | d_out x d_in | N | x | bits/G | ms per solve | weight cols/s | accumulate "
+             "TFLOP/s (% peak) | prepare TFLOP/s (% fp32) | quantize: update TFLOP/s (% fp32), sweep GB/s "
+             "(% HBM) | pack GB/s |",
+             "|---|---|---|---:|---|---|---:|---:|---:|---:|---:|---:|"]
+    for c in (1, 2, 3, 4, 5):
+        for layer in synth.config_layers(c):
+            print(f"[all-configs] cfg{c} {layer.name} {layer.d_out}x{layer.d_in} N={layer.n_tokens}", flush=True)
+            ls = LayerSolve(layer)
+            ms, st = ls.measure(args.all_configs_steps, 1)
+            m = stage_metrics(layer, st)
+            g = layer.group_size
+            lines.append(
+                f"| {c} | {layer.name} | {layer.d_out}x{layer.d_in} | {layer.n_tokens} | {layer.x_dtype} | "
+                f"b{layer.bits}/{g}{' act-order' if layer.desc_act else ''}{' static' if layer.static_groups else ''} | "
+                f"{ms:.2f} | {layer.d_in / (ms * 1e-3):,.0f} | "
+                f"{m['hessian']['TFLOP/s']:.0f} ({100 * m['hessian']['frac']:.1f}%) | "
+                f"{m['prepare']['TFLOP/s']:.1f} ({100 * m['prepare']['frac']:.1f}%) | "
+                f"{m['quantize']['update TFLOP/s']:.1f} ({100 * m['quantize']['frac']:.1f}%), "
+                f"{m['quantize']['sweep GB/s']:.0f} ({100 * m['quantize']['sweep frac of HBM']:.1f}%) | "
+                f"{m['pack']['GB/s']:.0f} |")
+            del ls
+            torch.cuda.empty_cache()
+    text = "\n".join(lines) + "\n"
+    with open(args.all_configs, "w") as f:
+        f.write(text)
+    print(text, flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the layer solve is measured on a single "
               "MI355X; multi-GPU sharding is described, not run.", file=sys.stderr)
         sys.exit(2)
-    import numpy as np
     import torch
 
-    import post_weight_quantization_07_amd as G
     import synth
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
-    dev = torch.device("cuda:0")
+    if args.all_configs:
+        all_configs(args)
+        return
     layer = synth.config_layers(3)[0]
     d_out, d_in, N = layer.d_out, layer.d_in, layer.n_tokens
-    cfg = G.QuantizeConfig(**layer.quant_kwargs())
     t_setup = time.perf_counter()
-
-    # ---- inputs resident in HBM -------------------------------------------
-    W_host = synth.weight(layer)
-    W = torch.from_numpy(synth.bf16_bits(W_host).view(np.int16)).to(dev).view(torch.bfloat16)
-    X = torch.empty((N, d_in), dtype=torch.bfloat16, device=dev)
-    row = 0
-    for bits in synth.activation_chunks_threaded(layer, workers=min(16, os.cpu_count() or 1), as_bf16_bits=True):
-        X[row:row + bits.shape[0]].copy_(torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16))
-        row += bits.shape[0]
-    assert row == N
-
-    # ---- outputs and workspaces (allocated once) --------------------------
-    S = torch.empty((d_in, d_in), dtype=torch.float32, device=dev)
-    U = torch.empty((d_in, d_in), dtype=torch.float32, device=dev)
-    perm = torch.empty(d_in, dtype=torch.int32, device=dev)
-    info = torch.empty(1, dtype=torch.int32, device=dev)
-    ws_h = torch.empty(max(256, G.gptq_hessian_workspace_size(d_in, N, torch.bfloat16)), dtype=torch.uint8, device=dev)
-    ws_p = torch.empty(max(256, G.gptq_prepare_workspace_size(d_in)), dtype=torch.uint8, device=dev)
-    ws_q = torch.empty(max(256, G.gptq_workspace_size(d_out, d_in, cfg)), dtype=torch.uint8, device=dev)
-    ng = cfg.n_groups(d_in)
-    out = {"codes": torch.empty((d_out, d_in), dtype=torch.uint8, device=dev),
-           "scales": torch.empty((ng, d_out), dtype=torch.float32, device=dev),
-           "zeros": torch.empty((ng, d_out), dtype=torch.int32, device=dev),
-           "g_idx": torch.empty(d_in, dtype=torch.int32, device=dev),
-           "row_loss": torch.empty(d_out, dtype=torch.float32, device=dev)}
-    qweight = torch.empty((d_in * cfg.bits // 32, d_out), dtype=torch.int32, device=dev)
-
-    if args.copy_calib_mib > 0:
-        nbytes = args.copy_calib_mib << 20
-        a = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
-        b = torch.empty_like(a)
-        b.copy_(a)
-        torch.cuda.synchronize()
-        del a, b
-
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
-    stage_ms = {"hessian": [], "prepare": [], "quantize": [], "pack": []}
-
-    def step(record: bool):
-        S.zero_()
-        if record:
-            ev[0].record()
-        G.gptq_hessian_accumulate(S, X, ws=ws_h)
-        if record:
-            ev[1].record()
-        G.gptq_prepare_hinv(S, N, cfg, U=U, perm=perm, info=info, ws=ws_p, check=False)
-        if record:
-            ev[2].record()
-        G.gptq_quantize_layer(W, U, perm, cfg, want_q=False, want_loss=True, out=out, ws=ws_q)
-        if record:
-            ev[3].record()
-        G.gptq_pack(out["codes"], cfg.bits, qweight=qweight)
-        if record:
-            ev[4].record()
-
+    ls = LayerSolve(layer, args.copy_calib_mib)
     torch.cuda.synchronize()
     t_setup = time.perf_counter() - t_setup
-    for _ in range(args.warmup):
-        step(False)
-    torch.cuda.synchronize()
-    if int(info.item()) != 0:
-        raise RuntimeError(f"prepare reported a failed pivot: info={int(info.item())}")
-
-    # ---- timed region: exactly K steps ------------------------------------
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step(False)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_per_step = wall * 1e3 / args.steps
-
-    # ---- per-stage launch durations (HIP events on the launch stream) -----
-    for _ in range(args.steps):
-        step(True)
-        torch.cuda.synchronize()
-        stage_ms["hessian"].append(ev[0].elapsed_time(ev[1]))
-        stage_ms["prepare"].append(ev[1].elapsed_time(ev[2]))
-        stage_ms["quantize"].append(ev[2].elapsed_time(ev[3]))
-        stage_ms["pack"].append(ev[3].elapsed_time(ev[4]))
-    st = {k: float(np.mean(v)) for k, v in stage_ms.items()}
-    codes_max = int(out["codes"].max().item())
-    assert 0 <= codes_max <= (1 << cfg.bits) - 1
-
-    f_h = float(N) * d_in * (d_in + 1)                    # algorithmic flops of X^T X (unique entries)
-    f_inv = 2.0 / 3.0 * d_in ** 3
-    f_upd = float(d_out) * d_in * (d_in - 1)
-    achieved = f_h / (st["hessian"] * 1e-3) / 1e12
+    ms_per_step, st = ls.measure(args.steps, args.warmup)
+    cfg = ls.cfg
+    m = stage_metrics(layer, st)
+    achieved = m["hessian"]["TFLOP/s"]
     rec = recorded_traffic()
-    roofline = {"kernel": "gptq_hessian_accumulate = " + HESSIAN_KERNEL + " (S += X^T X)", "bound": "mfma", "achieved": achieved,
-                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
-                "traffic": (rec["bytes_per_launch"] if rec else None),
-                "algorithmic_flops_per_launch": f_h, "launch_ms": st["hessian"]}
+    roofline = {"kernel": "gptq_hessian_accumulate = " + HESSIAN_KERNEL + " (S += X^T X)", "bound": "mfma",
+                "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": achieved / PEAK_BF16_TFLOPS, "traffic": (rec["bytes_per_launch"] if rec else None),
+                "algorithmic_flops_per_launch": m["hessian"]["flops"], "launch_ms": st["hessian"]}
 
     result = {
         "metric": METRIC,
@@ -240,13 +328,12 @@ def main():
                    "group_size": cfg.group_size, "sym": cfg.sym, "desc_act": cfg.desc_act,
                    "static_groups": cfg.static_groups, "damp_percent": cfg.damp_percent, "block_size": 128},
         "stages_ms": st,
-        "stage_tflops": {"hessian": achieved, "prepare_inverse": f_inv / (st["prepare"] * 1e-3) / 1e12,
-                         "quantize_update": f_upd / (st["quantize"] * 1e-3) / 1e12},
+        "stages": m,
         "roofline": roofline,
         "setup_s": t_setup,
     }
     if not args.no_cpu_baseline:
-        cb = cpu_baseline(layer, W_host, args)
+        cb = cpu_baseline(layer, ls.W_host, args)
         result["cpu_baseline"] = {k: cb[k] for k in ("value", "unit", "cores", "kind", "sample")}
         result["cpu_baseline"]["est_total_s"] = cb["est_total_s"]
         result["cpu_baseline"]["measured_s"] = cb["measured_s"]
