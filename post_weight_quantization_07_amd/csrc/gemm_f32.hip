@@ -41,14 +41,31 @@ struct GemmParams {
 };
 
 // Tile of workgroup b.  Workgroups go round-robin to the 8 XCDs (b % 8), each
-// with its own L2: the tile list is cut into 8 contiguous ranges, one per XCD.
-// Dense tiles are listed in groups of 8 tile rows, column by column inside a
-// group, so the tiles an XCD runs at once share rows of A and columns of B.
-// Lower-tile problems list the tiles (i >= j) row by row.  Triangular
-// operands make tiles unequal: they are listed heaviest first.
+// with its own L2: for equal tiles the tile list is cut into 8 contiguous
+// ranges, one per XCD.  Dense tiles are listed in groups of 8 tile rows,
+// column by column inside a group, so the tiles an XCD runs at once share rows
+// of A and columns of B.  Lower-tile problems list the tiles (i >= j) row by
+// row.
 GPTQ_DEV bool gemm_tile(const GemmParams& p, int b, int& z, int& tm, int& tn) {
   constexpr int kXcd = 8;
   const int G = p.tiles * p.batch;
+  if (p.tri != 0) {
+    // Unequal tiles: listed heaviest first in dispatch order (the batch index
+    // fastest), so every XCD gets an even mix and free slots take the
+    // heaviest tiles left.  B lower-triangular: work falls with the column;
+    // A lower-triangular: it grows with the row.
+    if (b >= G) return false;
+    const int t = b / p.batch;
+    z = b - t * p.batch;
+    if (p.tri == 1) {
+      tn = t / p.tiles_m;
+      tm = t - tn * p.tiles_m;
+    } else {
+      tm = p.tiles_m - 1 - t / p.tiles_n;
+      tn = t % p.tiles_n;
+    }
+    return true;
+  }
   const int x = b % kXcd, l = b / kXcd;
   const int base = G / kXcd, rem = G % kXcd;
   const int q = x * base + min(x, rem) + l;
@@ -61,16 +78,7 @@ GPTQ_DEV bool gemm_tile(const GemmParams& p, int b, int& z, int& tm, int& tn) {
     while ((i + 1) * (i + 2) / 2 <= t) ++i;
     tm = i;
     tn = t - i * (i + 1) / 2;
-  } else if (p.tri == 2) {
-    // A lower-triangular: the work of a tile grows with its row, so list
-    // groups of 8 tile columns (one per XCD range) with the heaviest rows first
-    const int g = t / (8 * p.tiles_m);
-    const int cols = min(8, p.tiles_n - 8 * g);
-    const int idx = t - g * 8 * p.tiles_m;
-    tm = p.tiles_m - 1 - idx / cols;
-    tn = 8 * g + idx % cols;
   } else {
-    // (with B lower-triangular the work falls with the column: heaviest first)
     const int g = t / (8 * p.tiles_n);
     const int rows = min(8, p.tiles_m - 8 * g);
     const int idx = t - g * 8 * p.tiles_n;
