@@ -23,7 +23,7 @@ hipError_t hessian_launch(const HessPlan& plan, float* S, int64_t d_in, const vo
                           int64_t n_tokens, int64_t ldx, void* ws, hipStream_t stream);
 
 // ---------------------------------------------------------------- prepare --
-constexpr int kPanel = 64;  // Cholesky panel / diagonal block width
+constexpr int kPanel = 128;  // Cholesky panel / diagonal block width
 
 struct PrepLayout {
   size_t off_hr, off_t, off_diag, off_lambda, ws_bytes;

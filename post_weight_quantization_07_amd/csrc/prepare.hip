@@ -16,11 +16,11 @@
 //   lambda     lambda = damp * mean(diag H)              (one workgroup, fixed order)
 //   order      perm by rank of -diag(H), ties by index   (stable sort by counting)
 //   gather     Hr[a][b] = H[p(a)][p(b)] + lambda d_ab, p(a) = perm[n-1-a], lower part
-//   panels     right-looking blocked Cholesky of Hr, 64-column panels:
-//                panel kernel: factor the 64x64 diagonal block (one wave, rows in
-//                registers), then solve the panel rows below against it;
-//                trailing update Hr[k+64:, k+64:] -= P P^T on MFMA (lower tiles)
-//   diag inv   invert every 64x64 diagonal block of the factor in place
+//   panels     right-looking blocked Cholesky of Hr, 128-column panels:
+//                panel kernel: factor and invert the 128x128 diagonal block in
+//                LDS, solve the panel rows below as a product with that
+//                inverse, leave the inverse in place of the block;
+//                trailing update Hr[k+128:, k+128:] -= P P^T on MFMA (lower tiles)
 //   trtri      recursive doubling: for neighbouring inverted blocks A^-1, C^-1
 //              and the factor block L21 below A, M21 = -C^-1 (L21 A^-1)
 //   reverse    U[i][j] = M[n-1-i][n-1-j] for j >= i, 0 below the diagonal
@@ -32,7 +32,7 @@
 namespace gptq {
 namespace {
 
-constexpr int kNB = kPanel;  // 64
+constexpr int kNB = kPanel;  // 128
 
 __global__ void finalize_kernel(float* S, int64_t n, float scale, float* diag) {
   const int64_t total = n * n;
@@ -105,225 +105,504 @@ __global__ void gather_kernel(const float* H, int64_t n, const int32_t* perm, co
   }
 }
 
-// Lower Cholesky of the 64x64 block held in L (LDS, pitch 68), blocked by 16
-// columns.  Sub-panel b (columns 16 b .. 16 b + 15, all rows) is factored by
-// one wave, lane r holding row r's 16 entries in registers; the rank-16 update
-// of the lower 16x16 blocks to its right then runs on MFMA, spread over the
-// workgroup's four waves.
+// ------------------------------------------------------------ panel kernel --
+// One launch per 128-column panel k.  Every workgroup factors the 128x128
+// diagonal block (the same arithmetic, so the same result) and inverts it, on
+// LDS: L holds the block and its factor, M its inverse.  The block is taken as
+// two 64-column halves (A11 A21 ; A21 A22):
+//   L11 = chol(A11);  L21 = A21 L11^-T;  L22 = chol(A22 - L21 L21^T)
+//   M = L^-1 = (L11^-1 0 ; -L22^-1 L21 L11^-1  L22^-1)
+// The triangular solve of the rows below the block against L is then a
+// product with M: X = P M^T, 32 rows per pass.  Workgroup 0 only stores M as
+// the diagonal block of the factor's inverse, which the recursive-doubling
+// inverse uses as its first level; workgroups 1.. solve the rows.
+constexpr int kLP = kNB + 4;    // LDS row pitch (floats)
+constexpr int kChunk = 32;      // panel rows solved per pass
+constexpr int kMaxPanelWG = 256;
+using Blk = float (*)[kLP];
+
+// v_mfma_f32_16x16x4_f32: lane l supplies A[l % 16][l / 16] and
+// B[l / 16][l % 16] and holds D[4 (l / 16) + e][l % 16] in element e.
+GPTQ_DEV f32x4_t mfma4(float a, float b, f32x4_t acc) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc, 0, 0, 0);
+}
+
+// acc += sign * A B over one 16-deep slice: A(m, k) = pa[ar + m][ac + k];
+// B(k, n) = pb[br + k][bc + n], or pb[br + n][bc + k] when BT.  MFMA step s
+// takes k = 4 q + s in lane group q (the same order for A and B), so a lane's
+// four A values, and its four B values when BT, are one 16-byte LDS read.
+template <bool BT>
+GPTQ_DEV f32x4_t mma16(const float (*pa)[kLP], int ar, int ac, const float (*pb)[kLP], int br, int bc,
+                       f32x4_t acc, float sign, int lane) {
+  const int m = lane & 15, q = lane >> 4;
+  const f32x4_t a = *reinterpret_cast<const f32x4_t*>(&pa[ar + m][ac + 4 * q]);
+  f32x4_t b;
+  if (BT) {
+    b = *reinterpret_cast<const f32x4_t*>(&pb[br + m][bc + 4 * q]);
+  } else {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) b[s] = pb[br + 4 * q + s][bc + m];
+  }
+#pragma unroll
+  for (int s = 0; s < 4; ++s) acc = mfma4(sign * a[s], b[s], acc);
+  return acc;
+}
+
+GPTQ_DEV f32x4_t load16(const float (*p)[kLP], int r, int c, int lane) {
+  const int m = lane & 15, q = lane >> 4;
+  f32x4_t v;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) v[e] = p[r + 4 * q + e][c + m];
+  return v;
+}
+
+GPTQ_DEV void store16(float (*p)[kLP], int r, int c, f32x4_t v, int lane) {
+  const int m = lane & 15, q = lane >> 4;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) p[r + 4 * q + e][c + m] = v[e];
+}
+
+// Operand fragments of one 16-deep slice, k = 4 q + s as in mma16:
+// rows(p, r, c): lane (m, q) holds p[r + m][c + 4 q .. 4 q + 3] (an A operand,
+// or a B operand read transposed); cols(p, r, c): p[r + 4 q + s][c + m] (a B
+// operand read as stored).
+GPTQ_DEV f32x4_t frag_rows(const float (*p)[kLP], int r, int c, int lane) {
+  return *reinterpret_cast<const f32x4_t*>(&p[r + (lane & 15)][c + 4 * (lane >> 4)]);
+}
+GPTQ_DEV f32x4_t frag_cols(const float (*p)[kLP], int r, int c, int lane) {
+  f32x4_t v;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) v[s] = p[r + 4 * (lane >> 4) + s][c + (lane & 15)];
+  return v;
+}
+GPTQ_DEV f32x4_t mma_frag(f32x4_t a, f32x4_t b, f32x4_t acc) {
+#pragma unroll
+  for (int s = 0; s < 4; ++s) acc = mfma4(a[s], b[s], acc);
+  return acc;
+}
+
+// Lower Cholesky of the 64x64 block of L at (base, base), blocked by 16
+// columns.  Sub-panel b (columns 16 b .. 16 b + 15 of the block, all its rows)
+// is factored by wave 0, lane r holding row base + r's 16 entries in
+// registers; the rank-16 update of the lower 16x16 blocks to its right runs on
+// MFMA, spread over the four waves.
 //
-// Sub-panel factor: right-looking, pipelined by one step: at step j column j
-// is complete; the step's update of column j + 1 is applied at once (the next
-// pivot depends on it, and l[j+1] comes by readlane), and its updates of the
-// sub-panel's later columns are applied during step j + 1 from the column
-// published in LDS one step earlier, so the LDS round trip overlaps the pivot
-// chain.  Every lane scales its column-j entry by 1 / sqrt(pivot): lanes above
-// the pivot only ever touch their own upper-triangle entries, which are
-// discarded (each sub-panel is written back with zeros above the diagonal,
-// also to LTq, the transposed layout of the row solve).  `fail` receives the
-// first pivot that is not positive.
-template <int b>
-GPTQ_DEV void factor_subpanel(float (*L)[68], float (*LTq)[4][16], f32x4_t (*colbuf)[kNB / 4], int lane,
-                              int& fail) {
+// Sub-panel factor, right-looking: at step j the pivot comes from lane j by
+// readlane, every lane scales its column-j entry by 1 / sqrt(pivot) (hardware
+// reciprocal square root, about 1 ulp; the pivot chain is the latency-critical
+// path), and each later column c of the sub-panel takes -l[lane][j] l[c][j]
+// with l[c][j] broadcast from lane c as a scalar operand.  The update of
+// column j + 1 comes first, since the next pivot waits for it.  Lanes above
+// the pivot only touch their own upper-triangle entries, which are discarded
+// (the sub-panel is written back with zeros above the diagonal).  A pivot that
+// is not positive (or not finite) leaves a NaN or zero on the diagonal, which
+// the caller checks.
+template <int base, int b>
+GPTQ_DEV void factor_subpanel(Blk L, int lane) {
   constexpr int c0 = 16 * b;
   float v[16];
 #pragma unroll
-  for (int c = 0; c < 16; ++c) v[c] = L[lane][c0 + c];
-  float lp = 0.f;
-  f32x4_t xp[4], xn[4];  // published column of the previous / current step (sub-panel window)
+  for (int c = 0; c < 16; ++c) v[c] = L[base + lane][base + c0 + c];
 #pragma unroll
   for (int jj = 0; jj < 16; ++jj) {
-    const int j = c0 + jj;
-    const float piv = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v[jj]), j));
-    if (!(piv > 0.f) && fail < 0) fail = j;
-    // hardware square root and reciprocal (about 1 ulp): the pivot chain is the
-    // latency-critical path of the factorization
-    const float inv = __builtin_amdgcn_rcpf(__builtin_amdgcn_sqrtf(piv));
-    const float l = v[jj] * inv;
+    const float piv = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v[jj]), c0 + jj));
+    const float l = v[jj] * __builtin_amdgcn_rsqf(piv);
     v[jj] = l;
-    reinterpret_cast<float*>(colbuf[jj & 1])[lane] = l;
-    // keep the publication above the reads of this buffer
-    asm volatile("" ::: "memory");
-    // read the column back now for the next step's update of columns j + 2 ..
 #pragma unroll
-    for (int q = (jj + 2) >> 2; q < 4; ++q) xn[q] = colbuf[jj & 1][c0 / 4 + q];
-    if (jj + 1 < 16) {
-      const float lj1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, l), j + 1));
-      v[jj + 1] = fmaf(-l, lj1, v[jj + 1]);
+    for (int c = jj + 1; c < 16; ++c) {
+      const float lc = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, l), c0 + c));
+      v[c] = fmaf(-l, lc, v[c]);
     }
-    if (jj >= 1) {
-#pragma unroll
-      for (int q = (jj + 1) >> 2; q < 4; ++q)
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (4 * q + e > jj) v[4 * q + e] = fmaf(-lp, xp[q][e], v[4 * q + e]);
-    }
-    lp = l;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) xp[q] = xn[q];
   }
-  // the sub-panel's columns are final: write them and their transpose for the
-  // row solve (LTq[c][q][u] = L[4u+q][c])
 #pragma unroll
-  for (int c = 0; c < 16; ++c) {
-    const float x = (c0 + c <= lane) ? v[c] : 0.f;
-    L[lane][c0 + c] = x;
-    LTq[c0 + c][lane & 3][lane >> 2] = x;
-  }
+  for (int c = 0; c < 16; ++c) L[base + lane][base + c0 + c] = (c0 + c <= lane) ? v[c] : 0.f;
 }
 
 // Rank-16 update after sub-panel b: for the lower 16x16 blocks (I, J),
-// b < J <= I <= 3, L[I][J] -= P_I P_J^T with P_I = L[16 I .., 16 b ..].
-// v_mfma_f32_16x16x4_f32: lane l supplies A[l % 16][l / 16], B[l / 16][l % 16]
-// and holds D[4 (l / 16) + e][l % 16].  Block t goes to wave t % 4.
-template <int b>
-GPTQ_DEV void trailing_update(float (*L)[68], int wave, int lane) {
-  constexpr int n = 3 - b;  // trailing blocks per edge
-  const int m = lane & 15, kq = lane >> 4;
+// b < J <= I <= 3, of the 64 block at base: L[I][J] -= P_I P_J^T with
+// P_I = L[I][b].  Block t goes to wave t % 4.
+template <int base, int b>
+GPTQ_DEV void trailing_update(Blk L, int wave, int lane) {
+  constexpr int nt = 3 - b;  // trailing blocks per edge
   int t = 0;
 #pragma unroll
-  for (int i = 0; i < n; ++i) {
+  for (int i = 0; i < nt; ++i) {
 #pragma unroll
     for (int jb = 0; jb <= i; ++jb, ++t) {
       if (t % 4 != wave) continue;
-      const int I = b + 1 + i, J = b + 1 + jb;
-      f32x4_t acc;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) acc[e] = L[16 * I + 4 * kq + e][16 * J + m];
-#pragma unroll
-      for (int tt = 0; tt < 4; ++tt) {
-        const float a = -L[16 * I + m][16 * b + 4 * tt + kq];
-        const float bb = L[16 * J + m][16 * b + 4 * tt + kq];
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a, bb, acc, 0, 0, 0);
-      }
-#pragma unroll
-      for (int e = 0; e < 4; ++e) L[16 * I + 4 * kq + e][16 * J + m] = acc[e];
+      const int I = base + 16 * (b + 1 + i), J = base + 16 * (b + 1 + jb);
+      f32x4_t acc = load16(L, I, J, lane);
+      acc = mma16<true>(L, I, base + 16 * b, L, J, base + 16 * b, acc, -1.f, lane);
+      store16(L, I, J, acc, lane);
     }
   }
 }
 
-// One launch per panel k: every workgroup factors the 64x64 diagonal block
-// (the same arithmetic, so the same result), workgroup 0 stores it, and the
-// workgroup then solves 64 panel rows x L^T = p against it.  Each row is
-// solved by a quad of lanes, lane q holding columns q, q+4, ..., q+60:
-// right-looking substitution (once x_c is known, every later column of the row
-// is updated at once) keeps the dependent chain at 64 steps, and x_c reaches
-// the other three lanes of the quad through a DPP quad broadcast.
-constexpr int kPanelRows = 64;
-
-template <int Q>
-GPTQ_DEV float quad_bcast(float v) {
-  constexpr int sel = Q | (Q << 2) | (Q << 4) | (Q << 6);
-  return __builtin_amdgcn_update_dpp(0.0f, v, sel, 0xf, 0xf, false);
+template <int base>
+GPTQ_DEV void factor64(Blk L, int wave, int lane) {
+  if (wave == 0) factor_subpanel<base, 0>(L, lane);
+  __syncthreads();
+  trailing_update<base, 0>(L, wave, lane);
+  __syncthreads();
+  if (wave == 0) factor_subpanel<base, 1>(L, lane);
+  __syncthreads();
+  trailing_update<base, 1>(L, wave, lane);
+  __syncthreads();
+  if (wave == 0) factor_subpanel<base, 2>(L, lane);
+  __syncthreads();
+  trailing_update<base, 2>(L, wave, lane);
+  __syncthreads();
+  if (wave == 0) factor_subpanel<base, 3>(L, lane);
+  __syncthreads();
 }
 
-template <int C>
-GPTQ_DEV void solve_step(float (&sv)[16], float (&xv)[16], const float (*LTq)[4][16], const float* dinv, int q) {
-  constexpr int owner = C & 3, u = C >> 2;
-  const float xc = quad_bcast<owner>(sv[u] * dinv[C]);
-  xv[u] = (q == owner) ? xc : xv[u];
-  // column C of L for this lane's columns 4 k + q (zeros above the diagonal)
-  const f32x4_t* lt = reinterpret_cast<const f32x4_t*>(&LTq[C][q][0]);
+// One doubling level of the inverse of a lower factor: for NP pairs of
+// neighbouring inverted diagonal blocks (A^-1 at c0, C^-1 at r0 = c0 + 16 H,
+// each 16 H wide, pair p at c0 = cb + 32 H p) with the factor block L21 below
+// A, M21 = -C^-1 (L21 A^-1), written into M at (r0, c0).  T = L21 A^-1 passes
+// through the same place.  The 16x16 output blocks of a pair are spread over
+// the waves so that every wave gets the same number of MFMA slices when H = 4.
+template <int H, int NP>
+GPTQ_DEV void inverse_level(Blk L, Blk M, int cb, int wave, int lane) {
+  constexpr int NI = NP * H * H;
+  f32x4_t acc[NI];
+  auto owner = [](int p, int I, int J) { return (p * H * H + I * H + (I + J) % H) % 4; };
 #pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    const f32x4_t l4 = lt[w];
+  for (int p = 0; p < NP; ++p) {
+    const int c0 = cb + 32 * H * p, r0 = c0 + 16 * H;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) sv[4 * w + e] = fmaf(-xc, l4[e], sv[4 * w + e]);
+    for (int I = 0; I < H; ++I)
+#pragma unroll
+      for (int J = 0; J < H; ++J) {
+        if (owner(p, I, J) != wave) continue;
+        f32x4_t t = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int K = J; K < H; ++K)  // A^-1 is lower triangular
+          t = mma16<false>(L, r0 + 16 * I, c0 + 16 * K, M, c0 + 16 * K, c0 + 16 * J, t, 1.f, lane);
+        store16(M, r0 + 16 * I, c0 + 16 * J, t, lane);
+      }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int p = 0; p < NP; ++p) {
+    const int c0 = cb + 32 * H * p, r0 = c0 + 16 * H;
+#pragma unroll
+    for (int I = 0; I < H; ++I)
+#pragma unroll
+      for (int J = 0; J < H; ++J) {
+        if (owner(p, I, J) != wave) continue;
+        f32x4_t t = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int K = 0; K <= I; ++K)  // C^-1 is lower triangular
+          t = mma16<false>(M, r0 + 16 * I, r0 + 16 * K, M, r0 + 16 * K, c0 + 16 * J, t, -1.f, lane);
+        acc[(p * H + I) * H + J] = t;
+      }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int p = 0; p < NP; ++p) {
+    const int c0 = cb + 32 * H * p, r0 = c0 + 16 * H;
+#pragma unroll
+    for (int I = 0; I < H; ++I)
+#pragma unroll
+      for (int J = 0; J < H; ++J)
+        if (owner(p, I, J) == wave) store16(M, r0 + 16 * I, c0 + 16 * J, acc[(p * H + I) * H + J], lane);
+  }
+  __syncthreads();
+}
+
+// M = inverse of the factored 64x64 block of L at (base, base): the four 16x16
+// diagonal blocks by forward substitution (wave 0, lane = 16 block + column,
+// one column of the inverse per lane, zeros above the diagonal), then two
+// doubling levels.
+template <int base>
+GPTQ_DEV void inverse64(Blk L, Blk M, int wave, int lane) {
+  if (wave == 0) {
+    const int o = base + 16 * (lane >> 4), c = lane & 15;
+    float x[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      float s = (i == c) ? 1.f : 0.f;
+#pragma unroll
+      for (int t = 0; t < i; ++t) s = fmaf(-L[o + i][o + t], x[t], s);
+      x[i] = s * __builtin_amdgcn_rcpf(L[o + i][o + i]);
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) M[o + i][o + c] = x[i];
+  }
+  __syncthreads();
+  inverse_level<1, 2>(L, M, base, wave, lane);
+  inverse_level<2, 1>(L, M, base, wave, lane);
+}
+
+// ---- the per-wave MFMA work of the 128 block, K-slices outermost so that a
+// wave's output blocks form independent accumulation chains sharing operands.
+// Block indices are in 16s; the 64-halves start at 0 and 64.
+
+// L21[I][J] = sum_{K <= J} A21[I][K] (L11^-1)[J][K]^T, wave = row I.
+template <int I>
+GPTQ_DEV void l21_row(Blk L, Blk M, int lane, f32x4_t (&acc)[4]) {
+#pragma unroll
+  for (int J = 0; J < 4; ++J) acc[J] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int K = 0; K < 4; ++K) {
+    const f32x4_t a = frag_rows(L, 64 + 16 * I, 16 * K, lane);
+#pragma unroll
+    for (int J = K; J < 4; ++J) acc[J] = mma_frag(a, frag_rows(M, 16 * J, 16 * K, lane), acc[J]);
   }
 }
 
-template <int... Cs>
-GPTQ_DEV void solve_all(float (&sv)[16], float (&xv)[16], const float (*LTq)[4][16], const float* dinv, int q,
-                        std::integer_sequence<int, Cs...>) {
-  (solve_step<Cs>(sv, xv, LTq, dinv, q), ...);
+// A22[I][J] -= sum_K L21[I][K] L21[J][K]^T for J in [J0, J0 + NJ) (J <= I).
+template <int I, int J0, int NJ>
+GPTQ_DEV void a22_row(Blk L, int lane) {
+  f32x4_t acc[NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) acc[j] = load16(L, 64 + 16 * I, 64 + 16 * (J0 + j), lane);
+#pragma unroll
+  for (int K = 0; K < 4; ++K) {
+    const f32x4_t a = -frag_rows(L, 64 + 16 * I, 16 * K, lane);
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) acc[j] = mma_frag(a, frag_rows(L, 64 + 16 * (J0 + j), 16 * K, lane), acc[j]);
+  }
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) store16(L, 64 + 16 * I, 64 + 16 * (J0 + j), acc[j], lane);
+}
+
+// T[I][J] = sum_{K >= J} L21[I][K] (L11^-1)[K][J], wave = row I; T goes to
+// M's lower-left 64 block.
+template <int I>
+GPTQ_DEV void t_row(Blk L, Blk M, int lane) {
+  f32x4_t acc[4];
+#pragma unroll
+  for (int J = 0; J < 4; ++J) acc[J] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int K = 0; K < 4; ++K) {
+    const f32x4_t a = frag_rows(L, 64 + 16 * I, 16 * K, lane);
+#pragma unroll
+    for (int J = 0; J <= K; ++J) acc[J] = mma_frag(a, frag_cols(M, 16 * K, 16 * J, lane), acc[J]);
+  }
+#pragma unroll
+  for (int J = 0; J < 4; ++J) store16(M, 64 + 16 * I, 16 * J, acc[J], lane);
+}
+
+// M21[I][J] = -sum_{K <= I} (L22^-1)[I][K] T[K][J], wave = column J.
+template <int J>
+GPTQ_DEV void m21_col(Blk M, int lane, f32x4_t (&acc)[4]) {
+#pragma unroll
+  for (int I = 0; I < 4; ++I) acc[I] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int K = 0; K < 4; ++K) {
+    const f32x4_t b = frag_cols(M, 64 + 16 * K, 16 * J, lane);
+#pragma unroll
+    for (int I = K; I < 4; ++I) acc[I] = mma_frag(-frag_rows(M, 64 + 16 * I, 64 + 16 * K, lane), b, acc[I]);
+  }
+}
+
+// X = P M^T for the 32 staged rows (L rows 0..31): output blocks (I, J) with
+// I in {0, 1} and J in {W, 7 - W}; block (I, J) needs slices K <= J.
+template <int W>
+GPTQ_DEV void solve_rows(Blk L, Blk M, int lane, f32x4_t (&acc)[4]) {
+  constexpr int J1 = W, J2 = 7 - W;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int K = 0; K <= J2; ++K) {
+    const f32x4_t a0 = frag_rows(L, 0, 16 * K, lane), a1 = frag_rows(L, 16, 16 * K, lane);
+    const f32x4_t b2 = frag_rows(M, 16 * J2, 16 * K, lane);
+    if (K <= J1) {
+      const f32x4_t b1 = frag_rows(M, 16 * J1, 16 * K, lane);
+      acc[0] = mma_frag(a0, b1, acc[0]);
+      acc[1] = mma_frag(a1, b1, acc[1]);
+    }
+    acc[2] = mma_frag(a0, b2, acc[2]);
+    acc[3] = mma_frag(a1, b2, acc[3]);
+  }
 }
 
 __global__ __launch_bounds__(256, 1) void panel_kernel(float* Hr, int64_t n, int64_t k, int32_t* info) {
-  __shared__ __attribute__((aligned(16))) float L[kNB][68];
-  __shared__ __attribute__((aligned(16))) float LTq[kNB][4][16];  // LTq[c][q][u] = L[4u+q][c]
-  __shared__ f32x4_t colbuf[2][kNB / 4];
-  __shared__ float dinv[kNB];
+  __shared__ __attribute__((aligned(16))) float L[kNB][kLP];
+  __shared__ __attribute__((aligned(16))) float M[kNB][kLP];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nb = static_cast<int>(std::min<int64_t>(kNB, n - k));
-  for (int e = tid; e < kNB * kNB; e += 256) {
-    const int r = e >> 6, c = e & 63;
-    float v = (r == c) ? 1.f : 0.f;
-    if (r < nb && c <= r) v = Hr[(k + r) * n + k + c];
-    L[r][c] = v;
-  }
-  // this thread's panel row (quad q holds columns q, q + 4, ..., q + 60):
-  // loaded now, so the load overlaps the factorization
-  const int q = tid & 3;
-  const int64_t row = k + kNB + static_cast<int64_t>(blockIdx.x) * kPanelRows + (tid >> 2);
-  const bool solve = (nb == kNB) && (row < n);
-  float sv[16], xv[16];
+  const int64_t below = (nb == kNB) ? n - k - kNB : 0;
+  const int64_t chunks = (below + kChunk - 1) / kChunk;
+  // workgroup 0 stores M; the others solve chunks blockIdx - 1, + (grid - 1), ...
+  const int64_t ch0 = static_cast<int64_t>(blockIdx.x) - 1, chs = static_cast<int64_t>(gridDim.x) - 1;
+  // 16-byte rows: every row of the block and of the panel starts 16-byte aligned
+  const bool vec = (n & 3) == 0 && nb == kNB;
+
+  // The diagonal block (lower part; identity past a ragged end) and this
+  // workgroup's first 32 panel rows.  Every load reads an in-range address
+  // (clamped into the block's lower part or the last row) and the value is
+  // selected after, so all loads are in flight at once.
+  float pv[kChunk * kNB / 256];
+  const int vr = tid >> 5, vc = 4 * (tid & 31);  // float4 layout: 8 rows x 32 float4 per pass
+  const int sr = tid >> 7, sc = tid & 127;       // scalar layout: 2 rows x 128 per pass
+  auto load_rows = [&](int64_t ch) {
+    const bool live = ch >= 0 && ch < chunks;
+    const int64_t r0 = k + kNB + ch * kChunk;
+    if (vec) {
 #pragma unroll
-  for (int u = 0; u < 16; ++u) {
-    sv[u] = solve ? Hr[row * n + k + 4 * u + q] : 0.f;
-    xv[u] = 0.f;
-  }
-  __syncthreads();
-  int fail = -1;
-  if (wave == 0) factor_subpanel<0>(L, LTq, colbuf, lane, fail);
-  __syncthreads();
-  trailing_update<0>(L, wave, lane);
-  __syncthreads();
-  if (wave == 0) factor_subpanel<1>(L, LTq, colbuf, lane, fail);
-  __syncthreads();
-  trailing_update<1>(L, wave, lane);
-  __syncthreads();
-  if (wave == 0) factor_subpanel<2>(L, LTq, colbuf, lane, fail);
-  __syncthreads();
-  trailing_update<2>(L, wave, lane);
-  __syncthreads();
-  if (wave == 0) {
-    factor_subpanel<3>(L, LTq, colbuf, lane, fail);
-    if (lane == 0 && blockIdx.x == 0 && fail >= 0 && fail < nb)
-      atomicCAS(info, 0, static_cast<int32_t>(n - (k + fail)));
-  }
-  __syncthreads();
-  if (tid < kNB) dinv[tid] = __builtin_amdgcn_rcpf(L[tid][tid]);
-  __syncthreads();
-  if (solve) {
-    solve_all(sv, xv, LTq, dinv, q, std::make_integer_sequence<int, kNB>{});
-    float* dst = Hr + row * n + k;
+      for (int i = 0; i < kChunk / 8; ++i) {
+        const int64_t row = r0 + 8 * i + vr;
+        const f32x4_t x = *reinterpret_cast<const f32x4_t*>(Hr + std::min<int64_t>(row, n - 1) * n + k + vc);
 #pragma unroll
-    for (int u = 0; u < 16; ++u) dst[4 * u + q] = xv[u];
+        for (int e = 0; e < 4; ++e) pv[4 * i + e] = (live && row < n) ? x[e] : 0.f;
+      }
+    } else {
+      const int64_t col = std::min<int64_t>(k + sc, n - 1);
+#pragma unroll
+      for (int i = 0; i < kChunk / 2; ++i) {
+        const int64_t row = r0 + 2 * i + sr;
+        const float x = Hr[std::min<int64_t>(row, n - 1) * n + col];
+        pv[i] = (live && row < n) ? x : 0.f;
+      }
+    }
+  };
+  auto stage_rows = [&]() {
+    if (vec) {
+#pragma unroll
+      for (int i = 0; i < kChunk / 8; ++i)
+        *reinterpret_cast<f32x4_t*>(&L[8 * i + vr][vc]) = f32x4_t{pv[4 * i], pv[4 * i + 1], pv[4 * i + 2], pv[4 * i + 3]};
+    } else {
+#pragma unroll
+      for (int i = 0; i < kChunk / 2; ++i) L[2 * i + sr][sc] = pv[i];
+    }
+  };
+  if (vec) {
+    f32x4_t lv[kNB / 8];
+#pragma unroll
+    for (int i = 0; i < kNB / 8; ++i) {
+      const int r = 8 * i + vr;
+      lv[i] = *reinterpret_cast<const f32x4_t*>(Hr + (k + r) * n + k + std::min(vc, r & ~3));
+    }
+    load_rows(ch0);
+#pragma unroll
+    for (int i = 0; i < kNB / 8; ++i) {
+      const int r = 8 * i + vr;
+      f32x4_t x = lv[i];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[e] = (vc + e <= r) ? x[e] : 0.f;
+      *reinterpret_cast<f32x4_t*>(&L[r][vc]) = x;
+    }
+  } else {
+    float lv[kNB * kNB / 256];
+#pragma unroll
+    for (int i = 0; i < kNB * kNB / 256; ++i) {
+      const int r = 2 * i + sr;
+      const int rr = std::min(r, nb - 1), cc = std::min(sc, rr);
+      const float x = Hr[(k + rr) * n + k + cc];
+      lv[i] = (r < nb && sc <= r) ? x : ((r == sc) ? 1.f : 0.f);
+    }
+    load_rows(ch0);
+#pragma unroll
+    for (int i = 0; i < kNB * kNB / 256; ++i) L[2 * i + sr][sc] = lv[i];
   }
-  // the factored diagonal block (L stays valid in LDS), after the solve so it
-  // does not hold up workgroup 0's rows
-  if (blockIdx.x == 0) {
-    for (int e = tid; e < nb * nb; e += 256) {
-      const int r = e / nb, c = e - r * nb;
-      Hr[(k + r) * n + k + c] = L[r][c];
+  __syncthreads();
+
+  factor64<0>(L, wave, lane);
+  inverse64<0>(L, M, wave, lane);
+  // L21 = A21 L11^-T, in registers until every wave has read A21
+  {
+    f32x4_t acc[4];
+    switch (wave) {
+      case 0: l21_row<0>(L, M, lane, acc); break;
+      case 1: l21_row<1>(L, M, lane, acc); break;
+      case 2: l21_row<2>(L, M, lane, acc); break;
+      default: l21_row<3>(L, M, lane, acc); break;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int J = 0; J < 4; ++J) store16(L, 64 + 16 * wave, 16 * J, acc[J], lane);
+    __syncthreads();
+  }
+  // A22 -= L21 L21^T on the ten lower 16x16 blocks (3, 3, 2, 2 per wave)
+  switch (wave) {
+    case 0: a22_row<3, 0, 3>(L, lane); break;
+    case 1: a22_row<2, 0, 3>(L, lane); break;
+    case 2: a22_row<1, 0, 2>(L, lane); break;
+    default: a22_row<0, 0, 1>(L, lane); a22_row<3, 3, 1>(L, lane); break;
+  }
+  __syncthreads();
+  factor64<64>(L, wave, lane);
+  // first pivot that was not positive: its diagonal entry is NaN or zero
+  if (wave == 0 && blockIdx.x == 0) {
+    const uint64_t bad1 = __ballot(lane < nb && !(L[lane][lane] > 0.f));
+    const uint64_t bad2 = __ballot(64 + lane < nb && !(L[64 + lane][64 + lane] > 0.f));
+    if (lane == 0 && (bad1 | bad2) != 0) {
+      const int f = bad1 ? __ffsll(static_cast<long long>(bad1)) - 1 : 64 + __ffsll(static_cast<long long>(bad2)) - 1;
+      atomicCAS(info, 0, static_cast<int32_t>(n - (k + f)));
     }
   }
-}
-
-// Invert every 64x64 diagonal block of the lower factor in place.  Wave 0,
-// lane c computes column c of the inverse by forward substitution.
-__global__ __launch_bounds__(256) void diag_inverse_kernel(float* Hr, int64_t n) {
-  __shared__ __attribute__((aligned(16))) float L[kNB][68];
-  const int64_t k = static_cast<int64_t>(blockIdx.x) * kNB;
-  const int nb = static_cast<int>(std::min<int64_t>(kNB, n - k));
-  const int tid = threadIdx.x, lane = tid & 63;
-  for (int e = tid; e < kNB * kNB; e += 256) {
-    const int r = e >> 6, c = e & 63;
-    float v = (r == c) ? 1.f : 0.f;
-    if (r < nb && c <= r) v = Hr[(k + r) * n + k + c];
-    L[r][c] = v;
+  inverse64<64>(L, M, wave, lane);
+  // M21 = -L22^-1 (L21 L11^-1)
+  switch (wave) {
+    case 0: t_row<0>(L, M, lane); break;
+    case 1: t_row<1>(L, M, lane); break;
+    case 2: t_row<2>(L, M, lane); break;
+    default: t_row<3>(L, M, lane); break;
   }
   __syncthreads();
-  if (tid >= 64) return;
-  float m[kNB];
+  {
+    f32x4_t acc[4];
+    switch (wave) {
+      case 0: m21_col<0>(M, lane, acc); break;
+      case 1: m21_col<1>(M, lane, acc); break;
+      case 2: m21_col<2>(M, lane, acc); break;
+      default: m21_col<3>(M, lane, acc); break;
+    }
+    __syncthreads();
 #pragma unroll
-  for (int i = 0; i < kNB; ++i) {
-    float s = (i == lane) ? 1.f : 0.f;
-#pragma unroll
-    for (int t = 0; t < i; ++t) s = fmaf(-L[i][t], m[t], s);
-    m[i] = (i >= lane) ? s * __builtin_amdgcn_rcpf(L[i][i]) : 0.f;
+    for (int I = 0; I < 4; ++I) store16(M, 64 + 16 * I, 16 * wave, acc[I], lane);
+    __syncthreads();
   }
-  for (int i = 0; i < nb; ++i)
-    if (lane < nb) Hr[(k + i) * n + k + lane] = m[i];
+
+  // M = L^-1 (lower; the blocks above the diagonal are never read)
+  if (blockIdx.x == 0) {
+    if (vec) {
+#pragma unroll
+      for (int i = 0; i < kNB / 8; ++i) {
+        const int r = 8 * i + vr;
+        f32x4_t x = *reinterpret_cast<const f32x4_t*>(&M[r][vc]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] = (vc + e <= r) ? x[e] : 0.f;
+        *reinterpret_cast<f32x4_t*>(Hr + (k + r) * n + k + vc) = x;
+      }
+    } else {
+#pragma unroll 16
+      for (int i = 0; i < kNB * kNB / 256; ++i) {
+        const int r = 2 * i + sr;
+        const float x = (sc <= r) ? M[r][sc] : 0.f;
+        if (r < nb && sc < nb) Hr[(k + r) * n + k + sc] = x;
+      }
+    }
+    return;
+  }
+  // X = P M^T, 32 rows at a time (staged in L's rows 0..31)
+  for (int64_t ch = ch0; ch < chunks; ch += chs) {
+    stage_rows();
+    __syncthreads();
+    load_rows(ch + chs);
+    f32x4_t acc[4];
+    switch (wave) {
+      case 0: solve_rows<0>(L, M, lane, acc); break;
+      case 1: solve_rows<1>(L, M, lane, acc); break;
+      case 2: solve_rows<2>(L, M, lane, acc); break;
+      default: solve_rows<3>(L, M, lane, acc); break;
+    }
+    const int64_t r0 = k + kNB + ch * kChunk;
+    const int m = lane & 15, q = lane >> 4;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int J = (t < 2) ? wave : 7 - wave;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int64_t row = r0 + 16 * (t & 1) + 4 * q + e;
+        if (row < n) Hr[row * n + k + 16 * J + m] = acc[t][e];
+      }
+    }
+    __syncthreads();
+  }
 }
 
 __global__ void reverse_kernel(const float* M, int64_t n, float* U) {
@@ -383,10 +662,11 @@ hipError_t prepare_launch(float* S, int64_t n, int64_t n_total, float damp, bool
   gather_kernel<<<grid_for(nn), 256, 0, st>>>(S, n, perm, lam, Hr);
   GPTQ_TRY(hipGetLastError());
 
-  // blocked right-looking Cholesky of Hr
+  // blocked right-looking Cholesky of Hr; the panel kernels leave the inverse
+  // of every diagonal block in place
   for (int64_t k = 0; k < n; k += kNB) {
     const int64_t below = std::max<int64_t>(0, n - k - kNB);
-    const int blocks = static_cast<int>(std::max<int64_t>(1, (below + kPanelRows - 1) / kPanelRows));
+    const int blocks = 1 + static_cast<int>(std::min<int64_t>((below + kChunk - 1) / kChunk, kMaxPanelWG - 1));
     panel_kernel<<<blocks, 256, 0, st>>>(Hr, n, k, info);
     GPTQ_TRY(hipGetLastError());
     if (below > 0) {
@@ -395,10 +675,8 @@ hipError_t prepare_launch(float* S, int64_t n, int64_t n_total, float damp, bool
                         0, 1, true, 0, st));
     }
   }
-  // triangular inverse: diagonal blocks, then recursive doubling
+  // triangular inverse by recursive doubling over the inverted diagonal blocks
   const int64_t nblk = (n + kNB - 1) / kNB;
-  diag_inverse_kernel<<<static_cast<int>(nblk), 256, 0, st>>>(Hr, n);
-  GPTQ_TRY(hipGetLastError());
   for (int64_t h = 1; h < nblk; h *= 2) {
     const int64_t w_el = h * kNB;           // width of A (elements)
     const int64_t groups_full = n / (2 * w_el);

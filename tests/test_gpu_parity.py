@@ -137,6 +137,21 @@ def test_prepare_not_spd_reported(G):
     np.testing.assert_allclose(np.diag(U.cpu().numpy()), 1.0 / np.sqrt(1.01), rtol=1e-6)
 
 
+@pytest.mark.parametrize("p", [20, 100, 250])
+def test_prepare_not_spd_position(G, p):
+    # H = I except H[p][p] = -1 (identity order): the damped pivot at sweep
+    # position p is the only negative one.  d = 300 spans three panels, the last
+    # one ragged; the factorization runs in reversed order, so p = 250, 100, 20
+    # fail in the first, second and third panel (the second in its right half).
+    banner(f"prepare: failed pivot position {p}")
+    d = 300
+    S = torch.eye(d, dtype=torch.float32, device=dev()) * 50.0
+    S[p, p] = -50.0
+    cfg = G.QuantizeConfig(bits=4, group_size=64, damp_percent=0.01, desc_act=False)
+    with pytest.raises(G.NotPositiveDefinite, match=f"sweep position {p}:"):
+        G.gptq_prepare_hinv(S, 100, cfg)
+
+
 # --------------------------------------------------------------- quantize ---
 
 SWEEP_CASES = [  # d_out, d_in, bits, G, sym, desc_act, static, w dtype
