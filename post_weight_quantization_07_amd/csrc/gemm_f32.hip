@@ -6,8 +6,10 @@
 // update W[:, j+B:] -= Err * U[j:j+B, j+B:] (GPTQ 实战 ch.5, section 5.1.8).
 //
 // 64x64 or 128x128 output tile per 256-thread workgroup (2x2 waves), 32-k
-// stages moved HBM -> LDS by buffer_load ... lds through a ring of three (two
-// in flight).
+// stages moved HBM -> LDS by buffer_load ... lds through a ring of slots: three
+// for 64x64 tiles (three workgroups per CU), two for 128x128 tiles, where one
+// stage of MFMA work covers the next stage's loads and the 64 KB ring lets two
+// workgroups share a CU (one's prologue and epilogue overlap the other's loop).
 // Requirements (checked by the callers): K, N, lda, ldb, ldc multiples of 4 and
 // 16-byte aligned base pointers; M arbitrary.  `tri` marks a lower-triangular
 // operand (B, or A) whose zero part a tile's K range skips: the triangular
@@ -19,7 +21,6 @@ namespace gptq {
 namespace {
 
 constexpr int kBK = 32;  // k per stage
-constexpr int kSlots = 3;
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
@@ -143,15 +144,16 @@ GPTQ_DEV float lds_f32(const uint8_t* base, uint32_t off) {
 }
 
 // T x T output tile (T = 64 or 128), 2x2 waves of (T/2) x (T/2) on
-// v_mfma_f32_16x16x4_f32.  The operands stream through a ring of three 32-k
-// stages (two in flight), one LDS array per slot so the compiler's wait
-// insertion sees no false aliasing.
+// v_mfma_f32_16x16x4_f32.  The operands stream through a ring of S 32-k stages
+// (S - 1 in flight), one LDS array per slot so the compiler's wait insertion
+// sees no false aliasing.
 template <bool TRANS_B, int T>
-__global__ __launch_bounds__(256, T == 64 ? 3 : 1) void gemm_f32_kernel(GemmParams p) {
-  constexpr int kOp = T * kBK * 4;  // one operand stage
-  constexpr int NB = T / 32;        // 16x16 blocks per wave and dimension
-  __shared__ __attribute__((aligned(1024))) uint8_t sa0[kOp], sa1[kOp], sa2[kOp];
-  __shared__ __attribute__((aligned(1024))) uint8_t sb0[kOp], sb1[kOp], sb2[kOp];
+__global__ __launch_bounds__(256, T == 64 ? 3 : 2) void gemm_f32_kernel(GemmParams p) {
+  constexpr int S = (T == 64) ? 3 : 2;  // ring slots
+  constexpr int kOp = T * kBK * 4;      // one operand stage
+  constexpr int NB = T / 32;            // 16x16 blocks per wave and dimension
+  __shared__ __attribute__((aligned(1024))) uint8_t sa0[kOp], sa1[kOp], sa2[S == 3 ? kOp : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t sb0[kOp], sb1[kOp], sb2[S == 3 ? kOp : 16];
   int z, tm, tn;
   if (!gemm_tile(p, blockIdx.x, z, tm, tn)) return;
   const int64_t m0 = static_cast<int64_t>(tm) * T;
@@ -253,38 +255,39 @@ __global__ __launch_bounds__(256, T == 64 ? 3 : 1) void gemm_f32_kernel(GemmPara
             acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[tt][i], b[tt][j], acc[i][j], 0, 0, 0);
     }
   };
-  // Stage x lives in slot x % 3.  Before computing stage x: wait until its
+  // Stage x lives in slot x % S.  Before computing stage x: wait until its
   // loads (and everything older) have landed, barrier (all waves' pieces are
-  // in; everyone is done with slot (x - 1) % 3), then refill that slot with
-  // stage x + 2.
+  // in; everyone is done with slot (x - 1) % S), then refill that slot with
+  // stage x + S - 1.  Issue order: stage 0, C, stage 1 (S = 3).
   auto step = [&](int x, const uint8_t* da, const uint8_t* db, uint8_t* na, uint8_t* nb) {
     if (x >= nstage) return;
-    if (x == 0) {
-      // issue order: stage 0, C, stage 1
-      const bool s1 = nstage > 1;
-      if (use_c) {
-        if (s1) __builtin_amdgcn_s_waitcnt(GPTQ_VMCNT(kCLoads + kLoadsPerStage));
-        else __builtin_amdgcn_s_waitcnt(GPTQ_VMCNT(kCLoads));
-      } else {
-        if (s1) __builtin_amdgcn_s_waitcnt(GPTQ_VMCNT(kLoadsPerStage));
-        else __builtin_amdgcn_s_waitcnt(GPTQ_VMCNT(0));
-      }
-    } else if (x + 1 < nstage) {
+    const int ahead = (S == 3 && x + 1 < nstage) ? kLoadsPerStage : 0;  // loads of stage x + 1
+    if (x == 0 && use_c) {
+      if (ahead) __builtin_amdgcn_s_waitcnt(GPTQ_VMCNT(kCLoads + kLoadsPerStage));
+      else __builtin_amdgcn_s_waitcnt(GPTQ_VMCNT(kCLoads));
+    } else if (ahead) {
       __builtin_amdgcn_s_waitcnt(GPTQ_VMCNT(kLoadsPerStage));
     } else {
       __builtin_amdgcn_s_waitcnt(GPTQ_VMCNT(0));
     }
     __builtin_amdgcn_s_barrier();
-    if (x + 2 < nstage) issue(x + 2, na, nb);
+    if (x + S - 1 < nstage) issue(x + S - 1, na, nb);
     compute(da, db);
   };
   if (nstage > 0) issue(0, sa0, sb0);
   if (use_c) load_c();
-  if (nstage > 1) issue(1, sa1, sb1);
-  for (int s = 0; s < nstage; s += 3) {
-    step(s, sa0, sb0, sa2, sb2);
-    step(s + 1, sa1, sb1, sa0, sb0);
-    step(s + 2, sa2, sb2, sa1, sb1);
+  if constexpr (S == 3) {
+    if (nstage > 1) issue(1, sa1, sb1);
+    for (int s = 0; s < nstage; s += 3) {
+      step(s, sa0, sb0, sa2, sb2);
+      step(s + 1, sa1, sb1, sa0, sb0);
+      step(s + 2, sa2, sb2, sa1, sb1);
+    }
+  } else {
+    for (int s = 0; s < nstage; s += 2) {
+      step(s, sa0, sb0, sa1, sb1);
+      step(s + 1, sa1, sb1, sa0, sb0);
+    }
   }
   // epilogue: each wave stages its (T/2) x (T/2) block in its own LDS slot
   // array (row-major; T = 128: 64-float rows, column bits 4-5 XOR-ed with
@@ -295,7 +298,8 @@ __global__ __launch_bounds__(256, T == 64 ? 3 : 1) void gemm_f32_kernel(GemmPara
   constexpr int kP = (T == 128) ? 64 : 36;
   auto xr = [&](int row) { return (T == 128) ? 16 * ((row >> 2) & 3) : 0; };
   __syncthreads();  // every wave is done with the ring
-  float* stg = reinterpret_cast<float*>(wave == 0 ? sa0 : wave == 1 ? sa1 : wave == 2 ? sa2 : sb0);
+  float* stg = reinterpret_cast<float*>(S == 3 ? (wave == 0 ? sa0 : wave == 1 ? sa1 : wave == 2 ? sa2 : sb0)
+                                              : (wave == 0 ? sa0 : wave == 1 ? sa1 : wave == 2 ? sb0 : sb1));
 #pragma unroll
   for (int i = 0; i < NB; ++i)
 #pragma unroll

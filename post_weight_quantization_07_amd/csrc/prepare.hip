@@ -435,38 +435,47 @@ __global__ __launch_bounds__(256, 1) void panel_kernel(float* Hr, int64_t n, int
   // workgroup's first 32 panel rows.  Every load reads an in-range address
   // (clamped into the block's lower part or the last row) and the value is
   // selected after, so all loads are in flight at once.
+  // pv holds the loaded values as they come and pmask which of them are real
+  // rows; the select waits until the rows are staged, so the loads of the
+  // next chunk stay in flight during this chunk's products.
   float pv[kChunk * kNB / 256];
+  uint32_t pmask = 0;
   const int vr = tid >> 5, vc = 4 * (tid & 31);  // float4 layout: 8 rows x 32 float4 per pass
   const int sr = tid >> 7, sc = tid & 127;       // scalar layout: 2 rows x 128 per pass
   auto load_rows = [&](int64_t ch) {
     const bool live = ch >= 0 && ch < chunks;
     const int64_t r0 = k + kNB + ch * kChunk;
+    pmask = 0;
     if (vec) {
 #pragma unroll
       for (int i = 0; i < kChunk / 8; ++i) {
         const int64_t row = r0 + 8 * i + vr;
         const f32x4_t x = *reinterpret_cast<const f32x4_t*>(Hr + std::min<int64_t>(row, n - 1) * n + k + vc);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) pv[4 * i + e] = (live && row < n) ? x[e] : 0.f;
+        for (int e = 0; e < 4; ++e) pv[4 * i + e] = x[e];
+        pmask |= (live && row < n) ? (1u << i) : 0u;
       }
     } else {
       const int64_t col = std::min<int64_t>(k + sc, n - 1);
 #pragma unroll
       for (int i = 0; i < kChunk / 2; ++i) {
         const int64_t row = r0 + 2 * i + sr;
-        const float x = Hr[std::min<int64_t>(row, n - 1) * n + col];
-        pv[i] = (live && row < n) ? x : 0.f;
+        pv[i] = Hr[std::min<int64_t>(row, n - 1) * n + col];
+        pmask |= (live && row < n) ? (1u << i) : 0u;
       }
     }
   };
   auto stage_rows = [&]() {
     if (vec) {
 #pragma unroll
-      for (int i = 0; i < kChunk / 8; ++i)
-        *reinterpret_cast<f32x4_t*>(&L[8 * i + vr][vc]) = f32x4_t{pv[4 * i], pv[4 * i + 1], pv[4 * i + 2], pv[4 * i + 3]};
+      for (int i = 0; i < kChunk / 8; ++i) {
+        const bool ok = (pmask >> i) & 1u;
+        *reinterpret_cast<f32x4_t*>(&L[8 * i + vr][vc]) =
+            ok ? f32x4_t{pv[4 * i], pv[4 * i + 1], pv[4 * i + 2], pv[4 * i + 3]} : f32x4_t{0.f, 0.f, 0.f, 0.f};
+      }
     } else {
 #pragma unroll
-      for (int i = 0; i < kChunk / 2; ++i) L[2 * i + sr][sc] = pv[i];
+      for (int i = 0; i < kChunk / 2; ++i) L[2 * i + sr][sc] = ((pmask >> i) & 1u) ? pv[i] : 0.f;
     }
   };
   if (vec) {
