@@ -171,9 +171,11 @@ __global__ __launch_bounds__(256, T == 64 ? 3 : 2) void gemm_f32_kernel(GemmPara
   if (p.tri == 2) ke = min(p.K, m0 + T);
   const int nstage = (ke > kb) ? static_cast<int>((ke - kb + kBK - 1) / kBK) : 0;
 
-  // C rows of this wave's block as float4 (row-contiguous), read between the
-  // first two stages so the latency overlaps the K loop.  A load instruction
-  // covers kCRows rows; lane l takes row l / (T / 8), columns 4 (l % (T / 8)).
+  // C rows of this wave's block as float4 (row-contiguous), read two stages
+  // before the end of the K loop: late enough that the workgroups starting
+  // together do not all pull their C tiles at once, early enough that they
+  // land during the last products.  A load instruction covers kCRows rows;
+  // lane l takes row l / (T / 8), columns 4 (l % (T / 8)).
   constexpr int kC4 = T / 8;            // float4 per block row
   constexpr int kCRows = 64 / kC4;      // rows per instruction
   constexpr int kCLoads = (T / 2) / kCRows;
@@ -256,26 +258,26 @@ __global__ __launch_bounds__(256, T == 64 ? 3 : 2) void gemm_f32_kernel(GemmPara
     }
   };
   // Stage x lives in slot x % S.  Before computing stage x: wait until its
-  // loads (and everything older) have landed, barrier (all waves' pieces are
-  // in; everyone is done with slot (x - 1) % S), then refill that slot with
-  // stage x + S - 1.  Issue order: stage 0, C, stage 1 (S = 3).
+  // loads have landed (the loads issued after them may stay in flight: stage
+  // x + 1 when S = 3, and C when it went out after stage x), barrier (all
+  // waves' pieces are in; everyone is done with slot (x - 1) % S), then refill
+  // that slot with stage x + S - 1; C follows the refill of step cst.
+  const int cst = max(0, nstage - 2);
   auto step = [&](int x, const uint8_t* da, const uint8_t* db, uint8_t* na, uint8_t* nb) {
     if (x >= nstage) return;
-    const int ahead = (S == 3 && x + 1 < nstage) ? kLoadsPerStage : 0;  // loads of stage x + 1
-    if (x == 0 && use_c) {
-      if (ahead) __builtin_amdgcn_s_waitcnt(GPTQ_VMCNT(kCLoads + kLoadsPerStage));
-      else __builtin_amdgcn_s_waitcnt(GPTQ_VMCNT(kCLoads));
-    } else if (ahead) {
-      __builtin_amdgcn_s_waitcnt(GPTQ_VMCNT(kLoadsPerStage));
-    } else {
-      __builtin_amdgcn_s_waitcnt(GPTQ_VMCNT(0));
-    }
+    int later = (S == 3 && x + 1 < nstage) ? kLoadsPerStage : 0;
+    if (use_c && cst <= x - 1 && cst >= x - (S - 1)) later += kCLoads;
+    if (later == 0) __builtin_amdgcn_s_waitcnt(GPTQ_VMCNT(0));
+    else if (later == kLoadsPerStage) __builtin_amdgcn_s_waitcnt(GPTQ_VMCNT(kLoadsPerStage));
+    else if (later == kCLoads) __builtin_amdgcn_s_waitcnt(GPTQ_VMCNT(kCLoads));
+    else __builtin_amdgcn_s_waitcnt(GPTQ_VMCNT(kCLoads + kLoadsPerStage));
     __builtin_amdgcn_s_barrier();
     if (x + S - 1 < nstage) issue(x + S - 1, na, nb);
+    if (use_c && x == cst) load_c();
     compute(da, db);
   };
   if (nstage > 0) issue(0, sa0, sb0);
-  if (use_c) load_c();
+  else if (use_c) load_c();
   if constexpr (S == 3) {
     if (nstage > 1) issue(1, sa1, sb1);
     for (int s = 0; s < nstage; s += 3) {

@@ -166,31 +166,39 @@ __global__ __launch_bounds__(256) void sweep_kernel(SweepParams p) {
   const int64_t row = static_cast<int64_t>(blockIdx.x) * kRowsPerWG + (tid >> 4);
   const bool row_ok = row < p.d_out;
 
-  // diagonal block of U (zeros outside the block's columns)
-  for (int e = tid; e < kB * kB / 4; e += 256) {
-    const int i = e / (kB / 4), c4 = 4 * (e % (kB / 4));
-    f32x4_t u = {0.f, 0.f, 0.f, 0.f};
-    if (i < p.ncols && c4 < p.ncols)
-      u = *reinterpret_cast<const f32x4_t*>(p.U + (p.j0 + i) * p.d_in + p.j0 + c4);
-    *reinterpret_cast<f32x4_t*>(&Ub[i][c4]) = u;
+  // The diagonal block of U (zeros outside the block's columns) and this
+  // lane's 8 weights.  Every load reads an in-range address (the block width
+  // is a multiple of 4; rows and columns past the end are clamped) and the
+  // value is selected after, so all of them are in flight at once.
+  constexpr int kUL = kB * kB / 4 / 256;  // float4 of the U block per thread
+  const int c0 = 8 * t;
+  f32x4_t ul[kUL], wa, wb;
+#pragma unroll
+  for (int u = 0; u < kUL; ++u) {
+    const int e = tid + 256 * u, i = e >> 5, c4 = 4 * (e & 31);
+    const int ic = std::min(i, p.ncols - 1), cc = std::min(c4, p.ncols - 4);
+    ul[u] = *reinterpret_cast<const f32x4_t*>(p.U + (p.j0 + ic) * p.d_in + p.j0 + cc);
+  }
+  {
+    const float* src = p.Wp + std::min<int64_t>(row, p.d_out - 1) * p.d_in + p.j0;
+    wa = *reinterpret_cast<const f32x4_t*>(src + std::min(c0, p.ncols - 4));
+    wb = *reinterpret_cast<const f32x4_t*>(src + std::min(c0 + 4, p.ncols - 4));
+  }
+#pragma unroll
+  for (int u = 0; u < kUL; ++u) {
+    const int e = tid + 256 * u, i = e >> 5, c4 = 4 * (e & 31);
+    *reinterpret_cast<f32x4_t*>(&Ub[i][c4]) = (i < p.ncols && c4 < p.ncols) ? ul[u] : f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
   __syncthreads();
 
   float v[8], sc[8], rc[8], zr[8], qc[8], qv[8], er[8], dv[8];
-  const int c0 = 8 * t;
   // 1 / U[i][i] of this lane's own columns (only the owner of a column uses it)
 #pragma unroll
   for (int k = 0; k < 8; ++k) dv[k] = (c0 + k < p.ncols) ? 1.0f / Ub[c0 + k][c0 + k] : 0.f;
-  {
-    const float* src = p.Wp + row * p.d_in + p.j0 + c0;
-    f32x4_t a = {0.f, 0.f, 0.f, 0.f}, b = {0.f, 0.f, 0.f, 0.f};
-    if (row_ok && c0 < p.ncols) a = *reinterpret_cast<const f32x4_t*>(src);
-    if (row_ok && c0 + 4 < p.ncols) b = *reinterpret_cast<const f32x4_t*>(src + 4);
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      v[k] = a[k];
-      v[k + 4] = b[k];
-    }
+  for (int k = 0; k < 4; ++k) {
+    v[k] = (row_ok && c0 < p.ncols) ? wa[k] : 0.f;
+    v[k + 4] = (row_ok && c0 + 4 < p.ncols) ? wb[k] : 0.f;
   }
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
@@ -204,16 +212,30 @@ __global__ __launch_bounds__(256) void sweep_kernel(SweepParams p) {
   // parameters fixed before this block: static groups, one group per row, or a
   // dynamic group wider than the block that started in an earlier block
   const bool wide_group_running = !p.preset && p.group > kB && (p.j0 % p.group) != 0;
-  if ((p.preset || wide_group_running) && row_ok) {
+  if (p.preset || wide_group_running) {
+    // columns and rows past the end read the block's last column / last row
+    // and are not used; the group indices first, then all scale and zero loads
+    const int64_t rr = std::min<int64_t>(row, p.d_out - 1);
+    int64_t g[8];
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-      const int64_t j = p.j0 + c0 + k;
-      if (c0 + k < p.ncols) {
-        int64_t g = 0;
-        if (p.group > 0) g = (p.preset && !p.identity) ? p.perm[j] / p.group : j / p.group;
-        sc[k] = p.scales[g * p.d_out + row];
-        rc[k] = 1.0f / sc[k];
-        zr[k] = static_cast<float>(p.zeros[g * p.d_out + row]);
+      const int64_t j = p.j0 + std::min(c0 + k, p.ncols - 1);
+      g[k] = 0;
+      if (p.group > 0) g[k] = (p.preset && !p.identity) ? p.perm[j] / p.group : j / p.group;
+    }
+    float sl[8];
+    int32_t zl[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      sl[k] = p.scales[g[k] * p.d_out + rr];
+      zl[k] = p.zeros[g[k] * p.d_out + rr];
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      if (row_ok && c0 + k < p.ncols) {
+        sc[k] = sl[k];
+        rc[k] = 1.0f / sl[k];
+        zr[k] = static_cast<float>(zl[k]);
       }
     }
   }
