@@ -120,6 +120,8 @@ constexpr int kLP = kNB + 4;    // LDS row pitch (floats)
 constexpr int kChunk = 32;      // panel rows solved per pass
 constexpr int kMaxPanelWG = 256;
 using Blk = float (*)[kLP];
+constexpr int kTP = 68;        // row pitch of the 64x64 product buffer
+using TBlk = float (*)[kTP];
 
 // v_mfma_f32_16x16x4_f32: lane l supplies A[l % 16][l / 16] and
 // B[l / 16][l % 16] and holds D[4 (l / 16) + e][l % 16] in element e.
@@ -131,8 +133,8 @@ GPTQ_DEV f32x4_t mfma4(float a, float b, f32x4_t acc) {
 // B(k, n) = pb[br + k][bc + n], or pb[br + n][bc + k] when BT.  MFMA step s
 // takes k = 4 q + s in lane group q (the same order for A and B), so a lane's
 // four A values, and its four B values when BT, are one 16-byte LDS read.
-template <bool BT>
-GPTQ_DEV f32x4_t mma16(const float (*pa)[kLP], int ar, int ac, const float (*pb)[kLP], int br, int bc,
+template <bool BT, int PA, int PB>
+GPTQ_DEV f32x4_t mma16(const float (*pa)[PA], int ar, int ac, const float (*pb)[PB], int br, int bc,
                        f32x4_t acc, float sign, int lane) {
   const int m = lane & 15, q = lane >> 4;
   const f32x4_t a = *reinterpret_cast<const f32x4_t*>(&pa[ar + m][ac + 4 * q]);
@@ -148,7 +150,8 @@ GPTQ_DEV f32x4_t mma16(const float (*pa)[kLP], int ar, int ac, const float (*pb)
   return acc;
 }
 
-GPTQ_DEV f32x4_t load16(const float (*p)[kLP], int r, int c, int lane) {
+template <int P>
+GPTQ_DEV f32x4_t load16(const float (*p)[P], int r, int c, int lane) {
   const int m = lane & 15, q = lane >> 4;
   f32x4_t v;
 #pragma unroll
@@ -156,7 +159,8 @@ GPTQ_DEV f32x4_t load16(const float (*p)[kLP], int r, int c, int lane) {
   return v;
 }
 
-GPTQ_DEV void store16(float (*p)[kLP], int r, int c, f32x4_t v, int lane) {
+template <int P>
+GPTQ_DEV void store16(float (*p)[P], int r, int c, f32x4_t v, int lane) {
   const int m = lane & 15, q = lane >> 4;
 #pragma unroll
   for (int e = 0; e < 4; ++e) p[r + 4 * q + e][c + m] = v[e];
@@ -166,10 +170,12 @@ GPTQ_DEV void store16(float (*p)[kLP], int r, int c, f32x4_t v, int lane) {
 // rows(p, r, c): lane (m, q) holds p[r + m][c + 4 q .. 4 q + 3] (an A operand,
 // or a B operand read transposed); cols(p, r, c): p[r + 4 q + s][c + m] (a B
 // operand read as stored).
-GPTQ_DEV f32x4_t frag_rows(const float (*p)[kLP], int r, int c, int lane) {
+template <int P>
+GPTQ_DEV f32x4_t frag_rows(const float (*p)[P], int r, int c, int lane) {
   return *reinterpret_cast<const f32x4_t*>(&p[r + (lane & 15)][c + 4 * (lane >> 4)]);
 }
-GPTQ_DEV f32x4_t frag_cols(const float (*p)[kLP], int r, int c, int lane) {
+template <int P>
+GPTQ_DEV f32x4_t frag_cols(const float (*p)[P], int r, int c, int lane) {
   f32x4_t v;
 #pragma unroll
   for (int s = 0; s < 4; ++s) v[s] = p[r + 4 * (lane >> 4) + s][c + (lane & 15)];
@@ -259,13 +265,11 @@ GPTQ_DEV void factor64(Blk L, int wave, int lane) {
 // One doubling level of the inverse of a lower factor: for NP pairs of
 // neighbouring inverted diagonal blocks (A^-1 at c0, C^-1 at r0 = c0 + 16 H,
 // each 16 H wide, pair p at c0 = cb + 32 H p) with the factor block L21 below
-// A, M21 = -C^-1 (L21 A^-1), written into M at (r0, c0).  T = L21 A^-1 passes
-// through the same place.  The 16x16 output blocks of a pair are spread over
-// the waves so that every wave gets the same number of MFMA slices when H = 4.
+// A, M21 = -C^-1 (L21 A^-1), written into M at (r0, c0); T = L21 A^-1 goes
+// through the buffer Tb (pair p at column 16 H p).  The 16x16 output blocks of
+// a pair are spread over the waves.
 template <int H, int NP>
-GPTQ_DEV void inverse_level(Blk L, Blk M, int cb, int wave, int lane) {
-  constexpr int NI = NP * H * H;
-  f32x4_t acc[NI];
+GPTQ_DEV void inverse_level(Blk L, Blk M, TBlk Tb, int cb, int wave, int lane) {
   auto owner = [](int p, int I, int J) { return (p * H * H + I * H + (I + J) % H) % 4; };
 #pragma unroll
   for (int p = 0; p < NP; ++p) {
@@ -279,7 +283,7 @@ GPTQ_DEV void inverse_level(Blk L, Blk M, int cb, int wave, int lane) {
 #pragma unroll
         for (int K = J; K < H; ++K)  // A^-1 is lower triangular
           t = mma16<false>(L, r0 + 16 * I, c0 + 16 * K, M, c0 + 16 * K, c0 + 16 * J, t, 1.f, lane);
-        store16(M, r0 + 16 * I, c0 + 16 * J, t, lane);
+        store16(Tb, 16 * I, 16 * H * p + 16 * J, t, lane);
       }
   }
   __syncthreads();
@@ -294,19 +298,9 @@ GPTQ_DEV void inverse_level(Blk L, Blk M, int cb, int wave, int lane) {
         f32x4_t t = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int K = 0; K <= I; ++K)  // C^-1 is lower triangular
-          t = mma16<false>(M, r0 + 16 * I, r0 + 16 * K, M, r0 + 16 * K, c0 + 16 * J, t, -1.f, lane);
-        acc[(p * H + I) * H + J] = t;
+          t = mma16<false>(M, r0 + 16 * I, r0 + 16 * K, Tb, 16 * K, 16 * H * p + 16 * J, t, -1.f, lane);
+        store16(M, r0 + 16 * I, c0 + 16 * J, t, lane);
       }
-  }
-  __syncthreads();
-#pragma unroll
-  for (int p = 0; p < NP; ++p) {
-    const int c0 = cb + 32 * H * p, r0 = c0 + 16 * H;
-#pragma unroll
-    for (int I = 0; I < H; ++I)
-#pragma unroll
-      for (int J = 0; J < H; ++J)
-        if (owner(p, I, J) == wave) store16(M, r0 + 16 * I, c0 + 16 * J, acc[(p * H + I) * H + J], lane);
   }
   __syncthreads();
 }
@@ -316,7 +310,7 @@ GPTQ_DEV void inverse_level(Blk L, Blk M, int cb, int wave, int lane) {
 // one column of the inverse per lane, zeros above the diagonal), then two
 // doubling levels.
 template <int base>
-GPTQ_DEV void inverse64(Blk L, Blk M, int wave, int lane) {
+GPTQ_DEV void inverse64(Blk L, Blk M, TBlk Tb, int wave, int lane) {
   if (wave == 0) {
     const int o = base + 16 * (lane >> 4), c = lane & 15;
     float x[16];
@@ -331,71 +325,128 @@ GPTQ_DEV void inverse64(Blk L, Blk M, int wave, int lane) {
     for (int i = 0; i < 16; ++i) M[o + i][o + c] = x[i];
   }
   __syncthreads();
-  inverse_level<1, 2>(L, M, base, wave, lane);
-  inverse_level<2, 1>(L, M, base, wave, lane);
+  inverse_level<1, 2>(L, M, Tb, base, wave, lane);
+  inverse_level<2, 1>(L, M, Tb, base, wave, lane);
 }
 
 // ---- the per-wave MFMA work of the 128 block, K-slices outermost so that a
-// wave's output blocks form independent accumulation chains sharing operands.
-// Block indices are in 16s; the 64-halves start at 0 and 64.
+// wave's output blocks form independent accumulation chains sharing operands;
+// the next slice's fragments are read before this slice's products (the
+// scheduling barriers keep that order).  Block indices are in 16s; the
+// 64-halves start at 0 and 64.
 
 // L21[I][J] = sum_{K <= J} A21[I][K] (L11^-1)[J][K]^T, wave = row I.
 template <int I>
 GPTQ_DEV void l21_row(Blk L, Blk M, int lane, f32x4_t (&acc)[4]) {
+  f32x4_t a, b[4], na, nb[4];
 #pragma unroll
-  for (int J = 0; J < 4; ++J) acc[J] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int J = 0; J < 4; ++J) {
+    acc[J] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    b[J] = frag_rows(M, 16 * J, 0, lane);
+  }
+  a = frag_rows(L, 64 + 16 * I, 0, lane);
 #pragma unroll
   for (int K = 0; K < 4; ++K) {
-    const f32x4_t a = frag_rows(L, 64 + 16 * I, 16 * K, lane);
+    if (K < 3) {
+      na = frag_rows(L, 64 + 16 * I, 16 * (K + 1), lane);
 #pragma unroll
-    for (int J = K; J < 4; ++J) acc[J] = mma_frag(a, frag_rows(M, 16 * J, 16 * K, lane), acc[J]);
+      for (int J = K + 1; J < 4; ++J) nb[J] = frag_rows(M, 16 * J, 16 * (K + 1), lane);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int J = K; J < 4; ++J) acc[J] = mma_frag(a, b[J], acc[J]);
+    __builtin_amdgcn_sched_barrier(0);
+    a = na;
+#pragma unroll
+    for (int J = K + 1; J < 4; ++J) b[J] = nb[J];
   }
 }
 
 // A22[I][J] -= sum_K L21[I][K] L21[J][K]^T for J in [J0, J0 + NJ) (J <= I).
 template <int I, int J0, int NJ>
 GPTQ_DEV void a22_row(Blk L, int lane) {
-  f32x4_t acc[NJ];
+  f32x4_t acc[NJ], a, b[NJ], na, nb[NJ];
 #pragma unroll
-  for (int j = 0; j < NJ; ++j) acc[j] = load16(L, 64 + 16 * I, 64 + 16 * (J0 + j), lane);
+  for (int j = 0; j < NJ; ++j) {
+    acc[j] = load16(L, 64 + 16 * I, 64 + 16 * (J0 + j), lane);
+    b[j] = frag_rows(L, 64 + 16 * (J0 + j), 0, lane);
+  }
+  a = frag_rows(L, 64 + 16 * I, 0, lane);
 #pragma unroll
   for (int K = 0; K < 4; ++K) {
-    const f32x4_t a = -frag_rows(L, 64 + 16 * I, 16 * K, lane);
+    if (K < 3) {
+      na = frag_rows(L, 64 + 16 * I, 16 * (K + 1), lane);
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) acc[j] = mma_frag(a, frag_rows(L, 64 + 16 * (J0 + j), 16 * K, lane), acc[j]);
+      for (int j = 0; j < NJ; ++j) nb[j] = frag_rows(L, 64 + 16 * (J0 + j), 16 * (K + 1), lane);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    const f32x4_t an = -a;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) acc[j] = mma_frag(an, b[j], acc[j]);
+    __builtin_amdgcn_sched_barrier(0);
+    a = na;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) b[j] = nb[j];
   }
 #pragma unroll
   for (int j = 0; j < NJ; ++j) store16(L, 64 + 16 * I, 64 + 16 * (J0 + j), acc[j], lane);
 }
 
-// T[I][J] = sum_{K >= J} L21[I][K] (L11^-1)[K][J], wave = row I; T goes to
-// M's lower-left 64 block.
+// T[I][J] = sum_{K >= J} L21[I][K] (L11^-1)[K][J], wave = row I, into Tb.
 template <int I>
-GPTQ_DEV void t_row(Blk L, Blk M, int lane) {
-  f32x4_t acc[4];
+GPTQ_DEV void t_row(Blk L, Blk M, TBlk Tb, int lane) {
+  f32x4_t acc[4], a, b[4], na, nb[4];
 #pragma unroll
   for (int J = 0; J < 4; ++J) acc[J] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  a = frag_rows(L, 64 + 16 * I, 0, lane);
+  b[0] = frag_cols(M, 0, 0, lane);
 #pragma unroll
   for (int K = 0; K < 4; ++K) {
-    const f32x4_t a = frag_rows(L, 64 + 16 * I, 16 * K, lane);
+    if (K < 3) {
+      na = frag_rows(L, 64 + 16 * I, 16 * (K + 1), lane);
 #pragma unroll
-    for (int J = 0; J <= K; ++J) acc[J] = mma_frag(a, frag_cols(M, 16 * K, 16 * J, lane), acc[J]);
+      for (int J = 0; J <= K + 1; ++J) nb[J] = frag_cols(M, 16 * (K + 1), 16 * J, lane);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int J = 0; J <= K; ++J) acc[J] = mma_frag(a, b[J], acc[J]);
+    __builtin_amdgcn_sched_barrier(0);
+    a = na;
+#pragma unroll
+    for (int J = 0; J <= K + 1 && J < 4; ++J) b[J] = nb[J];
   }
 #pragma unroll
-  for (int J = 0; J < 4; ++J) store16(M, 64 + 16 * I, 16 * J, acc[J], lane);
+  for (int J = 0; J < 4; ++J) store16(Tb, 16 * I, 16 * J, acc[J], lane);
 }
 
-// M21[I][J] = -sum_{K <= I} (L22^-1)[I][K] T[K][J], wave = column J.
+// M21[I][J] = -sum_{K <= I} (L22^-1)[I][K] T[K][J], wave = column J, into M.
 template <int J>
-GPTQ_DEV void m21_col(Blk M, int lane, f32x4_t (&acc)[4]) {
+GPTQ_DEV void m21_col(Blk M, TBlk Tb, int lane) {
+  f32x4_t acc[4], b, a[4], nbv, na[4];
 #pragma unroll
-  for (int I = 0; I < 4; ++I) acc[I] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int I = 0; I < 4; ++I) {
+    acc[I] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    a[I] = frag_rows(M, 64 + 16 * I, 64, lane);
+  }
+  b = frag_cols(Tb, 0, 16 * J, lane);
 #pragma unroll
   for (int K = 0; K < 4; ++K) {
-    const f32x4_t b = frag_cols(M, 64 + 16 * K, 16 * J, lane);
+    if (K < 3) {
+      nbv = frag_cols(Tb, 16 * (K + 1), 16 * J, lane);
 #pragma unroll
-    for (int I = K; I < 4; ++I) acc[I] = mma_frag(-frag_rows(M, 64 + 16 * I, 64 + 16 * K, lane), b, acc[I]);
+      for (int I = K + 1; I < 4; ++I) na[I] = frag_rows(M, 64 + 16 * I, 64 + 16 * (K + 1), lane);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    const f32x4_t bn = -b;
+#pragma unroll
+    for (int I = K; I < 4; ++I) acc[I] = mma_frag(a[I], bn, acc[I]);
+    __builtin_amdgcn_sched_barrier(0);
+    b = nbv;
+#pragma unroll
+    for (int I = K + 1; I < 4; ++I) a[I] = na[I];
   }
+#pragma unroll
+  for (int I = 0; I < 4; ++I) store16(M, 64 + 16 * I, 16 * J, acc[I], lane);
 }
 
 // X = P M^T for the 32 staged rows (L rows 0..31): output blocks (I, J) with
@@ -403,25 +454,40 @@ GPTQ_DEV void m21_col(Blk M, int lane, f32x4_t (&acc)[4]) {
 template <int W>
 GPTQ_DEV void solve_rows(Blk L, Blk M, int lane, f32x4_t (&acc)[4]) {
   constexpr int J1 = W, J2 = 7 - W;
+  f32x4_t c0, c1, c2, c3, n0, n1, n2, n3;
 #pragma unroll
   for (int t = 0; t < 4; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  c0 = frag_rows(L, 0, 0, lane);
+  c1 = frag_rows(L, 16, 0, lane);
+  c2 = frag_rows(M, 16 * J1, 0, lane);
+  c3 = frag_rows(M, 16 * J2, 0, lane);
 #pragma unroll
   for (int K = 0; K <= J2; ++K) {
-    const f32x4_t a0 = frag_rows(L, 0, 16 * K, lane), a1 = frag_rows(L, 16, 16 * K, lane);
-    const f32x4_t b2 = frag_rows(M, 16 * J2, 16 * K, lane);
-    if (K <= J1) {
-      const f32x4_t b1 = frag_rows(M, 16 * J1, 16 * K, lane);
-      acc[0] = mma_frag(a0, b1, acc[0]);
-      acc[1] = mma_frag(a1, b1, acc[1]);
+    if (K + 1 <= J2) {
+      n0 = frag_rows(L, 0, 16 * (K + 1), lane);
+      n1 = frag_rows(L, 16, 16 * (K + 1), lane);
+      if (K + 1 <= J1) n2 = frag_rows(M, 16 * J1, 16 * (K + 1), lane);
+      n3 = frag_rows(M, 16 * J2, 16 * (K + 1), lane);
     }
-    acc[2] = mma_frag(a0, b2, acc[2]);
-    acc[3] = mma_frag(a1, b2, acc[3]);
+    __builtin_amdgcn_sched_barrier(0);
+    if (K <= J1) {
+      acc[0] = mma_frag(c0, c2, acc[0]);
+      acc[1] = mma_frag(c1, c2, acc[1]);
+    }
+    acc[2] = mma_frag(c0, c3, acc[2]);
+    acc[3] = mma_frag(c1, c3, acc[3]);
+    __builtin_amdgcn_sched_barrier(0);
+    c0 = n0;
+    c1 = n1;
+    c2 = n2;
+    c3 = n3;
   }
 }
 
 __global__ __launch_bounds__(256, 1) void panel_kernel(float* Hr, int64_t n, int64_t k, int32_t* info) {
   __shared__ __attribute__((aligned(16))) float L[kNB][kLP];
   __shared__ __attribute__((aligned(16))) float M[kNB][kLP];
+  __shared__ __attribute__((aligned(16))) float Tb[kNB / 2][kTP];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nb = static_cast<int>(std::min<int64_t>(kNB, n - k));
   const int64_t below = (nb == kNB) ? n - k - kNB : 0;
@@ -510,7 +576,7 @@ __global__ __launch_bounds__(256, 1) void panel_kernel(float* Hr, int64_t n, int
   __syncthreads();
 
   factor64<0>(L, wave, lane);
-  inverse64<0>(L, M, wave, lane);
+  inverse64<0>(L, M, Tb, wave, lane);
   // L21 = A21 L11^-T, in registers until every wave has read A21
   {
     f32x4_t acc[4];
@@ -543,28 +609,22 @@ __global__ __launch_bounds__(256, 1) void panel_kernel(float* Hr, int64_t n, int
       atomicCAS(info, 0, static_cast<int32_t>(n - (k + f)));
     }
   }
-  inverse64<64>(L, M, wave, lane);
+  inverse64<64>(L, M, Tb, wave, lane);
   // M21 = -L22^-1 (L21 L11^-1)
   switch (wave) {
-    case 0: t_row<0>(L, M, lane); break;
-    case 1: t_row<1>(L, M, lane); break;
-    case 2: t_row<2>(L, M, lane); break;
-    default: t_row<3>(L, M, lane); break;
+    case 0: t_row<0>(L, M, Tb, lane); break;
+    case 1: t_row<1>(L, M, Tb, lane); break;
+    case 2: t_row<2>(L, M, Tb, lane); break;
+    default: t_row<3>(L, M, Tb, lane); break;
   }
   __syncthreads();
-  {
-    f32x4_t acc[4];
-    switch (wave) {
-      case 0: m21_col<0>(M, lane, acc); break;
-      case 1: m21_col<1>(M, lane, acc); break;
-      case 2: m21_col<2>(M, lane, acc); break;
-      default: m21_col<3>(M, lane, acc); break;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int I = 0; I < 4; ++I) store16(M, 64 + 16 * I, 16 * wave, acc[I], lane);
-    __syncthreads();
+  switch (wave) {
+    case 0: m21_col<0>(M, Tb, lane); break;
+    case 1: m21_col<1>(M, Tb, lane); break;
+    case 2: m21_col<2>(M, Tb, lane); break;
+    default: m21_col<3>(M, Tb, lane); break;
   }
+  __syncthreads();
 
   // M = L^-1 (lower; the blocks above the diagonal are never read)
   if (blockIdx.x == 0) {
