@@ -34,6 +34,13 @@ GPTQ_DEV float row_max16(float v) {
   v = fmaxf(v, __builtin_amdgcn_update_dpp(0.0f, v, 0x140, 0xf, 0xf, false)); // row_mirror
   return v;
 }
+GPTQ_DEV float row_sum16(float v) {
+  v += __builtin_amdgcn_update_dpp(0.0f, v, 0xB1, 0xf, 0xf, false);
+  v += __builtin_amdgcn_update_dpp(0.0f, v, 0x4E, 0xf, 0xf, false);
+  v += __builtin_amdgcn_update_dpp(0.0f, v, 0x141, 0xf, 0xf, false);
+  v += __builtin_amdgcn_update_dpp(0.0f, v, 0x140, 0xf, 0xf, false);
+  return v;
+}
 GPTQ_DEV float row_min16(float v) {
   v = fminf(v, __builtin_amdgcn_update_dpp(0.0f, v, 0xB1, 0xf, 0xf, false));
   v = fminf(v, __builtin_amdgcn_update_dpp(0.0f, v, 0x4E, 0xf, 0xf, false));

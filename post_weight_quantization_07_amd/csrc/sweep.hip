@@ -39,6 +39,8 @@ struct SweepParams {
   float* row_loss;      // optional [d_out]
   float* Err;           // this block's normalised errors, rows of ld_err floats
   int ld_err;
+  const float* Eb;      // bring-up: errors of the previous block of the pair (rows of ld_err floats), or null
+  const float* Uo;      // bring-up: U rows of that block, this block's columns (row stride d_in)
   int64_t d_out, d_in;
   int64_t j0;           // first sweep column of the block
   int ncols;            // columns in this block
@@ -72,8 +74,8 @@ GPTQ_DEV void group_params(float lo, float hi, const SweepParams& p, float& scal
 // 128 unrolled steps small matters: it has to stay in the instruction cache.
 template <int GS, int I>
 GPTQ_DEV void sweep_step(const SweepParams& p, const float (*Ub)[kB], const float (&dv)[8], int t,
-                         float (&v)[8], float (&sc)[8], float (&rc)[8], float (&zr)[8], float (&qc)[8],
-                         float (&qv)[8], float (&er)[8], float& loss, int64_t row, f32x4_t (&ua)[2],
+                         float (&v)[8], float (&sc)[8], float (&rc)[8], float (&zlo)[8], float (&zhi)[8],
+                         float (&qc)[8], float (&er)[8], int64_t row, f32x4_t (&ua)[2],
                          f32x4_t (&ub)[2]) {
   constexpr int r = I & 7, owner = I >> 3;
   // the next step's row of U is read now (two register sets), so its LDS
@@ -107,7 +109,8 @@ GPTQ_DEV void sweep_step(const SweepParams& p, const float (*Ub)[kB], const floa
         const bool in = (c >= I) && (c < I + GS);
         sc[k] = in ? s : sc[k];
         rc[k] = in ? y : rc[k];
-        zr[k] = in ? z : zr[k];
+        zlo[k] = in ? -z : zlo[k];
+        zhi[k] = in ? p.maxq - z : zhi[k];
       }
       if (t == owner && row < p.d_out) {
         const int64_t g = p.j0 / GS + I / GS;
@@ -117,7 +120,7 @@ GPTQ_DEV void sweep_step(const SweepParams& p, const float (*Ub)[kB], const floa
     }
   }
   const float w = v[r];
-  const float s = sc[r], z = zr[r];
+  const float s = sc[r];
   // w / s correctly rounded from the correctly rounded reciprocal y = 1 / s:
   // q0 = w y is within an ulp, the remainder w - s q0 is exact in one fma, and
   // q0 + (w - s q0) y rounds to the quotient (Markstein's correction step).
@@ -125,17 +128,17 @@ GPTQ_DEV void sweep_step(const SweepParams& p, const float (*Ub)[kB], const floa
   const float y = rc[r];
   const float q0 = w * y;
   const float quot = fmaf(fmaf(-s, q0, w), y, q0);
-  const float q = fminf(fmaxf(rintf(quot) + z, 0.f), p.maxq);
-  const float what = s * (q - z);
-  const float err = (w - what) * dv[r];
+  // the code relative to the zero point, qr = q - z: rint(w / s) clamped to
+  // [-z, maxq - z] is clamp(rint(w / s) + z, 0, maxq) - z exactly (integers);
+  // the dequantized weight is s qr and the error w - s qr (one fma)
+  const float qr = __builtin_amdgcn_fmed3f(rintf(quot), zlo[r], zhi[r]);
+  const float err = fmaf(-s, qr, w) * dv[r];
   const float eb = row_bcast<owner>(err);
-  qc[r] = (t == owner) ? q : qc[r];
-  qv[r] = (t == owner) ? what : qv[r];
+  qc[r] = (t == owner) ? qr : qc[r];
   er[r] = (t == owner) ? eb : er[r];
   // materialise the selects here: left alone, the compiler sinks them to the
   // end of the block and keeps every step's code alive until then
-  asm volatile("" : "+v"(qc[r]), "+v"(qv[r]), "+v"(er[r]));
-  loss = fmaf(eb, eb, loss);
+  asm volatile("" : "+v"(qc[r]), "+v"(er[r]));
   // the next column first: the next step's decision waits on it
   constexpr int rn = (I + 1) & 7;
   v[rn] = fmaf(-eb, rn < 4 ? u0[rn & 3] : u1[rn & 3], v[rn]);
@@ -150,17 +153,18 @@ GPTQ_DEV void sweep_step(const SweepParams& p, const float (*Ub)[kB], const floa
 
 template <int GS, int... Is>
 GPTQ_DEV void sweep_all(const SweepParams& p, const float (*Ub)[kB], const float (&dv)[8], int t, float (&v)[8],
-                        float (&sc)[8], float (&rc)[8], float (&zr)[8], float (&qc)[8], float (&qv)[8],
-                        float (&er)[8], float& loss, int64_t row, std::integer_sequence<int, Is...>) {
+                        float (&sc)[8], float (&rc)[8], float (&zlo)[8], float (&zhi)[8], float (&qc)[8],
+                        float (&er)[8], int64_t row, std::integer_sequence<int, Is...>) {
   f32x4_t ua[2], ub[2];
   ua[0] = *reinterpret_cast<const f32x4_t*>(&Ub[0][8 * t]);
   ub[0] = *reinterpret_cast<const f32x4_t*>(&Ub[0][8 * t + 4]);
-  (sweep_step<GS, Is>(p, Ub, dv, t, v, sc, rc, zr, qc, qv, er, loss, row, ua, ub), ...);
+  (sweep_step<GS, Is>(p, Ub, dv, t, v, sc, rc, zlo, zhi, qc, er, row, ua, ub), ...);
 }
 
 template <int GS>
 __global__ __launch_bounds__(256) void sweep_kernel(SweepParams p) {
   __shared__ __attribute__((aligned(16))) float Ub[kB][kB];
+  __shared__ __attribute__((aligned(16))) float Stg[kRowsPerWG][kB + 4];  // bring-up result
   const int tid = threadIdx.x;
   const int t = tid & 15;
   const int64_t row = static_cast<int64_t>(blockIdx.x) * kRowsPerWG + (tid >> 4);
@@ -184,14 +188,64 @@ __global__ __launch_bounds__(256) void sweep_kernel(SweepParams p) {
     wa = *reinterpret_cast<const f32x4_t*>(src + std::min(c0, p.ncols - 4));
     wb = *reinterpret_cast<const f32x4_t*>(src + std::min(c0 + 4, p.ncols - 4));
   }
+  // Bring-up of the second block of a pair: W[rows, block] -= Eb[rows, :] Uo
+  // (16 rows x 128 columns, K = 128, the previous block is full) on MFMA
+  // (v_mfma_f32_16x16x4_f32; MFMA step s takes k = 4 q + s in lane group q, so
+  // a lane's A values are one float4 of its error row).  Wave w computes the
+  // 16-column blocks 2 w and 2 w + 1; Uo goes through Ub, the result through
+  // Stg into the lanes' column layout.
+  const bool bring = p.Eb != nullptr;
+  f32x4_t bup0 = {0.f, 0.f, 0.f, 0.f}, bup1 = {0.f, 0.f, 0.f, 0.f};
+  if (bring) {
+    const int lane = tid & 63, wave = tid >> 6, m = lane & 15, q = lane >> 4;
+    f32x4_t uo[kUL], ea[kB / 16];
+#pragma unroll
+    for (int u = 0; u < kUL; ++u) {
+      const int e = tid + 256 * u, i = e >> 5, c4 = 4 * (e & 31);
+      uo[u] = *reinterpret_cast<const f32x4_t*>(p.Uo + i * p.d_in + std::min(c4, p.ncols - 4));
+    }
+    const int64_t er = std::min<int64_t>(static_cast<int64_t>(blockIdx.x) * kRowsPerWG + m, p.d_out - 1);
+#pragma unroll
+    for (int kk = 0; kk < kB / 16; ++kk)
+      ea[kk] = *reinterpret_cast<const f32x4_t*>(p.Eb + er * p.ld_err + 16 * kk + 4 * q);
+#pragma unroll
+    for (int u = 0; u < kUL; ++u) {
+      const int e = tid + 256 * u, i = e >> 5, c4 = 4 * (e & 31);
+      *reinterpret_cast<f32x4_t*>(&Ub[i][c4]) = (c4 < p.ncols) ? uo[u] : f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < kB / 16; ++kk) {
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4) {
+        const float b0 = Ub[16 * kk + 4 * q + s4][32 * wave + m];
+        const float b1 = Ub[16 * kk + 4 * q + s4][32 * wave + 16 + m];
+        bup0 = __builtin_amdgcn_mfma_f32_16x16x4f32(ea[kk][s4], b0, bup0, 0, 0, 0);
+        bup1 = __builtin_amdgcn_mfma_f32_16x16x4f32(ea[kk][s4], b1, bup1, 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      Stg[4 * q + e][32 * wave + m] = bup0[e];
+      Stg[4 * q + e][32 * wave + 16 + m] = bup1[e];
+    }
+    __syncthreads();  // every wave is done with Uo in Ub
+  }
 #pragma unroll
   for (int u = 0; u < kUL; ++u) {
     const int e = tid + 256 * u, i = e >> 5, c4 = 4 * (e & 31);
     *reinterpret_cast<f32x4_t*>(&Ub[i][c4]) = (i < p.ncols && c4 < p.ncols) ? ul[u] : f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
+  if (bring) {
+    const f32x4_t d0 = *reinterpret_cast<const f32x4_t*>(&Stg[tid >> 4][c0]);
+    const f32x4_t d1 = *reinterpret_cast<const f32x4_t*>(&Stg[tid >> 4][c0 + 4]);
+    wa -= d0;
+    wb -= d1;
+  }
   __syncthreads();
 
-  float v[8], sc[8], rc[8], zr[8], qc[8], qv[8], er[8], dv[8];
+  // zlo, zhi: the clamp bounds -z and maxq - z of each column's relative code
+  float v[8], sc[8], rc[8], zlo[8], zhi[8], qc[8], er[8], dv[8];
   // 1 / U[i][i] of this lane's own columns (only the owner of a column uses it)
 #pragma unroll
   for (int k = 0; k < 8; ++k) dv[k] = (c0 + k < p.ncols) ? 1.0f / Ub[c0 + k][c0 + k] : 0.f;
@@ -204,9 +258,9 @@ __global__ __launch_bounds__(256) void sweep_kernel(SweepParams p) {
   for (int k = 0; k < 8; ++k) {
     sc[k] = 1.f;
     rc[k] = 1.f;
-    zr[k] = 0.f;
+    zlo[k] = 0.f;
+    zhi[k] = p.maxq;
     qc[k] = 0.f;
-    qv[k] = 0.f;
     er[k] = 0.f;
   }
   // parameters fixed before this block: static groups, one group per row, or a
@@ -235,7 +289,8 @@ __global__ __launch_bounds__(256) void sweep_kernel(SweepParams p) {
       if (row_ok && c0 + k < p.ncols) {
         sc[k] = sl[k];
         rc[k] = 1.0f / sl[k];
-        zr[k] = static_cast<float>(zl[k]);
+        zlo[k] = -static_cast<float>(zl[k]);
+        zhi[k] = p.maxq - static_cast<float>(zl[k]);
       }
     }
   }
@@ -264,7 +319,8 @@ __global__ __launch_bounds__(256) void sweep_kernel(SweepParams p) {
     for (int k = 0; k < 8; ++k) {
       sc[k] = s;
       rc[k] = y;
-      zr[k] = z;
+      zlo[k] = -z;
+      zhi[k] = p.maxq - z;
     }
     if (t == 0 && row_ok) {
       const int64_t g = p.j0 / p.group;
@@ -274,8 +330,17 @@ __global__ __launch_bounds__(256) void sweep_kernel(SweepParams p) {
   }
   __syncthreads();
 
-  float loss = 0.f;
-  sweep_all<GS>(p, Ub, dv, t, v, sc, rc, zr, qc, qv, er, loss, row, std::make_integer_sequence<int, kB>{});
+  sweep_all<GS>(p, Ub, dv, t, v, sc, rc, zlo, zhi, qc, er, row, std::make_integer_sequence<int, kB>{});
+  // codes q = qr + z, dequantized weights s qr, and the row's loss (sum of the
+  // squared normalised errors over the row's 16 lanes)
+  float qv[8], loss = 0.f;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    qv[k] = sc[k] * qc[k];
+    qc[k] -= zlo[k];
+    loss = fmaf(er[k], er[k], loss);
+  }
+  loss = row_sum16(loss);
 
   if (!row_ok) return;
   // normalised errors of the block, for the trailing update
@@ -433,7 +498,7 @@ hipError_t quantize_launch(const void* W, bool w_bf16, int64_t d_out, int64_t d_
   const int blocks = static_cast<int>((d_out + kRowsPerWG - 1) / kRowsPerWG);
   // The trailing update runs once per pair of 128-column blocks (K = 256): the
   // second block of a pair is first brought up to date with the first block's
-  // errors.  The result is the lazy-batch sweep's (the same products, summed
+  // errors (a 128-deep product at the start of its sweep kernel).  The result is the lazy-batch sweep's (the same products, summed
   // in another order).  A dynamic group wider than a block reads columns past
   // the block at its start, so pairs are used only when such groups start on
   // pair boundaries.
@@ -446,11 +511,9 @@ hipError_t quantize_launch(const void* W, bool w_bf16, int64_t d_out, int64_t d_
       const int64_t jb = j0 + static_cast<int64_t>(h) * kB;
       if (jb >= d_in) break;
       const int ncols = static_cast<int>(std::min<int64_t>(kB, d_in - jb));
-      if (h > 0) {
-        e = gemm_f32(d_out, ncols, h * kB, -1.f, Err, SB, 0, U + j0 * d_in + jb, d_in, 0, false, 1.f, Wp + jb, d_in,
-                     0, 1, false, 0, st);
-        if (e != hipSuccess) return e;
-      }
+      // the second block of a pair is brought up to date inside its sweep
+      p.Eb = (h > 0) ? Err : nullptr;
+      p.Uo = (h > 0) ? U + j0 * d_in + jb : nullptr;
       p.j0 = jb;
       p.ncols = ncols;
       p.Err = Err + h * kB;
