@@ -47,6 +47,9 @@ def parse():
                     help="instead of the one-line result: time every layer of the five configurations and write "
                          "a markdown table to PATH")
     ap.add_argument("--all-configs-steps", type=int, default=3)
+    ap.add_argument("--shared", metavar="PATH", default=None,
+                    help="time the layers that read one input (q/k/v, gate/up of configurations 2-3) solved "
+                         "against one H and one U against separate solves; write a markdown table to PATH")
     return ap.parse_args()
 
 
@@ -148,9 +151,11 @@ def stage_metrics(layer, st):
 class LayerSolve:
     """Inputs resident in HBM, outputs and workspaces allocated once; step()
     runs one whole layer solve (zero S, accumulate all tokens in one call,
-    prepare, quantize, pack) on the current stream."""
+    prepare, quantize, pack) on the current stream.  With `members` (layers
+    that read `layer`'s input), their weights are stacked and solved against
+    one H and one U, as solve_layers_shared does."""
 
-    def __init__(self, layer, copy_calib_mib=0):
+    def __init__(self, layer, copy_calib_mib=0, members=None):
         import numpy as np
         import torch
 
@@ -158,9 +163,10 @@ class LayerSolve:
         import synth
         self.G, self.layer, self.torch = G, layer, torch
         dev = torch.device("cuda:0")
-        d_out, d_in, N = layer.d_out, layer.d_in, layer.n_tokens
+        members = members or [layer]
+        d_out, d_in, N = sum(L.d_out for L in members), layer.d_in, layer.n_tokens
         self.cfg = cfg = G.QuantizeConfig(**layer.quant_kwargs())
-        self.W_host = synth.weight(layer)
+        self.W_host = np.vstack([synth.weight(L) for L in members]) if len(members) > 1 else synth.weight(layer)
         if layer.w_dtype == "bf16":
             self.W = torch.from_numpy(synth.bf16_bits(self.W_host).view(np.int16)).to(dev).view(torch.bfloat16)
         else:
@@ -280,6 +286,39 @@ def all_configs(args):
     print(text, flush=True)
 
 
+def shared_groups_table(args):
+    """Layers that read one input (q/k/v, gate/up) solved against one H and one
+    U, against solving each on its own from the same input; a markdown table."""
+    import torch
+
+    import synth
+    lines = ["| cfg | group | layers | N | separate: ms (sum of solves) | shared: ms | speed-up | "
+             "shared weight cols/s |", "|---|---|---|---:|---:|---:|---:|---:|"]
+    for c in (2, 3):
+        for name, members in synth.shared_groups(c):
+            L0 = members[0]
+            desc = " + ".join(f"{L.name} {L.d_out}x{L.d_in}" for L in members)
+            print(f"[shared] cfg{c} {name}: {desc} N={L0.n_tokens}", flush=True)
+            sep = 0.0
+            for L in members:
+                ls = LayerSolve(L)
+                ms, _ = ls.measure(args.all_configs_steps, 1)
+                sep += ms
+                del ls
+                torch.cuda.empty_cache()
+            ls = LayerSolve(L0, members=members)
+            ms_sh, _ = ls.measure(args.all_configs_steps, 1)
+            del ls
+            torch.cuda.empty_cache()
+            cols = len(members) * L0.d_in
+            lines.append(f"| {c} | {name} | {desc} | {L0.n_tokens} | {sep:.2f} | {ms_sh:.2f} | {sep / ms_sh:.2f}x | "
+                         f"{cols / (ms_sh * 1e-3):,.0f} |")
+    text = "\n".join(lines) + "\n"
+    with open(args.shared, "w") as f:
+        f.write(text)
+    print(text, flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -293,6 +332,9 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     if args.all_configs:
         all_configs(args)
+        return
+    if args.shared:
+        shared_groups_table(args)
         return
     layer = synth.config_layers(3)[0]
     d_out, d_in, N = layer.d_out, layer.d_in, layer.n_tokens

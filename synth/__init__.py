@@ -75,6 +75,7 @@ class Layer:
     layer_id: int = 0
     seed: int = 0
     correlated: bool = False  # mix channels through a random matrix (small tests only)
+    w_key: int = -1           # >= 0: W drawn under this key instead of layer_id (layers sharing one X)
 
     def quant_kwargs(self) -> dict:
         return dict(bits=self.bits, group_size=self.group_size, sym=self.sym,
@@ -87,10 +88,11 @@ class Layer:
 
 def weight(layer: Layer) -> np.ndarray:
     """W as fp32 (bf16-exact values when the layer stores bf16)."""
-    g = rng(layer.seed, layer.cfg, layer.layer_id, ROLE_W)
+    wk = layer.layer_id if layer.w_key < 0 else layer.w_key
+    g = rng(layer.seed, layer.cfg, wk, ROLE_W)
     w = g.standard_normal((layer.d_out, layer.d_in), dtype=np.float32) * np.float32(0.02)
     if layer.w_outliers:
-        go = rng(layer.seed, layer.cfg, layer.layer_id, ROLE_W_OUTLIER)
+        go = rng(layer.seed, layer.cfg, wk, ROLE_W_OUTLIER)
         mask = go.random((layer.d_out, layer.d_in), dtype=np.float32) < np.float32(0.005)
         w = np.where(mask, w * np.float32(40.0), w).astype(np.float32)
     if layer.w_dtype == "bf16":
@@ -227,6 +229,33 @@ CONFIGS = {1: _cfg1, 2: _cfg2, 3: _cfg3, 4: _cfg4, 5: _cfg5}
 
 def config_layers(cfg: int) -> List[Layer]:
     return CONFIGS[cfg]()
+
+
+def shared_groups(cfg: int) -> List[Tuple[str, List[Layer]]]:
+    """Layers that read one input and so share one H and one U (q/k/v, gate/up):
+    every member has the first member's X (same layer_id) and its own W
+    (w_key).  k_proj and v_proj of configurations 3 and 4 are drawn under keys
+    past the configuration's layers."""
+    out = []
+    if cfg == 2:
+        q = config_layers(2)[0]
+        out.append(("qkv", [replace_layer(q, w_key=0), replace_layer(q, name="k_proj", w_key=1),
+                            replace_layer(q, name="v_proj", w_key=2)]))
+    elif cfg == 3:
+        q, gate = config_layers(3)[0], config_layers(3)[1]
+        out.append(("qkv", [replace_layer(q, w_key=0), replace_layer(q, name="k_proj", w_key=10),
+                            replace_layer(q, name="v_proj", w_key=11)]))
+        out.append(("gate_up", [replace_layer(gate, w_key=1), replace_layer(gate, name="up_proj", w_key=2)]))
+    elif cfg == 4:
+        q = [L for L in config_layers(4) if L.name == "q_proj_b3g32_dynamic"][0]
+        out.append(("qkv", [replace_layer(q, w_key=q.layer_id), replace_layer(q, name="k_proj_b3g32_dynamic", w_key=20),
+                            replace_layer(q, name="v_proj_b3g32_dynamic", w_key=21)]))
+    return out
+
+
+def replace_layer(layer: Layer, **kw) -> Layer:
+    from dataclasses import replace
+    return replace(layer, **kw)
 
 
 def scaled(layer: Layer, d_out: Optional[int] = None, d_in: Optional[int] = None,

@@ -464,3 +464,39 @@ def test_follow_own_codes_changes_nothing():
     # codes one level off everywhere are almost never float ties
     c = O.quantize_layer(W, p.U, p.perm, **kw, follow=np.clip(a.codes + 1, 0, 7), tie_tol=2.0 ** -12)
     assert c.ties <= 1
+
+
+# ----------------------------------------------------- shared-input layers ---
+
+def test_stacked_rows_equal_separate_layers():
+    # Layers that read one input share H and U; the sweep treats every output
+    # row on its own (each row's compensation only involves that row), so the
+    # sweep of the stacked rows [W1; W2] must return exactly the two layers'
+    # separate results.  A sweep that mixed rows (a transposed update, a
+    # group range taken over the wrong axis) would fail here.
+    H, _ = _rand_spd(24, 11)
+    p = O.prepare(H, 0.01, desc_act=True)
+    g = np.random.default_rng(12)
+    W1 = g.standard_normal((5, 24))
+    W2 = 3.0 * g.standard_normal((7, 24))
+    for static in (False, True):
+        both = O.quantize_layer(np.vstack([W1, W2]), p.U, p.perm, 3, 8, False, static)
+        a = O.quantize_layer(W1, p.U, p.perm, 3, 8, False, static)
+        b = O.quantize_layer(W2, p.U, p.perm, 3, 8, False, static)
+        np.testing.assert_array_equal(both.codes, np.vstack([a.codes, b.codes]))
+        np.testing.assert_array_equal(both.Q, np.vstack([a.Q, b.Q]))
+        np.testing.assert_array_equal(both.scales, np.hstack([a.scales, b.scales]))
+        np.testing.assert_array_equal(both.zeros, np.hstack([a.zeros, b.zeros]))
+
+
+def test_shared_groups_share_x_not_w():
+    # the generators' shared groups: one X (the first member's), distinct W
+    for cfg in (2, 3, 4):
+        for _, members in synth.shared_groups(cfg):
+            assert len({(L.seed, L.cfg, L.layer_id, L.d_in, L.n_tokens) for L in members}) == 1
+            assert len({L.w_key for L in members}) == len(members)
+    q, k, _ = synth.shared_groups(2)[0][1]
+    x_q = synth.activation_chunk(q, 0)
+    x_k = synth.activation_chunk(k, 0)
+    np.testing.assert_array_equal(x_q, x_k)
+    assert not np.array_equal(synth.weight(q), synth.weight(k))
