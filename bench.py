@@ -47,6 +47,9 @@ def parse():
                     help="instead of the one-line result: time every layer of the five configurations and write "
                          "a markdown table to PATH")
     ap.add_argument("--all-configs-steps", type=int, default=3)
+    ap.add_argument("--dequant", metavar="PATH", default=None,
+                    help="time gptq_dequant_matmul on the layer shapes of configurations 3 and 5 and write a "
+                         "markdown table to PATH")
     ap.add_argument("--shared", metavar="PATH", default=None,
                     help="time the layers that read one input (q/k/v, gate/up of configurations 2-3) solved "
                          "against one H and one U against separate solves; write a markdown table to PATH")
@@ -319,6 +322,65 @@ def shared_groups_table(args):
     print(text, flush=True)
 
 
+def dequant_table(args):
+    """gptq_dequant_matmul on the layer shapes of configurations 3 and 5:
+    microseconds per call and algorithmic bytes (packed weights, scales, zeros,
+    g_idx, x, y) per second against HBM; a markdown table."""
+    import numpy as np
+    import torch
+
+    import post_weight_quantization_07_amd as G
+    dev = torch.device("cuda:0")
+    lines = ["| d_out x d_in | bits / G | g_idx | tokens m | us per call | GB/s | % of 8 TB/s |",
+             "|---|---|---|---:|---:|---:|---:|"]
+    shapes = [(4096, 4096), (11008, 4096), (4096, 11008), (8192, 8192), (28672, 8192), (8192, 28672)]
+    cases = [(4, 128, False), (3, 32, True)]
+    gen = torch.Generator(device="cpu").manual_seed(0)
+    for d_out, d_in in shapes:
+        for bits, group, act in cases:
+            if act and (d_out, d_in) not in ((4096, 4096), (8192, 8192)):
+                continue
+            ng = -(-d_in // group)
+            codes = torch.randint(0, 1 << bits, (d_out, d_in), dtype=torch.uint8, generator=gen).to(dev)
+            qweight = G.gptq_pack(codes, bits)
+            scales = (torch.rand((ng, d_out), generator=gen) * 0.01 + 0.001).to(dev)
+            zeros = torch.randint(0, 1 << bits, (ng, d_out), dtype=torch.int32, generator=gen).to(dev)
+            if act:  # act-order dynamic groups: group of column k = sweep position // G
+                perm = torch.randperm(d_in, generator=gen)
+                g_idx = torch.empty(d_in, dtype=torch.int32)
+                g_idx[perm] = torch.arange(d_in, dtype=torch.int32) // group
+                g_idx = g_idx.to(dev)
+            else:
+                g_idx = (torch.arange(d_in, dtype=torch.int32) // group).to(dev)
+            for m in (1, 8, 16):
+                x = torch.randn((m, d_in), generator=gen).to(torch.bfloat16).to(dev)
+                y = torch.empty((m, d_out), dtype=torch.float32, device=dev)
+                ws = torch.empty(max(256, G.gptq_dequant_workspace_size(m, d_in, d_out)), dtype=torch.uint8,
+                                 device=dev)
+                for _ in range(5):
+                    G.gptq_dequant_matmul(x, qweight, scales, zeros, g_idx, bits, y=y, ws=ws)
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                reps = 50
+                torch.cuda.synchronize()
+                e0.record()
+                for _ in range(reps):
+                    G.gptq_dequant_matmul(x, qweight, scales, zeros, g_idx, bits, y=y, ws=ws)
+                e1.record()
+                torch.cuda.synchronize()
+                us = e0.elapsed_time(e1) * 1e3 / reps
+                nbytes = d_out * d_in * bits / 8 + ng * d_out * 8 + d_in * 4 + m * d_in * 2 + m * d_out * 4
+                gbs = nbytes / (us * 1e-6) / 1e9
+                lines.append(f"| {d_out}x{d_in} | {bits} / {group} | {'act-order' if act else 'k // G'} | {m} | "
+                             f"{us:.1f} | {gbs:.0f} | {100 * gbs / (PEAK_HBM_GBS):.1f}% |")
+                print(lines[-1], flush=True)
+            del codes, qweight, scales, zeros, g_idx
+            torch.cuda.empty_cache()
+    text = "\n".join(lines) + "\n"
+    with open(args.dequant, "w") as f:
+        f.write(text)
+    print(text, flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -335,6 +397,9 @@ def main():
         return
     if args.shared:
         shared_groups_table(args)
+        return
+    if args.dequant:
+        dequant_table(args)
         return
     layer = synth.config_layers(3)[0]
     d_out, d_in, N = layer.d_out, layer.d_in, layer.n_tokens

@@ -13,6 +13,10 @@
  *   gptq_quantize_layer       column sweep -> codes, scales, zeros, g_idx
  *   gptq_pack                 codes -> int32 qweight
  *
+ * and the quantized layer is applied with
+ *
+ *   gptq_dequant_matmul       y = x W^T, W dequantized from qweight / scales / zeros / g_idx
+ *
  * Conventions shared by every call
  *   - All array pointers are DEVICE pointers on the current HIP device; the
  *     caller owns every buffer (inputs, outputs, workspaces).  The library
@@ -155,6 +159,29 @@ gptq_status gptq_quantize_layer(const void* W, gptq_dtype wt, int64_t d_out, int
  */
 gptq_status gptq_pack(const uint8_t* codes, int64_t d_out, int64_t d_in, int32_t bits,
                       int32_t* qweight, void* stream);
+
+/*
+ * y = x W^T with W dequantized on the fly: W[n, k] = scales[g, n] *
+ * (code(n, k) - zeros[g, n]), g = g_idx[k] (chapter 5, section 5.1.10: a group
+ * shares one scale and zero point; the pages' inference kernels read the packed
+ * codes and dequantize inside the product).  Summed in fp32 in a fixed order
+ * (deterministic).
+ *   x        [m, d_in] bf16 or fp32, row-major, m >= 1 (any count; passes of 16 rows)
+ *   qweight  [d_in * bits / 32, d_out] int32 as written by gptq_pack
+ *   scales   [n_groups, d_out] fp32, zeros [n_groups, d_out] int32, g_idx [d_in]
+ *            int32 as written by gptq_quantize_layer; every g_idx entry must lie
+ *            in [0, n_groups) (not checked on the device)
+ *   y        [m, d_out] fp32 (overwritten)
+ *   ws       device workspace of gptq_dequant_workspace_size(m, d_in, d_out)
+ *            bytes, 256-byte aligned (partial sums of the K slices)
+ * Requires d_in % 32 == 0.  INVALID_ARG on bad sizes, bits or null pointers;
+ * WORKSPACE when ws is too small or misaligned.
+ */
+size_t gptq_dequant_workspace_size(int64_t m, int64_t d_in, int64_t d_out);
+gptq_status gptq_dequant_matmul(const void* x, gptq_dtype xt, int64_t m, int64_t d_in,
+                                const int32_t* qweight, const float* scales, const int32_t* zeros,
+                                const int32_t* g_idx, int32_t bits, int64_t d_out, int32_t n_groups,
+                                float* y, void* ws, size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }

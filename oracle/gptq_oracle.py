@@ -448,6 +448,25 @@ def unpack(qweight: np.ndarray, bits: int, d_in: int) -> np.ndarray:
     return codes
 
 
+def dequantize(qweight: np.ndarray, scales: np.ndarray, zeros: np.ndarray, g_idx: np.ndarray, bits: int,
+               d_in: int) -> np.ndarray:
+    """W_hat[n, k] = scale[g, n] (code(n, k) - zero[g, n]) with g = g_idx[k]
+    (ch.5 section 5.1.10: one scale and zero point per group), from the packed
+    codes and the per-group parameters, fp64."""
+    codes = unpack(qweight, bits, d_in).astype(np.float64)
+    g = np.asarray(g_idx, dtype=np.int64)
+    s = np.asarray(scales, dtype=np.float64)[g, :].T
+    z = np.asarray(zeros, dtype=np.float64)[g, :].T
+    return s * (codes - z)
+
+
+def dequant_matmul(x: np.ndarray, qweight: np.ndarray, scales: np.ndarray, zeros: np.ndarray,
+                   g_idx: np.ndarray, bits: int) -> np.ndarray:
+    """y = x W_hat^T in fp64 (the quantized layer applied to activations x [m, d_in])."""
+    x = np.asarray(x, dtype=np.float64)
+    return x @ dequantize(qweight, scales, zeros, g_idx, bits, x.shape[1]).T
+
+
 # ---------------------------------------------------------------------------
 # whole layer
 # ---------------------------------------------------------------------------

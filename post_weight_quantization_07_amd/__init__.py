@@ -1,7 +1,8 @@
 """MI355X (gfx950) GPTQ per-layer quantization solve.
 
 The four calls of the C ABI (include/gptq.h) with the same names, plus
-QuantizeConfig (BaseQuantizeConfig's fields), solve_layer, which chains them
+QuantizeConfig (BaseQuantizeConfig's fields), gptq_dequant_matmul (the
+quantized layer applied to activations), solve_layer, which chains them
 for one linear layer, and solve_layers_shared, which quantizes several layers
 that read the same input (q/k/v, gate/up) against one Hessian and one factor.
 All arithmetic runs in libgptq.so's HIP kernels.
@@ -13,12 +14,14 @@ from typing import Iterable, List, Optional, Sequence
 import torch
 
 from ._lib import (EXPORTS, GptqError, NotPositiveDefinite, QuantizeConfig, gptq_hessian_accumulate,  # noqa: F401
-                   gptq_hessian_workspace_size, gptq_pack, gptq_prepare_hinv, gptq_prepare_workspace_size,
-                   gptq_quantize_layer, gptq_workspace_size, library_path)
+                   gptq_dequant_matmul, gptq_dequant_workspace_size, gptq_hessian_workspace_size, gptq_pack,
+                   gptq_prepare_hinv, gptq_prepare_workspace_size, gptq_quantize_layer, gptq_workspace_size,
+                   library_path)
 
 __all__ = ["QuantizeConfig", "GptqError", "NotPositiveDefinite", "gptq_hessian_accumulate", "gptq_prepare_hinv",
            "gptq_quantize_layer", "gptq_pack", "gptq_hessian_workspace_size", "gptq_prepare_workspace_size",
-           "gptq_workspace_size", "solve_layer", "solve_layers_shared", "library_path"]
+           "gptq_workspace_size", "gptq_dequant_matmul", "gptq_dequant_workspace_size", "solve_layer",
+           "solve_layers_shared", "library_path"]
 
 
 def _accumulate(d_in: int, X_chunks: Iterable[torch.Tensor], device, stream):

@@ -21,7 +21,8 @@ GPTQ_F32, GPTQ_BF16 = 0, 1
 
 EXPORTS = ("gptq_config_validate", "gptq_status_string", "gptq_hessian_workspace_size",
            "gptq_hessian_accumulate", "gptq_prepare_workspace_size", "gptq_prepare_hinv",
-           "gptq_workspace_size", "gptq_quantize_layer", "gptq_pack")
+           "gptq_workspace_size", "gptq_quantize_layer", "gptq_pack", "gptq_dequant_workspace_size",
+           "gptq_dequant_matmul")
 
 
 class GptqError(RuntimeError):
@@ -63,6 +64,9 @@ def _lib():
             "gptq_quantize_layer": (c_int32, [vp, c_int32, i64, i64, vp, vp, cfgp, vp, vp, vp, vp, vp, vp,
                                               vp, sz, vp]),
             "gptq_pack": (c_int32, [vp, i64, i64, c_int32, vp, vp]),
+            "gptq_dequant_workspace_size": (sz, [i64, i64, i64]),
+            "gptq_dequant_matmul": (c_int32, [vp, c_int32, i64, i64, vp, vp, vp, vp, c_int32, i64, c_int32, vp, vp,
+                                              sz, vp]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(lib, name)
@@ -243,3 +247,33 @@ def gptq_pack(codes: torch.Tensor, bits: int, qweight: Optional[torch.Tensor] = 
         qweight = torch.empty((d_in * bits // 32, d_out), dtype=torch.int32, device=codes.device)
     _check(_lib().gptq_pack(_ptr(codes), d_out, d_in, int(bits), _ptr(qweight), _stream(stream)), "gptq_pack")
     return qweight
+
+
+def gptq_dequant_workspace_size(m: int, d_in: int, d_out: int) -> int:
+    return int(_lib().gptq_dequant_workspace_size(m, d_in, d_out))
+
+
+def gptq_dequant_matmul(x: torch.Tensor, qweight: torch.Tensor, scales: torch.Tensor, zeros: torch.Tensor,
+                        g_idx: torch.Tensor, bits: int, y: Optional[torch.Tensor] = None,
+                        ws: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """y [m, d_out] fp32 = x [m, d_in] (bf16 or fp32) times the transpose of the
+    weights dequantized from qweight / scales / zeros / g_idx."""
+    _dev(x, qweight, scales, zeros, g_idx)
+    if x.dim() != 2 or not x.is_contiguous():
+        raise ValueError("gptq_dequant_matmul: x must be a contiguous [m, d_in] matrix")
+    m, d_in = x.shape
+    d_out = qweight.shape[1]
+    n_groups = scales.shape[0]
+    if (qweight.shape[0] * 32 != d_in * bits or scales.shape != (n_groups, d_out) or zeros.shape != (n_groups, d_out)
+            or g_idx.shape != (d_in,) or qweight.dtype != torch.int32 or scales.dtype != torch.float32
+            or zeros.dtype != torch.int32 or g_idx.dtype != torch.int32):
+        raise ValueError("gptq_dequant_matmul: qweight / scales / zeros / g_idx do not match x and bits")
+    if y is None:
+        y = torch.empty((m, d_out), dtype=torch.float32, device=x.device)
+    if ws is None:
+        ws = _workspace(gptq_dequant_workspace_size(m, d_in, d_out), x.device)
+    _check(_lib().gptq_dequant_matmul(_ptr(x), _dtype_code(x), m, d_in, _ptr(qweight.contiguous()),
+                                      _ptr(scales.contiguous()), _ptr(zeros.contiguous()), _ptr(g_idx.contiguous()),
+                                      int(bits), d_out, n_groups, _ptr(y), _ptr(ws), ws.numel(), _stream(stream)),
+           "gptq_dequant_matmul")
+    return y

@@ -12,7 +12,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libgptq.so")
-SOURCES = ["hessian.hip", "gemm_f32.hip", "prepare.hip", "sweep.hip", "pack.hip", "abi.cpp"]
+SOURCES = ["hessian.hip", "gemm_f32.hip", "prepare.hip", "sweep.hip", "pack.hip", "dequant.hip", "abi.cpp"]
 
 ARCH = os.environ.get("GPTQ_OFFLOAD_ARCH", "gfx950")
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

@@ -58,4 +58,10 @@ hipError_t quantize_launch(const void* W, bool w_bf16, int64_t d_out, int64_t d_
 hipError_t pack_launch(const uint8_t* codes, int64_t d_out, int64_t d_in, int bits, int32_t* qweight,
                        hipStream_t stream);
 
+// ---------------------------------------------------------------- dequant --
+size_t dequant_workspace_bytes(int64_t m, int64_t d_in, int64_t d_out);
+hipError_t dequant_matmul_launch(const void* x, bool x_bf16, int64_t m, int64_t d_in, const int32_t* qweight,
+                                 const float* scales, const int32_t* zeros, const int32_t* g_idx, int bits,
+                                 int64_t d_out, int n_groups, float* y, void* ws, hipStream_t stream);
+
 }  // namespace gptq

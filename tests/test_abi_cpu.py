@@ -112,3 +112,23 @@ def test_python_config_mirrors_pages():
     with pytest.raises(ValueError):
         G.QuantizeConfig(damp_percent=1.0)
     assert G.QuantizeConfig(group_size=128).n_groups(4096) == 32
+
+
+def test_dequant_matmul_rejects_bad_arguments(lib):
+    fake = ctypes.c_void_p(4096)
+    ws = ctypes.c_void_p(1 << 20)
+    # d_in not a multiple of 32, bad bits, null pointers, bad sizes: INVALID_ARG
+    assert lib.gptq_dequant_matmul(fake, 0, 4, 48, fake, fake, fake, fake, 4, 64, 1, fake, ws, 1 << 20, None) == 1
+    assert lib.gptq_dequant_matmul(fake, 0, 4, 64, fake, fake, fake, fake, 5, 64, 1, fake, ws, 1 << 20, None) == 1
+    assert lib.gptq_dequant_matmul(None, 0, 4, 64, fake, fake, fake, fake, 4, 64, 1, fake, ws, 1 << 20, None) == 1
+    assert lib.gptq_dequant_matmul(fake, 0, 0, 64, fake, fake, fake, fake, 4, 64, 1, fake, ws, 1 << 20, None) == 1
+    assert lib.gptq_dequant_matmul(fake, 2, 4, 64, fake, fake, fake, fake, 4, 64, 1, fake, ws, 1 << 20, None) == 1
+    assert lib.gptq_dequant_matmul(fake, 0, 4, 64, fake, fake, fake, fake, 4, 64, 0, fake, ws, 1 << 20, None) == 1
+    # a workspace that is too small or misaligned: WORKSPACE
+    need = lib.gptq_dequant_workspace_size(4, 4096, 4096)
+    assert need > 256
+    assert lib.gptq_dequant_matmul(fake, 0, 4, 4096, fake, fake, fake, fake, 4, 4096, 32, fake, ws, need - 1,
+                                   None) == 4
+    assert lib.gptq_dequant_matmul(fake, 0, 4, 4096, fake, fake, fake, fake, 4, 4096, 32, fake,
+                                   ctypes.c_void_p((1 << 20) + 16), need, None) == 4
+    assert lib.gptq_dequant_workspace_size(4, 48, 64) == 0

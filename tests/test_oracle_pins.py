@@ -500,3 +500,23 @@ def test_shared_groups_share_x_not_w():
     x_k = synth.activation_chunk(k, 0)
     np.testing.assert_array_equal(x_q, x_k)
     assert not np.array_equal(synth.weight(q), synth.weight(k))
+
+
+# --------------------------------------------------- dequantizing product ---
+
+@pytest.mark.parametrize("bits,G,desc,static", [(4, 8, False, False), (3, 8, True, False), (2, 16, True, True),
+                                                (8, -1, False, False)])
+def test_dequantize_equals_sweep_q(bits, G, desc, static):
+    # the weights rebuilt from the stored tensors (packed codes, per-group
+    # scale and zero, g_idx) are the sweep's own dequantized weights, exactly:
+    # a wrong group lookup, a transposed parameter table or a bit-order slip
+    # in the unpacking changes them
+    H, _ = _rand_spd(32, 21)
+    p = O.prepare(H, 0.01, desc_act=desc)
+    W = np.random.default_rng(22).standard_normal((6, 32))
+    sw = O.quantize_layer(W, p.U, p.perm, bits, G, False, static)
+    Wq = O.dequantize(O.pack(sw.codes, bits), sw.scales, sw.zeros, sw.g_idx, bits, 32)
+    np.testing.assert_array_equal(Wq, sw.Q)
+    x = np.random.default_rng(23).standard_normal((3, 32))
+    y = O.dequant_matmul(x, O.pack(sw.codes, bits), sw.scales, sw.zeros, sw.g_idx, bits)
+    np.testing.assert_allclose(y, np.einsum("mk,nk->mn", x, sw.Q), rtol=1e-12, atol=1e-12)
