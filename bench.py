@@ -47,6 +47,9 @@ def parse():
                     help="instead of the one-line result: time every layer of the five configurations and write "
                          "a markdown table to PATH")
     ap.add_argument("--all-configs-steps", type=int, default=3)
+    ap.add_argument("--block", metavar="PATH", default=None,
+                    help="quantize a Llama-7B-shaped transformer block layer by layer (true-sequential) and "
+                         "write the per-stage times to PATH")
     ap.add_argument("--dequant", metavar="PATH", default=None,
                     help="time gptq_dequant_matmul on the layer shapes of configurations 3 and 5 and write a "
                          "markdown table to PATH")
@@ -381,6 +384,48 @@ def dequant_table(args):
     print(text, flush=True)
 
 
+def block_table(args):
+    """Layer-sequential quantization of a Llama-7B-shaped block (k/v/q, o,
+    up/gate, down): per-stage times of the driver's forward pieces and of the
+    group solves; a markdown table."""
+    import numpy as np
+    import torch
+
+    import post_weight_quantization_07_amd as G
+    import synth
+    from post_weight_quantization_07_amd.block import Block, quantize_block
+    shape = synth.BLOCKS["llama7b"]
+    dev = torch.device("cuda:0")
+    print(f"[block] generating {shape.n_tokens} tokens x {shape.d_model}", flush=True)
+    x0 = torch.from_numpy(synth.block_input(shape)).to(dev)
+    Wh = {n: torch.from_numpy(synth.weight(synth.block_linear_layer(shape, n))) for n in synth.BLOCK_LINEARS}
+    cfg = G.QuantizeConfig(**shape.quant_kwargs())
+    runs = []
+    for r in range(2):  # the first run warms up
+        blk = Block(shape.d_model, shape.n_heads, shape.d_ff, {n: w.to(dev) for n, w in Wh.items()})
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        res = quantize_block(blk, x0, shape.n_seq, shape.seq_len, cfg, timed=True)
+        torch.cuda.synchronize()
+        runs.append(((time.perf_counter() - t0) * 1e3, res.ms))
+        print(f"[block] run {r}: {runs[-1][0]:.1f} ms", flush=True)
+        del blk, res
+        torch.cuda.empty_cache()
+    total, ms = runs[-1]
+    cols = sum(synth.block_linear_layer(shape, n).d_in for n in synth.BLOCK_LINEARS)
+    solve_ms = sum(v for k, v in ms.items() if k.startswith("solve"))
+    lines = [f"| stage | ms |", "|---|---:|"]
+    for k in sorted(ms, key=lambda t: (t.split(" ")[0] != "forward", t)):
+        lines.append(f"| {k} | {ms[k]:.2f} |")
+    lines.append(f"| all solves (accumulate, prepare, quantize, pack of the four groups) | {solve_ms:.2f} |")
+    lines.append(f"| whole block, wall clock | {total:.2f} |")
+    lines.append(f"| weight columns/s over the block's seven layers (solves only) | {cols / (solve_ms * 1e-3):,.0f} |")
+    text = "\n".join(lines) + "\n"
+    with open(args.block, "w") as f:
+        f.write(text)
+    print(text, flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -400,6 +445,9 @@ def main():
         return
     if args.dequant:
         dequant_table(args)
+        return
+    if args.block:
+        block_table(args)
         return
     layer = synth.config_layers(3)[0]
     d_out, d_in, N = layer.d_out, layer.d_in, layer.n_tokens

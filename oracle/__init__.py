@@ -9,3 +9,4 @@ from .gptq_oracle import (NotSPD, Prepared, SweepResult, LayerResult, validate_c
                           prepare, quant_params, quantize_values, quantize_layer, naive_obq, rtn,
                           recon_error, recon_error_from_H, packed_words, pack, unpack, dequantize,
                           dequant_matmul, solve_layer)
+from . import block_oracle  # noqa: F401,E402

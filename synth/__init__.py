@@ -270,3 +270,65 @@ def scaled(layer: Layer, d_out: Optional[int] = None, d_in: Optional[int] = None
     if n_tokens is not None:
         kw["n_tokens"] = n_tokens
     return replace(layer, **kw)
+
+
+# --------------------------------------------------------------------------
+# A synthetic transformer block (random-init weights, synthetic hidden states)
+# for the layer-sequential driver.
+# --------------------------------------------------------------------------
+
+@dataclass(frozen=True)
+class BlockShape:
+    name: str
+    d_model: int
+    n_heads: int
+    d_ff: int
+    seq_len: int
+    n_seq: int
+    bits: int = 4
+    group_size: int = 128
+    sym: bool = True
+    desc_act: bool = False
+    static_groups: bool = False
+    damp_percent: float = 0.01
+    cfg: int = 6
+    seed: int = 0
+
+    def quant_kwargs(self) -> dict:
+        return dict(bits=self.bits, group_size=self.group_size, sym=self.sym, desc_act=self.desc_act,
+                    static_groups=self.static_groups, damp_percent=self.damp_percent)
+
+    @property
+    def n_tokens(self) -> int:
+        return self.seq_len * self.n_seq
+
+
+# the block's linear layers: name -> (d_out, d_in) as functions of the shape
+BLOCK_LINEARS = ("q_proj", "k_proj", "v_proj", "o_proj", "gate_proj", "up_proj", "down_proj")
+
+BLOCKS = {
+    "tiny": BlockShape("tiny", d_model=64, n_heads=4, d_ff=160, seq_len=32, n_seq=8, group_size=32),
+    "tiny_actorder": BlockShape("tiny_actorder", d_model=64, n_heads=4, d_ff=160, seq_len=32, n_seq=8, bits=3,
+                                group_size=32, desc_act=True, seed=1),
+    "llama7b": BlockShape("llama7b", d_model=4096, n_heads=32, d_ff=11008, seq_len=2048, n_seq=32),
+}
+
+
+def block_linear_layer(shape: BlockShape, name: str) -> Layer:
+    """The Layer whose W is the block's `name` weight (W recipe of the
+    configurations, key = position in BLOCK_LINEARS)."""
+    d, f = shape.d_model, shape.d_ff
+    dims = {"q_proj": (d, d), "k_proj": (d, d), "v_proj": (d, d), "o_proj": (d, d),
+            "gate_proj": (f, d), "up_proj": (f, d), "down_proj": (d, f)}
+    d_out, d_in = dims[name]
+    return Layer(name, d_out, d_in, shape.n_tokens, "bf16", "bf16", False, False, cfg=shape.cfg,
+                 layer_id=BLOCK_LINEARS.index(name), seed=shape.seed)
+
+
+def block_input(shape: BlockShape) -> np.ndarray:
+    """Hidden states entering the block, [n_seq * seq_len, d_model] fp32
+    (bf16-exact): the activation recipe (log-normal channel scales, 1% outlier
+    channels) under the block's own key."""
+    L = Layer("block_input", shape.d_model, shape.d_model, shape.n_tokens, "bf16", "bf16", False, True,
+              cfg=shape.cfg, layer_id=100, seed=shape.seed)
+    return activations(L)

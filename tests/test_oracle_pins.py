@@ -520,3 +520,32 @@ def test_dequantize_equals_sweep_q(bits, G, desc, static):
     x = np.random.default_rng(23).standard_normal((3, 32))
     y = O.dequant_matmul(x, O.pack(sw.codes, bits), sw.scales, sw.zeros, sw.g_idx, bits)
     np.testing.assert_allclose(y, np.einsum("mk,nk->mn", x, sw.Q), rtol=1e-12, atol=1e-12)
+
+
+# ------------------------------------------------ block forward (driver) ---
+
+def test_block_oracle_closed_forms():
+    from oracle import block_oracle as B
+    g = np.random.default_rng(31)
+    # equal keys: every causal attention weight is uniform, so position i gets
+    # the mean of the values of positions 0..i
+    n_seq, L, heads, d = 2, 5, 2, 8
+    q = g.standard_normal((n_seq * L, d))
+    k = np.tile(g.standard_normal((1, d)), (n_seq * L, 1))
+    v = g.standard_normal((n_seq * L, d))
+    out = B.causal_attention(q, k, v, n_seq, L, heads)
+    for s in range(n_seq):
+        vs = v[s * L:(s + 1) * L]
+        np.testing.assert_allclose(out[s * L:(s + 1) * L], np.cumsum(vs, axis=0) / np.arange(1, L + 1)[:, None],
+                                   rtol=1e-12, atol=1e-12)
+    # the first position attends only to itself
+    np.testing.assert_allclose(B.causal_attention(q, g.standard_normal(v.shape), v, n_seq, L, heads)[::L], v[::L],
+                               rtol=1e-12, atol=1e-12)
+    # zero weights leave the residual stream unchanged; RMSNorm rows have unit RMS
+    W = {n: np.zeros((d if n != "gate_proj" and n != "up_proj" else 12, d if n != "down_proj" else 12))
+         for n in synth.BLOCK_LINEARS}
+    x0 = g.standard_normal((n_seq * L, d))
+    st = B.block_stages(W, x0, n_seq, L, heads)
+    np.testing.assert_array_equal(st["out"], x0)
+    np.testing.assert_allclose(np.sqrt(np.mean(B.rms_norm(x0, 0.0) ** 2, axis=1)), 1.0, rtol=1e-12)
+    np.testing.assert_allclose(B.silu(np.array([0.0, 40.0, -40.0])), [0.0, 40.0, 0.0], atol=1e-15)
