@@ -165,7 +165,12 @@ gptq_status gptq_pack(const uint8_t* codes, int64_t d_out, int64_t d_in, int32_t
  * (code(n, k) - zeros[g, n]), g = g_idx[k] (chapter 5, section 5.1.10: a group
  * shares one scale and zero point; the pages' inference kernels read the packed
  * codes and dequantize inside the product).  Summed in fp32 in a fixed order
- * (deterministic).
+ * (deterministic).  32 consecutive k of one group are summed as
+ * s (sum x q - z sum x), so the rounding error is bounded by
+ * (d_in + 64) 2^-24 sum_k |x_k| s (q_k + z).  bf16 x with 3 or more tokens
+ * runs on bf16 MFMA with the integer codes as the exact operand; 32 k spread
+ * over several groups (act-order) use s (q - z) split into two bf16 parts
+ * there, so those products carry a relative error of about 2^-16.
  *   x        [m, d_in] bf16 or fp32, row-major, m >= 1 (any count; passes of 16 rows)
  *   qweight  [d_in * bits / 32, d_out] int32 as written by gptq_pack
  *   scales   [n_groups, d_out] fp32, zeros [n_groups, d_out] int32, g_idx [d_in]
@@ -173,9 +178,11 @@ gptq_status gptq_pack(const uint8_t* codes, int64_t d_out, int64_t d_in, int32_t
  *            in [0, n_groups) (not checked on the device)
  *   y        [m, d_out] fp32 (overwritten)
  *   ws       device workspace of gptq_dequant_workspace_size(m, d_in, d_out)
- *            bytes, 256-byte aligned (partial sums of the K slices)
- * Requires d_in % 32 == 0.  INVALID_ARG on bad sizes, bits or null pointers;
- * WORKSPACE when ws is too small or misaligned.
+ *            bytes, 256-byte aligned (partial sums of K slices); may be null
+ *            when that size is 0
+ * Requires d_in % 32 == 0, and qweight and scales each under 2^31 bytes
+ * (d_in * d_out * bits / 8 and n_groups * d_out * 4).  INVALID_ARG on bad
+ * sizes, bits or null pointers; WORKSPACE when ws is too small or misaligned.
  */
 size_t gptq_dequant_workspace_size(int64_t m, int64_t d_in, int64_t d_out);
 gptq_status gptq_dequant_matmul(const void* x, gptq_dtype xt, int64_t m, int64_t d_in,

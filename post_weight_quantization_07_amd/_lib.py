@@ -271,9 +271,11 @@ def gptq_dequant_matmul(x: torch.Tensor, qweight: torch.Tensor, scales: torch.Te
     if y is None:
         y = torch.empty((m, d_out), dtype=torch.float32, device=x.device)
     if ws is None:
-        ws = _workspace(gptq_dequant_workspace_size(m, d_in, d_out), x.device)
+        need = gptq_dequant_workspace_size(m, d_in, d_out)
+        ws = _workspace(need, x.device) if need > 0 else None
     _check(_lib().gptq_dequant_matmul(_ptr(x), _dtype_code(x), m, d_in, _ptr(qweight.contiguous()),
                                       _ptr(scales.contiguous()), _ptr(zeros.contiguous()), _ptr(g_idx.contiguous()),
-                                      int(bits), d_out, n_groups, _ptr(y), _ptr(ws), ws.numel(), _stream(stream)),
+                                      int(bits), d_out, n_groups, _ptr(y), _ptr(ws), 0 if ws is None else ws.numel(),
+                                      _stream(stream)),
            "gptq_dequant_matmul")
     return y

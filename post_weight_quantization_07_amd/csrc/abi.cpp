@@ -139,8 +139,11 @@ gptq_status gptq_dequant_matmul(const void* x, gptq_dtype xt, int64_t m, int64_t
   if (!x || !qweight || !scales || !zeros || !g_idx || !y) return GPTQ_ERR_INVALID_ARG;
   if (m <= 0 || d_out <= 0 || d_in <= 0 || d_in % 32 != 0 || n_groups <= 0) return GPTQ_ERR_INVALID_ARG;
   if (!bits_ok(bits) || (xt != GPTQ_F32 && xt != GPTQ_BF16)) return GPTQ_ERR_INVALID_ARG;
+  // qweight and scales / zeros are addressed with 32-bit byte offsets
+  if (d_in / 32 * bits * d_out * 4 >= (int64_t{1} << 31) || int64_t{n_groups} * d_out * 4 >= (int64_t{1} << 31))
+    return GPTQ_ERR_INVALID_ARG;
   const size_t need = gptq::dequant_workspace_bytes(m, d_in, d_out);
-  if (!ws || ws_bytes < need || !aligned256(ws)) return GPTQ_ERR_WORKSPACE;
+  if (need > 0 && (!ws || ws_bytes < need || !aligned256(ws))) return GPTQ_ERR_WORKSPACE;
   return from_hip(gptq::dequant_matmul_launch(x, xt == GPTQ_BF16, m, d_in, qweight, scales, zeros, g_idx, bits, d_out,
                                               n_groups, y, ws, static_cast<hipStream_t>(stream)));
 }

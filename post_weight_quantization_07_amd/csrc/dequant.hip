@@ -5,22 +5,39 @@
 // s_g (q - z_g) with its group's scale and zero point; the inference kernels
 // the pages list (ExLlama, Marlin, Triton) read the packed codes and
 // dequantize inside the product.  At decode batch sizes the product is bound
-// by reading the packed weights (bits / 8 bytes per weight), so this is a
-// bandwidth kernel, not a tile GEMM:
+// by reading the packed weights (bits / 8 bytes per weight).
 //
-//   Lanes map to output columns (64 per workgroup), so a packed word load is
-//   64 consecutive int32 of one qweight row.  K is walked in chunks of 32
-//   codes (bits words per column); code j of a chunk sits at bit bits * j of
-//   the chunk's words (a funnel shift where a 3-bit code straddles two words),
-//   all offsets compile-time.  x (up to MT tokens per pass) is staged in LDS as
-//   fp32 and read as wave-uniform broadcasts.  When a chunk's 32 columns share
-//   one group (every case but act-order with dynamic groups), its scale and
-//   zero point are read once per chunk and y += s * sum_k x_k (q_k - z);
-//   otherwise each code reads its own group's s and z.  The four waves of a
-//   workgroup take interleaved chunks of the workgroup's K range and are summed
-//   through LDS in wave order; K is further split over KS workgroups whose
-//   partial products a second kernel adds in slice order, so the result does
-//   not depend on scheduling.
+// K is walked in chunks of 32 codes (bits words per column), x and g_idx
+// staged in LDS per 16 chunks.  A chunk whose 32 columns share one group
+// (every case but act-order with dynamic groups) reads its scale and zero
+// point once; otherwise each code reads its own group's s and z.  Partial
+// sums are added in a fixed order, so the result does not depend on
+// scheduling.
+//
+// MFMA path (bf16 x, 3 tokens or more; v_mfma_f32_16x16x32_bf16): a wave
+// computes 16 tokens x 16 columns of one chunk.  Inside a chunk, codes 8 g ..
+// 8 g + 7 go to lane group g (lanes 16 g .. 16 g + 15), in both operands
+// alike, so lane group g of column n needs one packed word at 4 bits, two at
+// 8, half a word at 2, a 24-bit funnel-shifted field at 3.  For a one-group
+// chunk the B operand is the codes themselves (integers <= 255, exact in
+// bf16), a second MFMA adds x times -z, and the column's scale multiplies the
+// chunk's sum in fp32, so the products are exact and the rounding is that of
+// the same sum as in the VALU path.  A chunk spread over several groups uses
+// B = s (q - z) split into bf16 high and low parts (two MFMAs).  A workgroup
+// owns 64 output columns (16 per wave) over a K range; K is split over
+// workgroups as in the VALU path.
+//
+// VALU path (fp32 x, or 1-2 tokens): lanes map to output columns (64 per
+// workgroup, so a packed word load is 64 consecutive int32 of one qweight
+// row); a lane converts its chunk's 32 codes with compile-time offsets and
+// accumulates MT tokens.  A one-group chunk adds s (sum_k x_k q_k - z sum_k
+// x_k), the chunk's sum of x formed once per workgroup, which takes the
+// subtraction of z out of the per-code work (two operations per code at 2, 4
+// and 8 bits: a byte-to-float conversion and an FMA); its rounding error is
+// bounded by the sum of |x_k| s (q_k + z) instead of |x_k| s |q_k - z|.  The
+// four waves take interleaved chunks of the
+// workgroup's K range and are summed through LDS in wave order; K is split
+// over workgroups whose partial products a second kernel adds in slice order.
 #include "gptq_common.h"
 #include "gptq_internal.h"
 
@@ -29,9 +46,12 @@
 namespace gptq {
 namespace {
 
-constexpr int kCols = 64;          // output columns per workgroup
-constexpr int kChunk = 32;         // codes per chunk
-constexpr int kMaxChunksPerWG = 16;
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+
+constexpr int kValuCols = 64;  // output columns per workgroup
+constexpr int kChunk = 32;     // codes per chunk
+constexpr int kStage = 16;     // chunks per LDS stage
+constexpr int kMaxMT = 16;     // tokens per pass
 
 struct DqParams {
   const void* x;
@@ -43,13 +63,80 @@ struct DqParams {
   const float* scales;     // [n_groups, d_out]
   const int32_t* zeros;    // [n_groups, d_out]
   const int32_t* g_idx;    // [d_in]
-  int n_groups;
-  int chunks;          // d_in / 32
-  int cpw;             // chunks per workgroup
-  int ks;              // K slices
-  float* out;          // ks == 1: y rows m0.. (ld_out); else partial [ks][MT][d_out]
-  int64_t ld_out;
+  uint32_t qbytes;         // bytes of qweight, < 2^31
+  uint32_t gbytes;         // bytes of scales (and of zeros), < 2^31
+  int chunks;              // d_in / 32
+  int cpw;                 // chunks per workgroup
+  int ks;                  // K slices
+  float* y;                // [m_total, d_out]
+  float* part;             // VALU path, ks > 1: partial sums [ks][MT][d_out]
 };
+
+// qweight, scales and zeros are read through buffer descriptors: a lane's
+// column offset is its 32-bit VGPR offset, and the part common to the wave
+// (chunk row, group row) goes into the scalar offset, so a load costs no
+// vector address arithmetic.  Every offset stays inside the tensor.
+GPTQ_DEV __amdgpu_buffer_rsrc_t buffer_of(const void* ptr, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(ptr), 0, static_cast<int>(bytes), 0x00020000);
+}
+
+GPTQ_DEV uint32_t bload(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+}
+
+GPTQ_DEV int wave_uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// x[m0 + t][32 c0 ..] for the stage's chunks as fp32 into xs[chunk][t][j]
+// (0 for t >= m).  16-byte pieces (4 fp32 or 8 bf16), every load at an
+// in-range address (clamped row and piece), selected after.
+template <int MT>
+GPTQ_DEV void stage_x_f32(const DqParams& p, int64_t c0, int nc, float (*xs)[MT][kChunk + 4], int tid) {
+  const int per = p.xbf16 ? 8 : 4;                    // elements per piece
+  const int row_pieces = kStage * kChunk / per;       // pieces per token row of the stage
+  const int live = nc * kChunk / per;
+  for (int e0 = 0; e0 < MT * row_pieces; e0 += 256 * 4) {
+    u32x4_t v[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = e0 + tid + 256 * i;
+      const int t = std::min(e / row_pieces, MT - 1), k = std::min(e % row_pieces, live - 1);
+      const int64_t row = p.m0 + std::min<int64_t>(t, p.m - 1);
+      const int64_t col = c0 * kChunk + static_cast<int64_t>(k) * per;
+      v[i] = p.xbf16 ? *reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(p.x) + row * p.ldx + col)
+                     : *reinterpret_cast<const u32x4_t*>(static_cast<const float*>(p.x) + row * p.ldx + col);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = e0 + tid + 256 * i;
+      const int t = e / row_pieces, k = e % row_pieces;
+      if (t >= MT || k >= live) continue;
+      const int kk = k * per, cl = kk / kChunk, j = kk % kChunk;
+      if (p.xbf16) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          xs[cl][t][j + 2 * q] = (t < p.m) ? __uint_as_float(v[i][q] << 16) : 0.f;
+          xs[cl][t][j + 2 * q + 1] = (t < p.m) ? __uint_as_float(v[i][q] & 0xffff0000u) : 0.f;
+        }
+      } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) xs[cl][t][j + q] = (t < p.m) ? __uint_as_float(v[i][q]) : 0.f;
+      }
+    }
+  }
+}
+
+// g_idx of the stage's chunks, and whether each chunk lies in one group
+GPTQ_DEV void stage_groups(const DqParams& p, int64_t c0, int nc, int32_t (*gl)[kChunk], int* uni, int tid) {
+  for (int e = tid; e < nc * kChunk; e += 256) gl[e / kChunk][e % kChunk] = p.g_idx[c0 * kChunk + e];
+  __syncthreads();
+  if (tid < nc) {
+    int same = 1;
+    for (int j = 1; j < kChunk; ++j) same &= (gl[tid][j] == gl[tid][0]);
+    uni[tid] = same;
+  }
+}
+
+// ---------------------------------------------------------------- VALU path
 
 // code j (0..31) of a chunk held in BITS words
 template <int BITS, int J>
@@ -63,168 +150,456 @@ GPTQ_DEV uint32_t chunk_code(const uint32_t (&w)[BITS]) {
   }
 }
 
-template <int BITS, int MT, int... Js>
-GPTQ_DEV void chunk_uniform(const uint32_t (&w)[BITS], const float (*xs)[MT], float z, float (&acc)[MT],
-                            std::integer_sequence<int, Js...>) {
+// x & M with the mask hidden from the optimizer: with the mask visible it
+// turns each later byte extraction back into a bit-field extract of the
+// original word, one more operation per code
+template <uint32_t M>
+GPTQ_DEV uint32_t opaque_and(uint32_t x) {
+  uint32_t r;
+  asm("v_and_b32 %0, %1, %2" : "=v"(r) : "i"(M), "v"(x));
+  return r;
+}
+
+// code j of a chunk as a float.  Widths that divide 8 spread the word's codes
+// over bytes first (one shift and one mask per byte lane set, shared by the
+// codes of a word) so that each code then converts in one byte-to-float step.
+template <int BITS, int J>
+GPTQ_DEV float chunk_code_f(const uint32_t (&w)[BITS]) {
+  if constexpr (BITS == 8) {
+    return static_cast<float>((w[J >> 2] >> (8 * (J & 3))) & 0xffu);
+  } else if constexpr (BITS == 4) {
+    constexpr int i = J & 7;  // nibble i: byte i / 2 of the even or odd nibbles
+    const uint32_t v = opaque_and<0x0f0f0f0fu>((i & 1) ? (w[J >> 3] >> 4) : w[J >> 3]);
+    return static_cast<float>((v >> (8 * (i >> 1))) & 0xffu);
+  } else if constexpr (BITS == 2) {
+    constexpr int i = J & 15;  // 2-bit field i: byte i / 4 after a shift by 2 (i % 4)
+    const uint32_t v = opaque_and<0x03030303u>(w[J >> 4] >> (2 * (i & 3)));
+    return static_cast<float>((v >> (8 * (i >> 2))) & 0xffu);
+  } else {
+    return static_cast<float>(chunk_code<BITS, J>(w));
+  }
+}
+
+// acc[t] += sum_j x[t][j] q_j over the chunk; the zero point is applied once
+// per chunk by the caller, as z times the chunk's sum of x
+template <int BITS, int MT, int... J4s>
+GPTQ_DEV void valu_uniform(const uint32_t (&w)[BITS], const float (*xs)[kChunk + 4], float (&acc)[MT],
+                           std::integer_sequence<int, J4s...>) {
   (
       [&] {
-        const float qz = static_cast<float>(chunk_code<BITS, Js>(w)) - z;
+        // codes 4 J4 .. 4 J4 + 3 against one 16-byte read of x per token
+        const float q0 = chunk_code_f<BITS, 4 * J4s>(w), q1 = chunk_code_f<BITS, 4 * J4s + 1>(w);
+        const float q2 = chunk_code_f<BITS, 4 * J4s + 2>(w), q3 = chunk_code_f<BITS, 4 * J4s + 3>(w);
 #pragma unroll
-        for (int t = 0; t < MT; ++t) acc[t] = fmaf(xs[Js][t], qz, acc[t]);
+        for (int t = 0; t < MT; ++t) {
+          const f32x4_t xv = *reinterpret_cast<const f32x4_t*>(&xs[t][4 * J4s]);
+          acc[t] = fmaf(xv[0], q0, acc[t]);
+          acc[t] = fmaf(xv[1], q1, acc[t]);
+          acc[t] = fmaf(xv[2], q2, acc[t]);
+          acc[t] = fmaf(xv[3], q3, acc[t]);
+        }
       }(),
       ...);
 }
 
 template <int BITS, int MT, int... Js>
-GPTQ_DEV void chunk_grouped(const uint32_t (&w)[BITS], const float (*xs)[MT], const int32_t* gl, const DqParams& p,
-                            int64_t n, float (&y)[MT], std::integer_sequence<int, Js...>) {
+GPTQ_DEV void valu_grouped(const uint32_t (&w)[BITS], const float (*xs)[kChunk + 4], const int32_t* gl,
+                           __amdgpu_buffer_rsrc_t rs, __amdgpu_buffer_rsrc_t rz, uint32_t rowb, uint32_t vo,
+                           float (&y)[MT], std::integer_sequence<int, Js...>) {
   (
       [&] {
-        const int64_t g = gl[Js];
-        const float s = p.scales[g * p.d_out + n];
-        const float z = static_cast<float>(p.zeros[g * p.d_out + n]);
+        const uint32_t so = static_cast<uint32_t>(wave_uniform(gl[Js])) * rowb;  // group row of code j
+        const float s = __builtin_bit_cast(float, bload(rs, vo, so));
+        const float z = static_cast<float>(static_cast<int32_t>(bload(rz, vo, so)));
         const float wv = s * (static_cast<float>(chunk_code<BITS, Js>(w)) - z);
 #pragma unroll
-        for (int t = 0; t < MT; ++t) y[t] = fmaf(xs[Js][t], wv, y[t]);
+        for (int t = 0; t < MT; ++t) y[t] = fmaf(xs[t][Js], wv, y[t]);
       }(),
       ...);
 }
 
+// gix is g_idx again, as its own restrict argument, so that the reads of a
+// chunk's first entry (wave-uniform addresses) become scalar loads.
 template <int BITS, int MT>
-__global__ __launch_bounds__(256) void dequant_matmul_kernel(DqParams p) {
-  __shared__ __attribute__((aligned(16))) float xs[kMaxChunksPerWG][kChunk][MT];
-  __shared__ int32_t gl[kMaxChunksPerWG][kChunk];
-  __shared__ int uni[kMaxChunksPerWG];
-  __shared__ float ys[4][MT][kCols];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int nblocks = static_cast<int>((p.d_out + kCols - 1) / kCols);
+__global__ __launch_bounds__(256) void dequant_valu_kernel(DqParams p, const int32_t* __restrict__ gix) {
+  __shared__ __attribute__((aligned(16))) float xs[kStage][MT][kChunk + 4];
+  __shared__ int32_t gl[kStage][kChunk];
+  __shared__ int uni[kStage];
+  __shared__ float xsum[kStage][MT];
+  __shared__ float ys[4][MT][kValuCols];
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_uniform(tid >> 6);
+  const int nblocks = static_cast<int>((p.d_out + kValuCols - 1) / kValuCols);
   const int nb = blockIdx.x % nblocks, ks = blockIdx.x / nblocks;
-  const int c0 = ks * p.cpw, c1 = min(p.chunks, c0 + p.cpw), nc = max(0, c1 - c0);
-
-  // stage x[m0 + t][32 c0 ..] (fp32, zero rows past m) and the chunks' groups
-  for (int e = tid; e < nc * kChunk * MT; e += 256) {
-    const int t = e % MT, kk = e / MT;  // kk: column within the workgroup's range
-    const int64_t k = static_cast<int64_t>(c0) * kChunk + kk;
-    float v = 0.f;
-    if (t < p.m) {
-      const int64_t off = (p.m0 + t) * p.ldx + k;
-      v = p.xbf16 ? bf16_to_f32(static_cast<const uint16_t*>(p.x)[off]) : static_cast<const float*>(p.x)[off];
+  const int64_t c0 = static_cast<int64_t>(ks) * p.cpw;
+  const int nc = static_cast<int>(std::max<int64_t>(0, std::min<int64_t>(p.chunks, c0 + p.cpw) - c0));
+  const int64_t n = static_cast<int64_t>(nb) * kValuCols + lane;
+  const int64_t nl = std::min(n, p.d_out - 1);  // columns past the end read the last one
+  // the wave's chunks wave, wave + 4, ...: code words and first group's scale
+  // and zero point, issued before x is staged, at in-range chunk indices
+  const __amdgpu_buffer_rsrc_t rq = buffer_of(p.qweight, p.qbytes), rs = buffer_of(p.scales, p.gbytes),
+                               rz = buffer_of(p.zeros, p.gbytes);
+  const uint32_t rowb = static_cast<uint32_t>(p.d_out) * 4u, vo = static_cast<uint32_t>(nl) * 4u;
+  constexpr int kPerWave = kStage / 4;
+  uint32_t wq[kPerWave][BITS];
+  float sc[kPerWave];
+  int32_t zc[kPerWave];
+#pragma unroll
+  for (int i = 0; i < kPerWave; ++i) {
+    const int64_t c = std::min<int64_t>(c0 + std::min(wave + 4 * i, std::max(nc, 1) - 1), p.chunks - 1);
+#pragma unroll
+    for (int b = 0; b < BITS; ++b) wq[i][b] = bload(rq, vo, static_cast<uint32_t>(c * BITS + b) * rowb);
+    const uint32_t so = static_cast<uint32_t>(gix[c * kChunk]) * rowb;
+    sc[i] = __builtin_bit_cast(float, bload(rs, vo, so));
+    zc[i] = static_cast<int32_t>(bload(rz, vo, so));
+  }
+  if (nc > 0) {
+    stage_x_f32<MT>(p, c0, nc, xs, tid);
+    stage_groups(p, c0, nc, gl, uni, tid);  // ends past a barrier: xs is visible
+    for (int e = tid; e < nc * MT; e += 256) {
+      const int cl = e / MT, t = e % MT;
+      float v = 0.f;
+      for (int j = 0; j < kChunk; ++j) v += xs[cl][t][j];
+      xsum[cl][t] = v;
     }
-    xs[kk / kChunk][kk % kChunk][t] = v;
-  }
-  for (int e = tid; e < nc * kChunk; e += 256) gl[e / kChunk][e % kChunk] = p.g_idx[static_cast<int64_t>(c0) * kChunk + e];
-  __syncthreads();
-  if (tid < nc) {
-    int same = 1;
-    for (int j = 1; j < kChunk; ++j) same &= (gl[tid][j] == gl[tid][0]);
-    uni[tid] = same;
   }
   __syncthreads();
-
-  const int64_t n = static_cast<int64_t>(nb) * kCols + lane;
-  const int64_t nl = min(n, p.d_out - 1);  // loads of columns past the end read the last one
   float y[MT];
 #pragma unroll
   for (int t = 0; t < MT; ++t) y[t] = 0.f;
-  for (int cl = wave; cl < nc; cl += 4) {
-    const int64_t c = c0 + cl;
-    uint32_t w[BITS];
 #pragma unroll
-    for (int i = 0; i < BITS; ++i) w[i] = static_cast<uint32_t>(p.qweight[(c * BITS + i) * p.d_out + nl]);
+  for (int i = 0; i < kPerWave; ++i) {
+    const int cl = wave + 4 * i;
+    if (cl >= nc) continue;
+    const uint32_t(&w)[BITS] = wq[i];
     if (uni[cl]) {
-      const int64_t g = gl[cl][0];
-      const float s = p.scales[g * p.d_out + nl];
-      const float z = static_cast<float>(p.zeros[g * p.d_out + nl]);
+      const float s = sc[i];
+      const float z = static_cast<float>(zc[i]);
       float acc[MT];
 #pragma unroll
       for (int t = 0; t < MT; ++t) acc[t] = 0.f;
-      chunk_uniform<BITS, MT>(w, xs[cl], z, acc, std::make_integer_sequence<int, kChunk>{});
+      valu_uniform<BITS, MT>(w, xs[cl], acc, std::make_integer_sequence<int, kChunk / 4>{});
 #pragma unroll
-      for (int t = 0; t < MT; ++t) y[t] = fmaf(s, acc[t], y[t]);
+      for (int t = 0; t < MT; ++t) y[t] = fmaf(s, fmaf(-z, xsum[cl][t], acc[t]), y[t]);
     } else {
-      chunk_grouped<BITS, MT>(w, xs[cl], gl[cl], p, nl, y, std::make_integer_sequence<int, kChunk>{});
+      valu_grouped<BITS, MT>(w, xs[cl], gl[cl], rs, rz, rowb, vo, y, std::make_integer_sequence<int, kChunk>{});
     }
   }
   // the four waves' partial sums, added in wave order
 #pragma unroll
   for (int t = 0; t < MT; ++t) ys[wave][t][lane] = y[t];
   __syncthreads();
-  for (int e = tid; e < MT * kCols; e += 256) {
-    const int t = e / kCols, col = e % kCols;
-    const int64_t nn = static_cast<int64_t>(nb) * kCols + col;
+  for (int e = tid; e < MT * kValuCols; e += 256) {
+    const int t = e / kValuCols, col = e % kValuCols;
+    const int64_t nn = static_cast<int64_t>(nb) * kValuCols + col;
     if (nn >= p.d_out || t >= p.m) continue;
     const float v = ((ys[0][t][col] + ys[1][t][col]) + ys[2][t][col]) + ys[3][t][col];
-    if (p.ks == 1) p.out[(p.m0 + t) * p.ld_out + nn] = v;
-    else p.out[(static_cast<int64_t>(ks) * MT + t) * p.d_out + nn] = v;
+    if (p.ks == 1) p.y[(p.m0 + t) * p.d_out + nn] = v;
+    else p.part[(static_cast<int64_t>(ks) * MT + t) * p.d_out + nn] = v;
   }
 }
 
 // y[m0 + t][n] = sum over the K slices, in slice order
 template <int MT>
-__global__ void dequant_reduce_kernel(const float* part, int ks, int64_t m0, int64_t m, int64_t d_out, float* y,
-                                      int64_t ld_y) {
+__global__ void dequant_reduce_kernel(const float* part, int ks, int64_t m0, int64_t m, int64_t d_out, float* y) {
   const int64_t e = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x;
   if (e >= m * d_out) return;
   const int64_t t = e / d_out, n = e - t * d_out;
   float v = 0.f;
   for (int s = 0; s < ks; ++s) v += part[(static_cast<int64_t>(s) * MT + t) * d_out + n];
-  y[(m0 + t) * ld_y + n] = v;
+  y[(m0 + t) * d_out + n] = v;
 }
 
-struct DqPlan {
+// ---------------------------------------------------------------- MFMA path
+
+// Lane group g's 8 codes of a chunk in column n (codes 8 g .. 8 g + 7 of the
+// chunk) sit at bits 8 g BITS .. 8 g BITS + 8 BITS - 1 of the chunk's BITS
+// words, so a lane group loads only the word or two that hold them: word g
+// at 4 bits, word g / 2 (half g % 2) at 2, words 2 g and 2 g + 1 at 8, and at
+// 3 bits the words holding bit 24 g and 24 g + 23: (0, 1), (0, 1), (1, 2),
+// (2, 2).  LaneWords holds their byte offsets within the chunk's rows.
+template <int BITS>
+constexpr int kLaneWords = (BITS == 8 || BITS == 3) ? 2 : 1;
+
+template <int BITS>
+struct LaneWords {
+  uint32_t off[kLaneWords<BITS>];
+  GPTQ_DEV LaneWords(int g, int64_t d_out, int64_t n) {
+    const uint32_t rowb = static_cast<uint32_t>(d_out) * 4u, nb = static_cast<uint32_t>(n) * 4u;
+    if constexpr (BITS == 8) {
+      off[0] = (2 * g) * rowb + nb;
+      off[1] = (2 * g + 1) * rowb + nb;
+    } else if constexpr (BITS == 3) {
+      const int lo = (24 * g) >> 5;
+      off[0] = lo * rowb + nb;
+      off[1] = std::min(lo + 1, 2) * rowb + nb;
+    } else if constexpr (BITS == 4) {
+      off[0] = g * rowb + nb;
+    } else {
+      off[0] = (g >> 1) * rowb + nb;
+    }
+  }
+};
+
+// the words of chunk c: soff is the chunk's first row, c BITS d_out 4 bytes
+template <int BITS>
+GPTQ_DEV void lane_words(__amdgpu_buffer_rsrc_t rq, const LaneWords<BITS>& lw, uint32_t soff, int g,
+                         uint32_t (&w)[kLaneWords<BITS>]) {
+#pragma unroll
+  for (int i = 0; i < kLaneWords<BITS>; ++i) w[i] = bload(rq, lw.off[i], soff);
+  if constexpr (BITS == 2) w[0] >>= 16 * (g & 1);
+}
+
+// those 8 codes as floats (exact integers)
+template <int BITS>
+GPTQ_DEV void lane_codes(const uint32_t (&w)[kLaneWords<BITS>], int g, float (&q)[8]) {
+  if constexpr (BITS == 8) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      q[i] = static_cast<float>((w[0] >> (8 * i)) & 0xffu);
+      q[4 + i] = static_cast<float>((w[1] >> (8 * i)) & 0xffu);
+    }
+  } else if constexpr (BITS == 4) {
+    const uint32_t ev = opaque_and<0x0f0f0f0fu>(w[0]), od = opaque_and<0x0f0f0f0fu>(w[0] >> 4);
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      q[2 * b] = static_cast<float>((ev >> (8 * b)) & 0xffu);
+      q[2 * b + 1] = static_cast<float>((od >> (8 * b)) & 0xffu);
+    }
+  } else if constexpr (BITS == 2) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t v = opaque_and<0x03030303u>(w[0] >> (2 * k));  // codes k and 4 + k in bytes 0 and 1
+      q[k] = static_cast<float>(v & 0xffu);
+      q[4 + k] = static_cast<float>((v >> 8) & 0xffu);
+    }
+  } else {
+    const uint32_t f = __builtin_amdgcn_alignbit(w[1], w[0], static_cast<uint32_t>((24 * g) & 31));
+#pragma unroll
+    for (int i = 0; i < 8; ++i) q[i] = static_cast<float>((f >> (3 * i)) & 7u);
+  }
+}
+
+// two floats that are bf16 values (here integers of at most 8 significant
+// bits) as a bf16 pair, a in the low half: the low 16 bits of each are zero
+GPTQ_DEV uint32_t pack_exact_bf16(float a, float b) {
+  return (__builtin_bit_cast(uint32_t, b) & 0xffff0000u) | (__builtin_bit_cast(uint32_t, a) >> 16);
+}
+
+GPTQ_DEV uint32_t bf16_bits_of(float v) {
+  // round to nearest even; inputs are finite
+  const uint32_t u = __builtin_bit_cast(uint32_t, v);
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+GPTQ_DEV float bf16_value(uint32_t b) { return __builtin_bit_cast(float, b << 16); }
+
+GPTQ_DEV f32x4_t mfma32(const u32x4_t& a, const u32x4_t& b, const f32x4_t& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c,
+                                                 0, 0, 0);
+}
+
+template <int BITS>
+__global__ __launch_bounds__(256) void dequant_mfma_kernel(DqParams p, const int32_t* __restrict__ gix) {
+  __shared__ __attribute__((aligned(16))) uint16_t xb[kStage][16][kChunk + 8];  // bf16 x, [chunk][token][k]
+  __shared__ int32_t gl[kStage][kChunk];
+  __shared__ int uni[kStage];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int c16 = lane & 15, g = lane >> 4;
+  const int nblocks = static_cast<int>((p.d_out + kValuCols - 1) / kValuCols);
+  const int nb = blockIdx.x % nblocks, ks = blockIdx.x / nblocks;
+  const int64_t cb = static_cast<int64_t>(ks) * p.cpw;
+  const int64_t ce = std::min<int64_t>(p.chunks, cb + p.cpw);
+  const uint16_t* xh = static_cast<const uint16_t*>(p.x);
+  // wave w: columns 16 w .. 16 w + 15 of the workgroup
+  const int64_t n = static_cast<int64_t>(nb) * kValuCols + 16 * wave + c16;
+  const int64_t nl = std::min(n, p.d_out - 1);
+  const __amdgpu_buffer_rsrc_t rq = buffer_of(p.qweight, p.qbytes), rs = buffer_of(p.scales, p.gbytes),
+                               rz = buffer_of(p.zeros, p.gbytes);
+  const uint32_t rowb = static_cast<uint32_t>(p.d_out) * 4u, vo = static_cast<uint32_t>(nl) * 4u;
+  const LaneWords<BITS> lwo(g, p.d_out, nl);
+  f32x4_t y = {0.f, 0.f, 0.f, 0.f};  // tokens 4 g + e, column n
+  // the workgroup's K range in stages of up to 16 chunks
+  for (int64_t c0 = cb; c0 < ce; c0 += kStage) {
+    const int nc = static_cast<int>(std::min<int64_t>(kStage, ce - c0));  // >= 1
+    if (c0 != cb) __syncthreads();  // the previous stage's LDS reads are done
+    // the stage's code words, loaded at in-range chunk indices (chunks past
+    // nc repeat the last), in flight while x is staged
+    uint32_t wq[kStage][kLaneWords<BITS>];
+    float sc[kStage];
+    int32_t zc[kStage];
+#pragma unroll
+    for (int cl = 0; cl < kStage; ++cl) {
+      const int64_t c = c0 + std::min(cl, nc - 1);
+      lane_words<BITS>(rq, lwo, static_cast<uint32_t>(c * BITS) * rowb, g, wq[cl]);
+      // the chunk's first group's scale and zero point
+      const uint32_t so = static_cast<uint32_t>(gix[c * kChunk]) * rowb;
+      sc[cl] = __builtin_bit_cast(float, bload(rs, vo, so));
+      zc[cl] = static_cast<int32_t>(bload(rz, vo, so));
+    }
+    {
+      // 16 tokens x nc chunks of bf16 as 16-byte pieces, every load at an
+      // in-range address (rows past m repeat the last row, pieces past the
+      // range the last piece), selected after
+      constexpr int kRowPieces = kStage * kChunk / 8;
+      constexpr int kPieces = 16 * kRowPieces;
+      const int live = nc * kChunk / 8;
+      u32x4_t v[kPieces / 256];
+#pragma unroll
+      for (int i = 0; i < kPieces / 256; ++i) {
+        const int e = tid + 256 * i, t = e / kRowPieces, k8 = std::min(e % kRowPieces, live - 1);
+        const int64_t row = p.m0 + std::min<int64_t>(t, p.m - 1);
+        v[i] = *reinterpret_cast<const u32x4_t*>(xh + row * p.ldx + c0 * kChunk + 8 * k8);
+      }
+#pragma unroll
+      for (int i = 0; i < kPieces / 256; ++i) {
+        const int e = tid + 256 * i, t = e / kRowPieces, k8 = e % kRowPieces;
+        const u32x4_t z = {0u, 0u, 0u, 0u};
+        if (k8 < live) *reinterpret_cast<u32x4_t*>(&xb[k8 / 4][t][8 * (k8 % 4)]) = (t < p.m) ? v[i] : z;
+      }
+    }
+    stage_groups(p, c0, nc, gl, uni, tid);
+    __syncthreads();
+#pragma unroll
+    for (int cl = 0; cl < kStage; ++cl) {
+      if (cl >= nc) continue;
+      // A: x[token c16][8 g .. 8 g + 7]; B: codes 8 g .. 8 g + 7 of column n
+      const u32x4_t a = *reinterpret_cast<const u32x4_t*>(&xb[cl][c16][8 * g]);
+      float q[8];
+      lane_codes<BITS>(wq[cl], g, q);
+      // one group: B0 = the codes, B1 = -z, scaled by the column's s after,
+      // giving s (sum_k x_k q_k - z sum_k x_k); several groups: B0 + B1 =
+      // s (q - z) per code in bf16 high and low parts, scale 1
+      u32x4_t b0, b1;
+      float s;
+      if (uni[cl]) {
+        s = sc[cl];
+        const float z = static_cast<float>(zc[cl]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          b0[j] = pack_exact_bf16(q[2 * j], q[2 * j + 1]);
+          b1[j] = pack_exact_bf16(-z, -z);
+        }
+      } else {
+        s = 1.f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          uint32_t hw[2], lw[2];
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const uint32_t o = static_cast<uint32_t>(gl[cl][8 * g + 2 * j + h]) * rowb + vo;
+            const float sg = __builtin_bit_cast(float, bload(rs, o, 0u));
+            const float z = static_cast<float>(static_cast<int32_t>(bload(rz, o, 0u)));
+            const float v = sg * (q[2 * j + h] - z);
+            hw[h] = bf16_bits_of(v);
+            lw[h] = bf16_bits_of(v - bf16_value(hw[h]));
+          }
+          b0[j] = hw[0] | (hw[1] << 16);
+          b1[j] = lw[0] | (lw[1] << 16);
+        }
+      }
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+      acc = mfma32(a, b0, acc);
+      acc = mfma32(a, b1, acc);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) y[e] = fmaf(s, acc[e], y[e]);
+    }
+  }
+  if (n < p.d_out) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int t = 4 * g + e;
+      if (t >= p.m) continue;
+      if (p.ks == 1) p.y[(p.m0 + t) * p.d_out + n] = y[e];
+      else p.part[(static_cast<int64_t>(ks) * kMaxMT + t) * p.d_out + n] = y[e];
+    }
+  }
+}
+
+struct ValuPlan {
   int chunks, cpw, ks, nblocks;
 };
 
-DqPlan dq_plan(int64_t d_in, int64_t d_out) {
-  DqPlan pl{};
+ValuPlan valu_plan(int64_t d_in, int64_t d_out) {
+  ValuPlan pl{};
   pl.chunks = static_cast<int>(d_in / kChunk);
-  pl.nblocks = static_cast<int>((d_out + kCols - 1) / kCols);
+  pl.nblocks = static_cast<int>((d_out + kValuCols - 1) / kValuCols);
   // about 2048 workgroups, at least 4 chunks (one per wave) per workgroup
   int ks = std::max(1, (2048 + pl.nblocks - 1) / pl.nblocks);
   ks = std::min(ks, std::max(1, pl.chunks / 4));
-  pl.cpw = std::min(kMaxChunksPerWG, (pl.chunks + ks - 1) / ks);
+  pl.cpw = std::min(kStage, (pl.chunks + ks - 1) / ks);
   pl.ks = (pl.chunks + pl.cpw - 1) / pl.cpw;
   return pl;
 }
 
-constexpr int kMaxMT = 16;
-
 template <int BITS, int MT>
-hipError_t dq_pass(DqParams p, const DqPlan& pl, float* y, float* part, hipStream_t st) {
-  p.out = (pl.ks == 1) ? y : part;
-  dequant_matmul_kernel<BITS, MT><<<pl.nblocks * pl.ks, 256, 0, st>>>(p);
+hipError_t valu_pass(DqParams p, hipStream_t st) {
+  const ValuPlan pl = valu_plan(p.d_in, p.d_out);
+  p.cpw = pl.cpw;
+  p.ks = pl.ks;
+  dequant_valu_kernel<BITS, MT><<<pl.nblocks * pl.ks, 256, 0, st>>>(p, p.g_idx);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || pl.ks == 1) return e;
   const int64_t total = p.m * p.d_out;
-  dequant_reduce_kernel<MT><<<static_cast<unsigned>((total + 255) / 256), 256, 0, st>>>(part, pl.ks, p.m0, p.m,
-                                                                                      p.d_out, y, p.ld_out);
+  dequant_reduce_kernel<MT><<<static_cast<unsigned>((total + 255) / 256), 256, 0, st>>>(p.part, pl.ks, p.m0, p.m,
+                                                                                      p.d_out, p.y);
+  return hipGetLastError();
+}
+
+// MFMA path: a workgroup walks its K range in stages of 16 chunks.  Fewer K
+// slices than the VALU plan, so that the partial sums (written and read back,
+// 8 m d_out bytes per slice) stay a small part of the packed weights' bytes,
+// while keeping 512 workgroups or more; never more slices than the VALU plan,
+// whose partial buffer is the workspace.
+ValuPlan mfma_plan(int64_t d_in, int64_t d_out, int bits) {
+  ValuPlan pl = valu_plan(d_in, d_out);
+  const int64_t cap = std::max<int64_t>(d_in * bits / (512 * kMaxMT), (512 + pl.nblocks - 1) / pl.nblocks);
+  const int ks = static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(pl.ks, cap)));
+  pl.cpw = (pl.chunks + ks - 1) / ks;
+  pl.ks = (pl.chunks + pl.cpw - 1) / pl.cpw;
+  return pl;
+}
+
+template <int BITS>
+hipError_t mfma_pass(DqParams p, hipStream_t st) {
+  const ValuPlan pl = mfma_plan(p.d_in, p.d_out, BITS);
+  p.cpw = pl.cpw;
+  p.ks = pl.ks;
+  dequant_mfma_kernel<BITS><<<pl.nblocks * pl.ks, 256, 0, st>>>(p, p.g_idx);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || pl.ks == 1) return e;
+  const int64_t total = p.m * p.d_out;
+  dequant_reduce_kernel<kMaxMT><<<static_cast<unsigned>((total + 255) / 256), 256, 0, st>>>(p.part, pl.ks, p.m0,
+                                                                                          p.m, p.d_out, p.y);
   return hipGetLastError();
 }
 
 template <int BITS>
-hipError_t dq_bits(DqParams p, const DqPlan& pl, float* y, float* part, hipStream_t st) {
-  const int64_t mr = p.m;
-  if (mr <= 1) return dq_pass<BITS, 1>(p, pl, y, part, st);
-  if (mr <= 2) return dq_pass<BITS, 2>(p, pl, y, part, st);
-  if (mr <= 4) return dq_pass<BITS, 4>(p, pl, y, part, st);
-  if (mr <= 8) return dq_pass<BITS, 8>(p, pl, y, part, st);
-  return dq_pass<BITS, 16>(p, pl, y, part, st);
+hipError_t dq_bits(const DqParams& p, hipStream_t st) {
+  if (p.xbf16 && p.m >= 3) return mfma_pass<BITS>(p, st);
+  if (p.m <= 1) return valu_pass<BITS, 1>(p, st);
+  if (p.m <= 2) return valu_pass<BITS, 2>(p, st);
+  if (p.m <= 4) return valu_pass<BITS, 4>(p, st);
+  if (p.m <= 8) return valu_pass<BITS, 8>(p, st);
+  return valu_pass<BITS, 16>(p, st);
 }
 
 }  // namespace
 
 size_t dequant_workspace_bytes(int64_t m, int64_t d_in, int64_t d_out) {
   (void)m;
-  const DqPlan pl = dq_plan(d_in, d_out);
-  if (pl.ks == 1) return 256;
+  const ValuPlan pl = valu_plan(d_in, d_out);
+  if (pl.ks == 1) return 0;
   return (static_cast<size_t>(pl.ks) * kMaxMT * d_out * sizeof(float) + 255) & ~static_cast<size_t>(255);
 }
 
 hipError_t dequant_matmul_launch(const void* x, bool x_bf16, int64_t m, int64_t d_in, const int32_t* qweight,
                                  const float* scales, const int32_t* zeros, const int32_t* g_idx, int bits,
                                  int64_t d_out, int n_groups, float* y, void* ws, hipStream_t st) {
-  const DqPlan pl = dq_plan(d_in, d_out);
+  const int64_t qbytes = d_in / kChunk * bits * d_out * 4, gbytes = static_cast<int64_t>(n_groups) * d_out * 4;
+  if (qbytes >= (int64_t{1} << 31) || gbytes >= (int64_t{1} << 31)) return hipErrorInvalidValue;
   DqParams p{};
+  p.qbytes = static_cast<uint32_t>(qbytes);
+  p.gbytes = static_cast<uint32_t>(gbytes);
   p.x = x;
   p.xbf16 = x_bf16 ? 1 : 0;
   p.ldx = d_in;
@@ -234,21 +609,18 @@ hipError_t dequant_matmul_launch(const void* x, bool x_bf16, int64_t m, int64_t 
   p.scales = scales;
   p.zeros = zeros;
   p.g_idx = g_idx;
-  p.n_groups = n_groups;
-  p.chunks = pl.chunks;
-  p.cpw = pl.cpw;
-  p.ks = pl.ks;
-  p.ld_out = d_out;
-  float* part = static_cast<float*>(ws);
+  p.chunks = static_cast<int>(d_in / kChunk);
+  p.y = y;
+  p.part = static_cast<float*>(ws);
   for (int64_t m0 = 0; m0 < m; m0 += kMaxMT) {
     p.m0 = m0;
     p.m = std::min<int64_t>(kMaxMT, m - m0);
     hipError_t e;
     switch (bits) {
-      case 2: e = dq_bits<2>(p, pl, y, part, st); break;
-      case 3: e = dq_bits<3>(p, pl, y, part, st); break;
-      case 4: e = dq_bits<4>(p, pl, y, part, st); break;
-      case 8: e = dq_bits<8>(p, pl, y, part, st); break;
+      case 2: e = dq_bits<2>(p, st); break;
+      case 3: e = dq_bits<3>(p, st); break;
+      case 4: e = dq_bits<4>(p, st); break;
+      case 8: e = dq_bits<8>(p, st); break;
       default: return hipErrorInvalidValue;
     }
     if (e != hipSuccess) return e;

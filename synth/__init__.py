@@ -32,6 +32,7 @@ ROLE_SIGMA = 2
 ROLE_OUTLIER_CH = 3
 ROLE_W_OUTLIER = 4
 ROLE_MIX = 5
+ROLE_QPARAMS = 6
 
 
 def rng(seed: int, cfg: int, layer: int, role: int, chunk: int = 0) -> np.random.Generator:
@@ -332,3 +333,32 @@ def block_input(shape: BlockShape) -> np.ndarray:
     L = Layer("block_input", shape.d_model, shape.d_model, shape.n_tokens, "bf16", "bf16", False, True,
               cfg=shape.cfg, layer_id=100, seed=shape.seed)
     return activations(L)
+
+
+def quantized_layer(d_out: int, d_in: int, bits: int, group_size: int, act_order: bool, seed: int) -> dict:
+    """Seeded stand-ins for a quantized layer's stored tensors (the inputs of
+    the dequantizing product), drawn directly rather than by a solve:
+
+    * qweight [d_in * bits / 32, d_out] int32: uniformly random words; every
+      bit pattern is a packing of codes in [0, 2^bits)
+    * scales  [n_groups, d_out] float32: 0.008 exp(0.3 N(0, 1)) (the size of
+      a 4-bit step for weights of scale 0.02)
+    * zeros   [n_groups, d_out] int32: uniform in [0, 2^bits - 1]
+    * g_idx   [d_in] int32: k // G, or with act_order the group of the
+      position each column takes in a random permutation (groups formed in
+      permuted order), so that groups interleave across k
+
+    n_groups = ceil(d_in / G), with G = d_in when group_size is -1."""
+    g = d_in if group_size == -1 else group_size
+    n_groups = -(-d_in // g)
+    r = rng(seed, 0, d_out * 100003 + d_in, ROLE_QPARAMS)
+    qweight = r.integers(-2 ** 31, 2 ** 31, size=(d_in * bits // 32, d_out), dtype=np.int64).astype(np.int32)
+    scales = (0.008 * np.exp(0.3 * r.standard_normal((n_groups, d_out)))).astype(np.float32)
+    zeros = r.integers(0, 2 ** bits, size=(n_groups, d_out), dtype=np.int64).astype(np.int32)
+    if act_order:
+        pos = np.empty(d_in, dtype=np.int64)
+        pos[r.permutation(d_in)] = np.arange(d_in)
+        g_idx = (pos // g).astype(np.int32)
+    else:
+        g_idx = (np.arange(d_in) // g).astype(np.int32)
+    return {"qweight": qweight, "scales": scales, "zeros": zeros, "g_idx": g_idx}

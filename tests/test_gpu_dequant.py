@@ -1,11 +1,19 @@
 """The dequantizing product y = x W_hat^T against the oracle (fp64).
 
-W_hat is rebuilt from the solve's stored tensors (qweight, scales, zeros,
-g_idx).  The GPU sums in fp32; the bound used is the rigorous one for a sum of
-d_in terms, (d_in + 64) 2^-24 sum_k |x_k W_hat_nk|.  Cases cover every bit
+W_hat is rebuilt from a quantized layer's stored tensors (qweight, scales,
+zeros, g_idx): those of an oracle solve for the small cases, seeded stand-ins
+(synth.quantized_layer) for the long and full-size ones.  The GPU sums in
+fp32.  A chunk of 32 codes that lies in one group is
+summed as s (sum_k x_k q_k - z sum_k x_k): every term and partial sum is then
+bounded by |x_k| s (q_k + z) (codes and zero points are non-negative), so the
+rigorous bound for a sum of d_in such terms, (d_in + 64) 2^-24 sum_k |x_k| s
+(q_k + z), is used; it also holds for the paths that form s (q_k - z) per
+code, since q_k + z >= |q_k - z|.  Cases cover every bit
 width, ragged d_out, token counts across the 16-row passes, bf16 and fp32
 activations, groups that share a 32-code chunk (one scale per chunk) and
-act-order dynamic groups (a scale per code), and a full-size layer.
+act-order dynamic groups (a scale per code), K ranges of several 16-chunk
+stages with a short last one, and the full-size layer shapes of the 7B and 70B
+configurations (sampled output columns).
 """
 import numpy as np
 import pytest
@@ -32,21 +40,31 @@ def _params(bits, group, desc, static, d_out, d_in, seed):
     return res
 
 
-def _check(G, res, bits, x_host, x_dtype):
-    sw = res.sweep
-    qw = torch.from_numpy(res.qweight.astype(np.int32)).to(dev())
-    sc = torch.from_numpy(sw.scales.astype(np.float32)).to(dev())
-    zr = torch.from_numpy(sw.zeros.astype(np.int32)).to(dev())
-    gi = torch.from_numpy(sw.g_idx.astype(np.int32)).to(dev())
+def _check_tensors(G, qweight, scales, zeros, g_idx, bits, x_host, x_dtype, cols=None):
+    """GPU product against the oracle's; with `cols`, only those output
+    columns are compared (the oracle dequantizes just them)."""
     x = to_dev(x_host, x_dtype)
     xe = host(x).astype(np.float64)  # the exact values the GPU reads
-    y = G.gptq_dequant_matmul(x, qw, sc, zr, gi, bits)
-    ref = O.dequant_matmul(xe, res.qweight, sw.scales, sw.zeros, sw.g_idx, bits)
-    Wq = O.dequantize(res.qweight, sw.scales, sw.zeros, sw.g_idx, bits, xe.shape[1])
-    bound = (xe.shape[1] + 64) * 2.0 ** -24 * (np.abs(xe) @ np.abs(Wq).T)
-    err = np.abs(y.cpu().numpy().astype(np.float64) - ref)
+    y = G.gptq_dequant_matmul(x, torch.from_numpy(np.ascontiguousarray(qweight)).to(dev()),
+                              torch.from_numpy(np.ascontiguousarray(scales)).to(dev()),
+                              torch.from_numpy(np.ascontiguousarray(zeros)).to(dev()),
+                              torch.from_numpy(np.ascontiguousarray(g_idx)).to(dev()), bits)
+    y = y.cpu().numpy().astype(np.float64)
+    if cols is not None:
+        qweight, scales, zeros, y = qweight[:, cols], scales[:, cols], zeros[:, cols], y[:, cols]
+    ref = O.dequant_matmul(xe, qweight, scales, zeros, g_idx, bits)
+    # |s| (q + z): the dequantized weights with the zero points negated
+    Wb = O.dequantize(qweight, np.abs(scales), -zeros.astype(np.int64), g_idx, bits, xe.shape[1])
+    bound = (xe.shape[1] + 64) * 2.0 ** -24 * (np.abs(xe) @ Wb.T)
+    err = np.abs(y - ref)
     assert np.all(err <= bound + 1e-30), float(np.max(err / (bound + 1e-30)))
     return float(np.max(err / (bound + 1e-30)))
+
+
+def _check(G, res, bits, x_host, x_dtype):
+    sw = res.sweep
+    return _check_tensors(G, res.qweight.astype(np.int32), sw.scales.astype(np.float32), sw.zeros.astype(np.int32),
+                          sw.g_idx.astype(np.int32), bits, x_host, x_dtype)
 
 
 CASES = [  # bits, group, desc_act, static, d_out, d_in
@@ -68,22 +86,28 @@ def test_dequant_matmul_small(G, bits, group, desc, static, d_out, d_in, m, x_dt
     _check(G, res, bits, x, x_dtype)
 
 
-@pytest.mark.parametrize("m", [1, 16])
-def test_dequant_matmul_full_layer(G, m):
-    # parameters of a GPU solve of the configuration-3 q_proj shape (reduced N)
-    L = synth.scaled(synth.config_layers(3)[0], n_tokens=16384)
-    banner(f"dequant full layer {L.d_out}x{L.d_in} m={m}")
-    out = G.solve_layer(to_dev(synth.weight(L), L.w_dtype), [to_dev(synth.activations(L), L.x_dtype)],
-                        G.QuantizeConfig(**L.quant_kwargs()), want_q=False)
+# K ranges of several 16-chunk stages with a short last stage (515 chunks in
+# slices of 17 on the 16-token path), ragged columns and a ragged last group
+@pytest.mark.parametrize("bits,group,act", [(4, 128, False), (2, 64, False), (3, 128, False), (8, 128, False),
+                                            (4, 128, True)])
+@pytest.mark.parametrize("m", [16, 40])
+def test_dequant_matmul_long_k(G, bits, group, act, m):
+    d_out, d_in = 1000, 16480
+    banner(f"dequant long K b{bits} g{group} act={act} {d_out}x{d_in} m={m}")
+    t = synth.quantized_layer(d_out, d_in, bits, group, act, seed=bits)
+    x = synth.round_to_bf16(np.random.default_rng(m).standard_normal((m, d_in)).astype(np.float32))
+    _check_tensors(G, t["qweight"], t["scales"], t["zeros"], t["g_idx"], bits, x, "bf16")
 
-    class R:
-        pass
-    res = R()
-    res.qweight = out["qweight"].cpu().numpy()
-    res.sweep = R()
-    res.sweep.scales = out["scales"].cpu().numpy()
-    res.sweep.zeros = out["zeros"].cpu().numpy()
-    res.sweep.g_idx = out["g_idx"].cpu().numpy()
-    x = np.random.default_rng(100 + m).standard_normal((m, L.d_in)).astype(np.float32)
-    worst = _check(G, res, L.bits, x, "bf16")
+
+# the layer shapes of the 7B and 70B configurations at full size, 192 sampled
+# output columns (both ends and random ones) checked against the oracle
+@pytest.mark.parametrize("d_out,d_in", [(4096, 4096), (28672, 8192), (8192, 28672)])
+@pytest.mark.parametrize("m", [1, 16])
+def test_dequant_matmul_full_layer(G, d_out, d_in, m):
+    banner(f"dequant full layer {d_out}x{d_in} m={m}")
+    t = synth.quantized_layer(d_out, d_in, 4, 128, False, seed=3)
+    x = synth.round_to_bf16(np.random.default_rng(100 + m).standard_normal((m, d_in)).astype(np.float32))
+    r = np.random.default_rng(d_out)
+    cols = np.unique(np.concatenate([np.arange(64), np.arange(d_out - 64, d_out), r.integers(0, d_out, 64)]))
+    worst = _check_tensors(G, t["qweight"], t["scales"], t["zeros"], t["g_idx"], 4, x, "bf16", cols=cols)
     print(f"  worst error / bound {worst:.3e}", flush=True)
