@@ -168,14 +168,16 @@ gptq_status gptq_pack(const uint8_t* codes, int64_t d_out, int64_t d_in, int32_t
  * (deterministic).  32 consecutive k of one group are summed as
  * s (sum x q - z sum x), so the rounding error is bounded by
  * (d_in + 64) 2^-24 sum_k |x_k| s (q_k + z).  bf16 x with 3 or more tokens
- * runs on bf16 MFMA with the integer codes as the exact operand; 32 k spread
+ * runs on bf16 MFMA with the integer codes as the exact operand (at 4 bits
+ * as 16 + q against 16 + z, so there the bound has q_k + z + 32); 32 k spread
  * over several groups (act-order) use s (q - z) split into two bf16 parts
  * there, so those products carry a relative error of about 2^-16.
  *   x        [m, d_in] bf16 or fp32, row-major, m >= 1 (any count; passes of 16 rows)
  *   qweight  [d_in * bits / 32, d_out] int32 as written by gptq_pack
  *   scales   [n_groups, d_out] fp32, zeros [n_groups, d_out] int32, g_idx [d_in]
  *            int32 as written by gptq_quantize_layer; every g_idx entry must lie
- *            in [0, n_groups) (not checked on the device)
+ *            in [0, n_groups) and every zero point in [0, 2^bits) (not checked
+ *            on the device)
  *   y        [m, d_out] fp32 (overwritten)
  *   ws       device workspace of gptq_dequant_workspace_size(m, d_in, d_out)
  *            bytes, 256-byte aligned (partial sums of K slices); may be null

@@ -304,8 +304,18 @@ __global__ void dequant_reduce_kernel(const float* part, int ks, int64_t m0, int
   const int64_t e = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x;
   if (e >= m * d_out) return;
   const int64_t t = e / d_out, n = e - t * d_out;
+  const float* q = part + t * d_out + n;
+  const int64_t step = static_cast<int64_t>(MT) * d_out;
   float v = 0.f;
-  for (int s = 0; s < ks; ++s) v += part[(static_cast<int64_t>(s) * MT + t) * d_out + n];
+  int s = 0;
+  for (; s + 8 <= ks; s += 8) {
+    float l[8];  // eight slices' loads in flight, added in slice order
+#pragma unroll
+    for (int i = 0; i < 8; ++i) l[i] = q[(s + i) * step];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v += l[i];
+  }
+  for (; s < ks; ++s) v += q[s * step];
   y[(m0 + t) * d_out + n] = v;
 }
 
@@ -323,6 +333,7 @@ constexpr int kLaneWords = (BITS == 8 || BITS == 3) ? 2 : 1;
 template <int BITS>
 struct LaneWords {
   uint32_t off[kLaneWords<BITS>];
+  GPTQ_DEV LaneWords() {}
   GPTQ_DEV LaneWords(int g, int64_t d_out, int64_t n) {
     const uint32_t rowb = static_cast<uint32_t>(d_out) * 4u, nb = static_cast<uint32_t>(n) * 4u;
     if constexpr (BITS == 8) {
@@ -393,54 +404,89 @@ GPTQ_DEV uint32_t bf16_bits_of(float v) {
 
 GPTQ_DEV float bf16_value(uint32_t b) { return __builtin_bit_cast(float, b << 16); }
 
+// At 4 bits the operands of a lane group hold its 8 k in the order 0 4 1 5 2
+// 6 3 7 (dword j = k j and k j + 4): nibbles j and j + 4 of a code word are
+// 16 bits apart, so one shift and one mask-or turn them into a bf16 pair.
+// interleave_halves puts 8 bf16 of x into that order; operand_code gives the
+// k of half h of dword j.
+GPTQ_DEV u32x4_t interleave_halves(const u32x4_t& v) {
+  u32x4_t r;
+  r[0] = (v[0] & 0xffffu) | (v[2] << 16);
+  r[1] = (v[0] >> 16) | (v[2] & 0xffff0000u);
+  r[2] = (v[1] & 0xffffu) | (v[3] << 16);
+  r[3] = (v[1] >> 16) | (v[3] & 0xffff0000u);
+  return r;
+}
+
+template <int BITS>
+constexpr int operand_code(int j, int h) {
+  return BITS == 4 ? j + 4 * h : 2 * j + h;
+}
+
 GPTQ_DEV f32x4_t mfma32(const u32x4_t& a, const u32x4_t& b, const f32x4_t& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c,
                                                  0, 0, 0);
 }
 
-template <int BITS>
+// T column tiles of 16 per wave (64 T columns per workgroup: x staged once
+// serves them all) and SC chunks per LDS stage
+template <int BITS, int T, int SC>
 __global__ __launch_bounds__(256) void dequant_mfma_kernel(DqParams p, const int32_t* __restrict__ gix) {
-  __shared__ __attribute__((aligned(16))) uint16_t xb[kStage][16][kChunk + 8];  // bf16 x, [chunk][token][k]
-  __shared__ int32_t gl[kStage][kChunk];
-  __shared__ int uni[kStage];
+  __shared__ __attribute__((aligned(16))) uint16_t xb[SC][16][kChunk + 8];  // bf16 x, [chunk][token][k]
+  __shared__ int32_t gl[SC][kChunk];
+  __shared__ int uni[SC];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c16 = lane & 15, g = lane >> 4;
-  const int nblocks = static_cast<int>((p.d_out + kValuCols - 1) / kValuCols);
+  constexpr int kCols = 64 * T;
+  const int nblocks = static_cast<int>((p.d_out + kCols - 1) / kCols);
   const int nb = blockIdx.x % nblocks, ks = blockIdx.x / nblocks;
   const int64_t cb = static_cast<int64_t>(ks) * p.cpw;
   const int64_t ce = std::min<int64_t>(p.chunks, cb + p.cpw);
   const uint16_t* xh = static_cast<const uint16_t*>(p.x);
-  // wave w: columns 16 w .. 16 w + 15 of the workgroup
-  const int64_t n = static_cast<int64_t>(nb) * kValuCols + 16 * wave + c16;
-  const int64_t nl = std::min(n, p.d_out - 1);
   const __amdgpu_buffer_rsrc_t rq = buffer_of(p.qweight, p.qbytes), rs = buffer_of(p.scales, p.gbytes),
                                rz = buffer_of(p.zeros, p.gbytes);
-  const uint32_t rowb = static_cast<uint32_t>(p.d_out) * 4u, vo = static_cast<uint32_t>(nl) * 4u;
-  const LaneWords<BITS> lwo(g, p.d_out, nl);
-  f32x4_t y = {0.f, 0.f, 0.f, 0.f};  // tokens 4 g + e, column n
-  // the workgroup's K range in stages of up to 16 chunks
-  for (int64_t c0 = cb; c0 < ce; c0 += kStage) {
-    const int nc = static_cast<int>(std::min<int64_t>(kStage, ce - c0));  // >= 1
-    if (c0 != cb) __syncthreads();  // the previous stage's LDS reads are done
-    // the stage's code words, loaded at in-range chunk indices (chunks past
-    // nc repeat the last), in flight while x is staged
-    uint32_t wq[kStage][kLaneWords<BITS>];
-    float sc[kStage];
-    int32_t zc[kStage];
+  const uint32_t rowb = static_cast<uint32_t>(p.d_out) * 4u;
+  // wave w: columns 16 T w .. 16 T w + 16 T - 1 of the workgroup, tile t the
+  // 16 from 16 T w + 16 t
+  int64_t n[T];
+  uint32_t vo[T];
+  LaneWords<BITS> lwo[T];
 #pragma unroll
-    for (int cl = 0; cl < kStage; ++cl) {
+  for (int t = 0; t < T; ++t) {
+    n[t] = static_cast<int64_t>(nb) * kCols + 16 * T * wave + 16 * t + c16;
+    const int64_t nl = std::min(n[t], p.d_out - 1);
+    vo[t] = static_cast<uint32_t>(nl) * 4u;
+    lwo[t] = LaneWords<BITS>(g, p.d_out, nl);
+  }
+  f32x4_t y[T];  // tokens 4 g + e, column n[t]
+#pragma unroll
+  for (int t = 0; t < T; ++t) y[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  // the workgroup's K range in stages of up to SC chunks
+  for (int64_t c0 = cb; c0 < ce; c0 += SC) {
+    const int nc = static_cast<int>(std::min<int64_t>(SC, ce - c0));  // >= 1
+    if (c0 != cb) __syncthreads();  // the previous stage's LDS reads are done
+    // the stage's code words, scales and zero points (the chunk's first
+    // group's), loaded at in-range chunk indices (chunks past nc repeat the
+    // last), in flight while x is staged
+    uint32_t wq[SC][T][kLaneWords<BITS>];
+    float sc[SC][T];
+    int32_t zc[SC][T];
+#pragma unroll
+    for (int cl = 0; cl < SC; ++cl) {
       const int64_t c = c0 + std::min(cl, nc - 1);
-      lane_words<BITS>(rq, lwo, static_cast<uint32_t>(c * BITS) * rowb, g, wq[cl]);
-      // the chunk's first group's scale and zero point
       const uint32_t so = static_cast<uint32_t>(gix[c * kChunk]) * rowb;
-      sc[cl] = __builtin_bit_cast(float, bload(rs, vo, so));
-      zc[cl] = static_cast<int32_t>(bload(rz, vo, so));
+#pragma unroll
+      for (int t = 0; t < T; ++t) {
+        lane_words<BITS>(rq, lwo[t], static_cast<uint32_t>(c * BITS) * rowb, g, wq[cl][t]);
+        sc[cl][t] = __builtin_bit_cast(float, bload(rs, vo[t], so));
+        zc[cl][t] = static_cast<int32_t>(bload(rz, vo[t], so));
+      }
     }
     {
       // 16 tokens x nc chunks of bf16 as 16-byte pieces, every load at an
       // in-range address (rows past m repeat the last row, pieces past the
       // range the last piece), selected after
-      constexpr int kRowPieces = kStage * kChunk / 8;
+      constexpr int kRowPieces = SC * kChunk / 8;
       constexpr int kPieces = 16 * kRowPieces;
       const int live = nc * kChunk / 8;
       u32x4_t v[kPieces / 256];
@@ -454,63 +500,88 @@ __global__ __launch_bounds__(256) void dequant_mfma_kernel(DqParams p, const int
       for (int i = 0; i < kPieces / 256; ++i) {
         const int e = tid + 256 * i, t = e / kRowPieces, k8 = e % kRowPieces;
         const u32x4_t z = {0u, 0u, 0u, 0u};
-        if (k8 < live) *reinterpret_cast<u32x4_t*>(&xb[k8 / 4][t][8 * (k8 % 4)]) = (t < p.m) ? v[i] : z;
+        u32x4_t w = (t < p.m) ? v[i] : z;
+        if constexpr (BITS == 4) w = interleave_halves(w);
+        if (k8 < live) *reinterpret_cast<u32x4_t*>(&xb[k8 / 4][t][8 * (k8 % 4)]) = w;
       }
     }
     stage_groups(p, c0, nc, gl, uni, tid);
     __syncthreads();
 #pragma unroll
-    for (int cl = 0; cl < kStage; ++cl) {
+    for (int cl = 0; cl < SC; ++cl) {
       if (cl >= nc) continue;
-      // A: x[token c16][8 g .. 8 g + 7]; B: codes 8 g .. 8 g + 7 of column n
+      // A: x[token c16][8 g .. 8 g + 7], shared by the wave's tiles; B: codes
+      // 8 g .. 8 g + 7 of column n[t]
       const u32x4_t a = *reinterpret_cast<const u32x4_t*>(&xb[cl][c16][8 * g]);
-      float q[8];
-      lane_codes<BITS>(wq[cl], g, q);
-      // one group: B0 = the codes, B1 = -z, scaled by the column's s after,
-      // giving s (sum_k x_k q_k - z sum_k x_k); several groups: B0 + B1 =
-      // s (q - z) per code in bf16 high and low parts, scale 1
-      u32x4_t b0, b1;
-      float s;
-      if (uni[cl]) {
-        s = sc[cl];
-        const float z = static_cast<float>(zc[cl]);
+      const int one_group = uni[cl];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          b0[j] = pack_exact_bf16(q[2 * j], q[2 * j + 1]);
-          b1[j] = pack_exact_bf16(-z, -z);
-        }
-      } else {
-        s = 1.f;
+      for (int t = 0; t < T; ++t) {
+        // one group: B0 = the codes, B1 = -z, scaled by the column's s after,
+        // giving s (sum_k x_k q_k - z sum_k x_k); several groups: B0 + B1 =
+        // s (q - z) per code in bf16 high and low parts, scale 1.  At 4 bits
+        // both operands are in the order of interleave_halves and the
+        // one-group operands are built from the word directly: B0 = 16 + q,
+        // B1 = -(16 + z)
+        u32x4_t b0, b1;
+        float s;
+        if (BITS == 4 && one_group) {
+          s = sc[cl][t];
+          const uint32_t f = wq[cl][t][0];
+          b0[0] = ((f << 3) & 0x00780078u) | 0x41804180u;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          uint32_t hw[2], lw[2];
+          for (int j = 1; j < 4; ++j) b0[j] = ((f >> (4 * j - 3)) & 0x00780078u) | 0x41804180u;
+          const uint32_t hz = 0xc180u | (static_cast<uint32_t>(zc[cl][t]) << 3);
+          const uint32_t bz = hz | (hz << 16);
 #pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            const uint32_t o = static_cast<uint32_t>(gl[cl][8 * g + 2 * j + h]) * rowb + vo;
-            const float sg = __builtin_bit_cast(float, bload(rs, o, 0u));
-            const float z = static_cast<float>(static_cast<int32_t>(bload(rz, o, 0u)));
-            const float v = sg * (q[2 * j + h] - z);
-            hw[h] = bf16_bits_of(v);
-            lw[h] = bf16_bits_of(v - bf16_value(hw[h]));
+          for (int j = 0; j < 4; ++j) b1[j] = bz;
+        } else if (one_group) {
+          float q[8];
+          lane_codes<BITS>(wq[cl][t], g, q);
+          s = sc[cl][t];
+          const float z = static_cast<float>(zc[cl][t]);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            b0[j] = pack_exact_bf16(q[2 * j], q[2 * j + 1]);
+            b1[j] = pack_exact_bf16(-z, -z);
           }
-          b0[j] = hw[0] | (hw[1] << 16);
-          b1[j] = lw[0] | (lw[1] << 16);
-        }
-      }
-      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-      acc = mfma32(a, b0, acc);
-      acc = mfma32(a, b1, acc);
+        } else {
+          float q[8];
+          lane_codes<BITS>(wq[cl][t], g, q);
+          s = 1.f;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) y[e] = fmaf(s, acc[e], y[e]);
+          for (int j = 0; j < 4; ++j) {
+            uint32_t hw[2], lw[2];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+              const int i = operand_code<BITS>(j, h);  // the code in half h of dword j
+              const uint32_t o = static_cast<uint32_t>(gl[cl][8 * g + i]) * rowb + vo[t];
+              const float sg = __builtin_bit_cast(float, bload(rs, o, 0u));
+              const float z = static_cast<float>(static_cast<int32_t>(bload(rz, o, 0u)));
+              const float v = sg * (q[i] - z);
+              hw[h] = bf16_bits_of(v);
+              lw[h] = bf16_bits_of(v - bf16_value(hw[h]));
+            }
+            b0[j] = hw[0] | (hw[1] << 16);
+            b1[j] = lw[0] | (lw[1] << 16);
+          }
+        }
+        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+        acc = mfma32(a, b0, acc);
+        acc = mfma32(a, b1, acc);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) y[t][e] = fmaf(s, acc[e], y[t][e]);
+      }
     }
   }
-  if (n < p.d_out) {
+#pragma unroll
+  for (int t = 0; t < T; ++t) {
+    if (n[t] >= p.d_out) continue;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int t = 4 * g + e;
-      if (t >= p.m) continue;
-      if (p.ks == 1) p.y[(p.m0 + t) * p.d_out + n] = y[e];
-      else p.part[(static_cast<int64_t>(ks) * kMaxMT + t) * p.d_out + n] = y[e];
+      const int tok = 4 * g + e;
+      if (tok >= p.m) continue;
+      if (p.ks == 1) p.y[(p.m0 + tok) * p.d_out + n[t]] = y[t][e];
+      else p.part[(static_cast<int64_t>(ks) * kMaxMT + tok) * p.d_out + n[t]] = y[t][e];
     }
   }
 }
@@ -523,8 +594,8 @@ ValuPlan valu_plan(int64_t d_in, int64_t d_out) {
   ValuPlan pl{};
   pl.chunks = static_cast<int>(d_in / kChunk);
   pl.nblocks = static_cast<int>((d_out + kValuCols - 1) / kValuCols);
-  // about 2048 workgroups, at least 4 chunks (one per wave) per workgroup
-  int ks = std::max(1, (2048 + pl.nblocks - 1) / pl.nblocks);
+  // about 1024 workgroups, at least 4 chunks (one per wave) per workgroup
+  int ks = std::max(1, (1024 + pl.nblocks - 1) / pl.nblocks);
   ks = std::min(ks, std::max(1, pl.chunks / 4));
   pl.cpw = std::min(kStage, (pl.chunks + ks - 1) / ks);
   pl.ks = (pl.chunks + pl.cpw - 1) / pl.cpw;
@@ -545,15 +616,21 @@ hipError_t valu_pass(DqParams p, hipStream_t st) {
   return hipGetLastError();
 }
 
-// MFMA path: a workgroup walks its K range in stages of 16 chunks.  Fewer K
-// slices than the VALU plan, so that the partial sums (written and read back,
-// 8 m d_out bytes per slice) stay a small part of the packed weights' bytes,
-// while keeping 512 workgroups or more; never more slices than the VALU plan,
-// whose partial buffer is the workspace.
+// MFMA path: 64 T columns per workgroup (one tile per wave measured best: more
+// tiles raise the register count and lower occupancy), its K range in stages
+// of SC chunks.  Fewer K slices than the VALU plan, so that the partial sums
+// (written and read back, 8 m d_out bytes per slice) stay a small part of the
+// packed weights' bytes, while keeping 512 workgroups or more; never more
+// slices than the VALU plan, whose partial buffer is the workspace.
+constexpr int kMfmaTiles = 1;
+constexpr int kMfmaStage = 16;
+
 ValuPlan mfma_plan(int64_t d_in, int64_t d_out, int bits) {
-  ValuPlan pl = valu_plan(d_in, d_out);
+  const ValuPlan vp = valu_plan(d_in, d_out);
+  ValuPlan pl = vp;
+  pl.nblocks = static_cast<int>((d_out + 64 * kMfmaTiles - 1) / (64 * kMfmaTiles));
   const int64_t cap = std::max<int64_t>(d_in * bits / (512 * kMaxMT), (512 + pl.nblocks - 1) / pl.nblocks);
-  const int ks = static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(pl.ks, cap)));
+  const int ks = static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(vp.ks, cap)));
   pl.cpw = (pl.chunks + ks - 1) / ks;
   pl.ks = (pl.chunks + pl.cpw - 1) / pl.cpw;
   return pl;
@@ -564,7 +641,7 @@ hipError_t mfma_pass(DqParams p, hipStream_t st) {
   const ValuPlan pl = mfma_plan(p.d_in, p.d_out, BITS);
   p.cpw = pl.cpw;
   p.ks = pl.ks;
-  dequant_mfma_kernel<BITS><<<pl.nblocks * pl.ks, 256, 0, st>>>(p, p.g_idx);
+  dequant_mfma_kernel<BITS, kMfmaTiles, kMfmaStage><<<pl.nblocks * pl.ks, 256, 0, st>>>(p, p.g_idx);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || pl.ks == 1) return e;
   const int64_t total = p.m * p.d_out;

@@ -4,11 +4,12 @@ W_hat is rebuilt from a quantized layer's stored tensors (qweight, scales,
 zeros, g_idx): those of an oracle solve for the small cases, seeded stand-ins
 (synth.quantized_layer) for the long and full-size ones.  The GPU sums in
 fp32.  A chunk of 32 codes that lies in one group is
-summed as s (sum_k x_k q_k - z sum_k x_k): every term and partial sum is then
-bounded by |x_k| s (q_k + z) (codes and zero points are non-negative), so the
-rigorous bound for a sum of d_in such terms, (d_in + 64) 2^-24 sum_k |x_k| s
-(q_k + z), is used; it also holds for the paths that form s (q_k - z) per
-code, since q_k + z >= |q_k - z|.  Cases cover every bit
+summed as s (sum_k x_k q_k - z sum_k x_k), at 4 bits on the MFMA path as
+s (sum_k x_k (16 + q_k) - (16 + z) sum_k x_k): every term and partial sum is
+then bounded by |x_k| s (q_k + z + c), c = 32 at 4 bits and 0 otherwise (codes
+and zero points are non-negative), so the rigorous bound for a sum of d_in
+such terms, (d_in + 64) 2^-24 sum_k |x_k| s (q_k + z + c), is used; it also
+holds for the paths that form s (q_k - z) per code, since q_k + z >= |q_k - z|.  Cases cover every bit
 width, ragged d_out, token counts across the 16-row passes, bf16 and fp32
 activations, groups that share a 32-code chunk (one scale per chunk) and
 act-order dynamic groups (a scale per code), K ranges of several 16-chunk
@@ -53,8 +54,9 @@ def _check_tensors(G, qweight, scales, zeros, g_idx, bits, x_host, x_dtype, cols
     if cols is not None:
         qweight, scales, zeros, y = qweight[:, cols], scales[:, cols], zeros[:, cols], y[:, cols]
     ref = O.dequant_matmul(xe, qweight, scales, zeros, g_idx, bits)
-    # |s| (q + z): the dequantized weights with the zero points negated
-    Wb = O.dequantize(qweight, np.abs(scales), -zeros.astype(np.int64), g_idx, bits, xe.shape[1])
+    # |s| (q + z + c): the dequantized weights with the zero points negated and offset
+    c = 32 if bits == 4 else 0
+    Wb = O.dequantize(qweight, np.abs(scales), -(zeros.astype(np.int64) + c), g_idx, bits, xe.shape[1])
     bound = (xe.shape[1] + 64) * 2.0 ** -24 * (np.abs(xe) @ Wb.T)
     err = np.abs(y - ref)
     assert np.all(err <= bound + 1e-30), float(np.max(err / (bound + 1e-30)))
