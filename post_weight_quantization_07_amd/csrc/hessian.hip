@@ -205,7 +205,10 @@ GPTQ_DEV void pipe_mfma(const bf16x8_t (&a)[4], const bf16x8_t (&b)[4], f32x16_t
       acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
 }
 
-// MFMAs of the current stage with the reads of the next one interleaved 1:1
+// MFMAs of the current stage with the reads of the next one interleaved 1:1,
+// and the stage's four DMA loads (issued just before) spread one per four
+// MFMAs: issued back to back they held the wave at the address unit instead
+// of letting it issue MFMAs (measured 5% faster on the whole call)
 GPTQ_DEV void pipe_step(const bf16x8_t (&a)[4], const bf16x8_t (&b)[4], const uint8_t* nA, const uint8_t* nB,
                         const PipeLane& la, const PipeLane& lb, bf16x8_t (&na)[4], bf16x8_t (&nb)[4],
                         f32x16_t (&acc)[4][4]) {
@@ -213,8 +216,9 @@ GPTQ_DEV void pipe_step(const bf16x8_t (&a)[4], const bf16x8_t (&b)[4], const ui
   pipe_mfma(a, b, acc);
 #pragma unroll
   for (int k = 0; k < 16; ++k) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                    // one MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                    // one LDS read
+    if ((k & 3) == 0) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // one DMA load
   }
 }
 
