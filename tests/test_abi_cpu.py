@@ -124,6 +124,11 @@ def test_dequant_matmul_rejects_bad_arguments(lib):
     assert lib.gptq_dequant_matmul(fake, 0, 0, 64, fake, fake, fake, fake, 4, 64, 1, fake, ws, 1 << 20, None) == 1
     assert lib.gptq_dequant_matmul(fake, 2, 4, 64, fake, fake, fake, fake, 4, 64, 1, fake, ws, 1 << 20, None) == 1
     assert lib.gptq_dequant_matmul(fake, 0, 4, 64, fake, fake, fake, fake, 4, 64, 0, fake, ws, 1 << 20, None) == 1
+    # qweight or scales of 2^31 bytes or more (32-bit buffer offsets): INVALID_ARG, checked on the host
+    assert lib.gptq_dequant_matmul(fake, 0, 1, 65536, fake, fake, fake, fake, 4, 65536, 512, fake, ws, 1 << 40,
+                                   None) == 1
+    assert lib.gptq_dequant_matmul(fake, 0, 1, 4096, fake, fake, fake, fake, 4, 1 << 20, 512, fake, ws, 1 << 40,
+                                   None) == 1
     # a workspace that is too small or misaligned: WORKSPACE
     need = lib.gptq_dequant_workspace_size(4, 4096, 4096)
     assert need > 256
