@@ -502,6 +502,30 @@ def test_shared_groups_share_x_not_w():
     assert not np.array_equal(synth.weight(q), synth.weight(k))
 
 
+def test_quantized_layer_stand_ins():
+    # the seeded stand-in tensors of the dequantizing product's long and
+    # full-size cases: shapes and dtypes of the stored layer, positive scales,
+    # zero points in [0, 2^b), g_idx either k // G or every group exactly G
+    # columns (act-order), deterministic in the seed
+    for bits, G, act, d_in in [(4, 128, False, 1024), (3, 32, True, 512), (2, 64, True, 320), (8, -1, False, 256)]:
+        t = synth.quantized_layer(96, d_in, bits, G, act, seed=5)
+        ng = 1 if G == -1 else -(-d_in // G)
+        assert t["qweight"].shape == (d_in * bits // 32, 96) and t["qweight"].dtype == np.int32
+        assert t["scales"].shape == (ng, 96) and t["scales"].dtype == np.float32 and (t["scales"] > 0).all()
+        assert t["zeros"].shape == (ng, 96) and t["zeros"].min() >= 0 and t["zeros"].max() < 2 ** bits
+        gi = t["g_idx"]
+        assert gi.shape == (d_in,) and gi.dtype == np.int32
+        if act:
+            assert not np.array_equal(gi, np.arange(d_in) // G)
+            counts = np.bincount(gi, minlength=ng)
+            assert (counts[:-1] == G).all() and counts[-1] == d_in - G * (ng - 1)
+        else:
+            np.testing.assert_array_equal(gi, np.arange(d_in) // (d_in if G == -1 else G))
+        t2 = synth.quantized_layer(96, d_in, bits, G, act, seed=5)
+        for k in t:
+            np.testing.assert_array_equal(t[k], t2[k])
+
+
 # --------------------------------------------------- dequantizing product ---
 
 @pytest.mark.parametrize("bits,G,desc,static", [(4, 8, False, False), (3, 8, True, False), (2, 16, True, True),
