@@ -119,6 +119,7 @@ __global__ void gather_kernel(const float* H, int64_t n, const int32_t* perm, co
 constexpr int kLP = kNB + 4;    // LDS row pitch (floats)
 constexpr int kChunk = 32;      // panel rows solved per pass
 constexpr int kMaxPanelWG = 256;
+constexpr int kPanelGroup = 4;  // panels per trailing update of the Cholesky
 using Blk = float (*)[kLP];
 constexpr int kTP = 68;        // row pitch of the 64x64 product buffer
 using TBlk = float (*)[kTP];
@@ -732,16 +733,35 @@ hipError_t prepare_launch(float* S, int64_t n, int64_t n_total, float damp, bool
   GPTQ_TRY(hipGetLastError());
 
   // blocked right-looking Cholesky of Hr; the panel kernels leave the inverse
-  // of every diagonal block in place
-  for (int64_t k = 0; k < n; k += kNB) {
-    const int64_t below = std::max<int64_t>(0, n - k - kNB);
-    const int blocks = 1 + static_cast<int>(std::min<int64_t>((below + kChunk - 1) / kChunk, kMaxPanelWG - 1));
-    panel_kernel<<<blocks, 256, 0, st>>>(Hr, n, k, info);
-    GPTQ_TRY(hipGetLastError());
+  // of every diagonal block in place.  Panels go in groups of kPanelGroup:
+  // each later panel's block column is first brought up to date with the
+  // group's earlier panels (a tall product, K = 128 per earlier panel), and
+  // the trailing matrix past the group takes one update with all of the
+  // group's columns (K = 128 kPanelGroup; the group's L21 blocks are adjacent
+  // columns of Hr).  The same products as one update per panel, summed in
+  // another order; the large lower-triangle update reads and writes the
+  // trailing matrix once per group instead of once per panel.
+  for (int64_t k = 0; k < n; k += kNB * kPanelGroup) {
+    for (int h = 0; h < kPanelGroup; ++h) {
+      const int64_t kh = k + h * kNB;
+      if (kh >= n) break;
+      if (h > 0) {
+        const int64_t wc = std::min<int64_t>(kNB, n - kh);
+        const float* A = Hr + kh * n + k;  // rows kh .., the earlier panels' columns
+        GPTQ_TRY(gemm_f32(n - kh, wc, kh - k, -1.f, A, n, 0, A, n, 0, true, 1.f, Hr + kh * (n + 1), n, 0, 1,
+                          false, 0, st));
+      }
+      const int64_t below = std::max<int64_t>(0, n - kh - kNB);
+      const int blocks = 1 + static_cast<int>(std::min<int64_t>((below + kChunk - 1) / kChunk, kMaxPanelWG - 1));
+      panel_kernel<<<blocks, 256, 0, st>>>(Hr, n, kh, info);
+      GPTQ_TRY(hipGetLastError());
+    }
+    const int64_t ke = std::min<int64_t>(n, k + kNB * kPanelGroup);
+    const int64_t below = n - ke;
     if (below > 0) {
-      const float* P = Hr + (k + kNB) * n + k;
-      GPTQ_TRY(gemm_f32(below, below, kNB, -1.f, P, n, 0, P, n, 0, true, 1.f, Hr + (k + kNB) * (n + 1), n,
-                        0, 1, true, 0, st));
+      const float* P = Hr + ke * n + k;
+      GPTQ_TRY(gemm_f32(below, below, ke - k, -1.f, P, n, 0, P, n, 0, true, 1.f, Hr + ke * (n + 1), n, 0, 1, true,
+                        0, st));
     }
   }
   // triangular inverse by recursive doubling over the inverted diagonal blocks
