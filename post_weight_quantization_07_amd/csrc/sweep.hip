@@ -27,6 +27,7 @@ namespace {
 
 constexpr int kB = 128;         // lazy-batch width
 constexpr int kRowsPerWG = 16;  // 256 threads / 16 lanes
+constexpr int kUnitsPerGroup = 4;  // pairs of blocks per trailing update
 
 struct SweepParams {
   float* Wp;            // [d_out, d_in] fp32 working copy, sweep order
@@ -449,7 +450,7 @@ QuantLayout quant_layout(int64_t d_out, int64_t d_in) {
   QuantLayout L{};
   L.off_wp = 0;
   L.off_err = up(static_cast<size_t>(d_out) * d_in * sizeof(float));
-  L.ws_bytes = L.off_err + up(static_cast<size_t>(d_out) * 2 * kB * sizeof(float));
+  L.ws_bytes = L.off_err + up(static_cast<size_t>(d_out) * 2 * kB * kUnitsPerGroup * sizeof(float));
   return L;
 }
 
@@ -496,45 +497,65 @@ hipError_t quantize_launch(const void* W, bool w_bf16, int64_t d_out, int64_t d_
   p.preset = preset ? 1 : 0;
   p.identity = identity ? 1 : 0;
   const int blocks = static_cast<int>((d_out + kRowsPerWG - 1) / kRowsPerWG);
-  // The trailing update runs once per pair of 128-column blocks (K = 256): the
-  // second block of a pair is first brought up to date with the first block's
-  // errors (a 128-deep product at the start of its sweep kernel).  The result is the lazy-batch sweep's (the same products, summed
-  // in another order).  A dynamic group wider than a block reads columns past
-  // the block at its start, so pairs are used only when such groups start on
-  // pair boundaries.
+  // Blocks are swept in units of two (pairs): the second block of a pair is
+  // first brought up to date with the first block's errors (a 128-deep
+  // product at the start of its sweep kernel).  Two pairs form a group: the
+  // second pair's columns are first brought up to date with the first pair's
+  // errors (one d_out x 256 product, K = 256), and the trailing update of the
+  // columns past the group runs once per group (K = 512), so it reads and
+  // writes the rest of W once per 512 columns.  The result is the lazy-batch
+  // sweep's (the same products, summed in another order).  A dynamic group
+  // wider than a block reads columns past the block at its start, so units and
+  // groups are used only when such groups start on their boundaries: pairs for
+  // groups of 256 columns or a multiple, groups of pairs for groups up to 256
+  // or a multiple of 512.
   const bool pair = preset || group <= kB || group % (2 * kB) == 0;
   const int SB = pair ? 2 * kB : kB;
+  const bool grouped = pair && (preset || group <= 2 * kB || group % (2 * kB * kUnitsPerGroup) == 0);
+  const int NU = grouped ? kUnitsPerGroup : 1;  // units per trailing update
+  const int64_t GW = static_cast<int64_t>(NU) * SB;
   const int gs = (!preset && group <= kB) ? group : 0;
-  p.ld_err = SB;
-  for (int64_t j0 = 0; j0 < d_in; j0 += SB) {
-    for (int h = 0; h < SB / kB; ++h) {
-      const int64_t jb = j0 + static_cast<int64_t>(h) * kB;
-      if (jb >= d_in) break;
-      const int ncols = static_cast<int>(std::min<int64_t>(kB, d_in - jb));
-      // the second block of a pair is brought up to date inside its sweep
-      p.Eb = (h > 0) ? Err : nullptr;
-      p.Uo = (h > 0) ? U + j0 * d_in + jb : nullptr;
-      p.j0 = jb;
-      p.ncols = ncols;
-      p.Err = Err + h * kB;
-      switch (gs) {
-        case 0: sweep_kernel<0><<<blocks, 256, 0, st>>>(p); break;
-        case 1: sweep_kernel<1><<<blocks, 256, 0, st>>>(p); break;
-        case 2: sweep_kernel<2><<<blocks, 256, 0, st>>>(p); break;
-        case 4: sweep_kernel<4><<<blocks, 256, 0, st>>>(p); break;
-        case 8: sweep_kernel<8><<<blocks, 256, 0, st>>>(p); break;
-        case 16: sweep_kernel<16><<<blocks, 256, 0, st>>>(p); break;
-        case 32: sweep_kernel<32><<<blocks, 256, 0, st>>>(p); break;
-        case 64: sweep_kernel<64><<<blocks, 256, 0, st>>>(p); break;
-        case 128: sweep_kernel<128><<<blocks, 256, 0, st>>>(p); break;
-        default: return hipErrorInvalidValue;  // the ABI admits only groups dividing 128 here
+  p.ld_err = static_cast<int>(GW);
+  for (int64_t g0 = 0; g0 < d_in; g0 += GW) {
+    for (int u = 0; u < NU; ++u) {
+      const int64_t j0 = g0 + static_cast<int64_t>(u) * SB;
+      if (j0 >= d_in) break;
+      if (u > 0) {
+        // the unit's columns take the group's earlier units' errors
+        const int64_t w = std::min<int64_t>(SB, d_in - j0);
+        e = gemm_f32(d_out, w, j0 - g0, -1.f, Err, GW, 0, U + g0 * d_in + j0, d_in, 0, false, 1.f, Wp + j0, d_in, 0, 1,
+                     false, 0, st);
+        if (e != hipSuccess) return e;
       }
-      if ((e = hipGetLastError()) != hipSuccess) return e;
+      for (int h = 0; h < SB / kB; ++h) {
+        const int64_t jb = j0 + static_cast<int64_t>(h) * kB;
+        if (jb >= d_in) break;
+        const int ncols = static_cast<int>(std::min<int64_t>(kB, d_in - jb));
+        // the second block of a pair is brought up to date inside its sweep
+        p.Eb = (h > 0) ? Err + u * SB : nullptr;
+        p.Uo = (h > 0) ? U + j0 * d_in + jb : nullptr;
+        p.j0 = jb;
+        p.ncols = ncols;
+        p.Err = Err + u * SB + h * kB;
+        switch (gs) {
+          case 0: sweep_kernel<0><<<blocks, 256, 0, st>>>(p); break;
+          case 1: sweep_kernel<1><<<blocks, 256, 0, st>>>(p); break;
+          case 2: sweep_kernel<2><<<blocks, 256, 0, st>>>(p); break;
+          case 4: sweep_kernel<4><<<blocks, 256, 0, st>>>(p); break;
+          case 8: sweep_kernel<8><<<blocks, 256, 0, st>>>(p); break;
+          case 16: sweep_kernel<16><<<blocks, 256, 0, st>>>(p); break;
+          case 32: sweep_kernel<32><<<blocks, 256, 0, st>>>(p); break;
+          case 64: sweep_kernel<64><<<blocks, 256, 0, st>>>(p); break;
+          case 128: sweep_kernel<128><<<blocks, 256, 0, st>>>(p); break;
+          default: return hipErrorInvalidValue;  // the ABI admits only groups dividing 128 here
+        }
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+      }
     }
-    const int64_t rest = d_in - j0 - SB;
+    const int64_t rest = d_in - g0 - GW;
     if (rest > 0) {
-      e = gemm_f32(d_out, rest, SB, -1.f, Err, SB, 0, U + j0 * d_in + j0 + SB, d_in, 0, false, 1.f, Wp + j0 + SB, d_in,
-                   0, 1, false, 0, st);
+      e = gemm_f32(d_out, rest, GW, -1.f, Err, GW, 0, U + g0 * d_in + g0 + GW, d_in, 0, false, 1.f, Wp + g0 + GW,
+                   d_in, 0, 1, false, 0, st);
       if (e != hipSuccess) return e;
     }
   }
