@@ -168,6 +168,9 @@ SWEEP_CASES = [  # d_out, d_in, bits, G, sym, desc_act, static, w dtype
     (33, 768, 4, 384, True, False, False, "f32"),     # wide groups starting inside a block pair
     (24, 192, 4, 8, False, False, False, "f32"),      # group narrower than a lane's 8 columns
     (1, 128, 4, 128, True, False, False, "f32"),
+    (20, 1400, 4, 128, False, False, False, "f32"),   # two groups of block pairs, the last block ragged
+    (16, 2304, 4, 256, True, True, False, "bf16"),    # dynamic act-order groups of 256 over three pair groups
+    (16, 1536, 4, 512, True, False, False, "f32"),    # groups of 512: one trailing update per pair
 ]
 
 
