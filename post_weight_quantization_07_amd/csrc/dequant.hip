@@ -21,11 +21,13 @@
 // 8, half a word at 2, a 24-bit funnel-shifted field at 3.  For a one-group
 // chunk the B operand is the codes themselves (integers <= 255, exact in
 // bf16), a second MFMA adds x times -z, and the column's scale multiplies the
-// chunk's sum in fp32, so the products are exact and the rounding is that of
-// the same sum as in the VALU path.  A chunk spread over several groups uses
-// B = s (q - z) split into bf16 high and low parts (two MFMAs).  A workgroup
-// owns 64 output columns (16 per wave) over a K range; K is split over
-// workgroups as in the VALU path.
+// chunk's sum in fp32, so the products are exact.  At 4 bits the operands
+// are 16 + q and -(16 + z), built from the packed word with integer
+// operations only (interleave_halves), which widens the rounding bound by 32
+// per term.  A chunk spread over several groups uses B = s (q - z) split into
+// bf16 high and low parts (two MFMAs).  A workgroup owns 64 output columns
+// (16 per wave) and walks its K range in stages of 16 chunks; K is split
+// over workgroups, with fewer slices than the VALU path.
 //
 // VALU path (fp32 x, or 1-2 tokens): lanes map to output columns (64 per
 // workgroup, so a packed word load is 64 consecutive int32 of one qweight
@@ -35,9 +37,9 @@
 // subtraction of z out of the per-code work (two operations per code at 2, 4
 // and 8 bits: a byte-to-float conversion and an FMA); its rounding error is
 // bounded by the sum of |x_k| s (q_k + z) instead of |x_k| s |q_k - z|.  The
-// four waves take interleaved chunks of the
-// workgroup's K range and are summed through LDS in wave order; K is split
-// over workgroups whose partial products a second kernel adds in slice order.
+// four waves take interleaved chunks of the workgroup's K range and are
+// summed through LDS in wave order; K is split over workgroups whose partial
+// products a second kernel adds in slice order.
 #include "gptq_common.h"
 #include "gptq_internal.h"
 
@@ -69,7 +71,7 @@ struct DqParams {
   int cpw;                 // chunks per workgroup
   int ks;                  // K slices
   float* y;                // [m_total, d_out]
-  float* part;             // VALU path, ks > 1: partial sums [ks][MT][d_out]
+  float* part;             // ks > 1: partial sums [ks][MT][d_out] (MT = 16 on the MFMA path)
 };
 
 // qweight, scales and zeros are read through buffer descriptors: a lane's
