@@ -274,7 +274,47 @@ __global__ __launch_bounds__(kThreads, 1) void hessian_bf16_pipe_kernel(HessPara
     pipe_dma(rs, slotB(slot), ldx, colB, p.d_in, wave, lane);
   };
   bf16x8_t a0[4], b0[4], a1[4], b1[4];
-  if (nblk >= 2) {
+  // on a diagonal tile the lower-left quadrant is the mirror of the upper-right
+  // one: its wave only moves its share of the operands (the reduction mirrors)
+  const bool idle = (I == J) && wm == 1 && wn == 0;
+  if (idle && nblk >= 2) {
+    for (int x = 0; x < 7; ++x) issue(x, x);
+    __builtin_amdgcn_s_waitcnt(GPTQ_VMCNT(24));
+    __builtin_amdgcn_s_barrier();
+    for (int blk = 0; blk + 1 < nblk; ++blk) {
+      const int s = blk * kPSlots;
+#pragma unroll
+      for (int u = 0; u < 8; u += 2) {
+        __builtin_amdgcn_s_waitcnt(GPTQ_VMCNT(20));
+        __builtin_amdgcn_s_barrier();
+        issue(s + u + 7, u + 7);
+        __builtin_amdgcn_s_waitcnt(GPTQ_VMCNT(20));
+        __builtin_amdgcn_s_barrier();
+        issue(s + u + 8, u + 8);
+      }
+    }
+    const int L = (nblk - 1) * kPSlots;
+    __builtin_amdgcn_s_waitcnt(GPTQ_VMCNT(20));
+    __builtin_amdgcn_s_barrier();
+    issue(L + 7, 7);
+    __builtin_amdgcn_s_waitcnt(GPTQ_VMCNT(20));
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_s_waitcnt(GPTQ_VMCNT(16));
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_s_waitcnt(GPTQ_VMCNT(12));
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_s_waitcnt(GPTQ_VMCNT(8));
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_s_waitcnt(GPTQ_VMCNT(4));
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_s_waitcnt(GPTQ_VMCNT(0));
+    __builtin_amdgcn_s_barrier();
+  } else if (idle) {
+#pragma unroll
+    for (int x = 0; x < 8; ++x) issue(x, x);
+    __builtin_amdgcn_s_waitcnt(GPTQ_VMCNT(0));
+    __builtin_amdgcn_s_barrier();
+  } else if (nblk >= 2) {
     // Stage s lives in slot s % 8 and its operands in register set s % 2.
     // Before stage s: wait for the DMA of stage s + 1 (stages s + 2 .. s + 6
     // stay in flight: 4 loads each per wave), barrier, refill the slot of
@@ -443,7 +483,9 @@ __global__ __launch_bounds__(kThreads, 2) void hessian_f32_kernel(HessParams p) 
 // NE fragments x 64 lanes x 4 rows.  Sums the n_split partials of the block
 // in slice order, stages the sum in LDS and adds it to S row by row, then to
 // the mirror block (tile (J, I)) column by column, so both updates are
-// coalesced.  Every element of S is updated by exactly one thread.
+// coalesced.  On a diagonal tile of the bf16 kernel the lower-left quadrant
+// was not computed (its wave idles): the upper-right quadrant's blocks write
+// it as their mirror.  Every element of S is updated by exactly one thread.
 //   bf16 (TILE 256, BS 32, NE 4): fragment e, lane l -> rows 8 e + 4 (l / 32) + r, col l % 32
 //   fp32 (TILE 128, BS 16, NE 1): lane l -> rows 4 (l / 16) + r, col l % 16
 template <int TILE, int BS, int NE>
@@ -454,6 +496,8 @@ __global__ __launch_bounds__(NE * 64) void hessian_reduce_kernel(const float* __
   int I, J;
   tile_coords(t, nt, I, J);
   const int w = b >> 4, i = (b >> 2) & 3, j = b & 3;
+  if (I == J && w == 2 && NE == 4) return;  // filled by the mirror of quadrant 1
+  const bool mirror = (I != J) || (w == 1 && NE == 4);
   const int tid = threadIdx.x, e = tid >> 6, lane = tid & 63;
   constexpr int64_t kElems = static_cast<int64_t>(TILE) * TILE;
   const int64_t off = static_cast<int64_t>((w * 16 * NE + (i * 4 + j) * NE + e) * 64 + lane) << 2;
@@ -470,7 +514,7 @@ __global__ __launch_bounds__(NE * 64) void hessian_reduce_kernel(const float* __
   for (int idx = tid; idx < BS * BS; idx += NE * 64) {
     const int rr = idx / BS, cc = idx % BS;
     if (row0 + rr < d && col0 + cc < d) S[static_cast<int64_t>(row0 + rr) * d + col0 + cc] += blk[rr][cc];
-    if (I != J && col0 + rr < d && row0 + cc < d)
+    if (mirror && col0 + rr < d && row0 + cc < d)
       S[static_cast<int64_t>(col0 + rr) * d + row0 + cc] += blk[cc][rr];
   }
 }
