@@ -88,11 +88,26 @@ GPTQ_DEV uint32_t bload(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) 
 
 GPTQ_DEV int wave_uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
+// At 4 bits the operands of a lane group hold its 8 k in the order 0 4 1 5 2
+// 6 3 7 (dword j = k j and k j + 4): nibbles j and j + 4 of a code word are
+// 16 bits apart, so one shift and one mask-or turn them into a bf16 pair.
+// interleave_halves puts 8 bf16 of x into that order; operand_code gives the
+// k of half h of dword j.
+GPTQ_DEV u32x4_t interleave_halves(const u32x4_t& v) {
+  u32x4_t r;
+  r[0] = (v[0] & 0xffffu) | (v[2] << 16);
+  r[1] = (v[0] >> 16) | (v[2] & 0xffff0000u);
+  r[2] = (v[1] & 0xffffu) | (v[3] << 16);
+  r[3] = (v[1] >> 16) | (v[3] & 0xffff0000u);
+  return r;
+}
+
 // x[m0 + t][32 c0 ..] for the stage's chunks as fp32 into xs[chunk][t][j]
 // (0 for t >= m).  16-byte pieces (4 fp32 or 8 bf16), every load at an
 // in-range address (clamped row and piece), selected after.
 template <int MT>
-GPTQ_DEV void stage_x_f32(const DqParams& p, int64_t c0, int nc, float (*xs)[MT][kChunk + 4], int tid) {
+GPTQ_DEV void stage_x_f32(const DqParams& p, int64_t c0, int nc, float (*xs)[MT][kChunk + 4], int tid,
+                          uint32_t (*xi)[MT][kChunk / 2 + 4] = nullptr) {
   const int per = p.xbf16 ? 8 : 4;                    // elements per piece
   const int row_pieces = kStage * kChunk / per;       // pieces per token row of the stage
   const int live = nc * kChunk / per;
@@ -118,6 +133,11 @@ GPTQ_DEV void stage_x_f32(const DqParams& p, int64_t c0, int nc, float (*xs)[MT]
         for (int q = 0; q < 4; ++q) {
           xs[cl][t][j + 2 * q] = (t < p.m) ? __uint_as_float(v[i][q] << 16) : 0.f;
           xs[cl][t][j + 2 * q + 1] = (t < p.m) ? __uint_as_float(v[i][q] & 0xffff0000u) : 0.f;
+        }
+        if (xi) {
+          // the 8 bf16 as interleaved pairs (k, k + 4), the 4-bit operand order
+          const u32x4_t z = {0u, 0u, 0u, 0u};
+          *reinterpret_cast<u32x4_t*>(&xi[cl][t][j / 2]) = interleave_halves((t < p.m) ? v[i] : z);
         }
       } else {
 #pragma unroll
@@ -204,6 +224,40 @@ GPTQ_DEV void valu_uniform(const uint32_t (&w)[BITS], const float (*xs)[kChunk +
       ...);
 }
 
+// 4-bit codes against bf16 x: acc[t] += sum_k x[t][k] (16 + q_k) over the
+// chunk by v_dot2_f32_bf16, two codes per instruction.  Nibbles j and j + 4
+// of a code word sit 16 bits apart, so one shift and one mask-or give the
+// bf16 pair (16 + q_j, 16 + q_{j+4}) (0x4180 | q << 3); xi holds x as the
+// matching pairs (k, k + 4) of each 8 k.  The caller subtracts (16 + z) sum x.
+template <int MT>
+GPTQ_DEV void valu_uniform_dot4(const uint32_t (&w)[4], const uint32_t (*xi)[kChunk / 2 + 4], float (&acc)[MT]) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  // the bf16 pair (16, 16) held in a vector register: with both constants
+  // literal the mask and the or do not fuse into one v_and_or_b32 (a 3-operand
+  // instruction takes one scalar operand and no literal here)
+  const uint32_t magic = opaque_and<0xffffffffu>(0x41804180u);
+#pragma unroll
+  for (int wi = 0; wi < 4; ++wi) {
+    const uint32_t f = w[wi];
+    uint32_t b[4];
+    b[0] = ((f << 3) & 0x00780078u) | magic;
+#pragma unroll
+    for (int j = 1; j < 4; ++j) b[j] = ((f >> (4 * j - 3)) & 0x00780078u) | magic;
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+      const u32x4_t xv = *reinterpret_cast<const u32x4_t*>(&xi[t][4 * wi]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        // copied out first: __builtin_bit_cast of a vector-element lvalue
+        // (xv[j]) reads element 0 whatever j is
+        const uint32_t xj = xv[j];
+        acc[t] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, xj), __builtin_bit_cast(bf16x2_t, b[j]),
+                                                 acc[t], false);
+      }
+    }
+  }
+}
+
 template <int BITS, int MT, int... Js>
 GPTQ_DEV void valu_grouped(const uint32_t (&w)[BITS], const float (*xs)[kChunk + 4], const int32_t* gl,
                            __amdgpu_buffer_rsrc_t rs, __amdgpu_buffer_rsrc_t rz, uint32_t rowb, uint32_t vo,
@@ -222,9 +276,12 @@ GPTQ_DEV void valu_grouped(const uint32_t (&w)[BITS], const float (*xs)[kChunk +
 
 // gix is g_idx again, as its own restrict argument, so that the reads of a
 // chunk's first entry (wave-uniform addresses) become scalar loads.
-template <int BITS, int MT>
+// DOT: 4-bit codes with bf16 x, one-group chunks on v_dot2_f32_bf16
+template <int BITS, int MT, bool DOT>
 __global__ __launch_bounds__(256) void dequant_valu_kernel(DqParams p, const int32_t* __restrict__ gix) {
+  static_assert(!DOT || BITS == 4, "the dot form is for 4-bit codes");
   __shared__ __attribute__((aligned(16))) float xs[kStage][MT][kChunk + 4];
+  __shared__ __attribute__((aligned(16))) uint32_t xi[DOT ? kStage : 1][MT][kChunk / 2 + 4];
   __shared__ int32_t gl[kStage][kChunk];
   __shared__ int uni[kStage];
   __shared__ float xsum[kStage][MT];
@@ -255,7 +312,7 @@ __global__ __launch_bounds__(256) void dequant_valu_kernel(DqParams p, const int
     zc[i] = static_cast<int32_t>(bload(rz, vo, so));
   }
   if (nc > 0) {
-    stage_x_f32<MT>(p, c0, nc, xs, tid);
+    stage_x_f32<MT>(p, c0, nc, xs, tid, DOT ? xi : nullptr);
     stage_groups(p, c0, nc, gl, uni, tid);  // ends past a barrier: xs is visible
     for (int e = tid; e < nc * MT; e += 256) {
       const int cl = e / MT, t = e % MT;
@@ -279,9 +336,15 @@ __global__ __launch_bounds__(256) void dequant_valu_kernel(DqParams p, const int
       float acc[MT];
 #pragma unroll
       for (int t = 0; t < MT; ++t) acc[t] = 0.f;
-      valu_uniform<BITS, MT>(w, xs[cl], acc, std::make_integer_sequence<int, kChunk / 4>{});
+      if constexpr (DOT) {
+        valu_uniform_dot4<MT>(w, xi[cl], acc);
 #pragma unroll
-      for (int t = 0; t < MT; ++t) y[t] = fmaf(s, fmaf(-z, xsum[cl][t], acc[t]), y[t]);
+        for (int t = 0; t < MT; ++t) y[t] = fmaf(s, fmaf(-(16.f + z), xsum[cl][t], acc[t]), y[t]);
+      } else {
+        valu_uniform<BITS, MT>(w, xs[cl], acc, std::make_integer_sequence<int, kChunk / 4>{});
+#pragma unroll
+        for (int t = 0; t < MT; ++t) y[t] = fmaf(s, fmaf(-z, xsum[cl][t], acc[t]), y[t]);
+      }
     } else {
       valu_grouped<BITS, MT>(w, xs[cl], gl[cl], rs, rz, rowb, vo, y, std::make_integer_sequence<int, kChunk>{});
     }
@@ -405,20 +468,6 @@ GPTQ_DEV uint32_t bf16_bits_of(float v) {
 }
 
 GPTQ_DEV float bf16_value(uint32_t b) { return __builtin_bit_cast(float, b << 16); }
-
-// At 4 bits the operands of a lane group hold its 8 k in the order 0 4 1 5 2
-// 6 3 7 (dword j = k j and k j + 4): nibbles j and j + 4 of a code word are
-// 16 bits apart, so one shift and one mask-or turn them into a bf16 pair.
-// interleave_halves puts 8 bf16 of x into that order; operand_code gives the
-// k of half h of dword j.
-GPTQ_DEV u32x4_t interleave_halves(const u32x4_t& v) {
-  u32x4_t r;
-  r[0] = (v[0] & 0xffffu) | (v[2] << 16);
-  r[1] = (v[0] >> 16) | (v[2] & 0xffff0000u);
-  r[2] = (v[1] & 0xffffu) | (v[3] << 16);
-  r[3] = (v[1] >> 16) | (v[3] & 0xffff0000u);
-  return r;
-}
 
 template <int BITS>
 constexpr int operand_code(int j, int h) {
@@ -609,7 +658,8 @@ hipError_t valu_pass(DqParams p, hipStream_t st) {
   const ValuPlan pl = valu_plan(p.d_in, p.d_out);
   p.cpw = pl.cpw;
   p.ks = pl.ks;
-  dequant_valu_kernel<BITS, MT><<<pl.nblocks * pl.ks, 256, 0, st>>>(p, p.g_idx);
+  if (BITS == 4 && p.xbf16) dequant_valu_kernel<BITS, MT, BITS == 4><<<pl.nblocks * pl.ks, 256, 0, st>>>(p, p.g_idx);
+  else dequant_valu_kernel<BITS, MT, false><<<pl.nblocks * pl.ks, 256, 0, st>>>(p, p.g_idx);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || pl.ks == 1) return e;
   const int64_t total = p.m * p.d_out;
