@@ -102,48 +102,94 @@ GPTQ_DEV u32x4_t interleave_halves(const u32x4_t& v) {
   return r;
 }
 
-// x[m0 + t][32 c0 ..] for the stage's chunks as fp32 into xs[chunk][t][j]
-// (0 for t >= m).  16-byte pieces (4 fp32 or 8 bf16), every load at an
-// in-range address (clamped row and piece), selected after.
+// x[m0 + t][32 c0 ..] for the stage's chunks in 16-byte pieces (4 fp32 or 8
+// bf16): piece e is token e / row_pieces, piece e % row_pieces of that row.
+// load_x issues a thread's pieces (a clamped, in-range piece past the stage's
+// live chunks or tokens); store_x writes them to LDS after the code words'
+// loads are in flight: xs[chunk][t][j] as fp32 (0 for t >= m) and, for the dot
+// form, xi[chunk][t] as the interleaved bf16 pairs.
 template <int MT>
-GPTQ_DEV void stage_x_f32(const DqParams& p, int64_t c0, int nc, float (*xs)[MT][kChunk + 4], int tid,
-                          uint32_t (*xi)[MT][kChunk / 2 + 4] = nullptr) {
-  const int per = p.xbf16 ? 8 : 4;                    // elements per piece
-  const int row_pieces = kStage * kChunk / per;       // pieces per token row of the stage
-  const int live = nc * kChunk / per;
-  for (int e0 = 0; e0 < MT * row_pieces; e0 += 256 * 4) {
-    u32x4_t v[4];
+struct XPieces {
+  static constexpr int kN = (MT * kStage * kChunk / 4 + 255) / 256;  // fp32 x; bf16 uses half
+  u32x4_t v[kN];
+};
+
+template <int MT>
+GPTQ_DEV void load_x(const DqParams& p, int64_t c0, int nc, int tid, XPieces<MT>& xp) {
+  const int per = p.xbf16 ? 8 : 4;               // elements per piece
+  const int row_pieces = kStage * kChunk / per;  // pieces per token row of the stage
+  const int live = std::max(1, nc * kChunk / per);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int e = e0 + tid + 256 * i;
-      const int t = std::min(e / row_pieces, MT - 1), k = std::min(e % row_pieces, live - 1);
+  for (int i = 0; i < XPieces<MT>::kN; ++i) {
+    const int e = tid + 256 * i;
+    if (e < MT * row_pieces) {
+      const int t = e / row_pieces, k = std::min(e % row_pieces, live - 1);
       const int64_t row = p.m0 + std::min<int64_t>(t, p.m - 1);
       const int64_t col = c0 * kChunk + static_cast<int64_t>(k) * per;
-      v[i] = p.xbf16 ? *reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(p.x) + row * p.ldx + col)
-                     : *reinterpret_cast<const u32x4_t*>(static_cast<const float*>(p.x) + row * p.ldx + col);
+      xp.v[i] = p.xbf16 ? *reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(p.x) + row * p.ldx + col)
+                        : *reinterpret_cast<const u32x4_t*>(static_cast<const float*>(p.x) + row * p.ldx + col);
     }
+  }
+}
+
+// v moved between lanes by a DPP control (quad permutation or row shift;
+// lanes with no source read 0)
+template <int CTRL>
+GPTQ_DEV float dpp_move(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xf, 0xf, true));
+}
+
+// Also the chunk's sum of x per token into xsum[chunk][t]: a thread adds its
+// piece's elements in order, then the pieces of a chunk (4 consecutive lanes
+// for bf16, 8 for fp32, aligned) are added across lanes by DPP moves (quad
+// xor 1, xor 2, then for fp32 the neighbouring quad by a row shift of 4), and
+// the lane of the chunk's last piece writes the sum.  Every lane takes part
+// in the moves; lanes without a live piece carry zeros.
+template <int MT>
+GPTQ_DEV void store_x(const DqParams& p, int nc, int tid, const XPieces<MT>& xp, float (*xs)[MT][kChunk + 4],
+                      uint32_t (*xi)[MT][kChunk / 2 + 4], float (*xsum)[MT]) {
+  const int per = p.xbf16 ? 8 : 4;
+  const int row_pieces = kStage * kChunk / per;
+  const int live = nc * kChunk / per;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int e = e0 + tid + 256 * i;
-      const int t = e / row_pieces, k = e % row_pieces;
-      if (t >= MT || k >= live) continue;
-      const int kk = k * per, cl = kk / kChunk, j = kk % kChunk;
-      if (p.xbf16) {
+  for (int i = 0; i < XPieces<MT>::kN; ++i) {
+    const int e = tid + 256 * i;
+    const int t = e / row_pieces, k = e % row_pieces;
+    const bool here = t < MT && k < live;
+    const u32x4_t z = {0u, 0u, 0u, 0u};
+    const u32x4_t v = (here && t < p.m) ? xp.v[i] : z;
+    float f[8];
+    int nf = 4;
+    if (p.xbf16) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          xs[cl][t][j + 2 * q] = (t < p.m) ? __uint_as_float(v[i][q] << 16) : 0.f;
-          xs[cl][t][j + 2 * q + 1] = (t < p.m) ? __uint_as_float(v[i][q] & 0xffff0000u) : 0.f;
-        }
-        if (xi) {
-          // the 8 bf16 as interleaved pairs (k, k + 4), the 4-bit operand order
-          const u32x4_t z = {0u, 0u, 0u, 0u};
-          *reinterpret_cast<u32x4_t*>(&xi[cl][t][j / 2]) = interleave_halves((t < p.m) ? v[i] : z);
-        }
-      } else {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) xs[cl][t][j + q] = (t < p.m) ? __uint_as_float(v[i][q]) : 0.f;
+      for (int q = 0; q < 4; ++q) {
+        f[2 * q] = __uint_as_float(v[q] << 16);
+        f[2 * q + 1] = __uint_as_float(v[q] & 0xffff0000u);
       }
+      nf = 8;
+    } else {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) f[q] = __uint_as_float(v[q]);
     }
+    float sum = f[0];
+#pragma unroll
+    for (int q = 1; q < 8; ++q)
+      if (q < nf) sum += f[q];
+    sum += dpp_move<0xb1>(sum);  // quad lanes xor 1
+    sum += dpp_move<0x4e>(sum);  // quad lanes xor 2
+    if (!p.xbf16) sum += dpp_move<0x114>(sum);  // row shift right by 4: the chunk's first quad
+    if (!here) continue;
+    const int kk = k * per, cl = kk / kChunk, j = kk % kChunk;
+    if (p.xbf16) {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) xs[cl][t][j + q] = f[q];
+      // the 8 bf16 as interleaved pairs (k, k + 4), the 4-bit operand order
+      if (xi) *reinterpret_cast<u32x4_t*>(&xi[cl][t][j / 2]) = interleave_halves(v);
+    } else {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) xs[cl][t][j + q] = f[q];
+    }
+    if (j + per == kChunk) xsum[cl][t] = sum;
   }
 }
 
@@ -258,32 +304,51 @@ GPTQ_DEV void valu_uniform_dot4(const uint32_t (&w)[4], const uint32_t (*xi)[kCh
   }
 }
 
-template <int BITS, int MT, int... Js>
-GPTQ_DEV void valu_grouped(const uint32_t (&w)[BITS], const float (*xs)[kChunk + 4], const int32_t* gl,
-                           __amdgpu_buffer_rsrc_t rs, __amdgpu_buffer_rsrc_t rz, uint32_t rowb, uint32_t vo,
-                           float (&y)[MT], std::integer_sequence<int, Js...>) {
+// codes J0 .. J0 + 7 of a chunk spread over groups: gv holds the chunk's
+// g_idx in lanes base .. base + 31.  The eight codes' scale and zero-point
+// loads are issued together, then used: one wait per eight codes.
+template <int BITS, int MT, int J0, int... Us>
+GPTQ_DEV void valu_grouped8(const uint32_t (&w)[BITS], const float (*xs)[kChunk + 4], int32_t gv, int base,
+                            __amdgpu_buffer_rsrc_t rs, __amdgpu_buffer_rsrc_t rz, uint32_t rowb, uint32_t vo,
+                            float (&y)[MT], std::integer_sequence<int, Us...>) {
+  uint32_t sb[sizeof...(Us)], zb[sizeof...(Us)];
   (
       [&] {
-        const uint32_t so = static_cast<uint32_t>(wave_uniform(gl[Js])) * rowb;  // group row of code j
-        const float s = __builtin_bit_cast(float, bload(rs, vo, so));
-        const float z = static_cast<float>(static_cast<int32_t>(bload(rz, vo, so)));
-        const float wv = s * (static_cast<float>(chunk_code<BITS, Js>(w)) - z);
+        const uint32_t so = static_cast<uint32_t>(__builtin_amdgcn_readlane(gv, base + J0 + Us)) * rowb;
+        sb[Us] = bload(rs, vo, so);
+        zb[Us] = bload(rz, vo, so);
+      }(),
+      ...);
+  (
+      [&] {
+        const float z = static_cast<float>(static_cast<int32_t>(zb[Us]));
+        const float wv = __builtin_bit_cast(float, sb[Us]) * (static_cast<float>(chunk_code<BITS, J0 + Us>(w)) - z);
 #pragma unroll
-        for (int t = 0; t < MT; ++t) y[t] = fmaf(xs[t][Js], wv, y[t]);
+        for (int t = 0; t < MT; ++t) y[t] = fmaf(xs[t][J0 + Us], wv, y[t]);
       }(),
       ...);
 }
 
-// gix is g_idx again, as its own restrict argument, so that the reads of a
-// chunk's first entry (wave-uniform addresses) become scalar loads.
-// DOT: 4-bit codes with bf16 x, one-group chunks on v_dot2_f32_bf16
+template <int BITS, int MT, int... J8s>
+GPTQ_DEV void valu_grouped(const uint32_t (&w)[BITS], const float (*xs)[kChunk + 4], int32_t gv, int base,
+                           __amdgpu_buffer_rsrc_t rs, __amdgpu_buffer_rsrc_t rz, uint32_t rowb, uint32_t vo,
+                           float (&y)[MT], std::integer_sequence<int, J8s...>) {
+  (valu_grouped8<BITS, MT, 8 * J8s>(w, xs, gv, base, rs, rz, rowb, vo, y, std::make_integer_sequence<int, 8>{}), ...);
+}
+
+// gix is g_idx again, as its own restrict argument, so that its reads
+// (wave-uniform addresses: a chunk's entries) become scalar loads.
+// DOT: 4-bit codes with bf16 x, one-group chunks on v_dot2_f32_bf16.
+// A workgroup's x pieces are loaded first (they hit L2: every workgroup of
+// the K slice reads them), then each wave's chunks' g_idx (lanes 0-31 one
+// chunk, 32-63 the next), code words, scales and zero points; a ballot over
+// the g_idx lanes tells which chunks lie in one group, one barrier makes the
+// staged x visible, and each wave forms its chunks' sums of x itself.
 template <int BITS, int MT, bool DOT>
 __global__ __launch_bounds__(256) void dequant_valu_kernel(DqParams p, const int32_t* __restrict__ gix) {
   static_assert(!DOT || BITS == 4, "the dot form is for 4-bit codes");
   __shared__ __attribute__((aligned(16))) float xs[kStage][MT][kChunk + 4];
   __shared__ __attribute__((aligned(16))) uint32_t xi[DOT ? kStage : 1][MT][kChunk / 2 + 4];
-  __shared__ int32_t gl[kStage][kChunk];
-  __shared__ int uni[kStage];
   __shared__ float xsum[kStage][MT];
   __shared__ float ys[4][MT][kValuCols];
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_uniform(tid >> 6);
@@ -293,34 +358,41 @@ __global__ __launch_bounds__(256) void dequant_valu_kernel(DqParams p, const int
   const int nc = static_cast<int>(std::max<int64_t>(0, std::min<int64_t>(p.chunks, c0 + p.cpw) - c0));
   const int64_t n = static_cast<int64_t>(nb) * kValuCols + lane;
   const int64_t nl = std::min(n, p.d_out - 1);  // columns past the end read the last one
+  XPieces<MT> xp;
+  load_x<MT>(p, c0, nc, tid, xp);
   // the wave's chunks wave, wave + 4, ...: code words and first group's scale
-  // and zero point, issued before x is staged, at in-range chunk indices
+  // and zero point at in-range chunk indices, and whether the chunk is one group
   const __amdgpu_buffer_rsrc_t rq = buffer_of(p.qweight, p.qbytes), rs = buffer_of(p.scales, p.gbytes),
                                rz = buffer_of(p.zeros, p.gbytes);
   const uint32_t rowb = static_cast<uint32_t>(p.d_out) * 4u, vo = static_cast<uint32_t>(nl) * 4u;
   constexpr int kPerWave = kStage / 4;
+  auto chunk_of = [&](int i) {  // the wave's i-th chunk, clamped in range
+    return std::min<int64_t>(c0 + std::min(wave + 4 * i, std::max(nc, 1) - 1), p.chunks - 1);
+  };
+  int32_t gv[kPerWave / 2];
+#pragma unroll
+  for (int h = 0; h < kPerWave / 2; ++h) gv[h] = p.g_idx[chunk_of(2 * h + (lane >> 5)) * kChunk + (lane & 31)];
   uint32_t wq[kPerWave][BITS];
   float sc[kPerWave];
-  int32_t zc[kPerWave];
+  int32_t zc[kPerWave], g0[kPerWave];
 #pragma unroll
   for (int i = 0; i < kPerWave; ++i) {
-    const int64_t c = std::min<int64_t>(c0 + std::min(wave + 4 * i, std::max(nc, 1) - 1), p.chunks - 1);
+    const int64_t c = chunk_of(i);
 #pragma unroll
     for (int b = 0; b < BITS; ++b) wq[i][b] = bload(rq, vo, static_cast<uint32_t>(c * BITS + b) * rowb);
-    const uint32_t so = static_cast<uint32_t>(gix[c * kChunk]) * rowb;
+    g0[i] = gix[c * kChunk];
+    const uint32_t so = static_cast<uint32_t>(g0[i]) * rowb;
     sc[i] = __builtin_bit_cast(float, bload(rs, vo, so));
     zc[i] = static_cast<int32_t>(bload(rz, vo, so));
   }
-  if (nc > 0) {
-    stage_x_f32<MT>(p, c0, nc, xs, tid, DOT ? xi : nullptr);
-    stage_groups(p, c0, nc, gl, uni, tid);  // ends past a barrier: xs is visible
-    for (int e = tid; e < nc * MT; e += 256) {
-      const int cl = e / MT, t = e % MT;
-      float v = 0.f;
-      for (int j = 0; j < kChunk; ++j) v += xs[cl][t][j];
-      xsum[cl][t] = v;
-    }
+  bool one[kPerWave];
+#pragma unroll
+  for (int h = 0; h < kPerWave / 2; ++h) {
+    // each half against its chunk's first entry (a wave-uniform value)
+    one[2 * h] = static_cast<uint32_t>(__ballot(gv[h] != g0[2 * h])) == 0u;
+    one[2 * h + 1] = (__ballot(gv[h] != g0[2 * h + 1]) >> 32) == 0u;
   }
+  store_x<MT>(p, nc, tid, xp, xs, DOT ? xi : nullptr, xsum);
   __syncthreads();
   float y[MT];
 #pragma unroll
@@ -330,7 +402,7 @@ __global__ __launch_bounds__(256) void dequant_valu_kernel(DqParams p, const int
     const int cl = wave + 4 * i;
     if (cl >= nc) continue;
     const uint32_t(&w)[BITS] = wq[i];
-    if (uni[cl]) {
+    if (one[i]) {
       const float s = sc[i];
       const float z = static_cast<float>(zc[i]);
       float acc[MT];
@@ -346,7 +418,8 @@ __global__ __launch_bounds__(256) void dequant_valu_kernel(DqParams p, const int
         for (int t = 0; t < MT; ++t) y[t] = fmaf(s, fmaf(-z, xsum[cl][t], acc[t]), y[t]);
       }
     } else {
-      valu_grouped<BITS, MT>(w, xs[cl], gl[cl], rs, rz, rowb, vo, y, std::make_integer_sequence<int, kChunk>{});
+      valu_grouped<BITS, MT>(w, xs[cl], gv[i / 2], 32 * (i & 1), rs, rz, rowb, vo, y,
+                             std::make_integer_sequence<int, kChunk / 8>{});
     }
   }
   // the four waves' partial sums, added in wave order
