@@ -446,12 +446,19 @@ __global__ void dequant_reduce_kernel(const float* part, int ks, int64_t m0, int
   const int64_t step = static_cast<int64_t>(MT) * d_out;
   float v = 0.f;
   int s = 0;
-  for (; s + 8 <= ks; s += 8) {
-    float l[8];  // eight slices' loads in flight, added in slice order
+  for (; s + 16 <= ks; s += 16) {
+    float l[16];  // sixteen slices' loads in flight, added in slice order
 #pragma unroll
-    for (int i = 0; i < 8; ++i) l[i] = q[(s + i) * step];
+    for (int i = 0; i < 16; ++i) l[i] = q[(s + i) * step];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) v += l[i];
+    for (int i = 0; i < 16; ++i) v += l[i];
+  }
+  for (; s + 4 <= ks; s += 4) {
+    float l[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) l[i] = q[(s + i) * step];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v += l[i];
   }
   for (; s < ks; ++s) v += q[s * step];
   y[(m0 + t) * d_out + n] = v;
