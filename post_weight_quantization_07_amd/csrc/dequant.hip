@@ -25,9 +25,9 @@
 // are 16 + q and -(16 + z), built from the packed word with integer
 // operations only (interleave_halves), which widens the rounding bound by 32
 // per term.  A chunk spread over several groups uses B = s (q - z) split into
-// bf16 high and low parts (two MFMAs).  A workgroup owns 64 output columns
-// (16 per wave) and walks its K range in stages of 16 chunks; K is split
-// over workgroups, with fewer slices than the VALU path.
+// bf16 high and low parts (two MFMAs).  A workgroup of 4 waves owns 64
+// output columns (16 per wave) and walks its K range in stages of 16 chunks;
+// K is split over workgroups, with fewer slices than the VALU path.
 //
 // VALU path (fp32 x, or 1-2 tokens): lanes map to output columns (64 per
 // workgroup, so a packed word load is 64 consecutive int32 of one qweight
@@ -190,17 +190,6 @@ GPTQ_DEV void store_x(const DqParams& p, int nc, int tid, const XPieces<MT>& xp,
       for (int q = 0; q < 4; ++q) xs[cl][t][j + q] = f[q];
     }
     if (j + per == kChunk) xsum[cl][t] = sum;
-  }
-}
-
-// g_idx of the stage's chunks, and whether each chunk lies in one group
-GPTQ_DEV void stage_groups(const DqParams& p, int64_t c0, int nc, int32_t (*gl)[kChunk], int* uni, int tid) {
-  for (int e = tid; e < nc * kChunk; e += 256) gl[e / kChunk][e % kChunk] = p.g_idx[c0 * kChunk + e];
-  __syncthreads();
-  if (tid < nc) {
-    int same = 1;
-    for (int j = 1; j < kChunk; ++j) same &= (gl[tid][j] == gl[tid][0]);
-    uni[tid] = same;
   }
 }
 
@@ -561,14 +550,17 @@ GPTQ_DEV f32x4_t mfma32(const u32x4_t& a, const u32x4_t& b, const f32x4_t& c) {
 
 // T column tiles of 16 per wave (64 T columns per workgroup: x staged once
 // serves them all) and SC chunks per LDS stage
-template <int BITS, int T, int SC>
-__global__ __launch_bounds__(256) void dequant_mfma_kernel(DqParams p, const int32_t* __restrict__ gix) {
+template <int BITS, int T, int SC, int NW>
+__global__ __launch_bounds__(64 * NW) void dequant_mfma_kernel(DqParams p, const int32_t* __restrict__ gix) {
+  static_assert(SC % 2 == 0, "chunks go to the g_idx lanes in pairs");
+  constexpr int kThreads = 64 * NW;
   __shared__ __attribute__((aligned(16))) uint16_t xb[SC][16][kChunk + 8];  // bf16 x, [chunk][token][k]
-  __shared__ int32_t gl[SC][kChunk];
-  __shared__ int uni[SC];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  __shared__ int32_t gl[SC][kChunk];  // g_idx of the stage's chunks
+  __shared__ int uni[SC];             // whether each chunk lies in one group
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_uniform(tid >> 6);
   const int c16 = lane & 15, g = lane >> 4;
-  constexpr int kCols = 64 * T;
+  constexpr int kCols = 16 * T * NW;
+  constexpr int kPairsPerWave = (SC / 2 + NW - 1) / NW;  // chunk pairs whose g_idx a wave checks
   const int nblocks = static_cast<int>((p.d_out + kCols - 1) / kCols);
   const int nb = blockIdx.x % nblocks, ks = blockIdx.x / nblocks;
   const int64_t cb = static_cast<int64_t>(ks) * p.cpw;
@@ -596,9 +588,32 @@ __global__ __launch_bounds__(256) void dequant_mfma_kernel(DqParams p, const int
   for (int64_t c0 = cb; c0 < ce; c0 += SC) {
     const int nc = static_cast<int>(std::min<int64_t>(SC, ce - c0));  // >= 1
     if (c0 != cb) __syncthreads();  // the previous stage's LDS reads are done
+    // 16 tokens x nc chunks of bf16 x as 16-byte pieces, issued first (L2
+    // hits: every workgroup of the K slice reads them); every load at an
+    // in-range address (rows past m repeat the last row, pieces past the
+    // range the last piece), selected after
+    constexpr int kRowPieces = SC * kChunk / 8;
+    constexpr int kPieces = 16 * kRowPieces;
+    static_assert(kPieces % kThreads == 0, "whole passes over the stage's pieces");
+    const int live = nc * kChunk / 8;
+    u32x4_t v[kPieces / kThreads];
+#pragma unroll
+    for (int i = 0; i < kPieces / kThreads; ++i) {
+      const int e = tid + kThreads * i, t = e / kRowPieces, k8 = std::min(e % kRowPieces, live - 1);
+      const int64_t row = p.m0 + std::min<int64_t>(t, p.m - 1);
+      v[i] = *reinterpret_cast<const u32x4_t*>(xh + row * p.ldx + c0 * kChunk + 8 * k8);
+    }
+    // g_idx of chunk pairs wave, wave + NW, ..: lanes 0-31 hold chunk 2 h,
+    // lanes 32-63 chunk 2 h + 1 (in-range chunk indices)
+    int32_t gv[kPairsPerWave];
+#pragma unroll
+    for (int u = 0; u < kPairsPerWave; ++u) {
+      const int h = std::min(wave + NW * u, SC / 2 - 1);
+      gv[u] = p.g_idx[(c0 + std::min(2 * h + (lane >> 5), nc - 1)) * kChunk + (lane & 31)];
+    }
     // the stage's code words, scales and zero points (the chunk's first
     // group's), loaded at in-range chunk indices (chunks past nc repeat the
-    // last), in flight while x is staged
+    // last)
     uint32_t wq[SC][T][kLaneWords<BITS>];
     float sc[SC][T];
     int32_t zc[SC][T];
@@ -613,30 +628,28 @@ __global__ __launch_bounds__(256) void dequant_mfma_kernel(DqParams p, const int
         zc[cl][t] = static_cast<int32_t>(bload(rz, vo[t], so));
       }
     }
-    {
-      // 16 tokens x nc chunks of bf16 as 16-byte pieces, every load at an
-      // in-range address (rows past m repeat the last row, pieces past the
-      // range the last piece), selected after
-      constexpr int kRowPieces = SC * kChunk / 8;
-      constexpr int kPieces = 16 * kRowPieces;
-      const int live = nc * kChunk / 8;
-      u32x4_t v[kPieces / 256];
 #pragma unroll
-      for (int i = 0; i < kPieces / 256; ++i) {
-        const int e = tid + 256 * i, t = e / kRowPieces, k8 = std::min(e % kRowPieces, live - 1);
-        const int64_t row = p.m0 + std::min<int64_t>(t, p.m - 1);
-        v[i] = *reinterpret_cast<const u32x4_t*>(xh + row * p.ldx + c0 * kChunk + 8 * k8);
-      }
+    for (int i = 0; i < kPieces / kThreads; ++i) {
+      const int e = tid + kThreads * i, t = e / kRowPieces, k8 = e % kRowPieces;
+      const u32x4_t z = {0u, 0u, 0u, 0u};
+      u32x4_t w = (t < p.m) ? v[i] : z;
+      if constexpr (BITS == 4) w = interleave_halves(w);
+      if (k8 < live) *reinterpret_cast<u32x4_t*>(&xb[k8 / 4][t][8 * (k8 % 4)]) = w;
+    }
+    // the checked pairs' g_idx to LDS, and whether each chunk lies in one
+    // group: a ballot of the lanes that differ from the chunk's first entry
 #pragma unroll
-      for (int i = 0; i < kPieces / 256; ++i) {
-        const int e = tid + 256 * i, t = e / kRowPieces, k8 = e % kRowPieces;
-        const u32x4_t z = {0u, 0u, 0u, 0u};
-        u32x4_t w = (t < p.m) ? v[i] : z;
-        if constexpr (BITS == 4) w = interleave_halves(w);
-        if (k8 < live) *reinterpret_cast<u32x4_t*>(&xb[k8 / 4][t][8 * (k8 % 4)]) = w;
+    for (int u = 0; u < kPairsPerWave; ++u) {
+      const int h = wave + NW * u;
+      if (h >= SC / 2) continue;
+      gl[2 * h + (lane >> 5)][lane & 31] = gv[u];
+      const int32_t f0 = __builtin_amdgcn_readlane(gv[u], 0), f1 = __builtin_amdgcn_readlane(gv[u], 32);
+      const uint64_t d0 = __ballot(gv[u] != f0), d1 = __ballot(gv[u] != f1);
+      if (lane == 0) {
+        uni[2 * h] = static_cast<uint32_t>(d0) == 0u;
+        uni[2 * h + 1] = (d1 >> 32) == 0u;
       }
     }
-    stage_groups(p, c0, nc, gl, uni, tid);
     __syncthreads();
 #pragma unroll
     for (int cl = 0; cl < SC; ++cl) {
@@ -748,19 +761,24 @@ hipError_t valu_pass(DqParams p, hipStream_t st) {
   return hipGetLastError();
 }
 
-// MFMA path: 64 T columns per workgroup (one tile per wave measured best: more
-// tiles raise the register count and lower occupancy), its K range in stages
-// of SC chunks.  Fewer K slices than the VALU plan, so that the partial sums
+// MFMA path: 16 T NW columns per workgroup, its K range in stages of SC
+// chunks.  One staged x serves all NW waves: 8 waves stage half the x bytes
+// per column that 4 do, but measured slower on one-group chunks (55.5 against
+// 53 us at 16 tokens, 28672 x 8192 4-bit) and on 4-bit act-order; faster only
+// on 3-bit act-order at 8192 x 8192 (45 against 60 us).  One tile per wave
+// measured best (more tiles raise the register count and lower occupancy).  Fewer K slices than the VALU plan, so that the partial sums
 // (written and read back, 8 m d_out bytes per slice) stay a small part of the
 // packed weights' bytes, while keeping 512 workgroups or more; never more
 // slices than the VALU plan, whose partial buffer is the workspace.
 constexpr int kMfmaTiles = 1;
 constexpr int kMfmaStage = 16;
+constexpr int kMfmaWaves = 4;
 
 ValuPlan mfma_plan(int64_t d_in, int64_t d_out, int bits) {
   const ValuPlan vp = valu_plan(d_in, d_out);
   ValuPlan pl = vp;
-  pl.nblocks = static_cast<int>((d_out + 64 * kMfmaTiles - 1) / (64 * kMfmaTiles));
+  constexpr int kCols = 16 * kMfmaTiles * kMfmaWaves;
+  pl.nblocks = static_cast<int>((d_out + kCols - 1) / kCols);
   const int64_t cap = std::max<int64_t>(d_in * bits / (512 * kMaxMT), (512 + pl.nblocks - 1) / pl.nblocks);
   const int ks = static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(vp.ks, cap)));
   pl.cpw = (pl.chunks + ks - 1) / ks;
@@ -773,7 +791,8 @@ hipError_t mfma_pass(DqParams p, hipStream_t st) {
   const ValuPlan pl = mfma_plan(p.d_in, p.d_out, BITS);
   p.cpw = pl.cpw;
   p.ks = pl.ks;
-  dequant_mfma_kernel<BITS, kMfmaTiles, kMfmaStage><<<pl.nblocks * pl.ks, 256, 0, st>>>(p, p.g_idx);
+  dequant_mfma_kernel<BITS, kMfmaTiles, kMfmaStage, kMfmaWaves>
+      <<<pl.nblocks * pl.ks, 64 * kMfmaWaves, 0, st>>>(p, p.g_idx);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || pl.ks == 1) return e;
   const int64_t total = p.m * p.d_out;
