@@ -79,7 +79,7 @@ CASES = [  # bits, group, desc_act, static, d_out, d_in
 
 
 @pytest.mark.parametrize("bits,group,desc,static,d_out,d_in", CASES)
-@pytest.mark.parametrize("m", [1, 5, 16, 17, 40])
+@pytest.mark.parametrize("m", [1, 2, 5, 16, 17, 40])
 @pytest.mark.parametrize("x_dtype", ["f32", "bf16"])
 def test_dequant_matmul_small(G, bits, group, desc, static, d_out, d_in, m, x_dtype):
     banner(f"dequant b{bits} g{group} desc={desc} static={static} {d_out}x{d_in} m={m} x={x_dtype}")
@@ -89,10 +89,12 @@ def test_dequant_matmul_small(G, bits, group, desc, static, d_out, d_in, m, x_dt
 
 
 # K ranges of several 16-chunk stages with a short last stage (515 chunks in
-# slices of 17 on the 16-token path), ragged columns and a ragged last group
+# slices of 17 on the 16-token path), ragged columns and a ragged last group;
+# 1 and 2 tokens take the VALU kernel over 58 K slices of 9 chunks (the reduction
+# runs three loads-of-16 passes and a tail)
 @pytest.mark.parametrize("bits,group,act", [(4, 128, False), (2, 64, False), (3, 128, False), (8, 128, False),
                                             (4, 128, True)])
-@pytest.mark.parametrize("m", [16, 40])
+@pytest.mark.parametrize("m", [1, 2, 16, 40])
 def test_dequant_matmul_long_k(G, bits, group, act, m):
     d_out, d_in = 1000, 16480
     banner(f"dequant long K b{bits} g{group} act={act} {d_out}x{d_in} m={m}")
