@@ -337,11 +337,12 @@ def dequant_table(args):
     lines = ["| d_out x d_in | bits / G | g_idx | tokens m | us per call | GB/s | % of 8 TB/s |",
              "|---|---|---|---:|---:|---:|---:|"]
     shapes = [(4096, 4096), (11008, 4096), (4096, 11008), (8192, 8192), (28672, 8192), (8192, 28672)]
-    cases = [(4, 128, False), (3, 32, True)]
+    cases = [(4, 128, False), (3, 32, True), (4, 128, True)]
+    act_shapes = {(3, 32): ((4096, 4096), (8192, 8192)), (4, 128): ((4096, 4096), (28672, 8192))}
     gen = torch.Generator(device="cpu").manual_seed(0)
     for d_out, d_in in shapes:
         for bits, group, act in cases:
-            if act and (d_out, d_in) not in ((4096, 4096), (8192, 8192)):
+            if act and (d_out, d_in) not in act_shapes[(bits, group)]:
                 continue
             ng = -(-d_in // group)
             codes = torch.randint(0, 1 << bits, (d_out, d_in), dtype=torch.uint8, generator=gen).to(dev)
@@ -355,27 +356,44 @@ def dequant_table(args):
                 g_idx = g_idx.to(dev)
             else:
                 g_idx = (torch.arange(d_in, dtype=torch.int32) // group).to(dev)
-            for m in (1, 8, 16):
-                x = torch.randn((m, d_in), generator=gen).to(torch.bfloat16).to(dev)
-                y = torch.empty((m, d_out), dtype=torch.float32, device=dev)
-                ws = torch.empty(max(256, G.gptq_dequant_workspace_size(m, d_in, d_out)), dtype=torch.uint8,
-                                 device=dev)
-                for _ in range(5):
-                    G.gptq_dequant_matmul(x, qweight, scales, zeros, g_idx, bits, y=y, ws=ws)
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                reps = 50
-                torch.cuda.synchronize()
-                e0.record()
-                for _ in range(reps):
-                    G.gptq_dequant_matmul(x, qweight, scales, zeros, g_idx, bits, y=y, ws=ws)
-                e1.record()
-                torch.cuda.synchronize()
-                us = e0.elapsed_time(e1) * 1e3 / reps
-                nbytes = d_out * d_in * bits / 8 + ng * d_out * 8 + d_in * 4 + m * d_in * 2 + m * d_out * 4
-                gbs = nbytes / (us * 1e-6) / 1e9
-                lines.append(f"| {d_out}x{d_in} | {bits} / {group} | {'act-order' if act else 'k // G'} | {m} | "
-                             f"{us:.1f} | {gbs:.0f} | {100 * gbs / (PEAK_HBM_GBS):.1f}% |")
-                print(lines[-1], flush=True)
+            # act-order layers: as stored, and put in group order once by
+            # gptq_dequant_order (the timed call then gathers x and runs the
+            # product on the reordered codes)
+            modes = [False, True] if act else [False]
+            if act:
+                q_ord, g_ord, order = G.gptq_dequant_order(qweight, g_idx, bits)
+            for ordered in modes:
+                for m in (1, 8, 16):
+                    x = torch.randn((m, d_in), generator=gen).to(torch.bfloat16).to(dev)
+                    y = torch.empty((m, d_out), dtype=torch.float32, device=dev)
+                    if ordered:
+                        ws = torch.empty(G.gptq_dequant_ordered_workspace_size(m, d_in, d_out), dtype=torch.uint8,
+                                         device=dev)
+                        call = lambda: G.gptq_dequant_matmul_ordered(x, q_ord, scales, zeros, g_ord, order, bits,
+                                                                     y=y, ws=ws)
+                    else:
+                        ws = torch.empty(max(256, G.gptq_dequant_workspace_size(m, d_in, d_out)),
+                                         dtype=torch.uint8, device=dev)
+                        call = lambda: G.gptq_dequant_matmul(x, qweight, scales, zeros, g_idx, bits, y=y, ws=ws)
+                    for _ in range(5):
+                        call()
+                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    reps = 50
+                    torch.cuda.synchronize()
+                    e0.record()
+                    for _ in range(reps):
+                        call()
+                    e1.record()
+                    torch.cuda.synchronize()
+                    us = e0.elapsed_time(e1) * 1e3 / reps
+                    nbytes = d_out * d_in * bits / 8 + ng * d_out * 8 + d_in * 4 + m * d_in * 2 + m * d_out * 4
+                    gbs = nbytes / (us * 1e-6) / 1e9
+                    kind = ("act-order, group order" if ordered else "act-order") if act else "k // G"
+                    lines.append(f"| {d_out}x{d_in} | {bits} / {group} | {kind} | {m} | "
+                                 f"{us:.1f} | {gbs:.0f} | {100 * gbs / (PEAK_HBM_GBS):.1f}% |")
+                    print(lines[-1], flush=True)
+            if act:
+                del q_ord, g_ord, order
             del codes, qweight, scales, zeros, g_idx
             torch.cuda.empty_cache()
     text = "\n".join(lines) + "\n"

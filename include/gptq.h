@@ -17,6 +17,12 @@
  *
  *   gptq_dequant_matmul       y = x W^T, W dequantized from qweight / scales / zeros / g_idx
  *
+ * and a layer quantized with act-order (desc_act) groups can first be put in
+ * group order once, so that the product reads one scale per 32 codes:
+ *
+ *   gptq_dequant_order            channels sorted by group, codes repacked
+ *   gptq_dequant_matmul_ordered   y = x W^T on the reordered layer
+ *
  * Conventions shared by every call
  *   - All array pointers are DEVICE pointers on the current HIP device; the
  *     caller owns every buffer (inputs, outputs, workspaces).  The library
@@ -191,6 +197,47 @@ gptq_status gptq_dequant_matmul(const void* x, gptq_dtype xt, int64_t m, int64_t
                                 const int32_t* qweight, const float* scales, const int32_t* zeros,
                                 const int32_t* g_idx, int32_t bits, int64_t d_out, int32_t n_groups,
                                 float* y, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Group order for the dequantizing product of an act-order layer.  With
+ * desc_act (the AutoGPTQ examples walkthrough, section 1.4) g_idx assigns the
+ * input channels to groups in the order the columns were quantized, so 32
+ * consecutive channels usually span several groups and the product reads a
+ * scale and zero point per code.  This call sorts the channels by group,
+ * stably (order[j] = the original channel at sorted position j; channels of
+ * one group keep increasing k), repacks the codes in that order and writes
+ * g_idx in that order (non-decreasing).  y = x W^T is a sum over k, so
+ * gptq_dequant_matmul_ordered on these outputs gives the product of the
+ * original layer (chapter 5, section 5.1.10) with its terms in another order.
+ * A one-time step (when a layer is loaded): d_in^2 comparisons.
+ *   qweight, g_idx   as for gptq_dequant_matmul (every g_idx entry in
+ *                    [0, n_groups); not checked on the device)
+ *   qweight_out      [d_in * bits / 32, d_out] int32; must not overlap qweight
+ *   g_idx_out        [d_in] int32, order [d_in] int32 (a permutation of 0..d_in-1)
+ * Requires d_in % 32 == 0 and qweight under 2^31 bytes.  INVALID_ARG on bad
+ * sizes, bits or null pointers.
+ */
+gptq_status gptq_dequant_order(const int32_t* qweight, const int32_t* g_idx, int32_t bits, int64_t d_in,
+                               int64_t d_out, int32_t* qweight_out, int32_t* g_idx_out, int32_t* order,
+                               void* stream);
+
+/*
+ * gptq_dequant_matmul on a layer put in group order by gptq_dequant_order:
+ * x's channels are gathered in that order into the workspace, then the
+ * product runs on the reordered codes (same y as gptq_dequant_matmul on the
+ * original tensors, summed in the sorted channel order, same error bound).
+ *   x        [m, d_in] bf16 or fp32 in the ORIGINAL channel order
+ *   qweight, g_idx, order   the outputs of gptq_dequant_order
+ *   scales, zeros           the layer's, unchanged ([n_groups, d_out])
+ *   ws       device workspace of gptq_dequant_ordered_workspace_size(m, d_in, d_out)
+ *            bytes, 256-byte aligned (the gathered x, then the partial sums)
+ * Other arguments, requirements and errors as for gptq_dequant_matmul.
+ */
+size_t gptq_dequant_ordered_workspace_size(int64_t m, int64_t d_in, int64_t d_out);
+gptq_status gptq_dequant_matmul_ordered(const void* x, gptq_dtype xt, int64_t m, int64_t d_in,
+                                        const int32_t* qweight, const float* scales, const int32_t* zeros,
+                                        const int32_t* g_idx, const int32_t* order, int32_t bits, int64_t d_out,
+                                        int32_t n_groups, float* y, void* ws, size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -2,7 +2,9 @@
 
 The four calls of the C ABI (include/gptq.h) with the same names, plus
 QuantizeConfig (BaseQuantizeConfig's fields), gptq_dequant_matmul (the
-quantized layer applied to activations), solve_layer, which chains them
+quantized layer applied to activations; gptq_dequant_order and
+gptq_dequant_matmul_ordered for act-order layers put in group order once),
+solve_layer, which chains them
 for one linear layer, and solve_layers_shared, which quantizes several layers
 that read the same input (q/k/v, gate/up) against one Hessian and one factor.
 All arithmetic runs in libgptq.so's HIP kernels.
@@ -14,13 +16,15 @@ from typing import Iterable, List, Optional, Sequence
 import torch
 
 from ._lib import (EXPORTS, GptqError, NotPositiveDefinite, QuantizeConfig, gptq_hessian_accumulate,  # noqa: F401
-                   gptq_dequant_matmul, gptq_dequant_workspace_size, gptq_hessian_workspace_size, gptq_pack,
-                   gptq_prepare_hinv, gptq_prepare_workspace_size, gptq_quantize_layer, gptq_workspace_size,
-                   library_path)
+                   gptq_dequant_matmul, gptq_dequant_matmul_ordered, gptq_dequant_order,
+                   gptq_dequant_ordered_workspace_size, gptq_dequant_workspace_size, gptq_hessian_workspace_size,
+                   gptq_pack, gptq_prepare_hinv, gptq_prepare_workspace_size, gptq_quantize_layer,
+                   gptq_workspace_size, library_path)
 
 __all__ = ["QuantizeConfig", "GptqError", "NotPositiveDefinite", "gptq_hessian_accumulate", "gptq_prepare_hinv",
            "gptq_quantize_layer", "gptq_pack", "gptq_hessian_workspace_size", "gptq_prepare_workspace_size",
-           "gptq_workspace_size", "gptq_dequant_matmul", "gptq_dequant_workspace_size", "solve_layer",
+           "gptq_workspace_size", "gptq_dequant_matmul", "gptq_dequant_workspace_size", "gptq_dequant_order",
+           "gptq_dequant_matmul_ordered", "gptq_dequant_ordered_workspace_size", "solve_layer",
            "solve_layers_shared", "library_path"]
 
 

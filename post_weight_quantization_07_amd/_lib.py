@@ -22,7 +22,8 @@ GPTQ_F32, GPTQ_BF16 = 0, 1
 EXPORTS = ("gptq_config_validate", "gptq_status_string", "gptq_hessian_workspace_size",
            "gptq_hessian_accumulate", "gptq_prepare_workspace_size", "gptq_prepare_hinv",
            "gptq_workspace_size", "gptq_quantize_layer", "gptq_pack", "gptq_dequant_workspace_size",
-           "gptq_dequant_matmul")
+           "gptq_dequant_matmul", "gptq_dequant_order", "gptq_dequant_ordered_workspace_size",
+           "gptq_dequant_matmul_ordered")
 
 
 class GptqError(RuntimeError):
@@ -67,6 +68,10 @@ def _lib():
             "gptq_dequant_workspace_size": (sz, [i64, i64, i64]),
             "gptq_dequant_matmul": (c_int32, [vp, c_int32, i64, i64, vp, vp, vp, vp, c_int32, i64, c_int32, vp, vp,
                                               sz, vp]),
+            "gptq_dequant_order": (c_int32, [vp, vp, c_int32, i64, i64, vp, vp, vp, vp]),
+            "gptq_dequant_ordered_workspace_size": (sz, [i64, i64, i64]),
+            "gptq_dequant_matmul_ordered": (c_int32, [vp, c_int32, i64, i64, vp, vp, vp, vp, vp, c_int32, i64,
+                                                      c_int32, vp, vp, sz, vp]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(lib, name)
@@ -278,4 +283,56 @@ def gptq_dequant_matmul(x: torch.Tensor, qweight: torch.Tensor, scales: torch.Te
                                       int(bits), d_out, n_groups, _ptr(y), _ptr(ws), 0 if ws is None else ws.numel(),
                                       _stream(stream)),
            "gptq_dequant_matmul")
+    return y
+
+
+def gptq_dequant_order(qweight: torch.Tensor, g_idx: torch.Tensor, bits: int, stream=None):
+    """An act-order layer put in group order for the dequantizing product:
+    returns (qweight_sorted, g_idx_sorted, order), order[j] = the original
+    input channel at sorted position j (a stable sort of the channels by
+    group), the codes repacked in that order."""
+    _dev(qweight, g_idx)
+    d_in = g_idx.shape[0]
+    d_out = qweight.shape[1]
+    if (g_idx.dim() != 1 or qweight.dim() != 2 or qweight.shape[0] * 32 != d_in * bits
+            or qweight.dtype != torch.int32 or g_idx.dtype != torch.int32):
+        raise ValueError("gptq_dequant_order: qweight / g_idx do not match bits")
+    q_out = torch.empty_like(qweight)
+    g_out = torch.empty_like(g_idx)
+    order = torch.empty_like(g_idx)
+    _check(_lib().gptq_dequant_order(_ptr(qweight.contiguous()), _ptr(g_idx.contiguous()), int(bits), d_in, d_out,
+                                     _ptr(q_out), _ptr(g_out), _ptr(order), _stream(stream)),
+           "gptq_dequant_order")
+    return q_out, g_out, order
+
+
+def gptq_dequant_ordered_workspace_size(m: int, d_in: int, d_out: int) -> int:
+    return int(_lib().gptq_dequant_ordered_workspace_size(m, d_in, d_out))
+
+
+def gptq_dequant_matmul_ordered(x: torch.Tensor, qweight: torch.Tensor, scales: torch.Tensor, zeros: torch.Tensor,
+                                g_idx: torch.Tensor, order: torch.Tensor, bits: int, y: Optional[torch.Tensor] = None,
+                                ws: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """gptq_dequant_matmul on a layer reordered by gptq_dequant_order; x is
+    given in the original channel order."""
+    _dev(x, qweight, scales, zeros, g_idx, order)
+    if x.dim() != 2 or not x.is_contiguous():
+        raise ValueError("gptq_dequant_matmul_ordered: x must be a contiguous [m, d_in] matrix")
+    m, d_in = x.shape
+    d_out = qweight.shape[1]
+    n_groups = scales.shape[0]
+    if (qweight.shape[0] * 32 != d_in * bits or scales.shape != (n_groups, d_out) or zeros.shape != (n_groups, d_out)
+            or g_idx.shape != (d_in,) or order.shape != (d_in,) or qweight.dtype != torch.int32
+            or scales.dtype != torch.float32 or zeros.dtype != torch.int32 or g_idx.dtype != torch.int32
+            or order.dtype != torch.int32):
+        raise ValueError("gptq_dequant_matmul_ordered: tensors do not match x and bits")
+    if y is None:
+        y = torch.empty((m, d_out), dtype=torch.float32, device=x.device)
+    if ws is None:
+        ws = _workspace(gptq_dequant_ordered_workspace_size(m, d_in, d_out), x.device)
+    _check(_lib().gptq_dequant_matmul_ordered(_ptr(x), _dtype_code(x), m, d_in, _ptr(qweight.contiguous()),
+                                              _ptr(scales.contiguous()), _ptr(zeros.contiguous()),
+                                              _ptr(g_idx.contiguous()), _ptr(order.contiguous()), int(bits), d_out,
+                                              n_groups, _ptr(y), _ptr(ws), ws.numel(), _stream(stream)),
+           "gptq_dequant_matmul_ordered")
     return y

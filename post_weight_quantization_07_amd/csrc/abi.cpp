@@ -148,4 +148,35 @@ gptq_status gptq_dequant_matmul(const void* x, gptq_dtype xt, int64_t m, int64_t
                                               n_groups, y, ws, static_cast<hipStream_t>(stream)));
 }
 
+gptq_status gptq_dequant_order(const int32_t* qweight, const int32_t* g_idx, int32_t bits, int64_t d_in,
+                               int64_t d_out, int32_t* qweight_out, int32_t* g_idx_out, int32_t* order,
+                               void* stream) {
+  if (!qweight || !g_idx || !qweight_out || !g_idx_out || !order) return GPTQ_ERR_INVALID_ARG;
+  if (d_out <= 0 || d_in <= 0 || d_in % 32 != 0 || !bits_ok(bits)) return GPTQ_ERR_INVALID_ARG;
+  if (d_in / 32 * bits * d_out * 4 >= (int64_t{1} << 31)) return GPTQ_ERR_INVALID_ARG;
+  return from_hip(gptq::dequant_order_launch(qweight, g_idx, bits, d_in, d_out, qweight_out, g_idx_out, order,
+                                             static_cast<hipStream_t>(stream)));
+}
+
+size_t gptq_dequant_ordered_workspace_size(int64_t m, int64_t d_in, int64_t d_out) {
+  if (m <= 0 || d_in <= 0 || d_out <= 0 || d_in % 32 != 0) return 0;
+  return gptq::dequant_ordered_workspace_bytes(m, d_in, d_out);
+}
+
+gptq_status gptq_dequant_matmul_ordered(const void* x, gptq_dtype xt, int64_t m, int64_t d_in,
+                                        const int32_t* qweight, const float* scales, const int32_t* zeros,
+                                        const int32_t* g_idx, const int32_t* order, int32_t bits, int64_t d_out,
+                                        int32_t n_groups, float* y, void* ws, size_t ws_bytes, void* stream) {
+  if (!x || !qweight || !scales || !zeros || !g_idx || !order || !y) return GPTQ_ERR_INVALID_ARG;
+  if (m <= 0 || d_out <= 0 || d_in <= 0 || d_in % 32 != 0 || n_groups <= 0) return GPTQ_ERR_INVALID_ARG;
+  if (!bits_ok(bits) || (xt != GPTQ_F32 && xt != GPTQ_BF16)) return GPTQ_ERR_INVALID_ARG;
+  if (d_in / 32 * bits * d_out * 4 >= (int64_t{1} << 31) || int64_t{n_groups} * d_out * 4 >= (int64_t{1} << 31))
+    return GPTQ_ERR_INVALID_ARG;
+  const size_t need = gptq::dequant_ordered_workspace_bytes(m, d_in, d_out);
+  if (!ws || ws_bytes < need || !aligned256(ws)) return GPTQ_ERR_WORKSPACE;
+  return from_hip(gptq::dequant_matmul_ordered_launch(x, xt == GPTQ_BF16, m, d_in, qweight, scales, zeros, g_idx,
+                                                      order, bits, d_out, n_groups, y, ws,
+                                                      static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

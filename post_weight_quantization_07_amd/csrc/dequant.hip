@@ -811,6 +811,78 @@ hipError_t dq_bits(const DqParams& p, hipStream_t st) {
   return valu_pass<BITS, 16>(p, st);
 }
 
+// ------------------------------------------------- act-order channel order
+
+// The stable rank of channel k by group: the number of channels of a smaller
+// group plus those of its own group before it.  Every thread compares its key
+// with all d_in keys, staged through LDS 256 at a time (a one-time step;
+// d_in^2 comparisons).
+__global__ __launch_bounds__(256) void order_rank_kernel(const int32_t* g_idx, int64_t d_in, int32_t* order,
+                                                         int32_t* g_out) {
+  __shared__ int32_t tile[256];
+  const int64_t k = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  const int32_t key = g_idx[std::min(k, d_in - 1)];
+  int64_t rank = 0;
+  for (int64_t t0 = 0; t0 < d_in; t0 += 256) {
+    __syncthreads();
+    if (t0 + threadIdx.x < d_in) tile[threadIdx.x] = g_idx[t0 + threadIdx.x];
+    __syncthreads();
+    const int n = static_cast<int>(std::min<int64_t>(256, d_in - t0));
+    for (int j = 0; j < n; ++j) {
+      const int32_t g2 = tile[j];
+      rank += (g2 < key || (g2 == key && t0 + j < k)) ? 1 : 0;
+    }
+  }
+  if (k < d_in) {
+    order[rank] = static_cast<int32_t>(k);
+    g_out[rank] = key;
+  }
+}
+
+// chunk c of the reordered layer (words c bits .. c bits + bits - 1 of column
+// n): the codes of channels order[32 c + j], j < 32, taken from the original
+// packed stream (code k at bits k bits .. k bits + bits - 1 of the column) and
+// packed in the same stream order
+template <int BITS>
+__global__ __launch_bounds__(256) void order_pack_kernel(const int32_t* qweight, const int32_t* order, int64_t d_in,
+                                                         int64_t d_out, int32_t* qout) {
+  const int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  const int64_t chunks = d_in / kChunk;
+  if (e >= chunks * d_out) return;
+  const int64_t c = e / d_out, n = e - c * d_out;
+  constexpr uint32_t mask = (1u << BITS) - 1u;
+  uint32_t words[BITS];
+#pragma unroll
+  for (int i = 0; i < BITS; ++i) words[i] = 0u;
+#pragma unroll
+  for (int j = 0; j < kChunk; ++j) {
+    const int64_t k = order[c * kChunk + j];
+    const int64_t b = k * BITS;
+    const int64_t w = b >> 5;
+    const int sh = static_cast<int>(b & 31);
+    uint32_t v = static_cast<uint32_t>(qweight[w * d_out + n]) >> sh;
+    if (sh + BITS > 32) v |= static_cast<uint32_t>(qweight[(w + 1) * d_out + n]) << (32 - sh);
+    v &= mask;
+    const int ob = j * BITS, ow = ob >> 5, os = ob & 31;
+    words[ow] |= v << os;
+    if (os + BITS > 32) words[ow + 1] |= v >> (32 - os);
+  }
+#pragma unroll
+  for (int i = 0; i < BITS; ++i) qout[(c * BITS + i) * d_out + n] = static_cast<int32_t>(words[i]);
+}
+
+// xo[t][j] = x[t][order[j]] (2- or 4-byte elements)
+template <typename E>
+__global__ __launch_bounds__(256) void order_gather_kernel(const E* x, int64_t m, int64_t d_in, const int32_t* order,
+                                                           E* xo) {
+  const int64_t total = m * d_in;
+  for (int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; e < total;
+       e += static_cast<int64_t>(gridDim.x) * 256) {
+    const int64_t t = e / d_in, j = e - t * d_in;
+    xo[e] = x[t * d_in + order[j]];
+  }
+}
+
 }  // namespace
 
 size_t dequant_workspace_bytes(int64_t m, int64_t d_in, int64_t d_out) {
@@ -854,6 +926,47 @@ hipError_t dequant_matmul_launch(const void* x, bool x_bf16, int64_t m, int64_t 
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
+}
+
+hipError_t dequant_order_launch(const int32_t* qweight, const int32_t* g_idx, int bits, int64_t d_in, int64_t d_out,
+                                int32_t* qweight_out, int32_t* g_idx_out, int32_t* order, hipStream_t st) {
+  order_rank_kernel<<<static_cast<unsigned>((d_in + 255) / 256), 256, 0, st>>>(g_idx, d_in, order, g_idx_out);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t total = d_in / kChunk * d_out;
+  const unsigned grid = static_cast<unsigned>((total + 255) / 256);
+  switch (bits) {
+    case 2: order_pack_kernel<2><<<grid, 256, 0, st>>>(qweight, order, d_in, d_out, qweight_out); break;
+    case 3: order_pack_kernel<3><<<grid, 256, 0, st>>>(qweight, order, d_in, d_out, qweight_out); break;
+    case 4: order_pack_kernel<4><<<grid, 256, 0, st>>>(qweight, order, d_in, d_out, qweight_out); break;
+    case 8: order_pack_kernel<8><<<grid, 256, 0, st>>>(qweight, order, d_in, d_out, qweight_out); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+size_t dequant_ordered_workspace_bytes(int64_t m, int64_t d_in, int64_t d_out) {
+  const size_t xb = (static_cast<size_t>(m) * d_in * sizeof(float) + 255) & ~static_cast<size_t>(255);
+  return xb + dequant_workspace_bytes(m, d_in, d_out);
+}
+
+hipError_t dequant_matmul_ordered_launch(const void* x, bool x_bf16, int64_t m, int64_t d_in, const int32_t* qweight,
+                                         const float* scales, const int32_t* zeros, const int32_t* g_idx,
+                                         const int32_t* order, int bits, int64_t d_out, int n_groups, float* y,
+                                         void* ws, hipStream_t st) {
+  const size_t xb = (static_cast<size_t>(m) * d_in * sizeof(float) + 255) & ~static_cast<size_t>(255);
+  const int64_t total = m * d_in;
+  const unsigned grid = static_cast<unsigned>(std::min<int64_t>((total + 255) / 256, 4096));
+  if (x_bf16)
+    order_gather_kernel<uint16_t><<<grid, 256, 0, st>>>(static_cast<const uint16_t*>(x), m, d_in, order,
+                                                        static_cast<uint16_t*>(ws));
+  else
+    order_gather_kernel<float><<<grid, 256, 0, st>>>(static_cast<const float*>(x), m, d_in, order,
+                                                     static_cast<float*>(ws));
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return dequant_matmul_launch(ws, x_bf16, m, d_in, qweight, scales, zeros, g_idx, bits, d_out, n_groups, y,
+                               static_cast<char*>(ws) + xb, st);
 }
 
 }  // namespace gptq

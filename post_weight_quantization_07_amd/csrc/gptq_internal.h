@@ -63,5 +63,12 @@ size_t dequant_workspace_bytes(int64_t m, int64_t d_in, int64_t d_out);
 hipError_t dequant_matmul_launch(const void* x, bool x_bf16, int64_t m, int64_t d_in, const int32_t* qweight,
                                  const float* scales, const int32_t* zeros, const int32_t* g_idx, int bits,
                                  int64_t d_out, int n_groups, float* y, void* ws, hipStream_t stream);
+hipError_t dequant_order_launch(const int32_t* qweight, const int32_t* g_idx, int bits, int64_t d_in, int64_t d_out,
+                                int32_t* qweight_out, int32_t* g_idx_out, int32_t* order, hipStream_t stream);
+size_t dequant_ordered_workspace_bytes(int64_t m, int64_t d_in, int64_t d_out);
+hipError_t dequant_matmul_ordered_launch(const void* x, bool x_bf16, int64_t m, int64_t d_in, const int32_t* qweight,
+                                         const float* scales, const int32_t* zeros, const int32_t* g_idx,
+                                         const int32_t* order, int bits, int64_t d_out, int n_groups, float* y,
+                                         void* ws, hipStream_t stream);
 
 }  // namespace gptq

@@ -137,3 +137,21 @@ def test_dequant_matmul_rejects_bad_arguments(lib):
     assert lib.gptq_dequant_matmul(fake, 0, 4, 4096, fake, fake, fake, fake, 4, 4096, 32, fake,
                                    ctypes.c_void_p((1 << 20) + 16), need, None) == 4
     assert lib.gptq_dequant_workspace_size(4, 48, 64) == 0
+
+
+def test_dequant_order_rejects_bad_arguments(lib):
+    fake = ctypes.c_void_p(4096)
+    ws = ctypes.c_void_p(1 << 20)
+    assert lib.gptq_dequant_order(fake, fake, 4, 48, 64, fake, fake, fake, None) == 1      # d_in % 32
+    assert lib.gptq_dequant_order(fake, fake, 5, 64, 64, fake, fake, fake, None) == 1      # bits
+    assert lib.gptq_dequant_order(None, fake, 4, 64, 64, fake, fake, fake, None) == 1
+    assert lib.gptq_dequant_order(fake, fake, 4, 64, 64, fake, fake, None, None) == 1
+    assert lib.gptq_dequant_order(fake, fake, 4, 65536, 65536, fake, fake, fake, None) == 1  # 2^31-byte qweight
+    need = lib.gptq_dequant_ordered_workspace_size(4, 4096, 4096)
+    assert need >= lib.gptq_dequant_workspace_size(4, 4096, 4096) + 4 * 4096 * 4
+    mm = lambda order, ws_, n: lib.gptq_dequant_matmul_ordered(fake, 1, 4, 4096, fake, fake, fake, fake, order, 4,
+                                                               4096, 32, fake, ws_, n, None)
+    assert mm(None, ws, need) == 1                                   # no order
+    assert mm(fake, ws, need - 1) == 4                               # workspace too small
+    assert mm(fake, ctypes.c_void_p((1 << 20) + 16), need) == 4      # misaligned
+    assert mm(fake, None, need) == 4

@@ -41,15 +41,20 @@ def _params(bits, group, desc, static, d_out, d_in, seed):
     return res
 
 
-def _check_tensors(G, qweight, scales, zeros, g_idx, bits, x_host, x_dtype, cols=None):
+def _check_tensors(G, qweight, scales, zeros, g_idx, bits, x_host, x_dtype, cols=None, ordered=False):
     """GPU product against the oracle's; with `cols`, only those output
-    columns are compared (the oracle dequantizes just them)."""
+    columns are compared (the oracle dequantizes just them).  With `ordered`,
+    the layer is first put in group order on the GPU (gptq_dequant_order) and
+    the product runs on it (gptq_dequant_matmul_ordered); the reference is
+    still the oracle's product of the original tensors."""
     x = to_dev(x_host, x_dtype)
     xe = host(x).astype(np.float64)  # the exact values the GPU reads
-    y = G.gptq_dequant_matmul(x, torch.from_numpy(np.ascontiguousarray(qweight)).to(dev()),
-                              torch.from_numpy(np.ascontiguousarray(scales)).to(dev()),
-                              torch.from_numpy(np.ascontiguousarray(zeros)).to(dev()),
-                              torch.from_numpy(np.ascontiguousarray(g_idx)).to(dev()), bits)
+    d = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev())
+    if ordered:
+        qs, gs, order = G.gptq_dequant_order(d(qweight), d(g_idx), bits)
+        y = G.gptq_dequant_matmul_ordered(x, qs, d(scales), d(zeros), gs, order, bits)
+    else:
+        y = G.gptq_dequant_matmul(x, d(qweight), d(scales), d(zeros), d(g_idx), bits)
     y = y.cpu().numpy().astype(np.float64)
     if cols is not None:
         qweight, scales, zeros, y = qweight[:, cols], scales[:, cols], zeros[:, cols], y[:, cols]
@@ -115,3 +120,50 @@ def test_dequant_matmul_full_layer(G, d_out, d_in, m):
     cols = np.unique(np.concatenate([np.arange(64), np.arange(d_out - 64, d_out), r.integers(0, d_out, 64)]))
     worst = _check_tensors(G, t["qweight"], t["scales"], t["zeros"], t["g_idx"], 4, x, "bf16", cols=cols)
     print(f"  worst error / bound {worst:.3e}", flush=True)
+
+
+# act-order layers put in group order once: the order is the stable sort of
+# the channels by group, g_idx follows it, and every reordered code is the
+# original code of its channel (bit-exact)
+@pytest.mark.parametrize("bits,group,d_out,d_in", [(3, 32, 96, 256), (4, 32, 70, 384), (2, 64, 130, 512),
+                                                   (8, 128, 33, 1024), (4, 128, 1000, 16480)])
+def test_dequant_order(G, bits, group, d_out, d_in):
+    banner(f"dequant order b{bits} g{group} {d_out}x{d_in}")
+    t = synth.quantized_layer(d_out, d_in, bits, group, True, seed=11 * bits)
+    dq = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev())
+    qs, gs, order = G.gptq_dequant_order(dq(t["qweight"]), dq(t["g_idx"]), bits)
+    order, gs, qs = order.cpu().numpy(), gs.cpu().numpy(), qs.cpu().numpy()
+    g = t["g_idx"]
+    assert np.array_equal(np.sort(order), np.arange(d_in))
+    assert np.array_equal(gs, g[order])
+    # sorted by group, channels of one group in increasing k: the stable order
+    assert np.all((gs[1:] > gs[:-1]) | ((gs[1:] == gs[:-1]) & (order[1:] > order[:-1])))
+    codes = O.unpack(t["qweight"], bits, d_in)
+    assert np.array_equal(O.unpack(qs, bits, d_in), codes[:, order])
+
+
+# the product on the reordered layer equals the oracle's product of the
+# original one, within the same bound (a permutation of the sum's terms)
+@pytest.mark.parametrize("bits,group,desc,static,d_out,d_in", [c for c in CASES if c[2]])
+@pytest.mark.parametrize("m", [1, 2, 16, 40])
+@pytest.mark.parametrize("x_dtype", ["f32", "bf16"])
+def test_dequant_matmul_ordered_small(G, bits, group, desc, static, d_out, d_in, m, x_dtype):
+    banner(f"dequant ordered b{bits} g{group} static={static} {d_out}x{d_in} m={m} x={x_dtype}")
+    res = _params(bits, group, desc, static, d_out, d_in, 7 * bits + d_out)
+    x = np.random.default_rng(m).standard_normal((m, d_in)).astype(np.float32)
+    sw = res.sweep
+    _check_tensors(G, res.qweight.astype(np.int32), sw.scales.astype(np.float32), sw.zeros.astype(np.int32),
+                   sw.g_idx.astype(np.int32), bits, x, x_dtype, ordered=True)
+
+
+@pytest.mark.parametrize("d_out,d_in,bits,group,m", [(1000, 16480, 4, 128, 1), (1000, 16480, 4, 128, 16),
+                                                     (1000, 16480, 3, 32, 2), (28672, 8192, 4, 128, 16)])
+def test_dequant_matmul_ordered_long(G, d_out, d_in, bits, group, m):
+    banner(f"dequant ordered long b{bits} g{group} {d_out}x{d_in} m={m}")
+    t = synth.quantized_layer(d_out, d_in, bits, group, True, seed=5)
+    x = synth.round_to_bf16(np.random.default_rng(200 + m).standard_normal((m, d_in)).astype(np.float32))
+    cols = None
+    if d_out > 4096:
+        r = np.random.default_rng(d_out)
+        cols = np.unique(np.concatenate([np.arange(64), np.arange(d_out - 64, d_out), r.integers(0, d_out, 64)]))
+    _check_tensors(G, t["qweight"], t["scales"], t["zeros"], t["g_idx"], bits, x, "bf16", cols=cols, ordered=True)
