@@ -7,12 +7,16 @@
 // dequantize inside the product.  At decode batch sizes the product is bound
 // by reading the packed weights (bits / 8 bytes per weight).
 //
-// K is walked in chunks of 32 codes (bits words per column), x and g_idx
-// staged in LDS per 16 chunks.  A chunk whose 32 columns share one group
-// (every case but act-order with dynamic groups) reads its scale and zero
-// point once; otherwise each code reads its own group's s and z.  Partial
-// sums are added in a fixed order, so the result does not depend on
-// scheduling.
+// K is walked in chunks of 32 codes (bits words per column), x staged in LDS
+// per 16 chunks.  Whether a chunk's 32 channels share one group is read from
+// g_idx by a ballot (lanes 0-31 hold one chunk's entries, 32-63 the next).  A
+// one-group chunk (every case but act-order with dynamic groups) reads its
+// scale and zero point once; otherwise each code reads its own group's s and
+// z.  Partial sums are added in a fixed order, so the result does not depend
+// on scheduling.  An act-order layer can be put in group order once (the
+// order_* kernels at the end: channels stably sorted by group, codes
+// repacked, x gathered in that order per call), which makes its chunks
+// one-group again.
 //
 // MFMA path (bf16 x, 3 tokens or more; v_mfma_f32_16x16x32_bf16): a wave
 // computes 16 tokens x 16 columns of one chunk.  Inside a chunk, codes 8 g ..
@@ -33,13 +37,15 @@
 // workgroup, so a packed word load is 64 consecutive int32 of one qweight
 // row); a lane converts its chunk's 32 codes with compile-time offsets and
 // accumulates MT tokens.  A one-group chunk adds s (sum_k x_k q_k - z sum_k
-// x_k), the chunk's sum of x formed once per workgroup, which takes the
-// subtraction of z out of the per-code work (two operations per code at 2, 4
-// and 8 bits: a byte-to-float conversion and an FMA); its rounding error is
-// bounded by the sum of |x_k| s (q_k + z) instead of |x_k| s |q_k - z|.  The
-// four waves take interleaved chunks of the workgroup's K range and are
-// summed through LDS in wave order; K is split over workgroups whose partial
-// products a second kernel adds in slice order.
+// x_k), the chunk's sum of x formed once per workgroup while x is staged,
+// which takes the subtraction of z out of the per-code work (two operations
+// per code at 2, 4 and 8 bits: a byte-to-float conversion and an FMA; with
+// bf16 x at 4 bits one v_dot2_f32_bf16 per two codes on the MFMA path's
+// 16 + q operands); its rounding error is bounded by the sum of
+// |x_k| s (q_k + z) instead of |x_k| s |q_k - z|.  The four waves take
+// interleaved chunks of the workgroup's K range and are summed through LDS in
+// wave order; K is split over workgroups whose partial products a second
+// kernel adds in slice order.
 #include "gptq_common.h"
 #include "gptq_internal.h"
 
