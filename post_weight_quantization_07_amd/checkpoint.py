@@ -85,3 +85,33 @@ def load_quantized(in_dir: str, device="cpu") -> Tuple[QuantizeConfig, Dict[str,
         if missing:
             raise ValueError(f"load_quantized: {name}: missing {sorted(missing)}")
     return cfg, layers
+
+
+def dequant_layer(r: Mapping[str, torch.Tensor], bits: int, device="cuda:0") -> Dict[str, torch.Tensor]:
+    """A loaded layer in the form the dequantizing product reads, on `device`:
+    int32 qweight, zeros and g_idx, fp32 scales (the stored float16 values).
+    When some 32-channel chunk spans several groups (act-order with dynamic
+    groups) the layer is put in group order once by gptq_dequant_order, which
+    replaces qweight and g_idx and adds `order`; apply it with dequant_apply."""
+    from ._lib import gptq_dequant_order
+    g_host = r["g_idx"].detach().to("cpu", torch.int32)
+    out = {"qweight": r["qweight"].to(device, torch.int32).contiguous(),
+           "scales": r["scales"].to(device, torch.float32).contiguous(),
+           "zeros": r["zeros"].to(device).round().to(torch.int32).contiguous(),
+           "g_idx": g_host.to(device).contiguous()}
+    if g_host.numel() % 32 != 0:
+        raise ValueError("dequant_layer: d_in must be a multiple of 32")
+    chunks = g_host.view(-1, 32)
+    if bool((chunks != chunks[:, :1]).any()):
+        out["qweight"], out["g_idx"], out["order"] = gptq_dequant_order(out["qweight"], out["g_idx"], bits)
+    return out
+
+
+def dequant_apply(x: torch.Tensor, layer: Mapping[str, torch.Tensor], bits: int, **kw) -> torch.Tensor:
+    """y = x W^T for a layer prepared by dequant_layer (x in the original
+    channel order)."""
+    from ._lib import gptq_dequant_matmul, gptq_dequant_matmul_ordered
+    if "order" in layer:
+        return gptq_dequant_matmul_ordered(x, layer["qweight"], layer["scales"], layer["zeros"], layer["g_idx"],
+                                           layer["order"], bits, **kw)
+    return gptq_dequant_matmul(x, layer["qweight"], layer["scales"], layer["zeros"], layer["g_idx"], bits, **kw)
