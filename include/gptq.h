@@ -173,11 +173,12 @@ gptq_status gptq_pack(const uint8_t* codes, int64_t d_out, int64_t d_in, int32_t
  * codes and dequantize inside the product).  Summed in fp32 in a fixed order
  * (deterministic).  32 consecutive k of one group are summed as
  * s (sum x q - z sum x), so the rounding error is bounded by
- * (d_in + 64) 2^-24 sum_k |x_k| s (q_k + z).  bf16 x with 3 or more tokens
- * runs on bf16 MFMA with the integer codes as the exact operand (at 4 bits
- * as 16 + q against 16 + z, so there the bound has q_k + z + 32); 32 k spread
- * over several groups (act-order) use s (q - z) split into two bf16 parts
- * there, so those products carry a relative error of about 2^-16.
+ * (d_in + 64) 2^-24 sum_k |x_k| s (q_k + z); with bf16 x and 4-bit codes the
+ * codes enter as 16 + q against 16 + z (v_dot2 for 1-2 tokens, bf16 MFMA for
+ * 3 or more), so there the bound has q_k + z + 32.  bf16 x with 3 or more
+ * tokens runs on bf16 MFMA with the integer codes as the exact operand; 32 k
+ * spread over several groups (act-order) use s (q - z) split into two bf16
+ * parts there, so those products carry a relative error of about 2^-16.
  *   x        [m, d_in] bf16 or fp32, row-major, m >= 1 (any count; passes of 16 rows)
  *   qweight  [d_in * bits / 32, d_out] int32 as written by gptq_pack
  *   scales   [n_groups, d_out] fp32, zeros [n_groups, d_out] int32, g_idx [d_in]
