@@ -4,8 +4,8 @@ W_hat is rebuilt from a quantized layer's stored tensors (qweight, scales,
 zeros, g_idx): those of an oracle solve for the small cases, seeded stand-ins
 (synth.quantized_layer) for the long and full-size ones.  The GPU sums in
 fp32.  A chunk of 32 codes that lies in one group is
-summed as s (sum_k x_k q_k - z sum_k x_k), at 4 bits on the MFMA path as
-s (sum_k x_k (16 + q_k) - (16 + z) sum_k x_k): every term and partial sum is
+summed as s (sum_k x_k q_k - z sum_k x_k), at 4 bits with bf16 x (dot and
+MFMA forms) as s (sum_k x_k (16 + q_k) - (16 + z) sum_k x_k): every term and partial sum is
 then bounded by |x_k| s (q_k + z + c), c = 32 at 4 bits and 0 otherwise (codes
 and zero points are non-negative), so the rigorous bound for a sum of d_in
 such terms, (d_in + 64) 2^-24 sum_k |x_k| s (q_k + z + c), is used; it also
