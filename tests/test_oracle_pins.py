@@ -573,3 +573,26 @@ def test_block_oracle_closed_forms():
     np.testing.assert_array_equal(st["out"], x0)
     np.testing.assert_allclose(np.sqrt(np.mean(B.rms_norm(x0, 0.0) ** 2, axis=1)), 1.0, rtol=1e-12)
     np.testing.assert_allclose(B.silu(np.array([0.0, 40.0, -40.0])), [0.0, 40.0, 0.0], atol=1e-15)
+
+
+def test_dequant_matmul_channel_order_invariance():
+    # the group-ordered product relies on y = x W^T being a sum over the
+    # input channels: putting the channels in another order (here the stable
+    # sort by group, as the one-time group order does), with x's columns, the
+    # codes and g_idx moved alike, leaves y unchanged up to the order of the
+    # fp64 sum; after the sort every 32 consecutive channels lie in one group
+    for bits, G, d_in in [(4, 32, 384), (3, 32, 256), (8, 128, 512)]:
+        t = synth.quantized_layer(40, d_in, bits, G, True, seed=9)
+        gi = t["g_idx"]
+        order = np.argsort(gi, kind="stable")
+        codes = O.unpack(t["qweight"], bits, d_in)
+        q_sorted = O.pack(codes[:, order], bits)
+        x = np.random.default_rng(bits).standard_normal((3, d_in))
+        y = O.dequant_matmul(x, t["qweight"], t["scales"], t["zeros"], gi, bits)
+        y_sorted = O.dequant_matmul(x[:, order], q_sorted, t["scales"], t["zeros"], gi[order], bits)
+        np.testing.assert_allclose(y_sorted, y, rtol=1e-12, atol=1e-12 * np.abs(y).max())
+        assert np.all(np.diff(gi[order]) >= 0)
+        chunks = gi[order].reshape(-1, 32)
+        assert np.all(chunks == chunks[:, :1])
+        # and the unsorted act-order layer does have chunks spanning groups
+        assert np.any(gi.reshape(-1, 32) != gi.reshape(-1, 32)[:, :1])
