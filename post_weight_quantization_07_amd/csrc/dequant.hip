@@ -71,6 +71,7 @@ struct DqParams {
   const float* scales;     // [n_groups, d_out]
   const int32_t* zeros;    // [n_groups, d_out]
   const int32_t* g_idx;    // [d_in]
+  const int32_t* xorder;   // VALU path: x channel of sorted position j is xorder[j] (null: j)
   uint32_t qbytes;         // bytes of qweight, < 2^31
   uint32_t gbytes;         // bytes of scales (and of zeros), < 2^31
   int chunks;              // d_in / 32
@@ -132,8 +133,22 @@ GPTQ_DEV void load_x(const DqParams& p, int64_t c0, int nc, int tid, XPieces<MT>
       const int t = e / row_pieces, k = std::min(e % row_pieces, live - 1);
       const int64_t row = p.m0 + std::min<int64_t>(t, p.m - 1);
       const int64_t col = c0 * kChunk + static_cast<int64_t>(k) * per;
-      xp.v[i] = p.xbf16 ? *reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(p.x) + row * p.ldx + col)
-                        : *reinterpret_cast<const u32x4_t*>(static_cast<const float*>(p.x) + row * p.ldx + col);
+      if (p.xorder) {  // group order: gather the piece's channels
+        if (p.xbf16) {
+          const uint16_t* xr = static_cast<const uint16_t*>(p.x) + row * p.ldx;
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            xp.v[i][q] = static_cast<uint32_t>(xr[p.xorder[col + 2 * q]]) |
+                         (static_cast<uint32_t>(xr[p.xorder[col + 2 * q + 1]]) << 16);
+        } else {
+          const uint32_t* xr = static_cast<const uint32_t*>(p.x) + row * p.ldx;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) xp.v[i][q] = xr[p.xorder[col + q]];
+        }
+      } else {
+        xp.v[i] = p.xbf16 ? *reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(p.x) + row * p.ldx + col)
+                          : *reinterpret_cast<const u32x4_t*>(static_cast<const float*>(p.x) + row * p.ldx + col);
+      }
     }
   }
 }
@@ -898,9 +913,22 @@ size_t dequant_workspace_bytes(int64_t m, int64_t d_in, int64_t d_out) {
   return (static_cast<size_t>(pl.ks) * kMaxMT * d_out * sizeof(float) + 255) & ~static_cast<size_t>(255);
 }
 
+namespace {
+hipError_t dequant_passes(const void* x, bool x_bf16, int64_t m, int64_t d_in, const int32_t* qweight,
+                          const float* scales, const int32_t* zeros, const int32_t* g_idx, const int32_t* xorder,
+                          int bits, int64_t d_out, int n_groups, float* y, void* ws, hipStream_t st);
+}  // namespace
+
 hipError_t dequant_matmul_launch(const void* x, bool x_bf16, int64_t m, int64_t d_in, const int32_t* qweight,
                                  const float* scales, const int32_t* zeros, const int32_t* g_idx, int bits,
                                  int64_t d_out, int n_groups, float* y, void* ws, hipStream_t st) {
+  return dequant_passes(x, x_bf16, m, d_in, qweight, scales, zeros, g_idx, nullptr, bits, d_out, n_groups, y, ws, st);
+}
+
+namespace {
+hipError_t dequant_passes(const void* x, bool x_bf16, int64_t m, int64_t d_in, const int32_t* qweight,
+                          const float* scales, const int32_t* zeros, const int32_t* g_idx, const int32_t* xorder,
+                          int bits, int64_t d_out, int n_groups, float* y, void* ws, hipStream_t st) {
   const int64_t qbytes = d_in / kChunk * bits * d_out * 4, gbytes = static_cast<int64_t>(n_groups) * d_out * 4;
   if (qbytes >= (int64_t{1} << 31) || gbytes >= (int64_t{1} << 31)) return hipErrorInvalidValue;
   DqParams p{};
@@ -915,6 +943,7 @@ hipError_t dequant_matmul_launch(const void* x, bool x_bf16, int64_t m, int64_t 
   p.scales = scales;
   p.zeros = zeros;
   p.g_idx = g_idx;
+  p.xorder = xorder;
   p.chunks = static_cast<int>(d_in / kChunk);
   p.y = y;
   p.part = static_cast<float*>(ws);
@@ -933,6 +962,7 @@ hipError_t dequant_matmul_launch(const void* x, bool x_bf16, int64_t m, int64_t 
   }
   return hipSuccess;
 }
+}  // namespace
 
 hipError_t dequant_order_launch(const int32_t* qweight, const int32_t* g_idx, int bits, int64_t d_in, int64_t d_out,
                                 int32_t* qweight_out, int32_t* g_idx_out, int32_t* order, hipStream_t st) {
@@ -961,6 +991,11 @@ hipError_t dequant_matmul_ordered_launch(const void* x, bool x_bf16, int64_t m, 
                                          const int32_t* order, int bits, int64_t d_out, int n_groups, float* y,
                                          void* ws, hipStream_t st) {
   const size_t xb = (static_cast<size_t>(m) * d_in * sizeof(float) + 255) & ~static_cast<size_t>(255);
+  // the VALU passes (fp32 x, or bf16 with 1-2 tokens) gather x's channels as
+  // they stage it; the MFMA passes read a gathered copy
+  if (!x_bf16 || m <= 2)
+    return dequant_passes(x, x_bf16, m, d_in, qweight, scales, zeros, g_idx, order, bits, d_out, n_groups, y,
+                          static_cast<char*>(ws) + xb, st);
   const int64_t total = m * d_in;
   const unsigned grid = static_cast<unsigned>(std::min<int64_t>((total + 255) / 256, 4096));
   if (x_bf16)
