@@ -120,9 +120,16 @@ gptq_status gptq_hessian_accumulate(float* S, int64_t d_in, const void* X, gptq_
  *   U = upper-triangular factor with (H_d[perm][:, perm])^-1 = U^T U
  *       (chapter 5, section 5.1.8: "Cholesky(inverse(H))"), [d_in, d_in] fp32,
  *       zeros below the diagonal.
- *   info_dev (device int32): 0 on success; k > 0 when the damped Hessian is
- *       not positive definite, k-1 being the first sweep position at which a
- *       pivot failed (U is then undefined).  Read it after synchronising.
+ *   info_dev (device int32): 0 on success; -1 when diag(H) holds a NaN or an
+ *       infinity (non-finite calibration inputs; perm is then still a
+ *       permutation, NaN channels last, and U is undefined); k > 0 when the
+ *       damped Hessian is not positive definite (an all-zero S, for one, gives
+ *       lambda = 0 and fails at once, k = d_in).  The factorization runs from the last sweep
+ *       position backwards and stops at its first failed pivot, so k - 1 is
+ *       the LARGEST sweep position p for which the trailing block
+ *       H_d[perm][:, perm][p:, p:] is not positive definite (as computed in
+ *       fp32); every trailing block past p is.  U is then undefined.  Read it
+ *       after synchronising.
  * n_total must be > 0.
  */
 size_t gptq_prepare_workspace_size(int64_t d_in);

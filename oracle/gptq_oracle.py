@@ -21,7 +21,9 @@ Every function follows the passage it names.  Page labels used below:
 Precision: fp64 throughout, inputs taken as their exact fp32/bf16 values.
 Where a floating-point value decides an integer (the group scale and zero
 point, the rounded code) the decision is taken in fp32, the precision of the
-HIP kernels, so both sides round the same quantity the same way.
+HIP kernels, so both sides round the same quantity the same way.  The pages
+fix no precision for it; `decision=np.float64` takes those decisions in fp64
+instead (used to measure how many codes the choice moves).
 
 Parity status: every function below is pinned by tests/test_oracle_*.py
 (closed forms, brute force, an independent naive-OBS route, hand-derived
@@ -146,38 +148,51 @@ def prepare(H: np.ndarray, damp_percent: float, desc_act: bool) -> Prepared:
 # [guide] 1.4: sym selects symmetric quantization)
 # ---------------------------------------------------------------------------
 
-def quant_params(v: np.ndarray, bits: int, sym: bool) -> tuple[np.ndarray, np.ndarray]:
+def quant_params(v: np.ndarray, bits: int, sym: bool, decision=np.float32, zraw: Optional[np.ndarray] = None
+                 ) -> tuple[np.ndarray, np.ndarray]:
     """Scale and zero point of one group for every row; v is rows x m.
 
     The range always contains 0 (lo = min(0, min v), hi = max(0, max v)).
     sym widens it to [-a, a] with a = max|v| and fixes the zero point at the
     middle code 2^(bits-1).  An all-zero group uses [-1, 1].  Decisions are
-    taken in fp32.  Returns (scale fp32, zero fp32-integral)."""
-    maxq = np.float32(2 ** bits - 1)
-    v32 = np.asarray(v, dtype=np.float64).astype(np.float32)
-    lo = np.minimum(v32.min(axis=1), np.float32(0))
-    hi = np.maximum(v32.max(axis=1), np.float32(0))
+    taken in `decision` precision (fp32 by default).  Returns (scale,
+    zero integral), both of that dtype; zraw, if given, receives the
+    pre-rounding zero point -lo / scale (asymmetric only)."""
+    f = decision
+    maxq = f(2 ** bits - 1)
+    vd = np.asarray(v, dtype=np.float64).astype(f)
+    lo = np.minimum(vd.min(axis=1), f(0))
+    hi = np.maximum(vd.max(axis=1), f(0))
     if sym:
         a = np.maximum(-lo, hi)
         lo, hi = -a, a
     deg = hi == lo
-    lo = np.where(deg, np.float32(-1), lo).astype(np.float32)
-    hi = np.where(deg, np.float32(1), hi).astype(np.float32)
-    scale = ((hi - lo) / maxq).astype(np.float32)
+    lo = np.where(deg, f(-1), lo).astype(f)
+    hi = np.where(deg, f(1), hi).astype(f)
+    scale = ((hi - lo) / maxq).astype(f)
     if sym:
-        zero = np.full(scale.shape, np.float32(2 ** (bits - 1)), dtype=np.float32)
+        zero = np.full(scale.shape, f(2 ** (bits - 1)), dtype=f)
     else:
-        zero = np.rint((-lo) / scale).astype(np.float32)
+        zr = ((-lo) / scale).astype(f)
+        if zraw is not None:
+            zraw[...] = zr
+        zero = np.rint(zr).astype(f)
     return scale, zero
 
 
-def quantize_values(w: np.ndarray, scale: np.ndarray, zero: np.ndarray, bits: int):
-    """code = clamp(rint(w / s) + z, 0, maxq) (decided in fp32);
-    dequantized value s * (code - z) (exact in fp64)."""
-    maxq = np.float32(2 ** bits - 1)
-    w32 = np.asarray(w, dtype=np.float64).astype(np.float32)
-    q = np.clip(np.rint(w32 / scale) + zero, np.float32(0), maxq).astype(np.float32)
+def quantize_values(w: np.ndarray, scale: np.ndarray, zero: np.ndarray, bits: int, want_v: bool = False):
+    """code = clamp(rint(w / s) + z, 0, maxq), decided in the precision of
+    `scale` (fp32 unless the caller chose fp64); dequantized value
+    s * (code - z) (exact in fp64).  want_v also returns the pre-rounding
+    value w / s + z of that precision, as fp64."""
+    f = scale.dtype.type
+    maxq = f(2 ** bits - 1)
+    wd = np.asarray(w, dtype=np.float64).astype(f)
+    v = (wd / scale).astype(f) + zero
+    q = np.clip(np.rint(wd / scale) + zero, f(0), maxq).astype(f)
     what = scale.astype(np.float64) * (q.astype(np.float64) - zero.astype(np.float64))
+    if want_v:
+        return q.astype(np.int64), what, v.astype(np.float64)
     return q.astype(np.int64), what
 
 
@@ -196,22 +211,24 @@ class SweepResult:
     err: np.ndarray        # fp64  [d_out, d_in], normalised errors, sweep order
     row_loss: np.ndarray   # fp64  [d_out], sum of err^2 per row
     ties: int = 0          # decisions taken from `follow` at float ties
+    vals: Optional[np.ndarray] = None  # [d_out, d_in] pre-rounding w / s + z, sweep order (record_v)
+    zvals: Optional[np.ndarray] = None  # [n_groups, d_out] pre-rounding -lo / s of dynamic asym zeros (record_v)
 
 
 def _n_groups(d_in: int, group_size: int) -> int:
     return 1 if group_size == -1 else -(-d_in // group_size)
 
 
-def _static_params(W: np.ndarray, bits: int, group_size: int, sym: bool):
+def _static_params(W: np.ndarray, bits: int, group_size: int, sym: bool, decision=np.float32):
     """Group parameters fixed before the sweep from the un-updated weights of
     each original group (static_groups, [guide] 1.4 / [olmo] 三)."""
     d_out, d_in = W.shape
     ng = _n_groups(d_in, group_size)
-    scales = np.zeros((ng, d_out), dtype=np.float32)
-    zeros = np.zeros((ng, d_out), dtype=np.float32)
+    scales = np.zeros((ng, d_out), dtype=decision)
+    zeros = np.zeros((ng, d_out), dtype=decision)
     for g in range(ng):
         sl = slice(0, d_in) if group_size == -1 else slice(g * group_size, min(d_in, (g + 1) * group_size))
-        scales[g], zeros[g] = quant_params(W[:, sl], bits, sym)
+        scales[g], zeros[g] = quant_params(W[:, sl], bits, sym, decision)
     return scales, zeros
 
 
@@ -232,7 +249,7 @@ def _group_plan(d_in: int, perm: np.ndarray, group_size: int, static_groups: boo
 def quantize_layer(W: np.ndarray, U: np.ndarray, perm: np.ndarray, bits: int, group_size: int,
                    sym: bool, static_groups: bool, blocksize: Optional[int] = 128,
                    rows: Optional[Sequence[int]] = None, follow: Optional[np.ndarray] = None,
-                   tie_tol: float = 0.0) -> SweepResult:
+                   tie_tol: float = 0.0, record_v: bool = False, decision=np.float32) -> SweepResult:
     """GPTQ column sweep.
 
     blocksize=None runs the plain form: after column i is quantized its
@@ -252,7 +269,11 @@ def quantize_layer(W: np.ndarray, U: np.ndarray, perm: np.ndarray, bits: int, gr
     quantization steps) of the rounding boundary between them, both codes are
     correct up to rounding of the running weights; the sweep then takes the
     followed code and continues from it (counted in `ties`).  Every other
-    decision is this sweep's own."""
+    decision is this sweep's own.
+
+    record_v keeps every decision's pre-rounding value w / s + z (sweep
+    order) in `vals`; decision=np.float64 decides scales, zeros and codes in
+    fp64 instead of fp32."""
     W = np.asarray(W, dtype=np.float64)
     if rows is not None:
         W = W[np.asarray(rows)]
@@ -268,11 +289,11 @@ def quantize_layer(W: np.ndarray, U: np.ndarray, perm: np.ndarray, bits: int, gr
     ng = _n_groups(d_in, G)
     gpos, g_idx, dynamic = _group_plan(d_in, perm, G, static_groups)
     if dynamic:
-        scales = np.zeros((ng, d_out), dtype=np.float32)
-        zeros = np.zeros((ng, d_out), dtype=np.float32)
+        scales = np.zeros((ng, d_out), dtype=decision)
+        zeros = np.zeros((ng, d_out), dtype=decision)
     else:
         # G = -1 uses the whole (un-updated) row; static uses original groups
-        scales, zeros = _static_params(W, bits, G, sym)
+        scales, zeros = _static_params(W, bits, G, sym, decision)
 
     Wp = W[:, perm].copy()
     follow_p = None if follow is None else np.asarray(follow, dtype=np.int64)[:, perm]
@@ -280,15 +301,24 @@ def quantize_layer(W: np.ndarray, U: np.ndarray, perm: np.ndarray, bits: int, gr
     codes_p = np.zeros((d_out, d_in), dtype=np.int64)
     Q_p = np.zeros((d_out, d_in), dtype=np.float64)
     Err = np.zeros((d_out, d_in), dtype=np.float64)
+    vals = np.zeros((d_out, d_in), dtype=np.float64) if record_v else None
+    zvals = np.full((ng, d_out), np.nan) if record_v else None
+
+    def dyn_params(i: int, grp: np.ndarray):
+        zr = np.full(d_out, np.nan) if (zvals is not None and not sym) else None
+        scales[gpos[i]], zeros[gpos[i]] = quant_params(grp, bits, sym, decision, zr)
+        if zr is not None:
+            zvals[gpos[i]] = zr
 
     def step(i: int, cur: np.ndarray, col: int):
         """Quantize sweep column i held in cur[:, col]; return err column."""
         g = gpos[i]
         w = cur[:, col]
-        q, what = quantize_values(w, scales[g], zeros[g], bits)
+        q, what, v = quantize_values(w, scales[g], zeros[g], bits, want_v=True)
+        if vals is not None:
+            vals[:, i] = v
         if follow_p is not None:
             f = follow_p[:, i]
-            v = (w.astype(np.float32) / scales[g] + zeros[g]).astype(np.float64)
             tie = (np.abs(q - f) == 1) & (np.abs(v - (np.minimum(q, f) + 0.5)) <= tie_tol)
             if np.any(tie):
                 q = np.where(tie, f, q)
@@ -302,7 +332,7 @@ def quantize_layer(W: np.ndarray, U: np.ndarray, perm: np.ndarray, bits: int, gr
     if blocksize is None:
         for i in range(d_in):
             if dynamic and i % G == 0:
-                scales[gpos[i]], zeros[gpos[i]] = quant_params(Wp[:, i:i + G], bits, sym)
+                dyn_params(i, Wp[:, i:i + G])
             err = step(i, Wp, i)
             Err[:, i] = err
             Wp[:, i + 1:] -= np.outer(err, U[i, i + 1:])
@@ -318,7 +348,7 @@ def quantize_layer(W: np.ndarray, U: np.ndarray, perm: np.ndarray, bits: int, gr
                         grp = Wb[:, c:c + G]
                     else:   # group spans later blocks; Wb is untouched at a block start
                         grp = Wp[:, i:i + G]
-                    scales[gpos[i]], zeros[gpos[i]] = quant_params(grp, bits, sym)
+                    dyn_params(i, grp)
                 err = step(i, Wb, c)
                 Err[:, i] = err
                 Wb[:, c + 1:] -= np.outer(err, U[i, i + 1:b1])
@@ -331,7 +361,7 @@ def quantize_layer(W: np.ndarray, U: np.ndarray, perm: np.ndarray, bits: int, gr
     codes[:, perm] = codes_p
     Q[:, perm] = Q_p
     return SweepResult(codes=codes, Q=Q, scales=scales, zeros=zeros.astype(np.int64), g_idx=g_idx,
-                       err=Err, row_loss=np.sum(Err * Err, axis=1), ties=n_ties[0])
+                       err=Err, row_loss=np.sum(Err * Err, axis=1), ties=n_ties[0], vals=vals, zvals=zvals)
 
 
 def naive_obq(W: np.ndarray, Hp: np.ndarray, perm: np.ndarray, bits: int, group_size: int,

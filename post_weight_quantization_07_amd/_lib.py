@@ -36,6 +36,10 @@ class NotPositiveDefinite(GptqError):
     """The damped Hessian failed a Cholesky pivot; retry with a larger damp_percent."""
 
 
+class NonFiniteHessian(GptqError):
+    """diag(H) holds a NaN or an infinity: the calibration inputs are not finite."""
+
+
 class _CConfig(ctypes.Structure):
     _fields_ = [("bits", c_int32), ("group_size", c_int32), ("damp_percent", c_float),
                 ("desc_act", c_int32), ("static_groups", c_int32), ("sym", c_int32),
@@ -208,8 +212,12 @@ def gptq_prepare_hinv(S: torch.Tensor, n_total: int, cfg: QuantizeConfig, U: Opt
                                     _ptr(info), _ptr(ws), ws.numel(), _stream(stream)), "gptq_prepare_hinv")
     if check:
         k = int(info.item())
+        if k == -1:
+            raise NonFiniteHessian(GPTQ_ERR_NOT_SPD, "gptq_prepare_hinv: diag(H) is not finite (NaN or infinity "
+                                   "in the calibration inputs)")
         if k != 0:
-            raise NotPositiveDefinite(GPTQ_ERR_NOT_SPD, f"gptq_prepare_hinv: pivot failed at sweep position {k - 1}")
+            raise NotPositiveDefinite(GPTQ_ERR_NOT_SPD, "gptq_prepare_hinv: the damped Hessian's trailing block is "
+                                      f"not positive definite from sweep position {k - 1}")
     return U, perm, info
 
 

@@ -26,7 +26,7 @@ hipError_t hessian_launch(const HessPlan& plan, float* S, int64_t d_in, const vo
 constexpr int kPanel = 128;  // Cholesky panel / diagonal block width
 
 struct PrepLayout {
-  size_t off_hr, off_t, off_diag, off_lambda, ws_bytes;
+  size_t off_hr, off_t, off_diag, off_dinv, off_lambda, ws_bytes;
 };
 PrepLayout prepare_layout(int64_t d_in);
 hipError_t prepare_launch(float* S_to_H, int64_t d_in, int64_t n_total, float damp, bool desc_act,

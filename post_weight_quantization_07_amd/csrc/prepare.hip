@@ -19,8 +19,10 @@
 //   panels     right-looking blocked Cholesky of Hr, 128-column panels:
 //                panel kernel: factor and invert the 128x128 diagonal block in
 //                LDS, solve the panel rows below as a product with that
-//                inverse, leave the inverse in place of the block;
+//                inverse, store the inverse in a strip of its own (Dinv);
 //                trailing update Hr[k+128:, k+128:] -= P P^T on MFMA (lower tiles)
+//   place      every inverted diagonal block from Dinv into Hr (one launch
+//              after the last panel)
 //   trtri      recursive doubling: for neighbouring inverted blocks A^-1, C^-1
 //              and the factor block L21 below A, M21 = -C^-1 (L21 A^-1)
 //   reverse    U[i][j] = M[n-1-i][n-1-j] for j >= i, 0 below the diagonal
@@ -45,7 +47,9 @@ __global__ void finalize_kernel(float* S, int64_t n, float scale, float* diag) {
   }
 }
 
-// lambda = damp * mean(diag): fixed-order tree over 1024 threads.
+// lambda = damp * mean(diag): fixed-order tree over 1024 threads.  A diagonal
+// that is not finite (NaN or an infinity in X) sets info = -1; the panels then
+// leave info alone (they only replace a 0).
 __global__ __launch_bounds__(1024) void lambda_kernel(const float* diag, int64_t n, float damp,
                                                       float* lambda_out, int32_t* info) {
   __shared__ double part[1024];
@@ -59,11 +63,15 @@ __global__ __launch_bounds__(1024) void lambda_kernel(const float* diag, int64_t
   }
   if (threadIdx.x == 0) {
     lambda_out[0] = damp * static_cast<float>(part[0] / static_cast<double>(n));
-    info[0] = 0;
+    info[0] = isfinite(part[0]) ? 0 : -1;
   }
 }
 
 // perm[rank(i)] = i with rank(i) = #{j : d_j > d_i} + #{j < i : d_j == d_i}.
+// A NaN key counts as -infinity (last, ties by index), so the ranks are always
+// a permutation of 0 .. n-1 and every perm entry is written.
+GPTQ_DEV float order_key(float d) { return (d == d) ? d : -INFINITY; }
+
 __global__ __launch_bounds__(256) void order_kernel(const float* diag, int64_t n, int desc_act,
                                                     int32_t* perm) {
   __shared__ float tile[1024];
@@ -72,11 +80,11 @@ __global__ __launch_bounds__(256) void order_kernel(const float* diag, int64_t n
     if (i < n) perm[i] = static_cast<int32_t>(i);
     return;
   }
-  const float di = (i < n) ? diag[i] : 0.f;
+  const float di = (i < n) ? order_key(diag[i]) : 0.f;
   int64_t rank = 0;
   for (int64_t base = 0; base < n; base += 1024) {
     __syncthreads();
-    for (int t = threadIdx.x; t < 1024; t += 256) tile[t] = (base + t < n) ? diag[base + t] : 0.f;
+    for (int t = threadIdx.x; t < 1024; t += 256) tile[t] = (base + t < n) ? order_key(diag[base + t]) : 0.f;
     __syncthreads();
     const int lim = static_cast<int>(std::min<int64_t>(1024, n - base));
     for (int t = 0; t < lim; ++t) {
@@ -113,9 +121,13 @@ __global__ void gather_kernel(const float* H, int64_t n, const int32_t* perm, co
 //   L11 = chol(A11);  L21 = A21 L11^-T;  L22 = chol(A22 - L21 L21^T)
 //   M = L^-1 = (L11^-1 0 ; -L22^-1 L21 L11^-1  L22^-1)
 // The triangular solve of the rows below the block against L is then a
-// product with M: X = P M^T, 32 rows per pass.  Workgroup 0 only stores M as
-// the diagonal block of the factor's inverse, which the recursive-doubling
-// inverse uses as its first level; workgroups 1.. solve the rows.
+// product with M: X = P M^T, 32 rows per pass.  Workgroup 0 only stores M, the
+// diagonal block of the factor's inverse that the recursive-doubling inverse
+// uses as its first level, into the strip Dinv (block k / 128, row pitch 128);
+// workgroups 1.. solve the rows.  Nothing in the launch writes the diagonal
+// block of Hr that every workgroup reads at its start, so the result does not
+// depend on how many workgroups are resident at once (the grid may exceed the
+// CUs available to it, one workgroup per CU by LDS).
 constexpr int kLP = kNB + 4;    // LDS row pitch (floats)
 constexpr int kChunk = 32;      // panel rows solved per pass
 constexpr int kMaxPanelWG = 256;
@@ -485,7 +497,8 @@ GPTQ_DEV void solve_rows(Blk L, Blk M, int lane, f32x4_t (&acc)[4]) {
   }
 }
 
-__global__ __launch_bounds__(256, 1) void panel_kernel(float* Hr, int64_t n, int64_t k, int32_t* info) {
+__global__ __launch_bounds__(256, 1) void panel_kernel(float* Hr, int64_t n, int64_t k, int32_t* info,
+                                                         float* Dinv) {
   __shared__ __attribute__((aligned(16))) float L[kNB][kLP];
   __shared__ __attribute__((aligned(16))) float M[kNB][kLP];
   __shared__ __attribute__((aligned(16))) float Tb[kNB / 2][kTP];
@@ -627,24 +640,18 @@ __global__ __launch_bounds__(256, 1) void panel_kernel(float* Hr, int64_t n, int
   }
   __syncthreads();
 
-  // M = L^-1 (lower; the blocks above the diagonal are never read)
+  // M = L^-1 (lower, zeros above the diagonal) into block k / 128 of Dinv;
+  // past a ragged end the block holds the inverse of the identity padding,
+  // which the placement skips
   if (blockIdx.x == 0) {
-    if (vec) {
+    float* dst = Dinv + (k / kNB) * (kNB * kNB);
 #pragma unroll
-      for (int i = 0; i < kNB / 8; ++i) {
-        const int r = 8 * i + vr;
-        f32x4_t x = *reinterpret_cast<const f32x4_t*>(&M[r][vc]);
+    for (int i = 0; i < kNB / 8; ++i) {
+      const int r = 8 * i + vr;
+      f32x4_t x = *reinterpret_cast<const f32x4_t*>(&M[r][vc]);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) x[e] = (vc + e <= r) ? x[e] : 0.f;
-        *reinterpret_cast<f32x4_t*>(Hr + (k + r) * n + k + vc) = x;
-      }
-    } else {
-#pragma unroll 16
-      for (int i = 0; i < kNB * kNB / 256; ++i) {
-        const int r = 2 * i + sr;
-        const float x = (sc <= r) ? M[r][sc] : 0.f;
-        if (r < nb && sc < nb) Hr[(k + r) * n + k + sc] = x;
-      }
+      for (int e = 0; e < 4; ++e) x[e] = (vc + e <= r) ? x[e] : 0.f;
+      *reinterpret_cast<f32x4_t*>(dst + r * kNB + vc) = x;
     }
     return;
   }
@@ -675,6 +682,19 @@ __global__ __launch_bounds__(256, 1) void panel_kernel(float* Hr, int64_t n, int
   }
 }
 
+// Hr's diagonal blocks <- the inverted blocks of Dinv (the first level of the
+// factor's inverse), rows and columns past a ragged end left alone.
+__global__ void place_dinv_kernel(const float* Dinv, int64_t n, float* Hr) {
+  const int64_t nblk = (n + kNB - 1) / kNB;
+  const int64_t total = nblk * kNB * kNB;
+  for (int64_t e = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; e < total;
+       e += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    const int64_t b = e / (kNB * kNB), r = (e / kNB) % kNB, c = e % kNB;
+    const int64_t row = b * kNB + r, col = b * kNB + c;
+    if (row < n && col < n) Hr[row * n + col] = Dinv[e];
+  }
+}
+
 __global__ void reverse_kernel(const float* M, int64_t n, float* U) {
   const int64_t total = n * n;
   for (int64_t e = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; e < total;
@@ -700,6 +720,8 @@ PrepLayout prepare_layout(int64_t d) {
   off += up(static_cast<size_t>(d) * d / 4 * sizeof(float) + 64 * 64 * sizeof(float));
   L.off_diag = off;
   off += up(static_cast<size_t>(d) * sizeof(float));
+  L.off_dinv = off;  // inverted 128x128 diagonal blocks, one per panel
+  off += up(static_cast<size_t>((d + kNB - 1) / kNB) * kNB * kNB * sizeof(float));
   L.off_lambda = off;
   off += 256;
   L.ws_bytes = off;
@@ -721,6 +743,7 @@ hipError_t prepare_launch(float* S, int64_t n, int64_t n_total, float damp, bool
   float* T = reinterpret_cast<float*>(w + lay.off_t);
   float* diag = reinterpret_cast<float*>(w + lay.off_diag);
   float* lam = reinterpret_cast<float*>(w + lay.off_lambda);
+  float* Dinv = reinterpret_cast<float*>(w + lay.off_dinv);
   const int64_t nn = n * n;
 
   finalize_kernel<<<grid_for(nn), 256, 0, st>>>(S, n, static_cast<float>(2.0 / static_cast<double>(n_total)), diag);
@@ -753,7 +776,7 @@ hipError_t prepare_launch(float* S, int64_t n, int64_t n_total, float damp, bool
       }
       const int64_t below = std::max<int64_t>(0, n - kh - kNB);
       const int blocks = 1 + static_cast<int>(std::min<int64_t>((below + kChunk - 1) / kChunk, kMaxPanelWG - 1));
-      panel_kernel<<<blocks, 256, 0, st>>>(Hr, n, kh, info);
+      panel_kernel<<<blocks, 256, 0, st>>>(Hr, n, kh, info, Dinv);
       GPTQ_TRY(hipGetLastError());
     }
     const int64_t ke = std::min<int64_t>(n, k + kNB * kPanelGroup);
@@ -766,6 +789,8 @@ hipError_t prepare_launch(float* S, int64_t n, int64_t n_total, float damp, bool
   }
   // triangular inverse by recursive doubling over the inverted diagonal blocks
   const int64_t nblk = (n + kNB - 1) / kNB;
+  place_dinv_kernel<<<grid_for(nblk * kNB * kNB), 256, 0, st>>>(Dinv, n, Hr);
+  GPTQ_TRY(hipGetLastError());
   for (int64_t h = 1; h < nblk; h *= 2) {
     const int64_t w_el = h * kNB;           // width of A (elements)
     const int64_t groups_full = n / (2 * w_el);

@@ -1,21 +1,30 @@
 """Parity on every layer of the five layer-solve configurations, at full size.
 
 Configurations 1 and 2 (d_in <= 3072, N <= 16384) are small enough for the
-whole fp64 oracle solve: H, the ordering, the codes of a sweep that uses the
-GPU's factor, the reconstruction error against the oracle's own solve, pack.
+whole fp64 oracle solve: H, the ordering, the factor, the codes, the
+reconstruction error against the oracle's own solve (its own H and factor,
+no input from the GPU), pack.
 
 Configurations 3-5 run the GPU path in the launch configuration bench.py
 times (one accumulate call over all N tokens, prepare, quantize, pack) and
 check what the oracle can compute one by one or what holds at any size:
 - H: a block of sampled channels (all their pairs, diagonal included) in fp64;
 - ordering and g_idx bit-exact (stable sort of the GPU's own fp32 diagonal);
-- the factor: upper triangular, and the two-sided residual
-  || U H_p U^T e_j - e_j || on sampled sweep positions (U H_p U^T = I exactly);
-  on config 3's q_proj also the oracle's fp64 factor of the GPU's H;
-- the sweep on sampled output rows (rows are independent given U): codes
-  (the oracle follows the GPU's decision only at float ties, where both codes
-  are correct, so one tie does not turn the rest of its row into mismatches),
-  reconstruction error through H, pack words.
+- the factor: upper triangular; the two-sided residual
+  || U H_p U^T e_j - e_j || (U H_p U^T = I exactly) at one sampled position of
+  every 128-column panel; for d_in <= 11008 also the oracle's own fp64 factor
+  of the GPU's H, element by element;
+- the sweep on sampled output rows (rows are independent given U):
+  * independent: the oracle's sweep with the GPU's factor, every decision its
+    own.  Each row matches exactly or its first differing decision is a float
+    tie (both codes correct to working precision); the raw fraction of
+    differing codes is printed, and the reconstruction error must lie within
+    1% of this run's;
+  * with the oracle's own fp64 factor (d_in <= 11008): raw mismatch printed,
+    reconstruction within 1%;
+  * followed (diagnostic): the oracle takes the GPU's code at float ties only;
+    the codes still differing and the ties taken must each stay <= 0.1%;
+  * pack words bit-exact.
 X is generated chunk by chunk from the seeded generators and streamed to the
 device; only the sampled channels stay on the host.
 """
@@ -25,7 +34,7 @@ import torch
 
 import oracle as O
 import synth
-from gpu_helpers import banner, dev, rel_fro, sweep_parity, to_dev
+from gpu_helpers import banner, dev, independent_parity, rel_fro, sweep_parity, to_dev
 
 pytestmark = pytest.mark.gpu
 EPS32 = 2.0 ** -24
@@ -66,21 +75,35 @@ def test_config_whole_oracle(G, cfg, name):
     res = O.solve_layer(W, [X], **qk)
     H_g = out["H"].cpu().numpy().astype(np.float64)
     assert rel_fro(H_g, res.prep.H) <= 1e-5
+    dg = np.sqrt(np.outer(np.diag(res.prep.H), np.diag(res.prep.H)))
+    assert np.max(np.abs(H_g - res.prep.H) / dg) <= 1e-5
     perm_g = out["perm"].cpu().numpy().astype(np.int64)
     np.testing.assert_array_equal(perm_g, O.act_order(H_g) if L.desc_act else np.arange(L.d_in))
-    # the sweep with the GPU's factor: codes decided in fp32 on both sides,
-    # float ties followed
+    # the factor against the oracle's own (its fp64 H)
     U_g = out["U"].cpu().numpy().astype(np.float64)
+    u_err = rel_fro(U_g, res.prep.U)
     codes = out["codes"].cpu().numpy().astype(np.int64)
-    ref, mism, ties = sweep_parity(W, U_g, perm_g, L, codes)
-    np.testing.assert_array_equal(out["g_idx"].cpu().numpy(), ref.g_idx)
-    # reconstruction error against the oracle's own solve, through X
-    e_g = O.recon_error(W, out["Q"].cpu().numpy(), [X])
+    zeros_g = out["zeros"].cpu().numpy()
+    # independent: the oracle's sweep with the GPU's factor, every decision its own
+    ind, raw_s, rows_s, worst = independent_parity(W, U_g, perm_g, L, codes, zeros_g)
+    np.testing.assert_array_equal(out["g_idx"].cpu().numpy(), ind.g_idx)
+    # followed (diagnostic)
+    _, mism, ties = sweep_parity(W, U_g, perm_g, L, codes)
+    # reconstruction error through X against the independent sweep and the
+    # oracle's whole solve (its own H and factor, no GPU input)
+    Q_g = out["Q"].cpu().numpy()
+    e_g = O.recon_error(W, Q_g, [X])
+    e_i = O.recon_error(W, ind.Q, [X])
     e_r = O.recon_error(W, res.sweep.Q, [X])
-    print(f"  code mismatch {mism:.4%} (float ties followed {ties:.4%}); recon gpu/oracle {e_g / e_r:.5f}",
-          flush=True)
+    raw = float(np.mean(codes != res.sweep.codes))
+    rows_r = int(np.sum(np.any(codes != res.sweep.codes, axis=1)))
+    print(f"  U rel err vs oracle {u_err:.3e}; raw code mismatch vs oracle solve {raw:.4%} ({rows_r} of {L.d_out} "
+          f"rows), vs oracle sweep on the GPU factor {raw_s:.4%} ({rows_s} rows, first divergences <= {worst:.2e} "
+          f"steps from a boundary); followed: {mism:.4%} differing, {ties:.4%} ties; recon gpu/oracle solve "
+          f"{e_g / e_r:.6f}, gpu/independent sweep {e_g / e_i:.6f}", flush=True)
+    assert u_err <= 1e-5
     assert mism <= 1e-3 and ties <= 1e-3
-    assert abs(e_g / e_r - 1.0) <= 0.01
+    assert abs(e_g / e_r - 1.0) <= 0.01 and abs(e_g / e_i - 1.0) <= 0.01
     np.testing.assert_array_equal(out["qweight"].cpu().numpy(), O.pack(codes, L.bits))
 
 
@@ -100,22 +123,25 @@ def _stream_x(layer, cols):
     return X, sub
 
 
-def _two_sided_residual(U, hp_matvec, js):
-    """|| U H_p U^T e_j - e_j || for sweep positions js (fp64)."""
-    out = []
-    for j in js:
-        y = U[j].astype(np.float64)              # U^T e_j = row j of U
-        w = _rows_matvec(U, hp_matvec(y))
-        w[j] -= 1.0
-        out.append(float(np.linalg.norm(w)))
-    return np.array(out)
+def _two_sided_residual(U, hp_matmul, js):
+    """|| U H_p U^T e_j - e_j || for sweep positions js (fp64, all at once)."""
+    Y = U[js].astype(np.float64).T               # U^T e_j = row j of U, one column per j
+    Wm = _rows_matmul(U, hp_matmul(Y))
+    Wm[js, np.arange(len(js))] -= 1.0
+    return np.linalg.norm(Wm, axis=0)
 
 
-def _rows_matvec(M, v, block=2048):
-    out = np.empty(M.shape[0])
+def _rows_matmul(M, V, block=2048):
+    """M @ V in fp64 with M (fp32, possibly large) converted in row blocks."""
+    out = np.empty((M.shape[0],) + V.shape[1:])
     for a in range(0, M.shape[0], block):
-        out[a:a + block] = M[a:a + block].astype(np.float64) @ v
+        out[a:a + block] = M[a:a + block].astype(np.float64) @ V
     return out
+
+
+def _panel_positions(d, rng):
+    """One sampled sweep position inside every 128-column panel."""
+    return np.array([b + int(rng.integers(0, min(128, d - b))) for b in range(0, d, 128)])
 
 
 @pytest.mark.timeout(900)
@@ -158,43 +184,58 @@ def test_config_sampled(G, cfg, name):
     lam = L.damp_percent * float(np.mean(np.diag(H_g).astype(np.float64)))
     U_g = U.cpu().numpy()
 
-    def hp_matvec(y):
-        # H_p y with H_p = (H + lam I)[perm][:, perm]
-        yo = np.zeros(d)
-        yo[perm_g] = y
-        z = _rows_matvec(H_g, yo) + lam * yo
-        return z[perm_g]
+    def hp_matmul(Y):
+        # H_p Y with H_p = (H + lam I)[perm][:, perm]
+        Yo = np.zeros((d, Y.shape[1]))
+        Yo[perm_g] = Y
+        Z = _rows_matmul(H_g, Yo) + lam * Yo
+        return Z[perm_g]
 
-    js = np.sort(rng.choice(d, size=8, replace=False))
-    res = _two_sided_residual(U_g, hp_matvec, js)
-    tol = 8.0 * d * EPS32
-    print(f"  two-sided residual max {res.max():.3e} (tol {tol:.3e})", flush=True)
-    if cfg == 3 and name == "q_proj":
-        p = O.prepare(H_g.astype(np.float64), L.damp_percent, L.desc_act)
-        ev = np.linalg.eigvalsh(p.Hp)
-        kappa = float(ev[-1] / ev[0])
-        err = rel_fro(U_g, p.U)
-        res_o = _two_sided_residual(p.U, hp_matvec, js)
-        print(f"  cond(H_p) {kappa:.3e}, U rel err vs oracle factor {err:.3e}, "
-              f"oracle factor residual {res_o.max():.3e}", flush=True)
-        assert err <= 50 * kappa * EPS32 + 1e-6
-        assert res_o.max() <= 1e-9
+    js = _panel_positions(d, rng)
+    res = _two_sided_residual(U_g, hp_matmul, js)
+    # backward-stable Cholesky and triangular inverse in fp32: a residual of a
+    # few eps32 per sqrt(d); measured at most about 1.4e-6 on these layers
+    tol = 16.0 * np.sqrt(d) * EPS32
+    print(f"  two-sided residual at {len(js)} positions (one per panel): max {res.max():.3e} (tol {tol:.3e})",
+          flush=True)
     assert res.max() <= tol
+    p = None
+    if d <= 11008:
+        # the oracle's own fp64 factor (explicit inverse, then Cholesky) of the GPU's H
+        p = O.prepare(H_g.astype(np.float64), L.damp_percent, L.desc_act)
+        err = rel_fro(U_g, p.U)
+        res_o = _two_sided_residual(p.U, hp_matmul, js)
+        print(f"  U rel err vs the oracle's fp64 factor {err:.3e}; oracle factor residual {res_o.max():.3e}",
+              flush=True)
+        assert err <= 1e-5
+        assert res_o.max() <= 1e-9
 
-    # sweep on sampled output rows with the GPU's factor and order
+    # sweep on sampled output rows (rows are independent given U)
     rows = np.sort(rng.choice(L.d_out, size=64, replace=False))
     codes = out["codes"].cpu().numpy()[rows].astype(np.int64)
-    ref, mism, ties = sweep_parity(W_host[rows], U_g, perm_g, L, codes)
-    np.testing.assert_array_equal(out["g_idx"].cpu().numpy(), ref.g_idx)
+    zeros_g = out["zeros"].cpu().numpy()
+    Wr = W_host[rows]
+    ind, raw, nrows, worst = independent_parity(Wr, U_g, perm_g, L, codes, zeros_g, rows=rows)
+    np.testing.assert_array_equal(out["g_idx"].cpu().numpy(), ind.g_idx)
+    _, mism, ties = sweep_parity(Wr, U_g, perm_g, L, codes)
     Q = out["Q"].cpu().numpy()[rows].astype(np.float64)
-    D_g = W_host[rows] - Q
-    D_r = W_host[rows] - ref.Q
-    e_g = float(np.sum(_rows_matvec_t(H_g, D_g) * D_g))
-    e_r = float(np.sum(_rows_matvec_t(H_g, D_r) * D_r))
-    print(f"  sampled rows: code mismatch {mism:.5%} (float ties followed {ties:.5%}), "
-          f"recon ratio {e_g / e_r:.5f}", flush=True)
+
+    def recon(Qr):
+        D = Wr - Qr
+        return float(np.sum(_rows_matvec_t(H_g, D) * D))
+    e_g, e_i = recon(Q), recon(ind.Q)
+    msg = (f"  sampled rows: raw code mismatch {raw:.5%} ({nrows} of {len(rows)} rows differ, first divergences "
+           f"<= {worst:.2e} steps from a boundary), recon gpu/independent {e_g / e_i:.6f}; followed: {mism:.5%} "
+           f"differing, {ties:.5%} ties")
+    if p is not None:
+        own = O.quantize_layer(Wr, p.U, p.perm, L.bits, L.group_size, L.sym, L.static_groups)
+        raw_own = float(np.mean(codes != own.codes))
+        e_o = recon(own.Q)
+        msg += f"; oracle's own factor: raw mismatch {raw_own:.5%}, recon gpu/oracle {e_g / e_o:.6f}"
+        assert abs(e_g / e_o - 1.0) <= 0.01
+    print(msg, flush=True)
+    assert abs(e_g / e_i - 1.0) <= 0.01
     assert mism <= 1e-3 and ties <= 1e-3
-    assert abs(e_g / e_r - 1.0) <= 0.01
     np.testing.assert_array_equal(qw.cpu().numpy()[:, rows], O.pack(codes, L.bits))
 
 
