@@ -55,7 +55,8 @@ typedef enum {
   GPTQ_ERR_INVALID_ARG = 1,  /* rejected on the host, nothing enqueued */
   GPTQ_ERR_NOT_SPD = 2,      /* reserved for host wrappers reading info_dev */
   GPTQ_ERR_HIP = 3,          /* a HIP runtime call or kernel launch failed */
-  GPTQ_ERR_WORKSPACE = 4     /* workspace missing, too small or misaligned */
+  GPTQ_ERR_WORKSPACE = 4,    /* workspace missing, too small or misaligned */
+  GPTQ_ERR_TOO_LARGE = 5     /* needs more than the library's fixed scratch buffer */
 } gptq_status;
 
 typedef enum { GPTQ_F32 = 0, GPTQ_BF16 = 1 } gptq_dtype;
@@ -205,6 +206,33 @@ gptq_status gptq_dequant_matmul(const void* x, gptq_dtype xt, int64_t m, int64_t
                                 const int32_t* qweight, const float* scales, const int32_t* zeros,
                                 const int32_t* g_idx, int32_t bits, int64_t d_out, int32_t n_groups,
                                 float* y, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * gptq_dequant_matmul for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same kernels and the same y, bit for bit, with the partial
+ * sums of the K slices in a buffer the library owns instead of a caller
+ * workspace.  The buffer is a fixed device array of gptq_dequant_scratch_bytes()
+ * bytes (16 MiB) per GPU, held until the process ends; its device address is
+ * looked up once per device, on that device's first call.  The call allocates
+ * nothing (no hipMalloc, no library allocation).
+ *   Arguments as for gptq_dequant_matmul, without ws / ws_bytes.
+ *   gptq_dequant_noalloc_need(m, xt, d_in, bits, d_out) gives the scratch
+ *   bytes a call needs (at most 14.7 MB for every layer shape up to
+ *   28672 x 8192 with bf16 x at any m, or fp32 x at up to 8 tokens); a call
+ *   needing more than the buffer returns GPTQ_ERR_TOO_LARGE and enqueues
+ *   nothing.  The buffer needs no clearing: each call writes every partial
+ *   sum it reads.
+ *   Every call on one GPU shares the buffer: calls that may overlap in time
+ *   on one GPU (different streams, or host threads) race and must be
+ *   serialised by the caller.
+ */
+size_t gptq_dequant_scratch_bytes(void);
+size_t gptq_dequant_noalloc_need(int64_t m, gptq_dtype xt, int64_t d_in, int32_t bits, int64_t d_out);
+gptq_status gptq_dequant_matmul_noalloc(const void* x, gptq_dtype xt, int64_t m, int64_t d_in,
+                                        const int32_t* qweight, const float* scales, const int32_t* zeros,
+                                        const int32_t* g_idx, int32_t bits, int64_t d_out, int32_t n_groups,
+                                        float* y, void* stream);
 
 /*
  * Group order for the dequantizing product of an act-order layer.  With

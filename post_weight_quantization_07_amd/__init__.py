@@ -15,16 +15,18 @@ from typing import Iterable, List, Optional, Sequence
 
 import torch
 
-from ._lib import (EXPORTS, GptqError, NonFiniteHessian, NotPositiveDefinite, QuantizeConfig, gptq_hessian_accumulate,  # noqa: F401
-                   gptq_dequant_matmul, gptq_dequant_matmul_ordered, gptq_dequant_order,
-                   gptq_dequant_ordered_workspace_size, gptq_dequant_workspace_size, gptq_hessian_workspace_size,
-                   gptq_pack, gptq_prepare_hinv, gptq_prepare_workspace_size, gptq_quantize_layer,
-                   gptq_workspace_size, library_path)
+from ._lib import (EXPORTS, GptqError, NonFiniteHessian, NotPositiveDefinite, QuantizeConfig,  # noqa: F401
+                   gptq_dequant_matmul, gptq_dequant_matmul_noalloc, gptq_dequant_matmul_ordered,
+                   gptq_dequant_noalloc_need, gptq_dequant_order, gptq_dequant_ordered_workspace_size,
+                   gptq_dequant_scratch_bytes, gptq_dequant_workspace_size, gptq_hessian_accumulate,
+                   gptq_hessian_workspace_size, gptq_pack, gptq_prepare_hinv, gptq_prepare_workspace_size,
+                   gptq_quantize_layer, gptq_workspace_size, library_path)
 
-__all__ = ["QuantizeConfig", "GptqError", "NotPositiveDefinite", "NonFiniteHessian", "gptq_hessian_accumulate", "gptq_prepare_hinv",
-           "gptq_quantize_layer", "gptq_pack", "gptq_hessian_workspace_size", "gptq_prepare_workspace_size",
-           "gptq_workspace_size", "gptq_dequant_matmul", "gptq_dequant_workspace_size", "gptq_dequant_order",
-           "gptq_dequant_matmul_ordered", "gptq_dequant_ordered_workspace_size", "solve_layer",
+__all__ = ["QuantizeConfig", "GptqError", "NotPositiveDefinite", "NonFiniteHessian", "gptq_hessian_accumulate",
+           "gptq_prepare_hinv", "gptq_quantize_layer", "gptq_pack", "gptq_hessian_workspace_size",
+           "gptq_prepare_workspace_size", "gptq_workspace_size", "gptq_dequant_matmul", "gptq_dequant_workspace_size",
+           "gptq_dequant_order", "gptq_dequant_matmul_ordered", "gptq_dequant_ordered_workspace_size",
+           "gptq_dequant_matmul_noalloc", "gptq_dequant_noalloc_need", "gptq_dequant_scratch_bytes", "solve_layer",
            "solve_layers_shared", "library_path"]
 
 

@@ -16,14 +16,15 @@ import torch
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgptq.so")
 
-GPTQ_OK, GPTQ_ERR_INVALID_ARG, GPTQ_ERR_NOT_SPD, GPTQ_ERR_HIP, GPTQ_ERR_WORKSPACE = range(5)
+GPTQ_OK, GPTQ_ERR_INVALID_ARG, GPTQ_ERR_NOT_SPD, GPTQ_ERR_HIP, GPTQ_ERR_WORKSPACE, GPTQ_ERR_TOO_LARGE = range(6)
 GPTQ_F32, GPTQ_BF16 = 0, 1
 
 EXPORTS = ("gptq_config_validate", "gptq_status_string", "gptq_hessian_workspace_size",
            "gptq_hessian_accumulate", "gptq_prepare_workspace_size", "gptq_prepare_hinv",
            "gptq_workspace_size", "gptq_quantize_layer", "gptq_pack", "gptq_dequant_workspace_size",
            "gptq_dequant_matmul", "gptq_dequant_order", "gptq_dequant_ordered_workspace_size",
-           "gptq_dequant_matmul_ordered")
+           "gptq_dequant_matmul_ordered", "gptq_dequant_scratch_bytes", "gptq_dequant_noalloc_need",
+           "gptq_dequant_matmul_noalloc")
 
 
 class GptqError(RuntimeError):
@@ -76,6 +77,10 @@ def _lib():
             "gptq_dequant_ordered_workspace_size": (sz, [i64, i64, i64]),
             "gptq_dequant_matmul_ordered": (c_int32, [vp, c_int32, i64, i64, vp, vp, vp, vp, vp, c_int32, i64,
                                                       c_int32, vp, vp, sz, vp]),
+            "gptq_dequant_scratch_bytes": (sz, []),
+            "gptq_dequant_noalloc_need": (sz, [i64, c_int32, i64, c_int32, i64]),
+            "gptq_dequant_matmul_noalloc": (c_int32, [vp, c_int32, i64, i64, vp, vp, vp, vp, c_int32, i64, c_int32,
+                                                      vp, vp]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(lib, name)
@@ -291,6 +296,37 @@ def gptq_dequant_matmul(x: torch.Tensor, qweight: torch.Tensor, scales: torch.Te
                                       int(bits), d_out, n_groups, _ptr(y), _ptr(ws), 0 if ws is None else ws.numel(),
                                       _stream(stream)),
            "gptq_dequant_matmul")
+    return y
+
+
+def gptq_dequant_scratch_bytes() -> int:
+    return int(_lib().gptq_dequant_scratch_bytes())
+
+
+def gptq_dequant_noalloc_need(m: int, dtype: torch.dtype, d_in: int, bits: int, d_out: int) -> int:
+    code = GPTQ_BF16 if dtype == torch.bfloat16 else GPTQ_F32
+    return int(_lib().gptq_dequant_noalloc_need(m, code, d_in, bits, d_out))
+
+
+def gptq_dequant_matmul_noalloc(x: torch.Tensor, qweight: torch.Tensor, scales: torch.Tensor, zeros: torch.Tensor,
+                                g_idx: torch.Tensor, bits: int, y: torch.Tensor, stream=None) -> torch.Tensor:
+    """gptq_dequant_matmul with the library's fixed scratch buffer instead of a
+    workspace: the call itself allocates nothing (y is the caller's)."""
+    _dev(x, qweight, scales, zeros, g_idx, y)
+    if x.dim() != 2:
+        raise ValueError("gptq_dequant_matmul_noalloc: x must be a contiguous [m, d_in] matrix")
+    m, d_in = x.shape
+    d_out = qweight.shape[1]
+    n_groups = scales.shape[0]
+    if (qweight.shape[0] * 32 != d_in * bits or scales.shape != (n_groups, d_out) or zeros.shape != (n_groups, d_out)
+            or g_idx.shape != (d_in,) or y.shape != (m, d_out) or qweight.dtype != torch.int32
+            or scales.dtype != torch.float32 or zeros.dtype != torch.int32 or g_idx.dtype != torch.int32
+            or y.dtype != torch.float32):
+        raise ValueError("gptq_dequant_matmul_noalloc: tensors do not match x and bits")
+    _check(_lib().gptq_dequant_matmul_noalloc(_ptr(x), _dtype_code(x), m, d_in, _ptr(qweight), _ptr(scales),
+                                              _ptr(zeros), _ptr(g_idx), int(bits), d_out, n_groups, _ptr(y),
+                                              _stream(stream)),
+           "gptq_dequant_matmul_noalloc")
     return y
 
 

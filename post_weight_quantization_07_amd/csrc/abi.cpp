@@ -45,6 +45,7 @@ const char* gptq_status_string(gptq_status s) {
     case GPTQ_ERR_NOT_SPD: return "damped Hessian is not positive definite";
     case GPTQ_ERR_HIP: return "HIP runtime error";
     case GPTQ_ERR_WORKSPACE: return "workspace missing, too small or misaligned";
+    case GPTQ_ERR_TOO_LARGE: return "the call needs more scratch memory than the library's fixed buffer holds";
   }
   return "unknown status";
 }
@@ -144,6 +145,32 @@ gptq_status gptq_dequant_matmul(const void* x, gptq_dtype xt, int64_t m, int64_t
     return GPTQ_ERR_INVALID_ARG;
   const size_t need = gptq::dequant_workspace_bytes(m, d_in, d_out);
   if (need > 0 && (!ws || ws_bytes < need || !aligned256(ws))) return GPTQ_ERR_WORKSPACE;
+  return from_hip(gptq::dequant_matmul_launch(x, xt == GPTQ_BF16, m, d_in, qweight, scales, zeros, g_idx, bits, d_out,
+                                              n_groups, y, ws, static_cast<hipStream_t>(stream)));
+}
+
+size_t gptq_dequant_scratch_bytes(void) { return gptq::kDequantScratchBytes; }
+
+size_t gptq_dequant_noalloc_need(int64_t m, gptq_dtype xt, int64_t d_in, int32_t bits, int64_t d_out) {
+  if (m <= 0 || d_in <= 0 || d_out <= 0 || d_in % 32 != 0 || !bits_ok(bits)) return 0;
+  if (xt != GPTQ_F32 && xt != GPTQ_BF16) return 0;
+  return gptq::dequant_partial_bytes(m, d_in, d_out, xt == GPTQ_BF16, bits);
+}
+
+gptq_status gptq_dequant_matmul_noalloc(const void* x, gptq_dtype xt, int64_t m, int64_t d_in,
+                                        const int32_t* qweight, const float* scales, const int32_t* zeros,
+                                        const int32_t* g_idx, int32_t bits, int64_t d_out, int32_t n_groups,
+                                        float* y, void* stream) {
+  if (!x || !qweight || !scales || !zeros || !g_idx || !y) return GPTQ_ERR_INVALID_ARG;
+  if (m <= 0 || d_out <= 0 || d_in <= 0 || d_in % 32 != 0 || n_groups <= 0) return GPTQ_ERR_INVALID_ARG;
+  if (!bits_ok(bits) || (xt != GPTQ_F32 && xt != GPTQ_BF16)) return GPTQ_ERR_INVALID_ARG;
+  if (d_in / 32 * bits * d_out * 4 >= (int64_t{1} << 31) || int64_t{n_groups} * d_out * 4 >= (int64_t{1} << 31))
+    return GPTQ_ERR_INVALID_ARG;
+  if (gptq::dequant_partial_bytes(m, d_in, d_out, xt == GPTQ_BF16, bits) > gptq::kDequantScratchBytes)
+    return GPTQ_ERR_TOO_LARGE;
+  void* ws = nullptr;
+  const gptq_status st = from_hip(gptq::dequant_scratch(&ws));
+  if (st != GPTQ_OK) return st;
   return from_hip(gptq::dequant_matmul_launch(x, xt == GPTQ_BF16, m, d_in, qweight, scales, zeros, g_idx, bits, d_out,
                                               n_groups, y, ws, static_cast<hipStream_t>(stream)));
 }

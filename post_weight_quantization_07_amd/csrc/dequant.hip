@@ -50,6 +50,8 @@
 #include "gptq_internal.h"
 
 #include <algorithm>
+#include <atomic>
+#include <mutex>
 
 namespace gptq {
 namespace {
@@ -981,9 +983,65 @@ hipError_t dequant_order_launch(const int32_t* qweight, const int32_t* g_idx, in
   return hipGetLastError();
 }
 
+size_t dequant_partial_bytes(int64_t m, int64_t d_in, int64_t d_out, bool x_bf16, int bits) {
+  // what the passes of one call write: [ks][MT][d_out] floats for a VALU pass
+  // of up to MT tokens, [ks][16][d_out] for an MFMA pass; the first pass and
+  // a shorter last pass are the only distinct shapes
+  size_t need = 0;
+  const int64_t lens[2] = {std::min<int64_t>(kMaxMT, m), m % kMaxMT};
+  for (int64_t len : lens) {
+    if (len <= 0) continue;
+    size_t b = 0;
+    if (x_bf16 && len >= 3) {
+      const ValuPlan pl = mfma_plan(d_in, d_out, bits);
+      if (pl.ks > 1) b = static_cast<size_t>(pl.ks) * kMaxMT * d_out * sizeof(float);
+    } else {
+      const ValuPlan pl = valu_plan(d_in, d_out);
+      const int64_t mt = len <= 1 ? 1 : len <= 2 ? 2 : len <= 4 ? 4 : len <= 8 ? 8 : 16;
+      if (pl.ks > 1) b = static_cast<size_t>(pl.ks) * mt * d_out * sizeof(float);
+    }
+    need = std::max(need, b);
+  }
+  return need;
+}
+
 size_t dequant_ordered_workspace_bytes(int64_t m, int64_t d_in, int64_t d_out) {
   const size_t xb = (static_cast<size_t>(m) * d_in * sizeof(float) + 255) & ~static_cast<size_t>(255);
   return xb + dequant_workspace_bytes(m, d_in, d_out);
+}
+
+// ---------------------------------------------------- fixed scratch buffer
+// The partial sums of the K slices in a buffer the library owns, for callers
+// that cannot allocate.  One copy per GPU, at its own device address, kept
+// until the process ends; every call on that GPU shares it.
+static __device__ __align__(256) float scratch[kDequantScratchBytes / sizeof(float)];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+}  // namespace
+
+hipError_t dequant_scratch(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  void* ptr = g_scratch[dev].load(std::memory_order_acquire);
+  if (!ptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    ptr = g_scratch[dev].load(std::memory_order_relaxed);
+    if (!ptr) {
+      // the address of this device's copy (the current device); the host-side
+      // name of the array is not a device address
+      e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return e;
+      if (!ptr) return hipErrorInvalidSymbol;
+      g_scratch[dev].store(ptr, std::memory_order_release);
+    }
+  }
+  *out = ptr;
+  return hipSuccess;
 }
 
 hipError_t dequant_matmul_ordered_launch(const void* x, bool x_bf16, int64_t m, int64_t d_in, const int32_t* qweight,

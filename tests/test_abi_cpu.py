@@ -60,8 +60,8 @@ def test_config_validate_rules(lib):
 
 
 def test_status_strings(lib):
-    for s in range(5):
-        assert lib.gptq_status_string(s)
+    for s in range(6):
+        assert lib.gptq_status_string(s) != b"unknown status"
     assert b"positive definite" in lib.gptq_status_string(2)
 
 
@@ -155,3 +155,27 @@ def test_dequant_order_rejects_bad_arguments(lib):
     assert mm(fake, ws, need - 1) == 4                               # workspace too small
     assert mm(fake, ctypes.c_void_p((1 << 20) + 16), need) == 4      # misaligned
     assert mm(fake, None, need) == 4
+
+
+def test_dequant_noalloc_rejects_on_host(lib):
+    fake = ctypes.c_void_p(4096)
+    call = lambda *a: lib.gptq_dequant_matmul_noalloc(*a, None)
+    # bad arguments: INVALID_ARG before anything touches the GPU
+    assert call(None, 1, 4, 64, fake, fake, fake, fake, 4, 64, 1, fake) == 1
+    assert call(fake, 1, 4, 48, fake, fake, fake, fake, 4, 64, 1, fake) == 1        # d_in % 32
+    assert call(fake, 1, 4, 64, fake, fake, fake, fake, 5, 64, 1, fake) == 1        # bits
+    assert call(fake, 1, 0, 64, fake, fake, fake, fake, 4, 64, 1, fake) == 1        # m
+    assert call(fake, 3, 4, 64, fake, fake, fake, fake, 4, 64, 1, fake) == 1        # dtype
+    assert call(fake, 1, 4, 64, fake, fake, fake, None, 4, 64, 1, fake) == 1        # g_idx
+    # more partial sums than the fixed buffer holds: TOO_LARGE, nothing enqueued
+    cap = lib.gptq_dequant_scratch_bytes()
+    assert cap == 16 << 20
+    need = lib.gptq_dequant_noalloc_need(16, 0, 8192, 4, 28672)
+    assert need > cap
+    assert call(fake, 0, 16, 8192, fake, fake, fake, fake, 4, 28672, 64, fake) == 5
+    assert b"fixed buffer" in lib.gptq_status_string(5)
+    # the decode shapes of the layer configurations fit
+    for d_out, d_in in ((4096, 4096), (11008, 4096), (4096, 11008), (8192, 8192), (28672, 8192), (8192, 28672)):
+        for m in (1, 2, 3, 8, 16, 33):
+            assert lib.gptq_dequant_noalloc_need(m, 1, d_in, 4, d_out) <= cap
+    assert lib.gptq_dequant_noalloc_need(4, 1, 48, 4, 64) == 0
