@@ -41,8 +41,10 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="launch one device copy of this many MiB first (HBM counter calibration)")
-    ap.add_argument("--cpu-sample-tokens", type=int, default=16384)
-    ap.add_argument("--cpu-sample-rows", type=int, default=128)
+    ap.add_argument("--cpu-sample-tokens", type=int, default=0,
+                    help="time the oracle on this many tokens only (0: all N; the default is the whole layer)")
+    ap.add_argument("--cpu-sample-rows", type=int, default=0,
+                    help="time the oracle's sweep on this many rows only (0: all d_out)")
     ap.add_argument("--all-configs", metavar="PATH", default=None,
                     help="instead of the one-line result: time every layer of the five configurations and write "
                          "a markdown table to PATH")
@@ -79,24 +81,39 @@ def recorded_traffic():
     return rec
 
 
-def cpu_baseline(layer, W_host, args):
-    """The oracle, untuned, on a bounded sample of the same workload."""
+def cpu_baseline(layer, W_host, args, x_chunks=None):
+    """The oracle, untuned, on the same workload: by default the whole layer
+    solve (all N tokens, all d_out rows); --cpu-sample-tokens / -rows bound it
+    and scale the measured times up.  x_chunks: the activations as stored on
+    the device (bf16 bit patterns, token chunks in order), or None to draw
+    them again from the seeded generator."""
     import numpy as np
 
     import oracle as O
     import synth
     try:
         from threadpoolctl import threadpool_info
-        blas = [(i.get("internal_api"), i.get("num_threads")) for i in threadpool_info() if i.get("user_api") == "blas"]
+        info = threadpool_info()
+        blas = [(i.get("internal_api"), i.get("num_threads")) for i in info if i.get("user_api") == "blas"]
     except Exception:  # pragma: no cover
         blas = []
     threads = max([t for _, t in blas if t] or [os.cpu_count() or 1])
-    n_s = min(args.cpu_sample_tokens, layer.n_tokens)
-    rows = min(args.cpu_sample_rows, layer.d_out)
-    sig = synth.channel_sigma(layer)
-    chunks = [synth.activation_chunk(layer, c, sig) for c in range((n_s + synth.CHUNK_TOKENS - 1) // synth.CHUNK_TOKENS)]
+    n_s = layer.n_tokens if args.cpu_sample_tokens <= 0 else min(args.cpu_sample_tokens, layer.n_tokens)
+    rows = layer.d_out if args.cpu_sample_rows <= 0 else min(args.cpu_sample_rows, layer.d_out)
+    n_chunks = (n_s + synth.CHUNK_TOKENS - 1) // synth.CHUNK_TOKENS
+
+    def chunks():
+        # the stored bf16 values (exact in fp32), or the same values drawn again
+        if x_chunks is not None:
+            for c in range(n_chunks):
+                yield synth.bf16_to_f32(x_chunks[c])
+        else:
+            sig = synth.channel_sigma(layer)
+            for c in range(n_chunks):
+                yield synth.activation_chunk(layer, c, sig)
+
     t0 = time.perf_counter()
-    S, n = O.hessian_sum(chunks)
+    S, n = O.hessian_sum(chunks())
     t_h = time.perf_counter() - t0
     t0 = time.perf_counter()
     H = O.finalize_hessian(S, n)
@@ -110,14 +127,20 @@ def cpu_baseline(layer, W_host, args):
     O.pack(sw.codes, layer.bits)
     t_k = time.perf_counter() - t0
     total = t_h * (layer.n_tokens / n) + t_p + (t_q + t_k) * (layer.d_out / rows)
+    full = n == layer.n_tokens and rows == layer.d_out
+    if full:
+        sample = (f"full N: the whole layer solve, X^T X over all {n} tokens, damping + order + explicit inverse + "
+                  f"Cholesky of the {layer.d_in}x{layer.d_in} H, the blocked sweep of all {rows} rows, pack")
+    else:
+        sample = (f"X^T X on {n} of {layer.n_tokens} tokens (scaled x{layer.n_tokens / n:g}); full {layer.d_in}x"
+                  f"{layer.d_in} damping+order+inverse+Cholesky; sweep and pack on {rows} of {layer.d_out} rows "
+                  f"(scaled x{layer.d_out / rows:g})")
     return {
         "value": layer.d_in / total,
         "unit": "weight cols/s",
         "cores": int(threads),
         "kind": "oracle",
-        "sample": (f"X^T X on {n} of {layer.n_tokens} tokens (scaled x{layer.n_tokens / n:g}); full {layer.d_in}x"
-                   f"{layer.d_in} damping+order+inverse+Cholesky; sweep and pack on {rows} of {layer.d_out} rows "
-                   f"(scaled x{layer.d_out / rows:g}); numpy fp64, BLAS {blas}"),
+        "sample": f"{sample}; numpy {np.__version__} fp64, BLAS {blas}",
         "est_total_s": total,
         "measured_s": t_h + t_p + t_q + t_k,
         "stages_s": {"hessian": t_h, "prepare": t_p, "quantize": t_q, "pack": t_k},
@@ -161,7 +184,7 @@ class LayerSolve:
     that read `layer`'s input), their weights are stacked and solved against
     one H and one U, as solve_layers_shared does."""
 
-    def __init__(self, layer, copy_calib_mib=0, members=None):
+    def __init__(self, layer, copy_calib_mib=0, members=None, keep_host_x=False):
         import numpy as np
         import torch
 
@@ -180,10 +203,13 @@ class LayerSolve:
         bf16 = layer.x_dtype == "bf16"
         self.X = torch.empty((N, d_in), dtype=torch.bfloat16 if bf16 else torch.float32, device=dev)
         row = 0
+        self.x_host = [] if keep_host_x else None
         for x in synth.activation_chunks_threaded(layer, workers=min(16, os.cpu_count() or 1), as_bf16_bits=bf16):
             t = torch.from_numpy(x.view(np.int16)).view(torch.bfloat16) if bf16 else torch.from_numpy(x)
             self.X[row:row + x.shape[0]].copy_(t)
             row += x.shape[0]
+            if keep_host_x:
+                self.x_host.append(x)
         assert row == N
         self.S = torch.empty((d_in, d_in), dtype=torch.float32, device=dev)
         self.U = torch.empty((d_in, d_in), dtype=torch.float32, device=dev)
@@ -256,6 +282,72 @@ class LayerSolve:
         codes_max = int(self.out["codes"].max().item())
         assert 0 <= codes_max <= (1 << self.cfg.bits) - 1
         return ms_per_step, {k: float(np.mean(v)) for k, v in stage_ms.items()}
+
+    def phases(self, reps=3):
+        """Per-phase launch times of `reps` more steps from the library's own
+        HIP events (recorded around each launch on its stream); mean per step."""
+        from post_weight_quantization_07_amd import _lib
+        torch = self.torch
+        torch.cuda.synchronize()
+        _lib.phase_timing(True)
+        try:
+            for _ in range(reps):
+                self.step()
+            torch.cuda.synchronize()
+            ph = _lib.phase_read()
+        finally:
+            _lib.phase_timing(False)
+        return {k: (ms / reps, n // reps) for k, (ms, n) in ph.items()}
+
+
+def update_gemm_flops(d_out, d_in, group_size, static_groups):
+    """Algorithmic flops of the trailing-update products the quantize stage
+    launches (the rest of the cross-block updates runs inside the sweep
+    kernels): blocks are swept in pairs, pairs in groups of four; a later pair
+    of a group is first brought up to date with the group's earlier pairs, and
+    the columns past a group take one product with all of its errors."""
+    B = 128
+    g = group_size if group_size > 0 else 0
+    preset = static_groups or g == 0
+    pair = preset or g <= B or g % (2 * B) == 0
+    SB = 2 * B if pair else B
+    grouped = pair and (preset or g <= 2 * B or g % (2 * B * 4) == 0)
+    NU = 4 if grouped else 1
+    GW = NU * SB
+    f = 0.0
+    for g0 in range(0, d_in, GW):
+        for u in range(1, NU):
+            j0 = g0 + u * SB
+            if j0 >= d_in:
+                break
+            f += 2.0 * d_out * min(SB, d_in - j0) * (j0 - g0)
+        rest = d_in - g0 - GW
+        if rest > 0:
+            f += 2.0 * d_out * rest * GW
+    return f
+
+
+def kernel_metrics(layer, ph):
+    """Rates of the sweep and of the trailing-update products from their own
+    launch times: algorithmic bytes (sweep) or flops (update) over the summed
+    launch time, with the fraction of HBM / fp32 MFMA peak."""
+    d_out, d_in = layer.d_out, layer.d_in
+    G = layer.group_size if layer.group_size > 0 else d_in
+    sw_ms, sw_n = ph["sweep"]
+    up_ms, up_n = ph["trailing_update"]
+    b_sweep = float(d_out) * d_in * (9 + 8.0 / G)
+    f_up = update_gemm_flops(d_out, d_in, layer.group_size, layer.static_groups)
+    out = {"phases_ms": {k: round(v[0], 4) for k, v in ph.items()},
+           "phases_launches": {k: v[1] for k, v in ph.items()}}
+    if sw_ms > 0:
+        gbs = b_sweep / (sw_ms * 1e-3) / 1e9
+        out["sweep"] = {"launches": sw_n, "us_per_launch": 1e3 * sw_ms / max(1, sw_n), "bytes": b_sweep,
+                        "GB/s": gbs, "frac_hbm": gbs / PEAK_HBM_GBS}
+    if up_ms > 0:
+        tf = f_up / (up_ms * 1e-3) / 1e12
+        out["trailing_update"] = {"launches": up_n, "ms": up_ms, "flops": f_up, "TFLOP/s": tf,
+                                  "frac_fp32_peak": tf / PEAK_FP32_TFLOPS}
+    return out
 
 
 def all_configs(args):
@@ -470,12 +562,13 @@ def main():
     layer = synth.config_layers(3)[0]
     d_out, d_in, N = layer.d_out, layer.d_in, layer.n_tokens
     t_setup = time.perf_counter()
-    ls = LayerSolve(layer, args.copy_calib_mib)
+    ls = LayerSolve(layer, args.copy_calib_mib, keep_host_x=not args.no_cpu_baseline)
     torch.cuda.synchronize()
     t_setup = time.perf_counter() - t_setup
     ms_per_step, st = ls.measure(args.steps, args.warmup)
     cfg = ls.cfg
     m = stage_metrics(layer, st)
+    kern = kernel_metrics(layer, ls.phases())
     achieved = m["hessian"]["TFLOP/s"]
     rec = recorded_traffic()
     roofline = {"kernel": "gptq_hessian_accumulate = " + HESSIAN_KERNEL + " (S += X^T X)", "bound": "mfma",
@@ -502,14 +595,19 @@ def main():
                    "static_groups": cfg.static_groups, "damp_percent": cfg.damp_percent, "block_size": 128},
         "stages_ms": st,
         "stages": m,
+        "kernels": kern,
         "roofline": roofline,
         "setup_s": t_setup,
     }
     if not args.no_cpu_baseline:
-        cb = cpu_baseline(layer, ls.W_host, args)
+        x_host, W_host = ls.x_host, ls.W_host
+        del ls
+        torch.cuda.empty_cache()
+        cb = cpu_baseline(layer, W_host, args, x_host)
         result["cpu_baseline"] = {k: cb[k] for k in ("value", "unit", "cores", "kind", "sample")}
         result["cpu_baseline"]["est_total_s"] = cb["est_total_s"]
         result["cpu_baseline"]["measured_s"] = cb["measured_s"]
+        result["cpu_baseline"]["stages_s"] = cb["stages_s"]
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)

@@ -275,6 +275,24 @@ gptq_status gptq_dequant_matmul_ordered(const void* x, gptq_dtype xt, int64_t m,
                                         const int32_t* g_idx, const int32_t* order, int32_t bits, int64_t d_out,
                                         int32_t n_groups, float* y, void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * Per-phase launch timing, a measurement aid (not part of the solve; the pages
+ * fix nothing here).  gptq_phase_timing(1) clears the record and switches it
+ * on: from then on every launch of the calls above records a HIP event just
+ * before and just after itself on its stream, and is counted under its phase
+ * (gptq_phase_name: hessian_partial, hessian_reduce, prepare_elementwise,
+ * cholesky_panel, cholesky_update, triangular_inverse, quantize_elementwise,
+ * sweep, trailing_update, pack).  gptq_phase_timing(0) switches it off (the
+ * default; a launch site then costs one atomic load).  gptq_phase_read waits
+ * for the recorded events and writes, for phases 0 .. n-1, the summed event
+ * time of their launches (ms) and the launch count.  Host-global state: not
+ * for calls that run concurrently on several host threads while switched on.
+ */
+gptq_status gptq_phase_timing(int32_t enable);
+int32_t gptq_phase_count(void);
+const char* gptq_phase_name(int32_t phase);
+gptq_status gptq_phase_read(float* ms, int32_t* launches, int32_t n);
+
 #ifdef __cplusplus
 }
 #endif

@@ -24,7 +24,8 @@ EXPORTS = ("gptq_config_validate", "gptq_status_string", "gptq_hessian_workspace
            "gptq_workspace_size", "gptq_quantize_layer", "gptq_pack", "gptq_dequant_workspace_size",
            "gptq_dequant_matmul", "gptq_dequant_order", "gptq_dequant_ordered_workspace_size",
            "gptq_dequant_matmul_ordered", "gptq_dequant_scratch_bytes", "gptq_dequant_noalloc_need",
-           "gptq_dequant_matmul_noalloc")
+           "gptq_dequant_matmul_noalloc", "gptq_phase_timing", "gptq_phase_count", "gptq_phase_name",
+           "gptq_phase_read")
 
 
 class GptqError(RuntimeError):
@@ -81,6 +82,10 @@ def _lib():
             "gptq_dequant_noalloc_need": (sz, [i64, c_int32, i64, c_int32, i64]),
             "gptq_dequant_matmul_noalloc": (c_int32, [vp, c_int32, i64, i64, vp, vp, vp, vp, c_int32, i64, c_int32,
                                                       vp, vp]),
+            "gptq_phase_timing": (c_int32, [c_int32]),
+            "gptq_phase_count": (c_int32, []),
+            "gptq_phase_name": (ctypes.c_char_p, [c_int32]),
+            "gptq_phase_read": (c_int32, [vp, vp, c_int32]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(lib, name)
@@ -88,6 +93,21 @@ def _lib():
             fn.argtypes = args
         _LIB = lib
     return _LIB
+
+
+def phase_timing(enable: bool) -> None:
+    """Switch the library's per-phase launch timing on (clearing the record) or off."""
+    _check(_lib().gptq_phase_timing(1 if enable else 0), "gptq_phase_timing")
+
+
+def phase_read() -> dict:
+    """{phase name: (summed ms, launches)} of the launches recorded since timing was switched on."""
+    lib = _lib()
+    n = int(lib.gptq_phase_count())
+    ms = (c_float * n)()
+    cnt = (c_int32 * n)()
+    _check(lib.gptq_phase_read(ctypes.cast(ms, c_void_p), ctypes.cast(cnt, c_void_p), n), "gptq_phase_read")
+    return {lib.gptq_phase_name(i).decode(): (float(ms[i]), int(cnt[i])) for i in range(n)}
 
 
 def library_path() -> str:

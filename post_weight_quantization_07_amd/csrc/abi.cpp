@@ -206,4 +206,15 @@ gptq_status gptq_dequant_matmul_ordered(const void* x, gptq_dtype xt, int64_t m,
                                                       static_cast<hipStream_t>(stream)));
 }
 
+gptq_status gptq_phase_timing(int32_t enable) { return from_hip(gptq::phase_timing_set(enable != 0)); }
+
+int32_t gptq_phase_count(void) { return gptq::kNumPhases; }
+
+const char* gptq_phase_name(int32_t phase) { return gptq::phase_name(phase); }
+
+gptq_status gptq_phase_read(float* ms, int32_t* launches, int32_t n) {
+  if (!ms || !launches || n <= 0) return GPTQ_ERR_INVALID_ARG;
+  return from_hip(gptq::phase_timing_read(ms, launches, n));
+}
+
 }  // extern "C"

@@ -7,6 +7,27 @@
 
 namespace gptq {
 
+// ---------------------------------------------------------- phase timing --
+// A measurement aid (phase_timing.cpp): while switched on, each instrumented
+// launch records a HIP event before and after itself on its stream.
+enum Phase {
+  kPhHessian = 0, kPhHessReduce, kPhPrepElem, kPhPanel, kPhCholUpdate, kPhTrtri,
+  kPhQuantElem, kPhSweep, kPhUpdate, kPhPack, kNumPhases
+};
+bool phase_timing_on();
+void phase_mark(int phase, bool begin, hipStream_t st);
+hipError_t phase_timing_set(bool on);
+hipError_t phase_timing_read(float* ms, int32_t* launches, int n);
+const char* phase_name(int phase);
+struct PhaseScope {
+  int phase;
+  hipStream_t st;
+  PhaseScope(int p, hipStream_t s) : phase(p), st(s) { phase_mark(p, true, s); }
+  ~PhaseScope() { phase_mark(phase, false, st); }
+  PhaseScope(const PhaseScope&) = delete;
+  PhaseScope& operator=(const PhaseScope&) = delete;
+};
+
 // ---------------------------------------------------------------- hessian --
 struct HessPlan {
   int tile;          // output tile edge

@@ -572,10 +572,18 @@ hipError_t hessian_launch(const HessPlan& pl, float* S, int64_t d_in, const void
   const int blocks = pl.n_tiles * pl.n_split;
   const int d = static_cast<int>(d_in);
   if (bf16) {
-    hessian_bf16_pipe_kernel<<<blocks, kThreads, 0, stream>>>(p);
+    {
+      PhaseScope ph(kPhHessian, stream);
+      hessian_bf16_pipe_kernel<<<blocks, kThreads, 0, stream>>>(p);
+    }
+    PhaseScope ph(kPhHessReduce, stream);
     hessian_reduce_kernel<kBTile, 32, 4><<<pl.n_tiles * 64, 256, 0, stream>>>(p.partial, pl.n_split, pl.nt, d, S);
   } else {
-    hessian_f32_kernel<<<blocks, kThreads, 0, stream>>>(p);
+    {
+      PhaseScope ph(kPhHessian, stream);
+      hessian_f32_kernel<<<blocks, kThreads, 0, stream>>>(p);
+    }
+    PhaseScope ph(kPhHessReduce, stream);
     hessian_reduce_kernel<kFTile, 16, 1><<<pl.n_tiles * 64, 64, 0, stream>>>(p.partial, pl.n_split, pl.nt, d, S);
   }
   return hipGetLastError();

@@ -63,6 +63,7 @@ hipError_t pack_launch(const uint8_t* codes, int64_t d_out, int64_t d_in, int bi
   if (d_out <= 0 || d_in <= 0) return hipSuccess;
   const int64_t runs = (d_in + 31) / 32;
   dim3 grid(static_cast<unsigned>((d_out + 255) / 256), static_cast<unsigned>(runs));
+  PhaseScope ph(kPhPack, stream);
   pack_kernel<<<grid, 256, 0, stream>>>(codes, d_out, d_in, bits, qweight);
   return hipGetLastError();
 }

@@ -746,14 +746,17 @@ hipError_t prepare_launch(float* S, int64_t n, int64_t n_total, float damp, bool
   float* Dinv = reinterpret_cast<float*>(w + lay.off_dinv);
   const int64_t nn = n * n;
 
-  finalize_kernel<<<grid_for(nn), 256, 0, st>>>(S, n, static_cast<float>(2.0 / static_cast<double>(n_total)), diag);
-  GPTQ_TRY(hipGetLastError());
-  lambda_kernel<<<1, 1024, 0, st>>>(diag, n, damp, lam, info);
-  GPTQ_TRY(hipGetLastError());
-  order_kernel<<<static_cast<int>((n + 255) / 256), 256, 0, st>>>(diag, n, desc_act ? 1 : 0, perm);
-  GPTQ_TRY(hipGetLastError());
-  gather_kernel<<<grid_for(nn), 256, 0, st>>>(S, n, perm, lam, Hr);
-  GPTQ_TRY(hipGetLastError());
+  {
+    PhaseScope ph(kPhPrepElem, st);
+    finalize_kernel<<<grid_for(nn), 256, 0, st>>>(S, n, static_cast<float>(2.0 / static_cast<double>(n_total)), diag);
+    GPTQ_TRY(hipGetLastError());
+    lambda_kernel<<<1, 1024, 0, st>>>(diag, n, damp, lam, info);
+    GPTQ_TRY(hipGetLastError());
+    order_kernel<<<static_cast<int>((n + 255) / 256), 256, 0, st>>>(diag, n, desc_act ? 1 : 0, perm);
+    GPTQ_TRY(hipGetLastError());
+    gather_kernel<<<grid_for(nn), 256, 0, st>>>(S, n, perm, lam, Hr);
+    GPTQ_TRY(hipGetLastError());
+  }
 
   // blocked right-looking Cholesky of Hr; the panel kernels leave the inverse
   // of every diagonal block in place.  Panels go in groups of kPanelGroup:
@@ -771,24 +774,30 @@ hipError_t prepare_launch(float* S, int64_t n, int64_t n_total, float damp, bool
       if (h > 0) {
         const int64_t wc = std::min<int64_t>(kNB, n - kh);
         const float* A = Hr + kh * n + k;  // rows kh .., the earlier panels' columns
+        PhaseScope ph(kPhCholUpdate, st);
         GPTQ_TRY(gemm_f32(n - kh, wc, kh - k, -1.f, A, n, 0, A, n, 0, true, 1.f, Hr + kh * (n + 1), n, 0, 1,
                           false, 0, st));
       }
       const int64_t below = std::max<int64_t>(0, n - kh - kNB);
       const int blocks = 1 + static_cast<int>(std::min<int64_t>((below + kChunk - 1) / kChunk, kMaxPanelWG - 1));
-      panel_kernel<<<blocks, 256, 0, st>>>(Hr, n, kh, info, Dinv);
+      {
+        PhaseScope ph(kPhPanel, st);
+        panel_kernel<<<blocks, 256, 0, st>>>(Hr, n, kh, info, Dinv);
+      }
       GPTQ_TRY(hipGetLastError());
     }
     const int64_t ke = std::min<int64_t>(n, k + kNB * kPanelGroup);
     const int64_t below = n - ke;
     if (below > 0) {
       const float* P = Hr + ke * n + k;
+      PhaseScope ph(kPhCholUpdate, st);
       GPTQ_TRY(gemm_f32(below, below, ke - k, -1.f, P, n, 0, P, n, 0, true, 1.f, Hr + ke * (n + 1), n, 0, 1, true,
                         0, st));
     }
   }
   // triangular inverse by recursive doubling over the inverted diagonal blocks
   const int64_t nblk = (n + kNB - 1) / kNB;
+  PhaseScope ph_trtri(kPhTrtri, st);
   place_dinv_kernel<<<grid_for(nblk * kNB * kNB), 256, 0, st>>>(Dinv, n, Hr);
   GPTQ_TRY(hipGetLastError());
   for (int64_t h = 1; h < nblk; h *= 2) {
@@ -819,7 +828,7 @@ hipError_t prepare_launch(float* S, int64_t n, int64_t n_total, float damp, bool
     }
   }
   reverse_kernel<<<grid_for(nn), 256, 0, st>>>(Hr, n, U);
-  return hipGetLastError();
+  return hipGetLastError();  // the triangular inverse's phase closes after the reversal
 }
 
 }  // namespace gptq

@@ -465,18 +465,22 @@ hipError_t quantize_launch(const void* W, bool w_bf16, int64_t d_out, int64_t d_
   const int n_groups = group > 0 ? static_cast<int>((d_in + group - 1) / group) : 1;
   const bool preset = static_groups || group == 0;
 
-  gather_w_kernel<<<grid_for(d_out * d_in), 256, 0, st>>>(W, w_bf16 ? 1 : 0, d_out, d_in, perm, identity ? 1 : 0, Wp);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  if (preset) {
-    const int64_t pairs = static_cast<int64_t>(n_groups) * d_out;
-    const int blocks = static_cast<int>(std::max<int64_t>(1, std::min<int64_t>((pairs + 3) / 4, 16384)));
-    static_params_kernel<<<blocks, 256, 0, st>>>(W, w_bf16 ? 1 : 0, d_out, d_in, group, n_groups, bits, sym ? 1 : 0,
-                                                 scales, zeros);
+  hipError_t e;
+  {
+    PhaseScope ph(kPhQuantElem, st);
+    gather_w_kernel<<<grid_for(d_out * d_in), 256, 0, st>>>(W, w_bf16 ? 1 : 0, d_out, d_in, perm, identity ? 1 : 0,
+                                                            Wp);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (preset) {
+      const int64_t pairs = static_cast<int64_t>(n_groups) * d_out;
+      const int blocks = static_cast<int>(std::max<int64_t>(1, std::min<int64_t>((pairs + 3) / 4, 16384)));
+      static_params_kernel<<<blocks, 256, 0, st>>>(W, w_bf16 ? 1 : 0, d_out, d_in, group, n_groups, bits,
+                                                   sym ? 1 : 0, scales, zeros);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    g_idx_kernel<<<grid_for(d_in), 256, 0, st>>>(d_in, group, (!preset && !identity) ? 1 : 0, perm, g_idx);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  g_idx_kernel<<<grid_for(d_in), 256, 0, st>>>(d_in, group, (!preset && !identity) ? 1 : 0, perm, g_idx);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
 
   SweepParams p{};
   p.Wp = Wp;
@@ -523,6 +527,7 @@ hipError_t quantize_launch(const void* W, bool w_bf16, int64_t d_out, int64_t d_
       if (u > 0) {
         // the unit's columns take the group's earlier units' errors
         const int64_t w = std::min<int64_t>(SB, d_in - j0);
+        PhaseScope ph(kPhUpdate, st);
         e = gemm_f32(d_out, w, j0 - g0, -1.f, Err, GW, 0, U + g0 * d_in + j0, d_in, 0, false, 1.f, Wp + j0, d_in, 0, 1,
                      false, 0, st);
         if (e != hipSuccess) return e;
@@ -537,6 +542,7 @@ hipError_t quantize_launch(const void* W, bool w_bf16, int64_t d_out, int64_t d_
         p.j0 = jb;
         p.ncols = ncols;
         p.Err = Err + u * SB + h * kB;
+        PhaseScope ph(kPhSweep, st);
         switch (gs) {
           case 0: sweep_kernel<0><<<blocks, 256, 0, st>>>(p); break;
           case 1: sweep_kernel<1><<<blocks, 256, 0, st>>>(p); break;
@@ -554,6 +560,7 @@ hipError_t quantize_launch(const void* W, bool w_bf16, int64_t d_out, int64_t d_
     }
     const int64_t rest = d_in - g0 - GW;
     if (rest > 0) {
+      PhaseScope ph(kPhUpdate, st);
       e = gemm_f32(d_out, rest, GW, -1.f, Err, GW, 0, U + g0 * d_in + g0 + GW, d_in, 0, false, 1.f, Wp + g0 + GW,
                    d_in, 0, 1, false, 0, st);
       if (e != hipSuccess) return e;
