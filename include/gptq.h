@@ -35,6 +35,9 @@
  *   - Arguments are checked on the host before anything is enqueued; a bad
  *     argument returns GPTQ_ERR_INVALID_ARG and enqueues nothing.  A failed
  *     kernel launch returns GPTQ_ERR_HIP.
+ *   - Sizes: d_in and d_out at most 2^20, token counts (n_tokens, m) at most
+ *     2^40; larger (or non-positive where a positive size is required)
+ *     values return GPTQ_ERR_INVALID_ARG, and 0 from the size queries.
  *   - Workspaces: query the size with the matching *_workspace_size call and
  *     pass at least that many bytes, 256-byte aligned.  Their contents on
  *     entry do not matter and are undefined on exit.  Concurrent calls must
@@ -59,6 +62,8 @@ typedef enum {
   GPTQ_ERR_TOO_LARGE = 5     /* needs more than the library's fixed scratch buffer */
 } gptq_status;
 
+/* Element types of X, W and x, passed as int32_t (any other value:
+ * GPTQ_ERR_INVALID_ARG, or 0 from a size query). */
 typedef enum { GPTQ_F32 = 0, GPTQ_BF16 = 1 } gptq_dtype;
 
 /*
@@ -91,8 +96,9 @@ typedef struct {
  * GPTQ_ERR_INVALID_ARG. */
 gptq_status gptq_config_validate(const gptq_config* cfg);
 
-/* Human-readable name of a status code (static storage). */
-const char* gptq_status_string(gptq_status status);
+/* Human-readable name of a status code (static storage); any int32 value is
+ * accepted ("unknown status" for values outside gptq_status). */
+const char* gptq_status_string(int32_t status);
 
 /*
  * S += X^T X  (chapter 5, section 5.1.7: the layer Hessian is X X^T up to a
@@ -106,8 +112,8 @@ const char* gptq_status_string(gptq_status status);
  * Products are formed exactly (bf16) or in fp32 and summed in fp32.  The sum
  * is deterministic: a fixed token split and a fixed reduction order.
  */
-size_t gptq_hessian_workspace_size(int64_t d_in, int64_t n_tokens, gptq_dtype xt);
-gptq_status gptq_hessian_accumulate(float* S, int64_t d_in, const void* X, gptq_dtype xt,
+size_t gptq_hessian_workspace_size(int64_t d_in, int64_t n_tokens, int32_t xt);
+gptq_status gptq_hessian_accumulate(float* S, int64_t d_in, const void* X, int32_t xt,
                                     int64_t n_tokens, int64_t ldx, void* ws, size_t ws_bytes,
                                     void* stream);
 
@@ -156,7 +162,7 @@ gptq_status gptq_prepare_hinv(float* S_to_H, int64_t d_in, int64_t n_total, cons
  * Requires d_in % (32 / bits) == 0 (d_in % 32 == 0 for 3 bits).
  */
 size_t gptq_workspace_size(int64_t d_out, int64_t d_in, const gptq_config* cfg);
-gptq_status gptq_quantize_layer(const void* W, gptq_dtype wt, int64_t d_out, int64_t d_in,
+gptq_status gptq_quantize_layer(const void* W, int32_t wt, int64_t d_out, int64_t d_in,
                                 const float* U, const int32_t* perm, const gptq_config* cfg,
                                 uint8_t* codes, float* scales, int32_t* zeros, int32_t* g_idx,
                                 float* Q_or_null, float* row_loss_or_null, void* ws,
@@ -202,7 +208,7 @@ gptq_status gptq_pack(const uint8_t* codes, int64_t d_out, int64_t d_in, int32_t
  * sizes, bits or null pointers; WORKSPACE when ws is too small or misaligned.
  */
 size_t gptq_dequant_workspace_size(int64_t m, int64_t d_in, int64_t d_out);
-gptq_status gptq_dequant_matmul(const void* x, gptq_dtype xt, int64_t m, int64_t d_in,
+gptq_status gptq_dequant_matmul(const void* x, int32_t xt, int64_t m, int64_t d_in,
                                 const int32_t* qweight, const float* scales, const int32_t* zeros,
                                 const int32_t* g_idx, int32_t bits, int64_t d_out, int32_t n_groups,
                                 float* y, void* ws, size_t ws_bytes, void* stream);
@@ -228,8 +234,8 @@ gptq_status gptq_dequant_matmul(const void* x, gptq_dtype xt, int64_t m, int64_t
  *   serialised by the caller.
  */
 size_t gptq_dequant_scratch_bytes(void);
-size_t gptq_dequant_noalloc_need(int64_t m, gptq_dtype xt, int64_t d_in, int32_t bits, int64_t d_out);
-gptq_status gptq_dequant_matmul_noalloc(const void* x, gptq_dtype xt, int64_t m, int64_t d_in,
+size_t gptq_dequant_noalloc_need(int64_t m, int32_t xt, int64_t d_in, int32_t bits, int64_t d_out);
+gptq_status gptq_dequant_matmul_noalloc(const void* x, int32_t xt, int64_t m, int64_t d_in,
                                         const int32_t* qweight, const float* scales, const int32_t* zeros,
                                         const int32_t* g_idx, int32_t bits, int64_t d_out, int32_t n_groups,
                                         float* y, void* stream);
@@ -270,7 +276,7 @@ gptq_status gptq_dequant_order(const int32_t* qweight, const int32_t* g_idx, int
  * Other arguments, requirements and errors as for gptq_dequant_matmul.
  */
 size_t gptq_dequant_ordered_workspace_size(int64_t m, int64_t d_in, int64_t d_out);
-gptq_status gptq_dequant_matmul_ordered(const void* x, gptq_dtype xt, int64_t m, int64_t d_in,
+gptq_status gptq_dequant_matmul_ordered(const void* x, int32_t xt, int64_t m, int64_t d_in,
                                         const int32_t* qweight, const float* scales, const int32_t* zeros,
                                         const int32_t* g_idx, const int32_t* order, int32_t bits, int64_t d_out,
                                         int32_t n_groups, float* y, void* ws, size_t ws_bytes, void* stream);

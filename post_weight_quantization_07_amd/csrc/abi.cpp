@@ -27,6 +27,14 @@ gptq_status from_hip(hipError_t e) { return e == hipSuccess ? GPTQ_OK : GPTQ_ERR
 
 bool bits_ok(int32_t b) { return b == 2 || b == 3 || b == 4 || b == 8; }
 
+// size limits of every call: channels and output rows up to 2^20 (an H of
+// that size would take 4 TiB), tokens up to 2^40; beyond them no size
+// computation of the library can overflow
+constexpr int64_t kMaxDim = int64_t{1} << 20;
+constexpr int64_t kMaxTokens = int64_t{1} << 40;
+bool dim_ok(int64_t v) { return v > 0 && v <= kMaxDim; }
+bool tokens_ok(int64_t n) { return n >= 0 && n <= kMaxTokens; }
+
 // d_in % (32 / bits) == 0, and d_in % 32 == 0 for 3 bits: whole words per row
 bool packable(int64_t d_in, int32_t bits) {
   if (!bits_ok(bits) || d_in <= 0) return false;
@@ -38,7 +46,7 @@ bool packable(int64_t d_in, int32_t bits) {
 
 extern "C" {
 
-const char* gptq_status_string(gptq_status s) {
+const char* gptq_status_string(int32_t s) {
   switch (s) {
     case GPTQ_OK: return "ok";
     case GPTQ_ERR_INVALID_ARG: return "invalid argument";
@@ -61,14 +69,14 @@ gptq_status gptq_config_validate(const gptq_config* c) {
   return GPTQ_OK;
 }
 
-size_t gptq_hessian_workspace_size(int64_t d_in, int64_t n_tokens, gptq_dtype xt) {
-  if (d_in <= 0 || n_tokens < 0 || (xt != GPTQ_F32 && xt != GPTQ_BF16)) return 0;
+size_t gptq_hessian_workspace_size(int64_t d_in, int64_t n_tokens, int32_t xt) {
+  if (!dim_ok(d_in) || !tokens_ok(n_tokens) || (xt != GPTQ_F32 && xt != GPTQ_BF16)) return 0;
   return gptq::hessian_plan(d_in, n_tokens, xt == GPTQ_BF16, device_cus()).ws_bytes;
 }
 
-gptq_status gptq_hessian_accumulate(float* S, int64_t d_in, const void* X, gptq_dtype xt, int64_t n_tokens,
+gptq_status gptq_hessian_accumulate(float* S, int64_t d_in, const void* X, int32_t xt, int64_t n_tokens,
                                     int64_t ldx, void* ws, size_t ws_bytes, void* stream) {
-  if (!S || d_in <= 0 || n_tokens < 0 || (xt != GPTQ_F32 && xt != GPTQ_BF16)) return GPTQ_ERR_INVALID_ARG;
+  if (!S || !dim_ok(d_in) || !tokens_ok(n_tokens) || (xt != GPTQ_F32 && xt != GPTQ_BF16)) return GPTQ_ERR_INVALID_ARG;
   if (n_tokens == 0) return GPTQ_OK;
   const bool bf16 = (xt == GPTQ_BF16);
   const int64_t vec = bf16 ? 8 : 4;
@@ -82,13 +90,13 @@ gptq_status gptq_hessian_accumulate(float* S, int64_t d_in, const void* X, gptq_
 }
 
 size_t gptq_prepare_workspace_size(int64_t d_in) {
-  if (d_in <= 0) return 0;
+  if (!dim_ok(d_in)) return 0;
   return gptq::prepare_layout(d_in).ws_bytes;
 }
 
 gptq_status gptq_prepare_hinv(float* S_to_H, int64_t d_in, int64_t n_total, const gptq_config* cfg, float* U,
                               int32_t* perm, int32_t* info_dev, void* ws, size_t ws_bytes, void* stream) {
-  if (!S_to_H || !U || !perm || !info_dev || d_in <= 0 || n_total <= 0) return GPTQ_ERR_INVALID_ARG;
+  if (!S_to_H || !U || !perm || !info_dev || !dim_ok(d_in) || n_total <= 0) return GPTQ_ERR_INVALID_ARG;
   if (gptq_config_validate(cfg) != GPTQ_OK) return GPTQ_ERR_INVALID_ARG;
   if (d_in % 4 != 0 || !aligned16(S_to_H) || !aligned16(U)) return GPTQ_ERR_INVALID_ARG;
   const gptq::PrepLayout lay = gptq::prepare_layout(d_in);
@@ -99,16 +107,16 @@ gptq_status gptq_prepare_hinv(float* S_to_H, int64_t d_in, int64_t n_total, cons
 
 size_t gptq_workspace_size(int64_t d_out, int64_t d_in, const gptq_config* cfg) {
   (void)cfg;
-  if (d_out <= 0 || d_in <= 0) return 0;
+  if (!dim_ok(d_out) || !dim_ok(d_in)) return 0;
   return gptq::quant_layout(d_out, d_in).ws_bytes;
 }
 
-gptq_status gptq_quantize_layer(const void* W, gptq_dtype wt, int64_t d_out, int64_t d_in, const float* U,
+gptq_status gptq_quantize_layer(const void* W, int32_t wt, int64_t d_out, int64_t d_in, const float* U,
                                 const int32_t* perm, const gptq_config* cfg, uint8_t* codes, float* scales,
                                 int32_t* zeros, int32_t* g_idx, float* Q_or_null, float* row_loss_or_null,
                                 void* ws, size_t ws_bytes, void* stream) {
   if (gptq_config_validate(cfg) != GPTQ_OK) return GPTQ_ERR_INVALID_ARG;
-  if (!W || !U || !codes || !scales || !zeros || !g_idx || d_out <= 0 || d_in <= 0) return GPTQ_ERR_INVALID_ARG;
+  if (!W || !U || !codes || !scales || !zeros || !g_idx || !dim_ok(d_out) || !dim_ok(d_in)) return GPTQ_ERR_INVALID_ARG;
   if (wt != GPTQ_F32 && wt != GPTQ_BF16) return GPTQ_ERR_INVALID_ARG;
   if (cfg->desc_act && !perm) return GPTQ_ERR_INVALID_ARG;
   if (!packable(d_in, cfg->bits)) return GPTQ_ERR_INVALID_ARG;
@@ -123,22 +131,23 @@ gptq_status gptq_quantize_layer(const void* W, gptq_dtype wt, int64_t d_out, int
 
 gptq_status gptq_pack(const uint8_t* codes, int64_t d_out, int64_t d_in, int32_t bits, int32_t* qweight,
                       void* stream) {
-  if (!codes || !qweight || d_out <= 0) return GPTQ_ERR_INVALID_ARG;
+  if (!codes || !qweight || !dim_ok(d_out) || !dim_ok(d_in)) return GPTQ_ERR_INVALID_ARG;
   if (!packable(d_in, bits)) return GPTQ_ERR_INVALID_ARG;
   return from_hip(gptq::pack_launch(codes, d_out, d_in, bits, qweight, static_cast<hipStream_t>(stream)));
 }
 
 size_t gptq_dequant_workspace_size(int64_t m, int64_t d_in, int64_t d_out) {
-  if (m <= 0 || d_in <= 0 || d_out <= 0 || d_in % 32 != 0) return 0;
+  if (m <= 0 || !tokens_ok(m) || !dim_ok(d_in) || !dim_ok(d_out) || d_in % 32 != 0) return 0;
   return gptq::dequant_workspace_bytes(m, d_in, d_out);
 }
 
-gptq_status gptq_dequant_matmul(const void* x, gptq_dtype xt, int64_t m, int64_t d_in, const int32_t* qweight,
+gptq_status gptq_dequant_matmul(const void* x, int32_t xt, int64_t m, int64_t d_in, const int32_t* qweight,
                                 const float* scales, const int32_t* zeros, const int32_t* g_idx, int32_t bits,
                                 int64_t d_out, int32_t n_groups, float* y, void* ws, size_t ws_bytes,
                                 void* stream) {
   if (!x || !qweight || !scales || !zeros || !g_idx || !y) return GPTQ_ERR_INVALID_ARG;
-  if (m <= 0 || d_out <= 0 || d_in <= 0 || d_in % 32 != 0 || n_groups <= 0) return GPTQ_ERR_INVALID_ARG;
+  if (m <= 0 || !tokens_ok(m) || !dim_ok(d_out) || !dim_ok(d_in) || d_in % 32 != 0 || n_groups <= 0)
+    return GPTQ_ERR_INVALID_ARG;
   if (!bits_ok(bits) || (xt != GPTQ_F32 && xt != GPTQ_BF16)) return GPTQ_ERR_INVALID_ARG;
   // qweight and scales / zeros are addressed with 32-bit byte offsets
   if (d_in / 32 * bits * d_out * 4 >= (int64_t{1} << 31) || int64_t{n_groups} * d_out * 4 >= (int64_t{1} << 31))
@@ -151,18 +160,19 @@ gptq_status gptq_dequant_matmul(const void* x, gptq_dtype xt, int64_t m, int64_t
 
 size_t gptq_dequant_scratch_bytes(void) { return gptq::kDequantScratchBytes; }
 
-size_t gptq_dequant_noalloc_need(int64_t m, gptq_dtype xt, int64_t d_in, int32_t bits, int64_t d_out) {
-  if (m <= 0 || d_in <= 0 || d_out <= 0 || d_in % 32 != 0 || !bits_ok(bits)) return 0;
+size_t gptq_dequant_noalloc_need(int64_t m, int32_t xt, int64_t d_in, int32_t bits, int64_t d_out) {
+  if (m <= 0 || !tokens_ok(m) || !dim_ok(d_in) || !dim_ok(d_out) || d_in % 32 != 0 || !bits_ok(bits)) return 0;
   if (xt != GPTQ_F32 && xt != GPTQ_BF16) return 0;
   return gptq::dequant_partial_bytes(m, d_in, d_out, xt == GPTQ_BF16, bits);
 }
 
-gptq_status gptq_dequant_matmul_noalloc(const void* x, gptq_dtype xt, int64_t m, int64_t d_in,
+gptq_status gptq_dequant_matmul_noalloc(const void* x, int32_t xt, int64_t m, int64_t d_in,
                                         const int32_t* qweight, const float* scales, const int32_t* zeros,
                                         const int32_t* g_idx, int32_t bits, int64_t d_out, int32_t n_groups,
                                         float* y, void* stream) {
   if (!x || !qweight || !scales || !zeros || !g_idx || !y) return GPTQ_ERR_INVALID_ARG;
-  if (m <= 0 || d_out <= 0 || d_in <= 0 || d_in % 32 != 0 || n_groups <= 0) return GPTQ_ERR_INVALID_ARG;
+  if (m <= 0 || !tokens_ok(m) || !dim_ok(d_out) || !dim_ok(d_in) || d_in % 32 != 0 || n_groups <= 0)
+    return GPTQ_ERR_INVALID_ARG;
   if (!bits_ok(bits) || (xt != GPTQ_F32 && xt != GPTQ_BF16)) return GPTQ_ERR_INVALID_ARG;
   if (d_in / 32 * bits * d_out * 4 >= (int64_t{1} << 31) || int64_t{n_groups} * d_out * 4 >= (int64_t{1} << 31))
     return GPTQ_ERR_INVALID_ARG;
@@ -179,23 +189,24 @@ gptq_status gptq_dequant_order(const int32_t* qweight, const int32_t* g_idx, int
                                int64_t d_out, int32_t* qweight_out, int32_t* g_idx_out, int32_t* order,
                                void* stream) {
   if (!qweight || !g_idx || !qweight_out || !g_idx_out || !order) return GPTQ_ERR_INVALID_ARG;
-  if (d_out <= 0 || d_in <= 0 || d_in % 32 != 0 || !bits_ok(bits)) return GPTQ_ERR_INVALID_ARG;
+  if (!dim_ok(d_out) || !dim_ok(d_in) || d_in % 32 != 0 || !bits_ok(bits)) return GPTQ_ERR_INVALID_ARG;
   if (d_in / 32 * bits * d_out * 4 >= (int64_t{1} << 31)) return GPTQ_ERR_INVALID_ARG;
   return from_hip(gptq::dequant_order_launch(qweight, g_idx, bits, d_in, d_out, qweight_out, g_idx_out, order,
                                              static_cast<hipStream_t>(stream)));
 }
 
 size_t gptq_dequant_ordered_workspace_size(int64_t m, int64_t d_in, int64_t d_out) {
-  if (m <= 0 || d_in <= 0 || d_out <= 0 || d_in % 32 != 0) return 0;
+  if (m <= 0 || !tokens_ok(m) || !dim_ok(d_in) || !dim_ok(d_out) || d_in % 32 != 0) return 0;
   return gptq::dequant_ordered_workspace_bytes(m, d_in, d_out);
 }
 
-gptq_status gptq_dequant_matmul_ordered(const void* x, gptq_dtype xt, int64_t m, int64_t d_in,
+gptq_status gptq_dequant_matmul_ordered(const void* x, int32_t xt, int64_t m, int64_t d_in,
                                         const int32_t* qweight, const float* scales, const int32_t* zeros,
                                         const int32_t* g_idx, const int32_t* order, int32_t bits, int64_t d_out,
                                         int32_t n_groups, float* y, void* ws, size_t ws_bytes, void* stream) {
   if (!x || !qweight || !scales || !zeros || !g_idx || !order || !y) return GPTQ_ERR_INVALID_ARG;
-  if (m <= 0 || d_out <= 0 || d_in <= 0 || d_in % 32 != 0 || n_groups <= 0) return GPTQ_ERR_INVALID_ARG;
+  if (m <= 0 || !tokens_ok(m) || !dim_ok(d_out) || !dim_ok(d_in) || d_in % 32 != 0 || n_groups <= 0)
+    return GPTQ_ERR_INVALID_ARG;
   if (!bits_ok(bits) || (xt != GPTQ_F32 && xt != GPTQ_BF16)) return GPTQ_ERR_INVALID_ARG;
   if (d_in / 32 * bits * d_out * 4 >= (int64_t{1} << 31) || int64_t{n_groups} * d_out * 4 >= (int64_t{1} << 31))
     return GPTQ_ERR_INVALID_ARG;
