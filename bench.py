@@ -358,14 +358,16 @@ def all_configs(args):
     import synth
     lines = ["| cfg | layer | d_out x d_in | N | x | bits/G | ms per solve | weight cols/s | accumulate "
              "TFLOP/s (% peak) | prepare TFLOP/s (% fp32) | quantize: update TFLOP/s (% fp32), sweep GB/s "
-             "(% HBM) | pack GB/s |",
-             "|---|---|---|---:|---|---|---:|---:|---:|---:|---:|---:|"]
+             "(% HBM) | sweep kernel: us per block, GB/s (% HBM) | update products: TFLOP/s (% fp32) | pack GB/s |",
+             "|---|---|---|---:|---|---|---:|---:|---:|---:|---:|---:|---:|---:|"]
     for c in (1, 2, 3, 4, 5):
         for layer in synth.config_layers(c):
             print(f"[all-configs] cfg{c} {layer.name} {layer.d_out}x{layer.d_in} N={layer.n_tokens}", flush=True)
             ls = LayerSolve(layer)
             ms, st = ls.measure(args.all_configs_steps, 1)
             m = stage_metrics(layer, st)
+            km = kernel_metrics(layer, ls.phases(reps=1))
+            sw, up = km.get("sweep", {}), km.get("trailing_update", {})
             g = layer.group_size
             lines.append(
                 f"| {c} | {layer.name} | {layer.d_out}x{layer.d_in} | {layer.n_tokens} | {layer.x_dtype} | "
@@ -375,6 +377,8 @@ def all_configs(args):
                 f"{m['prepare']['TFLOP/s']:.1f} ({100 * m['prepare']['frac']:.1f}%) | "
                 f"{m['quantize']['update TFLOP/s']:.1f} ({100 * m['quantize']['frac']:.1f}%), "
                 f"{m['quantize']['sweep GB/s']:.0f} ({100 * m['quantize']['sweep frac of HBM']:.1f}%) | "
+                f"{sw.get('us_per_launch', 0):.1f}, {sw.get('GB/s', 0):.0f} ({100 * sw.get('frac_hbm', 0):.1f}%) | "
+                f"{up.get('TFLOP/s', 0):.1f} ({100 * up.get('frac_fp32_peak', 0):.1f}%) | "
                 f"{m['pack']['GB/s']:.0f} |")
             del ls
             torch.cuda.empty_cache()
