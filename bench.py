@@ -300,12 +300,15 @@ class LayerSolve:
         return {k: (ms / reps, n // reps) for k, (ms, n) in ph.items()}
 
 
-def update_gemm_flops(d_out, d_in, group_size, static_groups):
+def update_gemm_flops(d_out, d_in, group_size, static_groups, group_launch=False):
     """Algorithmic flops of the trailing-update products the quantize stage
-    launches (the rest of the cross-block updates runs inside the sweep
-    kernels): blocks are swept in pairs, pairs in groups of four; a later pair
-    of a group is first brought up to date with the group's earlier pairs, and
-    the columns past a group take one product with all of its errors."""
+    launches as separate products.  One sweep launch per group of 1024
+    columns (group_launch; layers whose rows fit one workgroup per CU, groups
+    inside a block): the products inside a group run in the sweep kernel and
+    the columns past each group take one product with all of its errors.
+    Otherwise blocks are swept in pairs, pairs in groups of four; a later pair
+    of a group is first brought up to date with the group's earlier pairs (a
+    product), the second block of a pair inside its sweep kernel."""
     B = 128
     g = group_size if group_size > 0 else 0
     preset = static_groups or g == 0
@@ -318,7 +321,7 @@ def update_gemm_flops(d_out, d_in, group_size, static_groups):
     for g0 in range(0, d_in, GW):
         for u in range(1, NU):
             j0 = g0 + u * SB
-            if j0 >= d_in:
+            if j0 >= d_in or group_launch:
                 break
             f += 2.0 * d_out * min(SB, d_in - j0) * (j0 - g0)
         rest = d_in - g0 - GW
@@ -327,22 +330,37 @@ def update_gemm_flops(d_out, d_in, group_size, static_groups):
     return f
 
 
+def cross_block_flops(d_out, d_in):
+    """Flops of every cross-block update of the lazy-batch sweep: each block's
+    columns take the errors of all earlier columns (2 d_out flops a pair)."""
+    B = 128
+    return sum(2.0 * d_out * min(B, d_in - j0) * j0 for j0 in range(0, d_in, B))
+
+
 def kernel_metrics(layer, ph):
-    """Rates of the sweep and of the trailing-update products from their own
-    launch times: algorithmic bytes (sweep) or flops (update) over the summed
-    launch time, with the fraction of HBM / fp32 MFMA peak."""
+    """Rates of the sweep kernel and of the trailing-update products from their
+    own launch times: algorithmic bytes (sweep) or flops (update) over the
+    summed launch time, with the fraction of HBM / fp32 MFMA peak.  The sweep
+    kernel also runs the cross-block products the separate launches do not
+    (inside a group, or the pair bring-up); their flops over the sweep time are
+    reported beside its bytes."""
     d_out, d_in = layer.d_out, layer.d_in
     G = layer.group_size if layer.group_size > 0 else d_in
     sw_ms, sw_n = ph["sweep"]
     up_ms, up_n = ph["trailing_update"]
+    n_blocks = -(-d_in // 128)
+    group_launch = 0 < sw_n < n_blocks
     b_sweep = float(d_out) * d_in * (9 + 8.0 / G)
-    f_up = update_gemm_flops(d_out, d_in, layer.group_size, layer.static_groups)
+    f_up = update_gemm_flops(d_out, d_in, layer.group_size, layer.static_groups, group_launch)
+    f_in = cross_block_flops(d_out, d_in) - f_up
     out = {"phases_ms": {k: round(v[0], 4) for k, v in ph.items()},
            "phases_launches": {k: v[1] for k, v in ph.items()}}
     if sw_ms > 0:
         gbs = b_sweep / (sw_ms * 1e-3) / 1e9
-        out["sweep"] = {"launches": sw_n, "us_per_launch": 1e3 * sw_ms / max(1, sw_n), "bytes": b_sweep,
-                        "GB/s": gbs, "frac_hbm": gbs / PEAK_HBM_GBS}
+        out["sweep"] = {"launches": sw_n, "blocks": n_blocks, "us_per_block": 1e3 * sw_ms / n_blocks,
+                        "bytes": b_sweep, "GB/s": gbs, "frac_hbm": gbs / PEAK_HBM_GBS,
+                        "in_kernel_product_flops": f_in,
+                        "in_kernel_TFLOP/s": f_in / (sw_ms * 1e-3) / 1e12}
     if up_ms > 0:
         tf = f_up / (up_ms * 1e-3) / 1e12
         out["trailing_update"] = {"launches": up_n, "ms": up_ms, "flops": f_up, "TFLOP/s": tf,
@@ -377,7 +395,7 @@ def all_configs(args):
                 f"{m['prepare']['TFLOP/s']:.1f} ({100 * m['prepare']['frac']:.1f}%) | "
                 f"{m['quantize']['update TFLOP/s']:.1f} ({100 * m['quantize']['frac']:.1f}%), "
                 f"{m['quantize']['sweep GB/s']:.0f} ({100 * m['quantize']['sweep frac of HBM']:.1f}%) | "
-                f"{sw.get('us_per_launch', 0):.1f}, {sw.get('GB/s', 0):.0f} ({100 * sw.get('frac_hbm', 0):.1f}%) | "
+                f"{sw.get('us_per_block', 0):.1f}, {sw.get('GB/s', 0):.0f} ({100 * sw.get('frac_hbm', 0):.1f}%) | "
                 f"{up.get('TFLOP/s', 0):.1f} ({100 * up.get('frac_fp32_peak', 0):.1f}%) | "
                 f"{m['pack']['GB/s']:.0f} |")
             del ls

@@ -126,7 +126,7 @@ gptq_status gptq_quantize_layer(const void* W, int32_t wt, int64_t d_out, int64_
   return from_hip(gptq::quantize_launch(W, wt == GPTQ_BF16, d_out, d_in, U, perm, cfg->bits, cfg->group_size,
                                         cfg->sym != 0, cfg->static_groups != 0, codes, scales, zeros, g_idx,
                                         Q_or_null, row_loss_or_null, ws, static_cast<hipStream_t>(stream),
-                                        cfg->desc_act == 0));
+                                        cfg->desc_act == 0, device_cus()));
 }
 
 gptq_status gptq_pack(const uint8_t* codes, int64_t d_out, int64_t d_in, int32_t bits, int32_t* qweight,

@@ -20,10 +20,11 @@ GPTQ_DEV int lane_id() { return static_cast<int>(threadIdx.x) & (kWave - 1); }
 GPTQ_DEV float bf16_to_f32(uint16_t b) { return __uint_as_float(static_cast<uint32_t>(b) << 16); }
 
 // Broadcast the value of lane `src` of every 16-lane DPP row to the whole row.
+// Every lane has a valid source, so no old value is needed (plain mov_dpp).
 template <int src>
 GPTQ_DEV float row_bcast(float v) {
   static_assert(src >= 0 && src < 16, "row lane");
-  return __builtin_amdgcn_update_dpp(0.0f, v, 0x150 + src, 0xf, 0xf, false);
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x150 + src, 0xf, 0xf, false));
 }
 
 // Reductions over one 16-lane row with DPP (quad_perm, row_half_mirror, row_mirror).

@@ -73,7 +73,7 @@ QuantLayout quant_layout(int64_t d_out, int64_t d_in);
 hipError_t quantize_launch(const void* W, bool w_bf16, int64_t d_out, int64_t d_in, const float* U,
                            const int32_t* perm, int bits, int group_size, bool sym, bool static_groups,
                            uint8_t* codes, float* scales, int32_t* zeros, int32_t* g_idx, float* Q,
-                           float* row_loss, void* ws, hipStream_t stream, bool identity);
+                           float* row_loss, void* ws, hipStream_t stream, bool identity, int n_cu);
 
 // ------------------------------------------------------------------- pack --
 hipError_t pack_launch(const uint8_t* codes, int64_t d_out, int64_t d_in, int bits, int32_t* qweight,

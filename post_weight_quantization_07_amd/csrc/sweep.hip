@@ -11,12 +11,19 @@
 //
 // Rows are independent given U, so the sweep is parallel over output rows and
 // sequential over the block's 128 columns.  Layout: 16 lanes (one DPP row) per
-// output row, lane t owning block columns 8t .. 8t+7 in registers.  At step i
-// every lane quantizes its own copy of register i%8, the owner lane's error is
-// broadcast to its row with DPP row_newbcast, and every lane applies the
-// rank-1 update to its 8 columns with U[i][8t .. 8t+7] read from LDS (zeros
-// left of the diagonal make the update uniform).  Group ranges reduce over the
-// 16-lane row with DPP mirrors.
+// output row; block column c lives in lane c % 16 of the row, register c / 16
+// (interleaved), so from step i = 16 k on no lane needs registers below k and
+// the step skips them.  At step i every lane decides its own copy of the
+// register holding column i, the owner lane's normalised error is broadcast to
+// its row with DPP row_newbcast, and every lane applies the rank-1 update to
+// its live registers with row i of the block's U read from LDS.
+//
+// The LDS copy of U has its diagonal set to zero (the reciprocals of the
+// diagonal are kept apart) and is zero left of it, so the update leaves the
+// column of step i and every earlier column unchanged: each register ends the
+// block holding the value its column had when it was decided, and codes and
+// errors are taken from it once after the sweep with the same arithmetic.  The
+// chain of a step is then the decision, the broadcast and one fma.
 #include "gptq_common.h"
 #include "gptq_internal.h"
 
@@ -51,6 +58,7 @@ struct SweepParams {
   int sym;
   int preset;           // 1: scales/zeros of every column are already in the outputs
   int identity;         // perm is the identity
+  int nblk;             // blocks per launch (group kernel)
 };
 
 GPTQ_DEV void group_params(float lo, float hi, const SweepParams& p, float& scale, float& zero) {
@@ -69,44 +77,89 @@ GPTQ_DEV void group_params(float lo, float hi, const SweepParams& p, float& scal
   zero = p.sym ? static_cast<float>(1 << (p.bits - 1)) : rintf(-lo / scale);
 }
 
+// The decision on one weight w with scale s (y = 1 / s correctly rounded),
+// clamp bounds zl = -z, zh = maxq - z and d = 1 / U[i][i]: the code relative
+// to the zero point, qr = q - z, and the normalised error.  w / s is formed
+// correctly rounded from y: q0 = w y is within an ulp, the remainder w - s q0
+// is exact in one fma, and q0 + (w - s q0) y rounds to the quotient
+// (Markstein's correction step).  rint(w / s) clamped to [-z, maxq - z] is
+// clamp(rint(w / s) + z, 0, maxq) - z exactly (integers); the dequantized
+// weight is s qr and the error w - s qr (one fma).
+GPTQ_DEV void decide(float w, float s, float y, float zl, float zh, float d, float& qr, float& err) {
+  const float q0 = w * y;
+  const float quot = fmaf(fmaf(-s, q0, w), y, q0);
+  qr = __builtin_amdgcn_fmed3f(rintf(quot), zl, zh);
+  err = fmaf(-s, qr, w) * d;
+}
+
+// This lane's values k = R .. 7 of one row of the block's U in LDS (two
+// float4 at src): only the live ones are read, each piece at its natural
+// alignment, so no read lands in a register that is already dead.
+typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f32x2_t;
+template <int R>
+GPTQ_DEV void read_urow(const float* src, float (&d)[8]) {
+  if constexpr (R == 0) {
+    const f32x4_t a = *reinterpret_cast<const f32x4_t*>(src);
+    d[0] = a[0]; d[1] = a[1]; d[2] = a[2]; d[3] = a[3];
+  } else if constexpr (R == 1 || R == 2) {
+    if constexpr (R == 1) d[1] = src[1];
+    const f32x2_t a = *reinterpret_cast<const f32x2_t*>(src + 2);
+    d[2] = a[0]; d[3] = a[1];
+  } else if constexpr (R == 3) {
+    d[3] = src[3];
+  }
+  if constexpr (R <= 4) {
+    const f32x4_t b = *reinterpret_cast<const f32x4_t*>(src + 4);
+    d[4] = b[0]; d[5] = b[1]; d[6] = b[2]; d[7] = b[3];
+  } else if constexpr (R == 5 || R == 6) {
+    if constexpr (R == 5) d[5] = src[5];
+    const f32x2_t b = *reinterpret_cast<const f32x2_t*>(src + 6);
+    d[6] = b[0]; d[7] = b[1];
+  } else {
+    d[7] = src[7];
+  }
+}
+
+constexpr int kURing = 3;  // rows of U in registers: the current one and two read ahead
+
 // GS > 0: dynamic groups of GS columns start inside the block (GS divides
 // 128), so the range code is emitted only at steps I % GS == 0; GS == 0: every
 // column's parameters are known before the block.  Keeping the code of the
 // 128 unrolled steps small matters: it has to stay in the instruction cache.
+// Ut: the block's U in LDS as [row i][lane t][register k] (8 floats a lane).
 template <int GS, int I>
-GPTQ_DEV void sweep_step(const SweepParams& p, const float (*Ub)[kB], const float (&dv)[8], int t,
-                         float (&v)[8], float (&sc)[8], float (&rc)[8], float (&zlo)[8], float (&zhi)[8],
-                         float (&qc)[8], float (&er)[8], int64_t row, f32x4_t (&ua)[2],
-                         f32x4_t (&ub)[2]) {
-  constexpr int r = I & 7, owner = I >> 3;
-  // the next step's row of U is read now (two register sets), so its LDS
-  // latency hides behind this whole step
-  if constexpr (I + 1 < kB) {
-    ua[(I + 1) & 1] = *reinterpret_cast<const f32x4_t*>(&Ub[I + 1][8 * t]);
-    ub[(I + 1) & 1] = *reinterpret_cast<const f32x4_t*>(&Ub[I + 1][8 * t + 4]);
+GPTQ_DEV void sweep_step(const SweepParams& p, const float* Ut, const float (&dv)[8], int t, float (&v)[8],
+                         float (&sc)[8], float (&rc)[8], float (&zlo)[8], float (&zhi)[8], int64_t row,
+                         float (&un)[kURing][8]) {
+  constexpr int r = I >> 4, owner = I & 15;
+  // the row of U two steps ahead is read now, so its LDS latency hides behind
+  // a whole step; registers below that step's are dead and not read
+  if constexpr (I + 2 < kB) {
+    constexpr int r2 = (I + 2) >> 4;
+    read_urow<r2>(Ut + ((I + 2) * 16 + t) * 8, un[(I + 2) % kURing]);
   }
-  const f32x4_t u0 = ua[I & 1], u1 = ub[I & 1];
-  // dynamic groups that start inside the block: range over the group's current values
+  const float (&u)[8] = un[I % kURing];
+  // dynamic groups that start inside the block: range over the group's
+  // current values (registers I / 16 .. (I + GS - 1) / 16, all 16 lanes)
   if constexpr (GS > 0 && (I % GS) == 0) {
     if (I < p.ncols) {
+      constexpr int klo = I / 16, khi = (I + GS - 1) / 16 < 8 ? (I + GS - 1) / 16 : 7;
       float lo = 0.f, hi = 0.f;
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const int c = 8 * t + k;
+      for (int k = klo; k <= khi; ++k) {
+        const int c = t + 16 * k;
         const bool in = (c >= I) && (c < I + GS) && (c < p.ncols);
         lo = in ? fminf(lo, v[k]) : lo;
         hi = in ? fmaxf(hi, v[k]) : hi;
       }
-      if constexpr (GS > 8) {  // the group spans several lanes of the row
-        lo = row_min16(lo);
-        hi = row_max16(hi);
-      }
+      lo = row_min16(lo);
+      hi = row_max16(hi);
       float s, z;
       group_params(lo, hi, p, s, z);
       const float y = 1.0f / s;
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const int c = 8 * t + k;
+      for (int k = klo; k <= khi; ++k) {
+        const int c = t + 16 * k;
         const bool in = (c >= I) && (c < I + GS);
         sc[k] = in ? s : sc[k];
         rc[k] = in ? y : rc[k];
@@ -120,86 +173,180 @@ GPTQ_DEV void sweep_step(const SweepParams& p, const float (*Ub)[kB], const floa
       }
     }
   }
-  const float w = v[r];
-  const float s = sc[r];
-  // w / s correctly rounded from the correctly rounded reciprocal y = 1 / s:
-  // q0 = w y is within an ulp, the remainder w - s q0 is exact in one fma, and
-  // q0 + (w - s q0) y rounds to the quotient (Markstein's correction step).
-  // Three dependent operations instead of the division sequence.
-  const float y = rc[r];
-  const float q0 = w * y;
-  const float quot = fmaf(fmaf(-s, q0, w), y, q0);
-  // the code relative to the zero point, qr = q - z: rint(w / s) clamped to
-  // [-z, maxq - z] is clamp(rint(w / s) + z, 0, maxq) - z exactly (integers);
-  // the dequantized weight is s qr and the error w - s qr (one fma)
-  const float qr = __builtin_amdgcn_fmed3f(rintf(quot), zlo[r], zhi[r]);
-  const float err = fmaf(-s, qr, w) * dv[r];
+  float qr, err;
+  decide(v[r], sc[r], rc[r], zlo[r], zhi[r], dv[r], qr, err);
   const float eb = row_bcast<owner>(err);
-  qc[r] = (t == owner) ? qr : qc[r];
-  er[r] = (t == owner) ? eb : er[r];
-  // materialise the selects here: left alone, the compiler sinks them to the
-  // end of the block and keeps every step's code alive until then
-  asm volatile("" : "+v"(qc[r]), "+v"(er[r]));
   // the next column first: the next step's decision waits on it
-  constexpr int rn = (I + 1) & 7;
-  v[rn] = fmaf(-eb, rn < 4 ? u0[rn & 3] : u1[rn & 3], v[rn]);
+  constexpr int rn = (I + 1) >> 4;
+  if constexpr (I + 1 < kB) v[rn] = fmaf(-eb, u[rn], v[rn]);
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    if (k != rn) v[k] = fmaf(-eb, u0[k], v[k]);
-    if (k + 4 != rn) v[k + 4] = fmaf(-eb, u1[k], v[k + 4]);
-  }
+  for (int k = r; k < 8; ++k)
+    if (k != rn) v[k] = fmaf(-eb, u[k], v[k]);
   // keep each step a scheduling region of its own (bounded register pressure)
   __builtin_amdgcn_sched_barrier(0);
 }
 
 template <int GS, int... Is>
-GPTQ_DEV void sweep_all(const SweepParams& p, const float (*Ub)[kB], const float (&dv)[8], int t, float (&v)[8],
-                        float (&sc)[8], float (&rc)[8], float (&zlo)[8], float (&zhi)[8], float (&qc)[8],
-                        float (&er)[8], int64_t row, std::integer_sequence<int, Is...>) {
-  f32x4_t ua[2], ub[2];
-  ua[0] = *reinterpret_cast<const f32x4_t*>(&Ub[0][8 * t]);
-  ub[0] = *reinterpret_cast<const f32x4_t*>(&Ub[0][8 * t + 4]);
-  (sweep_step<GS, Is>(p, Ub, dv, t, v, sc, rc, zlo, zhi, qc, er, row, ua, ub), ...);
+GPTQ_DEV void sweep_all(const SweepParams& p, const float* Ut, const float (&dv)[8], int t, float (&v)[8],
+                        float (&sc)[8], float (&rc)[8], float (&zlo)[8], float (&zhi)[8], int64_t row,
+                        std::integer_sequence<int, Is...>) {
+  float un[kURing][8];
+  read_urow<0>(Ut + t * 8, un[0]);
+  read_urow<0>(Ut + (16 + t) * 8, un[1]);
+  (sweep_step<GS, Is>(p, Ut, dv, t, v, sc, rc, zlo, zhi, row, un), ...);
 }
 
+// The block's U (rows and columns jb .. jb + ncols) for the interleaved LDS
+// layout: thread tid takes the (row i, lane l) pairs tid + 256 u, u < 8, and
+// lane l's columns l + 16 k.  Every address is in range (rows and columns past
+// the end are clamped); the values are selected when stored.
+GPTQ_DEV void load_ublock(const SweepParams& p, int64_t jb, int ncols, int tid, float (&ul)[64]) {
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int pi = tid + 256 * u, i = std::min(pi >> 4, ncols - 1), l = pi & 15;
+    const float* src = p.U + (jb + i) * p.d_in + jb;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) ul[8 * u + k] = src[std::min(l + 16 * k, ncols - 1)];
+  }
+}
+
+// Ut[i][l][k] = U[i][l + 16 k] off the diagonal, zero on it and outside the
+// block; the diagonal goes to Dg.
+GPTQ_DEV void store_ublock(float* Ut, float* Dg, const float (&ul)[64], int ncols, int tid) {
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int pi = tid + 256 * u, i = pi >> 4, l = pi & 15;
+    float x[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int c = l + 16 * k;
+      const bool in = i < ncols && c < ncols;
+      x[k] = (in && i != c) ? ul[8 * u + k] : 0.f;
+      if (in && i == c) Dg[c] = ul[8 * u + k];
+    }
+    *reinterpret_cast<f32x4_t*>(Ut + 8 * pi) = f32x4_t{x[0], x[1], x[2], x[3]};
+    *reinterpret_cast<f32x4_t*>(Ut + 8 * pi + 4) = f32x4_t{x[4], x[5], x[6], x[7]};
+  }
+}
+
+// This lane's weights of the block (columns t + 16 k), in range for any row.
+GPTQ_DEV void load_wblock(const SweepParams& p, int64_t jb, int ncols, int64_t row, int t, float (&w)[8]) {
+  const float* src = p.Wp + std::min<int64_t>(row, p.d_out - 1) * p.d_in + jb;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) w[k] = src[std::min(t + 16 * k, ncols - 1)];
+}
+
+// Registers at the start of a block: weights (zero past the block and for
+// rows past the end), 1 / U[c][c] of this lane's columns, neutral parameters.
+GPTQ_DEV void init_block(const SweepParams& p, const float* Dg, const float (&w)[8], bool row_ok, int t,
+                         float (&v)[8], float (&dv)[8], float (&sc)[8], float (&rc)[8], float (&zlo)[8],
+                         float (&zhi)[8]) {
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const int c = t + 16 * k;
+    dv[k] = (c < p.ncols) ? 1.0f / Dg[c] : 0.f;
+    v[k] = (row_ok && c < p.ncols) ? w[k] : 0.f;
+    sc[k] = 1.f;
+    rc[k] = 1.f;
+    zlo[k] = 0.f;
+    zhi[k] = p.maxq;
+  }
+}
+
+// Scales and zero points fixed before the block (static groups, or one group
+// per row) of this lane's 8 columns.  Columns and rows past the end read the
+// block's last column / last row and are not used; the group indices first,
+// then all scale and zero loads, so they are in flight at once.
+GPTQ_DEV void load_preset(const SweepParams& p, int64_t row, bool row_ok, int t, float (&sc)[8], float (&rc)[8],
+                          float (&zlo)[8], float (&zhi)[8]) {
+  const int64_t rr = std::min<int64_t>(row, p.d_out - 1);
+  int64_t g[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const int64_t j = p.j0 + std::min(t + 16 * k, p.ncols - 1);
+    g[k] = 0;
+    if (p.group > 0) g[k] = (p.preset && !p.identity) ? p.perm[j] / p.group : j / p.group;
+  }
+  float sl[8];
+  int32_t zl[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    sl[k] = p.scales[g[k] * p.d_out + rr];
+    zl[k] = p.zeros[g[k] * p.d_out + rr];
+  }
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    if (row_ok && t + 16 * k < p.ncols) {
+      sc[k] = sl[k];
+      rc[k] = 1.0f / sl[k];
+      zlo[k] = -static_cast<float>(zl[k]);
+      zhi[k] = p.maxq - static_cast<float>(zl[k]);
+    }
+  }
+}
+
+// After a block's sweep: every register holds the value its column was
+// decided on, so the codes and errors are decided again with the same
+// arithmetic (bit for bit the chain's); the normalised errors go to `e` (the
+// row's block of the error panel, all 128 columns, zero past the block),
+// codes q = qr + z and dequantized weights s qr to their original columns.
+// Returns this lane's part of the row's loss (sum of squared normalised
+// errors); er receives the errors.
+GPTQ_DEV float finish_block(const SweepParams& p, int64_t row, bool row_ok, int t, float* e, const float (&v)[8],
+                            const float (&dv)[8], const float (&sc)[8], const float (&rc)[8],
+                            const float (&zlo)[8], const float (&zhi)[8], float (&er)[8]) {
+  float qr[8], loss = 0.f;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    decide(v[k], sc[k], rc[k], zlo[k], zhi[k], dv[k], qr[k], er[k]);
+    loss = fmaf(er[k], er[k], loss);
+  }
+  if (!row_ok) return loss;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) e[t + 16 * k] = er[k];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const int c = t + 16 * k;
+    if (c < p.ncols) {
+      const int64_t j = p.j0 + c;
+      const int64_t oc = p.identity ? j : p.perm[j];
+      p.codes[row * p.d_in + oc] = static_cast<uint8_t>(qr[k] - zlo[k]);
+      if (p.Q) p.Q[row * p.d_in + oc] = sc[k] * qr[k];
+    }
+  }
+  return loss;
+}
+
+// One block per launch.  The second block of a pair is first brought up to
+// date with the first block's errors (a 128-deep product on MFMA at the start
+// of its sweep).
 template <int GS>
 __global__ __launch_bounds__(256) void sweep_kernel(SweepParams p) {
-  __shared__ __attribute__((aligned(16))) float Ub[kB][kB];
+  __shared__ __attribute__((aligned(16))) float Ut[kB * kB];
   __shared__ __attribute__((aligned(16))) float Stg[kRowsPerWG][kB + 4];  // bring-up result
+  __shared__ float Dg[kB];
   const int tid = threadIdx.x;
-  const int t = tid & 15;
-  const int64_t row = static_cast<int64_t>(blockIdx.x) * kRowsPerWG + (tid >> 4);
+  const int t = tid & 15, rl = tid >> 4;
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * kRowsPerWG + rl;
   const bool row_ok = row < p.d_out;
 
-  // The diagonal block of U (zeros outside the block's columns) and this
-  // lane's 8 weights.  Every load reads an in-range address (the block width
-  // is a multiple of 4; rows and columns past the end are clamped) and the
-  // value is selected after, so all of them are in flight at once.
-  constexpr int kUL = kB * kB / 4 / 256;  // float4 of the U block per thread
-  const int c0 = 8 * t;
-  f32x4_t ul[kUL], wa, wb;
-#pragma unroll
-  for (int u = 0; u < kUL; ++u) {
-    const int e = tid + 256 * u, i = e >> 5, c4 = 4 * (e & 31);
-    const int ic = std::min(i, p.ncols - 1), cc = std::min(c4, p.ncols - 4);
-    ul[u] = *reinterpret_cast<const f32x4_t*>(p.U + (p.j0 + ic) * p.d_in + p.j0 + cc);
-  }
-  {
-    const float* src = p.Wp + std::min<int64_t>(row, p.d_out - 1) * p.d_in + p.j0;
-    wa = *reinterpret_cast<const f32x4_t*>(src + std::min(c0, p.ncols - 4));
-    wb = *reinterpret_cast<const f32x4_t*>(src + std::min(c0 + 4, p.ncols - 4));
-  }
+  // the block's U and this lane's weights, all in flight at once
+  float ul[64], w[8];
+  load_ublock(p, p.j0, p.ncols, tid, ul);
+  load_wblock(p, p.j0, p.ncols, row, t, w);
   // Bring-up of the second block of a pair: W[rows, block] -= Eb[rows, :] Uo
   // (16 rows x 128 columns, K = 128, the previous block is full) on MFMA
   // (v_mfma_f32_16x16x4_f32; MFMA step s takes k = 4 q + s in lane group q, so
   // a lane's A values are one float4 of its error row).  Wave w computes the
-  // 16-column blocks 2 w and 2 w + 1; Uo goes through Ub, the result through
-  // Stg into the lanes' column layout.
+  // 16-column blocks 2 w and 2 w + 1; Uo goes row-major through the LDS of
+  // Ut, the result through Stg.
   const bool bring = p.Eb != nullptr;
-  f32x4_t bup0 = {0.f, 0.f, 0.f, 0.f}, bup1 = {0.f, 0.f, 0.f, 0.f};
   if (bring) {
+    float (*Ub)[kB] = reinterpret_cast<float (*)[kB]>(Ut);
     const int lane = tid & 63, wave = tid >> 6, m = lane & 15, q = lane >> 4;
+    constexpr int kUL = kB * kB / 4 / 256;
     f32x4_t uo[kUL], ea[kB / 16];
+    f32x4_t bup0 = {0.f, 0.f, 0.f, 0.f}, bup1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int u = 0; u < kUL; ++u) {
       const int e = tid + 256 * u, i = e >> 5, c4 = 4 * (e & 31);
@@ -230,71 +377,21 @@ __global__ __launch_bounds__(256) void sweep_kernel(SweepParams p) {
       Stg[4 * q + e][32 * wave + m] = bup0[e];
       Stg[4 * q + e][32 * wave + 16 + m] = bup1[e];
     }
-    __syncthreads();  // every wave is done with Uo in Ub
+    __syncthreads();  // every wave is done with Uo in Ut
   }
-#pragma unroll
-  for (int u = 0; u < kUL; ++u) {
-    const int e = tid + 256 * u, i = e >> 5, c4 = 4 * (e & 31);
-    *reinterpret_cast<f32x4_t*>(&Ub[i][c4]) = (i < p.ncols && c4 < p.ncols) ? ul[u] : f32x4_t{0.f, 0.f, 0.f, 0.f};
-  }
+  store_ublock(Ut, Dg, ul, p.ncols, tid);
   if (bring) {
-    const f32x4_t d0 = *reinterpret_cast<const f32x4_t*>(&Stg[tid >> 4][c0]);
-    const f32x4_t d1 = *reinterpret_cast<const f32x4_t*>(&Stg[tid >> 4][c0 + 4]);
-    wa -= d0;
-    wb -= d1;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) w[k] -= Stg[rl][t + 16 * k];
   }
   __syncthreads();
 
-  // zlo, zhi: the clamp bounds -z and maxq - z of each column's relative code
-  float v[8], sc[8], rc[8], zlo[8], zhi[8], qc[8], er[8], dv[8];
-  // 1 / U[i][i] of this lane's own columns (only the owner of a column uses it)
-#pragma unroll
-  for (int k = 0; k < 8; ++k) dv[k] = (c0 + k < p.ncols) ? 1.0f / Ub[c0 + k][c0 + k] : 0.f;
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    v[k] = (row_ok && c0 < p.ncols) ? wa[k] : 0.f;
-    v[k + 4] = (row_ok && c0 + 4 < p.ncols) ? wb[k] : 0.f;
-  }
-#pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    sc[k] = 1.f;
-    rc[k] = 1.f;
-    zlo[k] = 0.f;
-    zhi[k] = p.maxq;
-    qc[k] = 0.f;
-    er[k] = 0.f;
-  }
+  float v[8], sc[8], rc[8], zlo[8], zhi[8], dv[8];
+  init_block(p, Dg, w, row_ok, t, v, dv, sc, rc, zlo, zhi);
   // parameters fixed before this block: static groups, one group per row, or a
   // dynamic group wider than the block that started in an earlier block
   const bool wide_group_running = !p.preset && p.group > kB && (p.j0 % p.group) != 0;
-  if (p.preset || wide_group_running) {
-    // columns and rows past the end read the block's last column / last row
-    // and are not used; the group indices first, then all scale and zero loads
-    const int64_t rr = std::min<int64_t>(row, p.d_out - 1);
-    int64_t g[8];
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const int64_t j = p.j0 + std::min(c0 + k, p.ncols - 1);
-      g[k] = 0;
-      if (p.group > 0) g[k] = (p.preset && !p.identity) ? p.perm[j] / p.group : j / p.group;
-    }
-    float sl[8];
-    int32_t zl[8];
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      sl[k] = p.scales[g[k] * p.d_out + rr];
-      zl[k] = p.zeros[g[k] * p.d_out + rr];
-    }
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      if (row_ok && c0 + k < p.ncols) {
-        sc[k] = sl[k];
-        rc[k] = 1.0f / sl[k];
-        zlo[k] = -static_cast<float>(zl[k]);
-        zhi[k] = p.maxq - static_cast<float>(zl[k]);
-      }
-    }
-  }
+  if (p.preset || wide_group_running) load_preset(p, row, row_ok, t, sc, rc, zlo, zhi);
   // a dynamic group wider than the block starts here: range over W[row, j0 : j0+group)
   if (!p.preset && p.group > kB && (p.j0 % p.group) == 0) {
     float lo = 0.f, hi = 0.f;
@@ -329,51 +426,184 @@ __global__ __launch_bounds__(256) void sweep_kernel(SweepParams p) {
       p.zeros[g * p.d_out + row] = static_cast<int32_t>(z);
     }
   }
-  __syncthreads();
 
-  sweep_all<GS>(p, Ub, dv, t, v, sc, rc, zlo, zhi, qc, er, row, std::make_integer_sequence<int, kB>{});
-  // codes q = qr + z, dequantized weights s qr, and the row's loss (sum of the
-  // squared normalised errors over the row's 16 lanes)
-  float qv[8], loss = 0.f;
-#pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    qv[k] = sc[k] * qc[k];
-    qc[k] -= zlo[k];
-    loss = fmaf(er[k], er[k], loss);
-  }
-  loss = row_sum16(loss);
-
+  sweep_all<GS>(p, Ut, dv, t, v, sc, rc, zlo, zhi, row, std::make_integer_sequence<int, kB>{});
+  float er[8];
+  const float loss = row_sum16(finish_block(p, row, row_ok, t, p.Err + std::min<int64_t>(row, p.d_out - 1) * p.ld_err,
+                                            v, dv, sc, rc, zlo, zhi, er));
   if (!row_ok) return;
-  // normalised errors of the block, for the trailing update
-  float* e = p.Err + row * p.ld_err + c0;
-  *reinterpret_cast<f32x4_t*>(e) = f32x4_t{er[0], er[1], er[2], er[3]};
-  *reinterpret_cast<f32x4_t*>(e + 4) = f32x4_t{er[4], er[5], er[6], er[7]};
-  // codes and dequantized weights, written in original column order
-  if (p.identity && c0 + 8 <= p.ncols) {
-    const int64_t base = row * p.d_in + p.j0 + c0;
-    uint32_t lo = 0, hi = 0;
+  if (p.row_loss && t == 0) p.row_loss[row] = (p.j0 == 0 ? 0.f : p.row_loss[row]) + loss;
+}
+
+// One launch sweeps a whole group of kGW columns (up to 8 blocks) for 16 rows
+// per workgroup, for layers whose rows fit one workgroup per CU.  The group's
+// normalised errors of the workgroup's rows stay in LDS (El), and each block is
+// brought up to date with the errors of the blocks before it in the group
+// inside the kernel: W[rows, block] -= E[rows, j0 : jb] U[j0 : jb, block] on
+// MFMA (v_mfma_f32_16x16x4_f32, A = errors from El, B = rows of U straight
+// from memory).  This replaces the per-block launches and the products inside
+// a group; the product past the group stays one GEMM per group.  The sum is
+// the lazy-batch sweep's, taken in another order.  Only groups that fit inside
+// a block (or parameters fixed before the sweep) are handled here.
+//
+// 512 threads: waves 0-3 sweep (the chain of a block is bound by the latency
+// of its dependent operations, with one chain wave per SIMD), waves 4-7
+// produce.  While the chain waves sweep block b, the producer waves bring
+// block b + 1 up to date with the errors of blocks 0 .. b - 1 on the same
+// SIMDs' matrix cores and load its U and weights; once block b is swept they
+// add its own errors (K = 128), stage the weights and the block's U in LDS,
+// and the chain waves go on.  Two workgroup barriers a block, in the same
+// order on both sides: A(b) (block b staged) and B(b) (block b swept).
+constexpr int kGW = 2 * kB * kUnitsPerGroup;  // columns per group
+constexpr int kELd = kGW + 4;                 // El row stride in floats
+constexpr int kWnLd = kB + 4;                 // staged weights: row stride in floats
+// error of (row r, group column k): four consecutive MFMA k-steps of lane
+// group q = k & 3 are one float4
+GPTQ_DEV int el_index(int r, int k) { return r * kELd + (k & 3) * (kGW / 4) + (k >> 2); }
+
+// Producer side of the bring-up of block jb from the group errors of columns
+// [k0, k0 + 128 n) (El, k relative to the group start g0): acc[h] += E U for
+// the wave's two 16-column tiles h.  MFMA k-step s takes k = 4 s + q in lane
+// group q: A = El (row m, k), B = U[g0 + k][jb + column m of the tile].  Rows
+// of U go through a ring of kRing register sets, four k-steps each.
+GPTQ_DEV void bring_up(const SweepParams& p, const float* El, int64_t g0, int64_t jb, int ncols, int k0, int n,
+                       int pw, int m, int q, f32x4_t& acc0, f32x4_t& acc1) {
+  const int ca = std::min(32 * pw + m, ncols - 1), cb = std::min(32 * pw + 16 + m, ncols - 1);
+  const float* ua = p.U + (g0 + k0 + q) * p.d_in + jb + ca;
+  const float* ub = p.U + (g0 + k0 + q) * p.d_in + jb + cb;
+  const int64_t kstep = 4 * p.d_in;  // one MFMA k-step down U
+  const int nit = 8 * n;             // iterations of four k-steps, a multiple of kRing
+  constexpr int kRing = 4;
+  float ra[kRing][4], rb[kRing][4];
+  auto fetch = [&](int it, float (&da)[4], float (&db)[4]) {
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      lo |= static_cast<uint32_t>(qc[k]) << (8 * k);
-      hi |= static_cast<uint32_t>(qc[k + 4]) << (8 * k);
+    for (int e = 0; e < 4; ++e) {
+      const int64_t off = (4 * static_cast<int64_t>(it) + e) * kstep;
+      da[e] = ua[off];
+      db[e] = ub[off];
     }
-    *reinterpret_cast<uint2*>(p.codes + base) = make_uint2(lo, hi);
-    if (p.Q) {
-      *reinterpret_cast<f32x4_t*>(p.Q + base) = f32x4_t{qv[0], qv[1], qv[2], qv[3]};
-      *reinterpret_cast<f32x4_t*>(p.Q + base + 4) = f32x4_t{qv[4], qv[5], qv[6], qv[7]};
-    }
-  } else {
+  };
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      if (c0 + k < p.ncols) {
-        const int64_t j = p.j0 + c0 + k;
-        const int64_t oc = p.identity ? j : p.perm[j];
-        p.codes[row * p.d_in + oc] = static_cast<uint8_t>(qc[k]);
-        if (p.Q) p.Q[row * p.d_in + oc] = qv[k];
+  for (int d = 0; d < kRing - 1; ++d) fetch(d, ra[d], rb[d]);
+  const float* ea = El + m * kELd + q * (kGW / 4) + k0 / 4;
+  f32x4_t an = *reinterpret_cast<const f32x4_t*>(ea);
+  for (int it0 = 0; it0 < nit; it0 += kRing) {
+#pragma unroll
+    for (int d = 0; d < kRing; ++d) {
+      const int it = it0 + d;
+      // past the end the ring refetches the last rows (unused): no branch, so
+      // the loads stay in flight across the loop's back edge; the errors of
+      // the next step are read one step early as well
+      fetch(std::min(it + kRing - 1, nit - 1), ra[(d + kRing - 1) % kRing], rb[(d + kRing - 1) % kRing]);
+      const f32x4_t a = an;
+      an = *reinterpret_cast<const f32x4_t*>(ea + 4 * std::min(it + 1, nit - 1));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(a[e], ra[d][e], acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(a[e], rb[d][e], acc1, 0, 0, 0);
+      }
+      // keep the ring in program order: this step's loads stay behind the
+      // earlier steps' products, so each set lands kRing - 1 steps early
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+}
+
+template <int GS>
+__global__ __launch_bounds__(512) void sweep_group_kernel(SweepParams p) {
+  __shared__ __attribute__((aligned(16))) float Ut[kB * kB];
+  __shared__ __attribute__((aligned(16))) float El[kRowsPerWG * kELd];
+  __shared__ __attribute__((aligned(16))) float Wn[kRowsPerWG * kWnLd];
+  __shared__ float Dg[kB];
+  const int64_t g0 = p.j0;
+  const int64_t row0 = static_cast<int64_t>(blockIdx.x) * kRowsPerWG;
+  auto block_cols = [&](int b) { return static_cast<int>(std::min<int64_t>(kB, p.d_in - g0 - int64_t{kB} * b)); };
+
+  if (threadIdx.x >= 256) {
+    // ------------------------------------------------------------ producers
+    const int pt = threadIdx.x - 256;
+    const int pw = pt >> 6, lane = pt & 63, m = lane & 15, q = lane >> 4;
+    // weights in the MFMA output layout: tile h, element e = row 4 q + e,
+    // column 32 pw + 16 h + m of the block
+    auto load_w = [&](int64_t jb, int ncols, float (&wv)[2][4]) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int64_t r = std::min<int64_t>(row0 + 4 * q + e, p.d_out - 1);
+          wv[h][e] = p.Wp[r * p.d_in + jb + std::min(32 * pw + 16 * h + m, ncols - 1)];
+        }
+    };
+    auto stage_w = [&](const float (&wv)[2][4], const f32x4_t& acc0, const f32x4_t& acc1) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        Wn[(4 * q + e) * kWnLd + 32 * pw + m] = wv[0][e] - acc0[e];
+        Wn[(4 * q + e) * kWnLd + 32 * pw + 16 + m] = wv[1][e] - acc1[e];
+      }
+    };
+    {
+      float ul[64], wv[2][4];
+      const int nc = block_cols(0);
+      load_ublock(p, g0, nc, pt, ul);
+      load_w(g0, nc, wv);
+      const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
+      stage_w(wv, z, z);
+      store_ublock(Ut, Dg, ul, nc, pt);
+    }
+    for (int b = 0; b < p.nblk; ++b) {
+      __syncthreads();  // A(b): block b staged
+      const bool next = b + 1 < p.nblk;
+      const int64_t jn = g0 + int64_t{kB} * (b + 1);
+      const int nc = next ? block_cols(b + 1) : kB;
+      float ul[64], wv[2][4];
+      f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+      if (next) {
+        load_ublock(p, jn, nc, pt, ul);
+        load_w(jn, nc, wv);
+        if (b > 0) bring_up(p, El, g0, jn, nc, 0, b, pw, m, q, acc0, acc1);  // blocks 0 .. b - 1
+      }
+      __syncthreads();  // B(b): block b swept, its errors in El, Ut free
+      if (next) {
+        bring_up(p, El, g0, jn, nc, kB * b, 1, pw, m, q, acc0, acc1);  // block b
+        stage_w(wv, acc0, acc1);
+        store_ublock(Ut, Dg, ul, nc, pt);
       }
     }
+    return;
   }
-  if (p.row_loss && t == 0) p.row_loss[row] = (p.j0 == 0 ? 0.f : p.row_loss[row]) + loss;
+
+  // ---------------------------------------------------------------- chain
+  const int tid = threadIdx.x;
+  const int t = tid & 15, rl = tid >> 4;
+  const int64_t row = row0 + rl;
+  const bool row_ok = row < p.d_out;
+  float loss = 0.f;
+  for (int b = 0; b < p.nblk; ++b) {
+    SweepParams pb = p;
+    pb.j0 = g0 + int64_t{kB} * b;
+    pb.ncols = block_cols(b);
+    __syncthreads();  // A(b)
+    float w[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) w[k] = Wn[rl * kWnLd + t + 16 * k];
+    float v[8], sc[8], rc[8], zlo[8], zhi[8], dv[8];
+    init_block(pb, Dg, w, row_ok, t, v, dv, sc, rc, zlo, zhi);
+    if (p.preset) load_preset(pb, row, row_ok, t, sc, rc, zlo, zhi);
+
+    sweep_all<GS>(pb, Ut, dv, t, v, sc, rc, zlo, zhi, row, std::make_integer_sequence<int, kB>{});
+
+    // errors to the group's panel (for the product past the group) and to El
+    // (for the next blocks' bring-up); rows past the end keep finite zeros
+    const int kb = kB * b;
+    float er[8];
+    loss += finish_block(pb, row, row_ok, t, p.Err + std::min<int64_t>(row, p.d_out - 1) * p.ld_err + kb, v, dv, sc,
+                         rc, zlo, zhi, er);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) El[el_index(rl, kb + t + 16 * k)] = er[k];
+    __syncthreads();  // B(b)
+  }
+  loss = row_sum16(loss);
+  if (row_ok && p.row_loss && t == 0) p.row_loss[row] = (g0 == 0 ? 0.f : p.row_loss[row]) + loss;
 }
 
 // Wp[r][i] = W[r][perm[i]] in fp32.
@@ -457,7 +687,7 @@ QuantLayout quant_layout(int64_t d_out, int64_t d_in) {
 hipError_t quantize_launch(const void* W, bool w_bf16, int64_t d_out, int64_t d_in, const float* U,
                            const int32_t* perm, int bits, int group_size, bool sym, bool static_groups,
                            uint8_t* codes, float* scales, int32_t* zeros, int32_t* g_idx, float* Q,
-                           float* row_loss, void* ws, hipStream_t st, bool identity) {
+                           float* row_loss, void* ws, hipStream_t st, bool identity, int n_cu) {
   const QuantLayout lay = quant_layout(d_out, d_in);
   float* Wp = reinterpret_cast<float*>(static_cast<char*>(ws) + lay.off_wp);
   float* Err = reinterpret_cast<float*>(static_cast<char*>(ws) + lay.off_err);
@@ -513,13 +743,53 @@ hipError_t quantize_launch(const void* W, bool w_bf16, int64_t d_out, int64_t d_
   // groups are used only when such groups start on their boundaries: pairs for
   // groups of 256 columns or a multiple, groups of pairs for groups up to 256
   // or a multiple of 512.
+  // Layers whose rows fit one workgroup per CU (one wave per SIMD, so the
+  // sweep is latency-bound and launches cost as much as the sweep): one
+  // launch per group, the products inside the group on MFMA in the kernel.
+  const int gs = (!preset && group <= kB) ? group : 0;
+  if ((preset || group <= kB) && blocks <= n_cu) {
+    p.ld_err = kGW;
+    p.Eb = nullptr;
+    p.Uo = nullptr;
+    p.Err = Err;
+    for (int64_t g0 = 0; g0 < d_in; g0 += kGW) {
+      p.j0 = g0;
+      p.nblk = static_cast<int>(std::min<int64_t>(kGW / kB, (d_in - g0 + kB - 1) / kB));
+      p.ncols = static_cast<int>(std::min<int64_t>(kB, d_in - g0));
+      {
+        PhaseScope ph(kPhSweep, st);
+        switch (gs) {
+          case 0: sweep_group_kernel<0><<<blocks, 512, 0, st>>>(p); break;
+          case 1: sweep_group_kernel<1><<<blocks, 512, 0, st>>>(p); break;
+          case 2: sweep_group_kernel<2><<<blocks, 512, 0, st>>>(p); break;
+          case 4: sweep_group_kernel<4><<<blocks, 512, 0, st>>>(p); break;
+          case 8: sweep_group_kernel<8><<<blocks, 512, 0, st>>>(p); break;
+          case 16: sweep_group_kernel<16><<<blocks, 512, 0, st>>>(p); break;
+          case 32: sweep_group_kernel<32><<<blocks, 512, 0, st>>>(p); break;
+          case 64: sweep_group_kernel<64><<<blocks, 512, 0, st>>>(p); break;
+          case 128: sweep_group_kernel<128><<<blocks, 512, 0, st>>>(p); break;
+          default: return hipErrorInvalidValue;  // the ABI admits only groups dividing 128 here
+        }
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+      }
+      const int64_t rest = d_in - g0 - kGW;
+      if (rest > 0) {
+        PhaseScope ph(kPhUpdate, st);
+        e = gemm_f32(d_out, rest, kGW, -1.f, Err, kGW, 0, U + g0 * d_in + g0 + kGW, d_in, 0, false, 1.f, Wp + g0 + kGW,
+                     d_in, 0, 1, false, 0, st);
+        if (e != hipSuccess) return e;
+      }
+    }
+    return hipSuccess;
+  }
+
   const bool pair = preset || group <= kB || group % (2 * kB) == 0;
   const int SB = pair ? 2 * kB : kB;
   const bool grouped = pair && (preset || group <= 2 * kB || group % (2 * kB * kUnitsPerGroup) == 0);
   const int NU = grouped ? kUnitsPerGroup : 1;  // units per trailing update
   const int64_t GW = static_cast<int64_t>(NU) * SB;
-  const int gs = (!preset && group <= kB) ? group : 0;
   p.ld_err = static_cast<int>(GW);
+  p.nblk = 1;
   for (int64_t g0 = 0; g0 < d_in; g0 += GW) {
     for (int u = 0; u < NU; ++u) {
       const int64_t j0 = g0 + static_cast<int64_t>(u) * SB;

@@ -232,6 +232,9 @@ SWEEP_CASES = [  # d_out, d_in, bits, G, sym, desc_act, static, w dtype
     (20, 1400, 4, 128, False, False, False, "f32"),   # two groups of block pairs, the last block ragged
     (16, 2304, 4, 256, True, True, False, "bf16"),    # dynamic act-order groups of 256 over three pair groups
     (16, 1536, 4, 512, True, False, False, "f32"),    # groups of 512: one trailing update per pair
+    (40, 2560, 4, 32, True, True, False, "bf16"),     # one sweep launch per group, three groups
+    (4100, 384, 4, 128, True, False, False, "bf16"),  # more rows than one workgroup per CU: a launch per block
+    (4100, 288, 3, 64, False, True, True, "f32"),     # the same, static act-order groups, last block ragged
 ]
 
 
