@@ -14,16 +14,19 @@
 // output row; block column c lives in lane c % 16 of the row, register c / 16
 // (interleaved), so from step i = 16 k on no lane needs registers below k and
 // the step skips them.  At step i every lane decides its own copy of the
-// register holding column i, the owner lane's normalised error is broadcast to
-// its row with DPP row_newbcast, and every lane applies the rank-1 update to
-// its live registers with row i of the block's U read from LDS.
+// register holding column i, the owner lane's error is broadcast to its row
+// with DPP row_newbcast, and every lane applies the rank-1 update to its live
+// registers with row i of the block's U read from LDS.
 //
-// The LDS copy of U has its diagonal set to zero (the reciprocals of the
-// diagonal are kept apart) and is zero left of it, so the update leaves the
-// column of step i and every earlier column unchanged: each register ends the
-// block holding the value its column had when it was decided, and codes and
-// errors are taken from it once after the sweep with the same arithmetic.  The
-// chain of a step is then the decision, the broadcast and one fma.
+// The LDS copy of U holds each row divided by its diagonal element, so the
+// broadcast value is the plain remainder (negated: s q - w) and the update an
+// accumulate that reads it through DPP.  Its diagonal is set to zero (the
+// diagonal is kept apart for the normalised errors) and it is zero left of
+// the diagonal, so the update leaves the column of step i and every earlier
+// column unchanged: each register ends the block holding the value its column
+// had when it was decided, and codes and errors are taken from it once after
+// the sweep with the same arithmetic.  The chain of a step is then the
+// decision and one fma.
 #include "gptq_common.h"
 #include "gptq_internal.h"
 
@@ -128,7 +131,7 @@ constexpr int kURing = 3;  // rows of U in registers: the current one and two re
 // 128 unrolled steps small matters: it has to stay in the instruction cache.
 // Ut: the block's U in LDS as [row i][lane t][register k] (8 floats a lane).
 template <int GS, int I>
-GPTQ_DEV void sweep_step(const SweepParams& p, const float* Ut, const float (&dv)[8], int t, float (&v)[8],
+GPTQ_DEV void sweep_step(const SweepParams& p, const float* Ut, int t, float (&v)[8],
                          float (&sc)[8], float (&rc)[8], float (&zlo)[8], float (&zhi)[8], int64_t row,
                          float (&un)[kURing][8]) {
   constexpr int r = I >> 4, owner = I & 15;
@@ -173,60 +176,80 @@ GPTQ_DEV void sweep_step(const SweepParams& p, const float* Ut, const float (&dv
       }
     }
   }
-  float qr, err;
-  decide(v[r], sc[r], rc[r], zlo[r], zhi[r], dv[r], qr, err);
-  const float eb = row_bcast<owner>(err);
+  // the owner's remainder s qr - w (the negated error before normalisation:
+  // the rows of U in LDS carry the factor 1 / U[i][i]), broadcast to the row;
+  // each update is then an accumulate v += e u[k] that reads the broadcast
+  // through DPP
+  const float w = v[r];
+  const float q0 = w * rc[r];
+  const float quot = fmaf(fmaf(-sc[r], q0, w), rc[r], q0);
+  const float qr = __builtin_amdgcn_fmed3f(rintf(quot), zlo[r], zhi[r]);
+  const float eb = row_bcast<owner>(fmaf(sc[r], qr, -w));
   // the next column first: the next step's decision waits on it
   constexpr int rn = (I + 1) >> 4;
-  if constexpr (I + 1 < kB) v[rn] = fmaf(-eb, u[rn], v[rn]);
+  if constexpr (I + 1 < kB) v[rn] = fmaf(eb, u[rn], v[rn]);
 #pragma unroll
   for (int k = r; k < 8; ++k)
-    if (k != rn) v[k] = fmaf(-eb, u[k], v[k]);
+    if (k != rn) v[k] = fmaf(eb, u[k], v[k]);
   // keep each step a scheduling region of its own (bounded register pressure)
   __builtin_amdgcn_sched_barrier(0);
 }
 
 template <int GS, int... Is>
-GPTQ_DEV void sweep_all(const SweepParams& p, const float* Ut, const float (&dv)[8], int t, float (&v)[8],
+GPTQ_DEV void sweep_all(const SweepParams& p, const float* Ut, int t, float (&v)[8],
                         float (&sc)[8], float (&rc)[8], float (&zlo)[8], float (&zhi)[8], int64_t row,
                         std::integer_sequence<int, Is...>) {
   float un[kURing][8];
   read_urow<0>(Ut + t * 8, un[0]);
   read_urow<0>(Ut + (16 + t) * 8, un[1]);
-  (sweep_step<GS, Is>(p, Ut, dv, t, v, sc, rc, zlo, zhi, row, un), ...);
+  (sweep_step<GS, Is>(p, Ut, t, v, sc, rc, zlo, zhi, row, un), ...);
 }
 
 // The block's U (rows and columns jb .. jb + ncols) for the interleaved LDS
 // layout: thread tid takes the (row i, lane l) pairs tid + 256 u, u < 8, and
 // lane l's columns l + 16 k.  Every address is in range (rows and columns past
 // the end are clamped); the values are selected when stored.
-GPTQ_DEV void load_ublock(const SweepParams& p, int64_t jb, int ncols, int tid, float (&ul)[64]) {
+GPTQ_DEV void load_ublock(const SweepParams& p, int64_t jb, int ncols, int tid, float (&ul)[64], float (&dg)[8]) {
 #pragma unroll
   for (int u = 0; u < 8; ++u) {
     const int pi = tid + 256 * u, i = std::min(pi >> 4, ncols - 1), l = pi & 15;
     const float* src = p.U + (jb + i) * p.d_in + jb;
 #pragma unroll
     for (int k = 0; k < 8; ++k) ul[8 * u + k] = src[std::min(l + 16 * k, ncols - 1)];
+    dg[u] = src[i];
   }
 }
 
-// Ut[i][l][k] = U[i][l + 16 k] off the diagonal, zero on it and outside the
-// block; the diagonal goes to Dg.
-GPTQ_DEV void store_ublock(float* Ut, float* Dg, const float (&ul)[64], int ncols, int tid) {
+// The loaded block of U scaled in registers for its LDS copy: U[i][l + 16 k]
+// / U[i][i] (the product with the correctly rounded reciprocal) off the
+// diagonal, zero on it and outside the block.
+GPTQ_DEV void scale_ublock(float (&ul)[64], const float (&dg)[8], int ncols, int tid) {
 #pragma unroll
   for (int u = 0; u < 8; ++u) {
     const int pi = tid + 256 * u, i = pi >> 4, l = pi & 15;
-    float x[8];
+    const float d = 1.0f / dg[u];
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
       const int c = l + 16 * k;
-      const bool in = i < ncols && c < ncols;
-      x[k] = (in && i != c) ? ul[8 * u + k] : 0.f;
-      if (in && i == c) Dg[c] = ul[8 * u + k];
+      ul[8 * u + k] = (i < ncols && c < ncols && i != c) ? ul[8 * u + k] * d : 0.f;
     }
-    *reinterpret_cast<f32x4_t*>(Ut + 8 * pi) = f32x4_t{x[0], x[1], x[2], x[3]};
-    *reinterpret_cast<f32x4_t*>(Ut + 8 * pi + 4) = f32x4_t{x[4], x[5], x[6], x[7]};
   }
+}
+
+// Ut[i][l][k] from the scaled registers; the diagonal goes to Dg.
+GPTQ_DEV void write_ublock(float* Ut, float* Dg, const float (&ul)[64], const float (&dg)[8], int ncols, int tid) {
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int pi = tid + 256 * u, i = pi >> 4, l = pi & 15;
+    if (l == (i & 15) && i < ncols) Dg[i] = dg[u];
+    *reinterpret_cast<f32x4_t*>(Ut + 8 * pi) = f32x4_t{ul[8 * u], ul[8 * u + 1], ul[8 * u + 2], ul[8 * u + 3]};
+    *reinterpret_cast<f32x4_t*>(Ut + 8 * pi + 4) = f32x4_t{ul[8 * u + 4], ul[8 * u + 5], ul[8 * u + 6], ul[8 * u + 7]};
+  }
+}
+
+GPTQ_DEV void store_ublock(float* Ut, float* Dg, float (&ul)[64], const float (&dg)[8], int ncols, int tid) {
+  scale_ublock(ul, dg, ncols, tid);
+  write_ublock(Ut, Dg, ul, dg, ncols, tid);
 }
 
 // This lane's weights of the block (columns t + 16 k), in range for any row.
@@ -331,8 +354,8 @@ __global__ __launch_bounds__(256) void sweep_kernel(SweepParams p) {
   const bool row_ok = row < p.d_out;
 
   // the block's U and this lane's weights, all in flight at once
-  float ul[64], w[8];
-  load_ublock(p, p.j0, p.ncols, tid, ul);
+  float ul[64], dg[8], w[8];
+  load_ublock(p, p.j0, p.ncols, tid, ul, dg);
   load_wblock(p, p.j0, p.ncols, row, t, w);
   // Bring-up of the second block of a pair: W[rows, block] -= Eb[rows, :] Uo
   // (16 rows x 128 columns, K = 128, the previous block is full) on MFMA
@@ -379,7 +402,7 @@ __global__ __launch_bounds__(256) void sweep_kernel(SweepParams p) {
     }
     __syncthreads();  // every wave is done with Uo in Ut
   }
-  store_ublock(Ut, Dg, ul, p.ncols, tid);
+  store_ublock(Ut, Dg, ul, dg, p.ncols, tid);
   if (bring) {
 #pragma unroll
     for (int k = 0; k < 8; ++k) w[k] -= Stg[rl][t + 16 * k];
@@ -427,7 +450,7 @@ __global__ __launch_bounds__(256) void sweep_kernel(SweepParams p) {
     }
   }
 
-  sweep_all<GS>(p, Ut, dv, t, v, sc, rc, zlo, zhi, row, std::make_integer_sequence<int, kB>{});
+  sweep_all<GS>(p, Ut, t, v, sc, rc, zlo, zhi, row, std::make_integer_sequence<int, kB>{});
   float er[8];
   const float loss = row_sum16(finish_block(p, row, row_ok, t, p.Err + std::min<int64_t>(row, p.d_out - 1) * p.ld_err,
                                             v, dv, sc, rc, zlo, zhi, er));
@@ -509,6 +532,33 @@ GPTQ_DEV void bring_up(const SweepParams& p, const float* El, int64_t g0, int64_
   }
 }
 
+// The last 128 k of a bring-up (the block just swept), split: its rows of U
+// are read before that block's sweep ends (tail_fetch), the products run once
+// its errors are in El (tail_mfma).
+GPTQ_DEV void tail_fetch(const SweepParams& p, int64_t g0, int64_t jb, int ncols, int k0, int pw, int m, int q,
+                         float (&tb)[32][2]) {
+  const int ca = std::min(32 * pw + m, ncols - 1), cb = std::min(32 * pw + 16 + m, ncols - 1);
+  const float* src = p.U + (g0 + k0 + q) * p.d_in + jb;
+#pragma unroll
+  for (int s = 0; s < 32; ++s) {
+    tb[s][0] = src[4 * s * p.d_in + ca];
+    tb[s][1] = src[4 * s * p.d_in + cb];
+  }
+}
+
+GPTQ_DEV void tail_mfma(const float* El, int k0, int m, int q, const float (&tb)[32][2], f32x4_t& acc0,
+                        f32x4_t& acc1) {
+  const float* ea = El + m * kELd + q * (kGW / 4) + k0 / 4;
+  f32x4_t a[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) a[j] = *reinterpret_cast<const f32x4_t*>(ea + 4 * j);
+#pragma unroll
+  for (int s = 0; s < 32; ++s) {
+    acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s >> 2][s & 3], tb[s][0], acc0, 0, 0, 0);
+    acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s >> 2][s & 3], tb[s][1], acc1, 0, 0, 0);
+  }
+}
+
 template <int GS>
 __global__ __launch_bounds__(512) void sweep_group_kernel(SweepParams p) {
   __shared__ __attribute__((aligned(16))) float Ut[kB * kB];
@@ -542,31 +592,33 @@ __global__ __launch_bounds__(512) void sweep_group_kernel(SweepParams p) {
       }
     };
     {
-      float ul[64], wv[2][4];
+      float ul[64], dg[8], wv[2][4];
       const int nc = block_cols(0);
-      load_ublock(p, g0, nc, pt, ul);
+      load_ublock(p, g0, nc, pt, ul, dg);
       load_w(g0, nc, wv);
       const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
       stage_w(wv, z, z);
-      store_ublock(Ut, Dg, ul, nc, pt);
+      store_ublock(Ut, Dg, ul, dg, nc, pt);
     }
     for (int b = 0; b < p.nblk; ++b) {
       __syncthreads();  // A(b): block b staged
       const bool next = b + 1 < p.nblk;
       const int64_t jn = g0 + int64_t{kB} * (b + 1);
       const int nc = next ? block_cols(b + 1) : kB;
-      float ul[64], wv[2][4];
+      float ul[64], dg[8], wv[2][4], tb[32][2];
       f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
       if (next) {
-        load_ublock(p, jn, nc, pt, ul);
+        load_ublock(p, jn, nc, pt, ul, dg);
         load_w(jn, nc, wv);
+        tail_fetch(p, g0, jn, nc, kB * b, pw, m, q, tb);
         if (b > 0) bring_up(p, El, g0, jn, nc, 0, b, pw, m, q, acc0, acc1);  // blocks 0 .. b - 1
+        scale_ublock(ul, dg, nc, pt);
       }
       __syncthreads();  // B(b): block b swept, its errors in El, Ut free
       if (next) {
-        bring_up(p, El, g0, jn, nc, kB * b, 1, pw, m, q, acc0, acc1);  // block b
+        tail_mfma(El, kB * b, m, q, tb, acc0, acc1);  // block b
         stage_w(wv, acc0, acc1);
-        store_ublock(Ut, Dg, ul, nc, pt);
+        write_ublock(Ut, Dg, ul, dg, nc, pt);
       }
     }
     return;
@@ -590,7 +642,7 @@ __global__ __launch_bounds__(512) void sweep_group_kernel(SweepParams p) {
     init_block(pb, Dg, w, row_ok, t, v, dv, sc, rc, zlo, zhi);
     if (p.preset) load_preset(pb, row, row_ok, t, sc, rc, zlo, zhi);
 
-    sweep_all<GS>(pb, Ut, dv, t, v, sc, rc, zlo, zhi, row, std::make_integer_sequence<int, kB>{});
+    sweep_all<GS>(pb, Ut, t, v, sc, rc, zlo, zhi, row, std::make_integer_sequence<int, kB>{});
 
     // errors to the group's panel (for the product past the group) and to El
     // (for the next blocks' bring-up); rows past the end keep finite zeros
