@@ -363,8 +363,15 @@ def kernel_metrics(layer, ph):
                         "in_kernel_TFLOP/s": f_in / (sw_ms * 1e-3) / 1e12}
     if up_ms > 0:
         tf = f_up / (up_ms * 1e-3) / 1e12
-        out["trailing_update"] = {"launches": up_n, "ms": up_ms, "flops": f_up, "TFLOP/s": tf,
-                                  "frac_fp32_peak": tf / PEAK_FP32_TFLOPS}
+        if group_launch:
+            # fp32 products on the bf16 matrix cores: each operand split into
+            # three bf16 parts, six part products a flop, so the ceiling is the
+            # bf16 dense peak over six (fp32-equivalent flops)
+            peak, how = PEAK_BF16_TFLOPS / 6.0, "bf16 matrix cores, three-part split, six products"
+        else:
+            peak, how = PEAK_FP32_TFLOPS, "fp32 matrix cores"
+        out["trailing_update"] = {"launches": up_n, "ms": up_ms, "flops": f_up, "TFLOP/s": tf, "on": how,
+                                  "peak_TFLOP/s": peak, "frac_peak": tf / peak}
     return out
 
 
@@ -376,7 +383,7 @@ def all_configs(args):
     import synth
     lines = ["| cfg | layer | d_out x d_in | N | x | bits/G | ms per solve | weight cols/s | accumulate "
              "TFLOP/s (% peak) | prepare TFLOP/s (% fp32) | quantize: update TFLOP/s (% fp32), sweep GB/s "
-             "(% HBM) | sweep kernel: us per block, GB/s (% HBM) | update products: TFLOP/s (% fp32) | pack GB/s |",
+             "(% HBM) | sweep kernel: us per block, GB/s (% HBM) | update products: TFLOP/s (% of their peak) | pack GB/s |",
              "|---|---|---|---:|---|---|---:|---:|---:|---:|---:|---:|---:|---:|"]
     for c in (1, 2, 3, 4, 5):
         for layer in synth.config_layers(c):
@@ -396,7 +403,7 @@ def all_configs(args):
                 f"{m['quantize']['update TFLOP/s']:.1f} ({100 * m['quantize']['frac']:.1f}%), "
                 f"{m['quantize']['sweep GB/s']:.0f} ({100 * m['quantize']['sweep frac of HBM']:.1f}%) | "
                 f"{sw.get('us_per_block', 0):.1f}, {sw.get('GB/s', 0):.0f} ({100 * sw.get('frac_hbm', 0):.1f}%) | "
-                f"{up.get('TFLOP/s', 0):.1f} ({100 * up.get('frac_fp32_peak', 0):.1f}%) | "
+                f"{up.get('TFLOP/s', 0):.1f} ({100 * up.get('frac_peak', 0):.1f}% of {up.get('peak_TFLOP/s', 0):.0f}) | "
                 f"{m['pack']['GB/s']:.0f} |")
             del ls
             torch.cuda.empty_cache()

@@ -12,8 +12,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libgptq.so")
-SOURCES = ["hessian.hip", "gemm_f32.hip", "prepare.hip", "sweep.hip", "pack.hip", "dequant.hip", "abi.cpp",
-           "phase_timing.cpp"]
+SOURCES = ["hessian.hip", "gemm_f32.hip", "gemm_x3.hip", "prepare.hip", "sweep.hip", "pack.hip", "dequant.hip",
+           "abi.cpp", "phase_timing.cpp"]
 
 ARCH = os.environ.get("GPTQ_OFFLOAD_ARCH", "gfx950")
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

@@ -1,0 +1,245 @@
+// fp32 products on the bf16 matrix cores.
+//
+// On gfx950 a v_mfma_f32_16x16x4_f32 runs at the fp32 vector rate and holds
+// the SIMD's vector ALU while it runs; the bf16 matrix cores are 16 times
+// faster per flop and leave the vector ALU to other waves.  An fp32 value x
+// splits exactly into three bf16 parts, x = hi + mid + lo: hi = bf16(x), the
+// remainder x - hi is exact (Sterbenz), mid = bf16 of it, and what is left
+// has at most 6 significant bits, so lo holds it exactly.  A product x y is
+// then the sum of the nine part products; the six kept here (hi hi, hi mid,
+// mid hi, hi lo, mid mid, lo hi) leave out terms below 2^-24 |x y|, and each
+// part product is exact in the fp32 accumulator.  The result has the accuracy
+// of an fp32 product (it is not bit-equal to one: the sums round in another
+// order).  It serves the GPTQ lazy-batch update W[:, j+B:] -= Err U[j:j+B,
+// j+B:] (GPTQ 实战 ch.5, section 5.1.8).
+//
+// Operands are given as three planes of bf16 bit patterns in the blocked
+// panel layout (x3_offset): A over [M][K], B transposed over [N][K]; C fp32
+// row-major.  A block of 128 rows x 16 k is 4 KB contiguous, so one stage of
+// one plane of a tile is one contiguous read.
+// 128 x 128 output tile per 256-thread workgroup (2 x 2 waves of 64 x 64,
+// v_mfma_f32_32x32x16_bf16), 16-k stages (24 KB: both operands, three
+// planes) moved to LDS by buffer_load ... lds through a ring of three slots,
+// two workgroups a CU (measured at 4096 x 3072 x 1024: 156 us against 194 us
+// for one workgroup with a six-slot ring and 163 us for three with two).
+#include "gptq_common.h"
+#include "gptq_internal.h"
+
+#include <algorithm>
+
+namespace gptq {
+
+namespace {
+
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+constexpr int kT = 128;        // output tile edge
+constexpr int kSK = 16;        // k per stage (one MFMA k-step)
+constexpr int kSlots = 3;      // ring depth: two stages in flight; two workgroups a CU
+constexpr int kPlaneStage = kT * kSK * 2;    // bytes of one plane of one operand stage (4 KB)
+constexpr int kSlotBytes = 6 * kPlaneStage;  // A and B, three planes each (24 KB)
+
+#define GPTQ_X3_VMCNT(n) (((n) & 15) | (((n) >> 4) << 14) | 0x0F70)
+
+struct X3Params {
+  const uint16_t* A;  // 3 planes of [M][K], blocked
+  const uint16_t* B;  // 3 planes of [N][K], blocked
+  int64_t M, N, K;
+  int64_t sA, sB;     // plane strides in elements
+  float* C;
+  int64_t ldc;
+  float alpha;
+  int tiles_m, tiles_n;
+};
+
+GPTQ_DEV __amdgpu_buffer_rsrc_t x3_rsrc(const uint16_t* base, int64_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a >> 32));
+  const int64_t cl = bytes < 0 ? 0 : (bytes > 0x7FFFFFF0LL ? 0x7FFFFFF0LL : bytes);
+  const int n = __builtin_amdgcn_readfirstlane(static_cast<int>(cl));
+  void* b = reinterpret_cast<void*>((static_cast<uint64_t>(hi) << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(b, static_cast<short>(0), n, 0x00020000);
+}
+
+// One plane of one operand stage: the 4 KB block of 128 rows x 16 k (32
+// bytes a row, two 16-byte chunks), four 1 KB pieces of 32 rows.  Physical
+// chunk p of row r in LDS holds logical chunk p ^ ((r >> 3) & 1): an MFMA
+// operand read (16 consecutive rows, one chunk each) then covers all 64
+// banks; the permutation stays inside each row's 32 bytes, so a piece is
+// still one contiguous 1 KB read.  Wave w moves piece w of each plane; rs
+// spans the tile's row block, st is the stage.
+GPTQ_DEV void x3_dma(__amdgpu_buffer_rsrc_t rs, uint8_t* dst, int st, int wave, int lane) {
+  const int r = 32 * wave + (lane >> 1);
+  const int c = (lane & 1) ^ ((r >> 3) & 1);
+  const uint32_t voff = static_cast<uint32_t>((st * 2048 + r * 16 + 8 * c) * 2);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(dst + wave * 1024), 16, voff, 0, 0, 0);
+}
+
+// the 8 bf16 of row r, k 8 h .. 8 h + 7 (h = lane >> 5) of a stage plane
+GPTQ_DEV bf16x8_t x3_read(const uint8_t* plane, int r, int h) {
+  const int pc = h ^ ((r >> 3) & 1);
+  return *reinterpret_cast<const bf16x8_t*>(plane + r * 32 + pc * 16);
+}
+
+__global__ __launch_bounds__(256, 2) void gemm_x3_kernel(X3Params p) {
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[kSlots * kSlotBytes];
+  // Workgroups go round-robin to the 8 XCDs (b % 8), each with its own L2:
+  // the tile list is cut into 8 contiguous ranges, one per XCD, listed in
+  // groups of 8 tile rows, column by column inside a group, so the tiles an
+  // XCD runs at once share rows of A and columns of B.
+  constexpr int kXcd = 8;
+  const int b = blockIdx.x, G = p.tiles_m * p.tiles_n;
+  const int x = b % kXcd, xl = b / kXcd;
+  const int base = G / kXcd, rem = G % kXcd;
+  const int t = x * base + min(x, rem) + xl;
+  const int g = t / (8 * p.tiles_n);
+  const int rows = min(8, p.tiles_m - 8 * g);
+  const int idx = t - g * 8 * p.tiles_n;
+  const int tn = idx / rows, tm = 8 * g + idx % rows;
+  const int64_t m0 = static_cast<int64_t>(tm) * kT, n0 = static_cast<int64_t>(tn) * kT;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+
+  // a tile's row block: K / 16 blocks of 4 KB (rows past M or N are padding)
+  __amdgpu_buffer_rsrc_t ra[3], rb[3];
+#pragma unroll
+  for (int pl = 0; pl < 3; ++pl) {
+    ra[pl] = x3_rsrc(p.A + pl * p.sA + m0 * p.K, kT * p.K * 2);
+    rb[pl] = x3_rsrc(p.B + pl * p.sB + n0 * p.K, kT * p.K * 2);
+  }
+  auto issue = [&](int st) {
+    uint8_t* d = ring + (st % kSlots) * kSlotBytes;
+#pragma unroll
+    for (int pl = 0; pl < 3; ++pl) {
+      x3_dma(ra[pl], d + pl * kPlaneStage, st, wave, lane);
+      x3_dma(rb[pl], d + (3 + pl) * kPlaneStage, st, wave, lane);
+    }
+  };
+  constexpr int kLoads = 6;  // DMA instructions per wave per stage
+
+  f32x16_t acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+  const int h = lane >> 5, l32 = lane & 31;
+  auto compute = [&](const uint8_t* d) {
+    bf16x8_t a[2][3], bb[2][3];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int pl = 0; pl < 3; ++pl) {
+        a[i][pl] = x3_read(d + pl * kPlaneStage, wm * 64 + 32 * i + l32, h);
+        bb[i][pl] = x3_read(d + (3 + pl) * kPlaneStage, wn * 64 + 32 * i + l32, h);
+      }
+    // the six part products, smallest first, each over the four
+    // independent accumulators in turn
+    constexpr int PA[6] = {2, 1, 0, 1, 0, 0}, PB[6] = {0, 1, 2, 0, 1, 0};
+#pragma unroll
+    for (int q = 0; q < 6; ++q)
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj)
+          acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i][PA[q]], bb[jj][PB[q]], acc[i][jj], 0, 0, 0);
+  };
+
+  const int nstage = static_cast<int>((p.K + kSK - 1) / kSK);
+  // stage x lives in slot x % kSlots; before computing it: its loads have
+  // landed (later stages may stay in flight), barrier (everyone is done with
+  // slot (x - 1) % kSlots), refill that slot with stage x + kSlots - 1
+  for (int st = 0; st < kSlots - 1 && st < nstage; ++st) issue(st);
+  for (int xs = 0; xs < nstage; ++xs) {
+    const int ahead = min(kSlots - 2, nstage - 1 - xs);  // stages issued after xs
+    switch (ahead) {
+      case 4: __builtin_amdgcn_s_waitcnt(GPTQ_X3_VMCNT(4 * kLoads)); break;
+      case 3: __builtin_amdgcn_s_waitcnt(GPTQ_X3_VMCNT(3 * kLoads)); break;
+      case 2: __builtin_amdgcn_s_waitcnt(GPTQ_X3_VMCNT(2 * kLoads)); break;
+      case 1: __builtin_amdgcn_s_waitcnt(GPTQ_X3_VMCNT(kLoads)); break;
+      default: __builtin_amdgcn_s_waitcnt(GPTQ_X3_VMCNT(0)); break;
+    }
+    __builtin_amdgcn_s_barrier();
+    if (xs + kSlots - 1 < nstage) issue(xs + kSlots - 1);
+    compute(ring + (xs % kSlots) * kSlotBytes);
+  }
+
+  // C += alpha acc: accumulator element e of lane l in a 32 x 32 block is row
+  // 8 (e / 4) + 4 (l / 32) + e % 4, column l % 32.  Every C value is loaded
+  // before the first store, so the loads are in flight together.
+  float cv[2][2][16];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) {
+      const int64_t n = n0 + wn * 64 + 32 * jj + l32;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int64_t m = m0 + wm * 64 + 32 * i + 8 * (e >> 2) + 4 * h + (e & 3);
+        cv[i][jj][e] = (m < p.M && n < p.N) ? p.C[m * p.ldc + n] : 0.f;
+      }
+    }
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) {
+      const int64_t n = n0 + wn * 64 + 32 * jj + l32;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int64_t m = m0 + wm * 64 + 32 * i + 8 * (e >> 2) + 4 * h + (e & 3);
+        if (m < p.M && n < p.N) p.C[m * p.ldc + n] = fmaf(p.alpha, acc[i][jj][e], cv[i][jj][e]);
+      }
+    }
+}
+
+// planes of the transposed block in the blocked layout: element (n, k) of
+// plane pl = part pl of src[k][n] for k < K, n < N (src row-major, ld
+// elements); 64 x 64 tiles through LDS.  Padding rows n >= N are not written.
+__global__ __launch_bounds__(256) void split3_t_kernel(const float* src, int64_t ld, int64_t K, int64_t N,
+                                                       uint16_t* out, int64_t plane) {
+  __shared__ float tile[64][65];
+  const int64_t k0 = static_cast<int64_t>(blockIdx.y) * 64, nb = static_cast<int64_t>(blockIdx.x) * 64;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  for (int r = ty; r < 64; r += 4) {
+    const int64_t k = k0 + r, n = nb + tx;
+    tile[r][tx] = (k < K && n < N) ? src[k * ld + n] : 0.f;
+  }
+  __syncthreads();
+  for (int r = ty; r < 64; r += 4) {
+    const int64_t n = nb + r, k = k0 + tx;
+    if (n < N && k < K) {
+      uint16_t hh, mm, ll;
+      split3(tile[tx][r], hh, mm, ll);
+      const int64_t o = x3_offset(n, k, K);
+      out[o] = hh;
+      out[plane + o] = mm;
+      out[2 * plane + o] = ll;
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t gemm_x3(int64_t M, int64_t N, int64_t K, float alpha, const uint16_t* A, int64_t sA, const uint16_t* Bt,
+                   int64_t sB, float* C, int64_t ldc, hipStream_t stream) {
+  if (M <= 0 || N <= 0) return hipSuccess;
+  X3Params p{A, Bt, M, N, K, sA, sB, C, ldc, alpha, 0, 0};
+  p.tiles_m = static_cast<int>((M + kT - 1) / kT);
+  p.tiles_n = static_cast<int>((N + kT - 1) / kT);
+  gemm_x3_kernel<<<p.tiles_m * p.tiles_n, 256, 0, stream>>>(p);
+  return hipGetLastError();
+}
+
+hipError_t split3_t(const float* src, int64_t ld, int64_t K, int64_t N, uint16_t* out, hipStream_t stream) {
+  if (K <= 0 || N <= 0) return hipSuccess;
+  const dim3 grid(static_cast<unsigned>((N + 63) / 64), static_cast<unsigned>((K + 63) / 64));
+  split3_t_kernel<<<grid, 256, 0, stream>>>(src, ld, K, N, out, x3_plane_elems(N, K));
+  return hipGetLastError();
+}
+
+}  // namespace gptq

@@ -19,6 +19,24 @@ GPTQ_DEV int lane_id() { return static_cast<int>(threadIdx.x) & (kWave - 1); }
 // bf16 bit pattern -> fp32 (exact)
 GPTQ_DEV float bf16_to_f32(uint16_t b) { return __uint_as_float(static_cast<uint32_t>(b) << 16); }
 
+// fp32 -> bf16 bit pattern, round to nearest even (finite values)
+GPTQ_DEV uint16_t f32_to_bf16_rn(float x) {
+  const uint32_t u = __float_as_uint(x);
+  return static_cast<uint16_t>((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+
+// The exact split x = hi + mid + lo into bf16 parts: hi = bf16(x), the
+// remainder x - hi is exact (Sterbenz), mid = bf16 of it, and the rest has at
+// most 6 significant bits, so lo is exact (finite x above the fp32 normal
+// range's bottom by 2^23).
+GPTQ_DEV void split3(float x, uint16_t& h, uint16_t& m, uint16_t& l) {
+  h = f32_to_bf16_rn(x);
+  const float r1 = x - bf16_to_f32(h);
+  m = f32_to_bf16_rn(r1);
+  const float r2 = r1 - bf16_to_f32(m);
+  l = f32_to_bf16_rn(r2);
+}
+
 // Broadcast the value of lane `src` of every 16-lane DPP row to the whole row.
 // Every lane has a valid source, so no old value is needed (plain mov_dpp).
 template <int src>

@@ -65,11 +65,34 @@ hipError_t gemm_f32(int64_t M, int64_t N, int64_t K, float alpha, const float* A
                     float* C, int64_t ldc, int64_t sC, int batch, bool lower_tiles, int tri,
                     hipStream_t stream);
 
+// fp32 product on the bf16 matrix cores (gemm_x3.hip): C[M,N] += alpha * A B
+// with A given as three bf16 planes over [M][K] (plane stride sA) and B as
+// three planes of its transpose over [N][K] (plane stride sB), each the exact
+// split x = hi + mid + lo of the fp32 values; six part products.  Planes use
+// the blocked panel layout below (rows padded to 128, K multiple of 16).
+// split3_t writes the planes of the transpose of a row-major fp32 block
+// src[K][N] (row stride ld), plane stride x3_plane_elems(N, K).
+//
+// Blocked panel layout: element (r, k) of a plane of K columns sits at
+// x3_offset(r, k, K): blocks of 128 rows x 16 k, 4 KB contiguous, row-major
+// inside a block, blocks ordered by row block, then k block.
+__host__ __device__ inline int64_t x3_offset(int64_t r, int64_t k, int64_t K) {
+  return ((r >> 7) * (K >> 4) + (k >> 4)) * 2048 + (r & 127) * 16 + (k & 15);
+}
+__host__ __device__ inline int64_t x3_plane_elems(int64_t rows, int64_t K) { return ((rows + 127) >> 7) * 128 * K; }
+hipError_t gemm_x3(int64_t M, int64_t N, int64_t K, float alpha, const uint16_t* A, int64_t sA, const uint16_t* Bt,
+                   int64_t sB, float* C, int64_t ldc, hipStream_t stream);
+hipError_t split3_t(const float* src, int64_t ld, int64_t K, int64_t N, uint16_t* out, hipStream_t stream);
+
 // --------------------------------------------------------------- quantize --
 struct QuantLayout {
   size_t off_wp, off_err, ws_bytes;
+  size_t off_ea, off_bt;  // one launch per group: error planes, transposed U planes
 };
-QuantLayout quant_layout(int64_t d_out, int64_t d_in);
+// one sweep launch per group of columns: layers whose rows fit one workgroup
+// per CU, with groups inside a block or parameters fixed before the sweep
+bool group_launch(int64_t d_out, int group_size, bool static_groups, int n_cu);
+QuantLayout quant_layout(int64_t d_out, int64_t d_in, bool group);
 hipError_t quantize_launch(const void* W, bool w_bf16, int64_t d_out, int64_t d_in, const float* U,
                            const int32_t* perm, int bits, int group_size, bool sym, bool static_groups,
                            uint8_t* codes, float* scales, int32_t* zeros, int32_t* g_idx, float* Q,

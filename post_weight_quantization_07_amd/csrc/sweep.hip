@@ -62,6 +62,8 @@ struct SweepParams {
   int preset;           // 1: scales/zeros of every column are already in the outputs
   int identity;         // perm is the identity
   int nblk;             // blocks per launch (group kernel)
+  uint16_t* Ea;         // group kernel: the group's errors as three bf16 planes (blocked panel layout)
+  int64_t ea_plane;     // elements per plane
 };
 
 GPTQ_DEV void group_params(float lo, float hi, const SweepParams& p, float& scale, float& zero) {
@@ -325,8 +327,10 @@ GPTQ_DEV float finish_block(const SweepParams& p, int64_t row, bool row_ok, int 
     loss = fmaf(er[k], er[k], loss);
   }
   if (!row_ok) return loss;
+  if (e) {
 #pragma unroll
-  for (int k = 0; k < 8; ++k) e[t + 16 * k] = er[k];
+    for (int k = 0; k < 8; ++k) e[t + 16 * k] = er[k];
+  }
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
     const int c = t + 16 * k;
@@ -644,14 +648,25 @@ __global__ __launch_bounds__(512) void sweep_group_kernel(SweepParams p) {
 
     sweep_all<GS>(pb, Ut, t, v, sc, rc, zlo, zhi, row, std::make_integer_sequence<int, kB>{});
 
-    // errors to the group's panel (for the product past the group) and to El
-    // (for the next blocks' bring-up); rows past the end keep finite zeros
+    // errors to El (for the next blocks' bring-up; rows past the end keep
+    // finite zeros) and, split into three bf16 planes, to the group's panel
+    // for the product past the group
     const int kb = kB * b;
     float er[8];
-    loss += finish_block(pb, row, row_ok, t, p.Err + std::min<int64_t>(row, p.d_out - 1) * p.ld_err + kb, v, dv, sc,
-                         rc, zlo, zhi, er);
+    loss += finish_block(pb, row, row_ok, t, nullptr, v, dv, sc, rc, zlo, zhi, er);
 #pragma unroll
     for (int k = 0; k < 8; ++k) El[el_index(rl, kb + t + 16 * k)] = er[k];
+    if (row_ok) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        uint16_t hh, mm, ll;
+        split3(er[k], hh, mm, ll);
+        const int64_t o = x3_offset(row, kb + t + 16 * k, kGW);
+        p.Ea[o] = hh;
+        p.Ea[p.ea_plane + o] = mm;
+        p.Ea[2 * p.ea_plane + o] = ll;
+      }
+    }
     __syncthreads();  // B(b)
   }
   loss = row_sum16(loss);
@@ -727,12 +742,26 @@ int grid_for(int64_t total) {
 
 }  // namespace
 
-QuantLayout quant_layout(int64_t d_out, int64_t d_in) {
+bool group_launch(int64_t d_out, int group_size, bool static_groups, int n_cu) {
+  const int group = group_size > 0 ? group_size : 0;
+  const bool preset = static_groups || group == 0;
+  return (preset || group <= kB) && (d_out + kRowsPerWG - 1) / kRowsPerWG <= n_cu;
+}
+
+QuantLayout quant_layout(int64_t d_out, int64_t d_in, bool group) {
   auto up = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
   QuantLayout L{};
   L.off_wp = 0;
   L.off_err = up(static_cast<size_t>(d_out) * d_in * sizeof(float));
   L.ws_bytes = L.off_err + up(static_cast<size_t>(d_out) * 2 * kB * kUnitsPerGroup * sizeof(float));
+  if (group) {
+    // the group's errors and the transposed rows of U past the group, three
+    // bf16 planes each, for the product on the bf16 matrix cores
+    L.off_ea = L.ws_bytes;
+    L.ws_bytes += up(3 * static_cast<size_t>(x3_plane_elems(d_out, kGW)) * sizeof(uint16_t));
+    L.off_bt = L.ws_bytes;
+    L.ws_bytes += up(3 * static_cast<size_t>(x3_plane_elems(d_in, kGW)) * sizeof(uint16_t));
+  }
   return L;
 }
 
@@ -740,7 +769,8 @@ hipError_t quantize_launch(const void* W, bool w_bf16, int64_t d_out, int64_t d_
                            const int32_t* perm, int bits, int group_size, bool sym, bool static_groups,
                            uint8_t* codes, float* scales, int32_t* zeros, int32_t* g_idx, float* Q,
                            float* row_loss, void* ws, hipStream_t st, bool identity, int n_cu) {
-  const QuantLayout lay = quant_layout(d_out, d_in);
+  const bool by_group = group_launch(d_out, group_size, static_groups, n_cu);
+  const QuantLayout lay = quant_layout(d_out, d_in, by_group);
   float* Wp = reinterpret_cast<float*>(static_cast<char*>(ws) + lay.off_wp);
   float* Err = reinterpret_cast<float*>(static_cast<char*>(ws) + lay.off_err);
   const int group = group_size > 0 ? group_size : 0;
@@ -799,11 +829,14 @@ hipError_t quantize_launch(const void* W, bool w_bf16, int64_t d_out, int64_t d_
   // sweep is latency-bound and launches cost as much as the sweep): one
   // launch per group, the products inside the group on MFMA in the kernel.
   const int gs = (!preset && group <= kB) ? group : 0;
-  if ((preset || group <= kB) && blocks <= n_cu) {
+  if (by_group) {
     p.ld_err = kGW;
     p.Eb = nullptr;
     p.Uo = nullptr;
     p.Err = Err;
+    p.Ea = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + lay.off_ea);
+    p.ea_plane = x3_plane_elems(d_out, kGW);
+    uint16_t* Bt = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + lay.off_bt);
     for (int64_t g0 = 0; g0 < d_in; g0 += kGW) {
       p.j0 = g0;
       p.nblk = static_cast<int>(std::min<int64_t>(kGW / kB, (d_in - g0 + kB - 1) / kB));
@@ -824,11 +857,14 @@ hipError_t quantize_launch(const void* W, bool w_bf16, int64_t d_out, int64_t d_
         }
         if ((e = hipGetLastError()) != hipSuccess) return e;
       }
+      // the columns past the group: W[:, c0:] -= E U[g0 : g0 + kGW, c0:] on the
+      // bf16 matrix cores (three-part split of both operands)
       const int64_t rest = d_in - g0 - kGW;
       if (rest > 0) {
         PhaseScope ph(kPhUpdate, st);
-        e = gemm_f32(d_out, rest, kGW, -1.f, Err, kGW, 0, U + g0 * d_in + g0 + kGW, d_in, 0, false, 1.f, Wp + g0 + kGW,
-                     d_in, 0, 1, false, 0, st);
+        const int64_t c0 = g0 + kGW;
+        if ((e = split3_t(U + g0 * d_in + c0, d_in, kGW, rest, Bt, st)) != hipSuccess) return e;
+        e = gemm_x3(d_out, rest, kGW, -1.f, p.Ea, p.ea_plane, Bt, x3_plane_elems(rest, kGW), Wp + c0, d_in, st);
         if (e != hipSuccess) return e;
       }
     }

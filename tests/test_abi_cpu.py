@@ -97,7 +97,12 @@ def test_workspace_sizes(lib):
     assert lib.gptq_hessian_workspace_size(0, 10, 1) == 0
     assert lib.gptq_hessian_workspace_size(4096, 262144, 1) > 0
     assert lib.gptq_prepare_workspace_size(4096) >= 4096 * 4096 * 4
-    assert lib.gptq_workspace_size(4096, 4096, None) >= 4096 * 4096 * 4
+    assert lib.gptq_workspace_size(4096, 4096, ctypes.byref(_cfg())) >= 4096 * 4096 * 4
+    # one sweep launch per group (here: the default CU count without a device)
+    # adds the bf16 error and U planes; the size needs a valid config
+    assert (lib.gptq_workspace_size(4096, 4096, ctypes.byref(_cfg(group_size=128)))
+            > lib.gptq_workspace_size(4096, 4096, ctypes.byref(_cfg(group_size=256))))
+    assert lib.gptq_workspace_size(4096, 4096, None) == 0
 
 
 def test_python_config_mirrors_pages():
