@@ -46,11 +46,13 @@ struct X3Params {
   const uint16_t* A;  // 3 planes of [M][K], blocked
   const uint16_t* B;  // 3 planes of [N][K], blocked
   int64_t M, N, K;
+  int64_t ldk;        // width of the planes' blocked layout (>= K): the product uses its first K columns
   int64_t sA, sB;     // plane strides in elements
   float* C;
   int64_t ldc;
   float alpha;
   int tiles_m, tiles_n;
+  int lower;          // only the tiles on or below the diagonal; nothing written above the 64-block diagonal
 };
 
 GPTQ_DEV __amdgpu_buffer_rsrc_t x3_rsrc(const uint16_t* base, int64_t bytes) {
@@ -89,15 +91,26 @@ __global__ __launch_bounds__(256, 2) void gemm_x3_kernel(X3Params p) {
   // the tile list is cut into 8 contiguous ranges, one per XCD, listed in
   // groups of 8 tile rows, column by column inside a group, so the tiles an
   // XCD runs at once share rows of A and columns of B.
+  // Lower-tile problems list the tiles (i >= j) row by row.
   constexpr int kXcd = 8;
-  const int b = blockIdx.x, G = p.tiles_m * p.tiles_n;
+  const int b = blockIdx.x, G = p.lower ? p.tiles_m * (p.tiles_m + 1) / 2 : p.tiles_m * p.tiles_n;
   const int x = b % kXcd, xl = b / kXcd;
   const int base = G / kXcd, rem = G % kXcd;
   const int t = x * base + min(x, rem) + xl;
-  const int g = t / (8 * p.tiles_n);
-  const int rows = min(8, p.tiles_m - 8 * g);
-  const int idx = t - g * 8 * p.tiles_n;
-  const int tn = idx / rows, tm = 8 * g + idx % rows;
+  int tm, tn;
+  if (p.lower) {
+    int i = static_cast<int>((__builtin_sqrtf(8.f * t + 1.f) - 1.f) * 0.5f);
+    while (i * (i + 1) / 2 > t) --i;
+    while ((i + 1) * (i + 2) / 2 <= t) ++i;
+    tm = i;
+    tn = t - i * (i + 1) / 2;
+  } else {
+    const int g = t / (8 * p.tiles_n);
+    const int rows = min(8, p.tiles_m - 8 * g);
+    const int idx = t - g * 8 * p.tiles_n;
+    tn = idx / rows;
+    tm = 8 * g + idx % rows;
+  }
   const int64_t m0 = static_cast<int64_t>(tm) * kT, n0 = static_cast<int64_t>(tn) * kT;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -107,8 +120,8 @@ __global__ __launch_bounds__(256, 2) void gemm_x3_kernel(X3Params p) {
   __amdgpu_buffer_rsrc_t ra[3], rb[3];
 #pragma unroll
   for (int pl = 0; pl < 3; ++pl) {
-    ra[pl] = x3_rsrc(p.A + pl * p.sA + m0 * p.K, kT * p.K * 2);
-    rb[pl] = x3_rsrc(p.B + pl * p.sB + n0 * p.K, kT * p.K * 2);
+    ra[pl] = x3_rsrc(p.A + pl * p.sA + m0 * p.ldk, kT * p.ldk * 2);
+    rb[pl] = x3_rsrc(p.B + pl * p.sB + n0 * p.ldk, kT * p.ldk * 2);
   }
   auto issue = [&](int st) {
     uint8_t* d = ring + (st % kSlots) * kSlotBytes;
@@ -192,7 +205,8 @@ __global__ __launch_bounds__(256, 2) void gemm_x3_kernel(X3Params p) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int64_t m = m0 + wm * 64 + 32 * i + 8 * (e >> 2) + 4 * h + (e & 3);
-        if (m < p.M && n < p.N) p.C[m * p.ldc + n] = fmaf(p.alpha, acc[i][jj][e], cv[i][jj][e]);
+        if (m < p.M && n < p.N && !(p.lower && (m >> 6) < (n >> 6)))
+          p.C[m * p.ldc + n] = fmaf(p.alpha, acc[i][jj][e], cv[i][jj][e]);
       }
     }
 }
@@ -226,12 +240,14 @@ __global__ __launch_bounds__(256) void split3_t_kernel(const float* src, int64_t
 }  // namespace
 
 hipError_t gemm_x3(int64_t M, int64_t N, int64_t K, float alpha, const uint16_t* A, int64_t sA, const uint16_t* Bt,
-                   int64_t sB, float* C, int64_t ldc, hipStream_t stream) {
+                   int64_t sB, float* C, int64_t ldc, hipStream_t stream, int64_t ldk, bool lower) {
   if (M <= 0 || N <= 0) return hipSuccess;
-  X3Params p{A, Bt, M, N, K, sA, sB, C, ldc, alpha, 0, 0};
+  if (ldk <= 0) ldk = K;
+  X3Params p{A, Bt, M, N, K, ldk, sA, sB, C, ldc, alpha, 0, 0, lower ? 1 : 0};
   p.tiles_m = static_cast<int>((M + kT - 1) / kT);
   p.tiles_n = static_cast<int>((N + kT - 1) / kT);
-  gemm_x3_kernel<<<p.tiles_m * p.tiles_n, 256, 0, stream>>>(p);
+  const int tiles = lower ? p.tiles_m * (p.tiles_m + 1) / 2 : p.tiles_m * p.tiles_n;
+  gemm_x3_kernel<<<tiles, 256, 0, stream>>>(p);
   return hipGetLastError();
 }
 

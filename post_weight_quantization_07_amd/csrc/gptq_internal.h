@@ -47,7 +47,7 @@ hipError_t hessian_launch(const HessPlan& plan, float* S, int64_t d_in, const vo
 constexpr int kPanel = 128;  // Cholesky panel / diagonal block width
 
 struct PrepLayout {
-  size_t off_hr, off_t, off_diag, off_dinv, off_lambda, ws_bytes;
+  size_t off_hr, off_t, off_diag, off_dinv, off_lambda, off_p, ws_bytes;
 };
 PrepLayout prepare_layout(int64_t d_in);
 hipError_t prepare_launch(float* S_to_H, int64_t d_in, int64_t n_total, float damp, bool desc_act,
@@ -80,8 +80,11 @@ __host__ __device__ inline int64_t x3_offset(int64_t r, int64_t k, int64_t K) {
   return ((r >> 7) * (K >> 4) + (k >> 4)) * 2048 + (r & 127) * 16 + (k & 15);
 }
 __host__ __device__ inline int64_t x3_plane_elems(int64_t rows, int64_t K) { return ((rows + 127) >> 7) * 128 * K; }
+// ldk: width of the planes' layout when the product uses only their first K
+// columns (0: K).  lower: square C, only tiles on or below the diagonal, and
+// nothing written above the 64-block diagonal (the Cholesky update).
 hipError_t gemm_x3(int64_t M, int64_t N, int64_t K, float alpha, const uint16_t* A, int64_t sA, const uint16_t* Bt,
-                   int64_t sB, float* C, int64_t ldc, hipStream_t stream);
+                   int64_t sB, float* C, int64_t ldc, hipStream_t stream, int64_t ldk = 0, bool lower = false);
 hipError_t split3_t(const float* src, int64_t ld, int64_t K, int64_t N, uint16_t* out, hipStream_t stream);
 
 // --------------------------------------------------------------- quantize --

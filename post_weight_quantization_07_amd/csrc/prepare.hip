@@ -132,6 +132,7 @@ constexpr int kLP = kNB + 4;    // LDS row pitch (floats)
 constexpr int kChunk = 32;      // panel rows solved per pass
 constexpr int kMaxPanelWG = 256;
 constexpr int kPanelGroup = 4;  // panels per trailing update of the Cholesky
+constexpr int kPGW = kNB * kPanelGroup;  // columns of a panel group
 using Blk = float (*)[kLP];
 constexpr int kTP = 68;        // row pitch of the 64x64 product buffer
 using TBlk = float (*)[kTP];
@@ -498,7 +499,7 @@ GPTQ_DEV void solve_rows(Blk L, Blk M, int lane, f32x4_t (&acc)[4]) {
 }
 
 __global__ __launch_bounds__(256, 1) void panel_kernel(float* Hr, int64_t n, int64_t k, int32_t* info,
-                                                         float* Dinv) {
+                                                         float* Dinv, uint16_t* P, int64_t pplane, int64_t kg) {
   __shared__ __attribute__((aligned(16))) float L[kNB][kLP];
   __shared__ __attribute__((aligned(16))) float M[kNB][kLP];
   __shared__ __attribute__((aligned(16))) float Tb[kNB / 2][kTP];
@@ -675,7 +676,17 @@ __global__ __launch_bounds__(256, 1) void panel_kernel(float* Hr, int64_t n, int
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int64_t row = r0 + 16 * (t & 1) + 4 * q + e;
-        if (row < n) Hr[row * n + k + 16 * J + m] = acc[t][e];
+        if (row < n) {
+          Hr[row * n + k + 16 * J + m] = acc[t][e];
+          // and as three bf16 planes, column (k - kg) + 16 J + m of the
+          // group's panel: the operands of the Cholesky updates
+          uint16_t hh, mm, ll;
+          split3(acc[t][e], hh, mm, ll);
+          const int64_t o = x3_offset(row, k - kg + 16 * J + m, kPGW);
+          P[o] = hh;
+          P[pplane + o] = mm;
+          P[2 * pplane + o] = ll;
+        }
       }
     }
     __syncthreads();
@@ -724,6 +735,8 @@ PrepLayout prepare_layout(int64_t d) {
   off += up(static_cast<size_t>((d + kNB - 1) / kNB) * kNB * kNB * sizeof(float));
   L.off_lambda = off;
   off += 256;
+  L.off_p = off;  // a panel group's factor columns as three bf16 planes (blocked layout)
+  off += up(3 * static_cast<size_t>(x3_plane_elems(d, kPGW)) * sizeof(uint16_t));
   L.ws_bytes = off;
   return L;
 }
@@ -744,6 +757,8 @@ hipError_t prepare_launch(float* S, int64_t n, int64_t n_total, float damp, bool
   float* diag = reinterpret_cast<float*>(w + lay.off_diag);
   float* lam = reinterpret_cast<float*>(w + lay.off_lambda);
   float* Dinv = reinterpret_cast<float*>(w + lay.off_dinv);
+  uint16_t* P = reinterpret_cast<uint16_t*>(w + lay.off_p);
+  const int64_t pplane = x3_plane_elems(n, kPGW);
   const int64_t nn = n * n;
 
   {
@@ -763,15 +778,19 @@ hipError_t prepare_launch(float* S, int64_t n, int64_t n_total, float damp, bool
   // each later panel's block column is first brought up to date with the
   // group's earlier panels (a tall product, K = 128 per earlier panel), and
   // the trailing matrix past the group takes one update with all of the
-  // group's columns (K = 128 kPanelGroup; the group's L21 blocks are adjacent
-  // columns of Hr).  The same products as one update per panel, summed in
-  // another order; the large lower-triangle update reads and writes the
-  // trailing matrix once per group instead of once per panel.
-  for (int64_t k = 0; k < n; k += kNB * kPanelGroup) {
+  // group's columns (K = 128 kPanelGroup).  The same products as one update
+  // per panel, summed in another order; the large lower-triangle update reads
+  // and writes the trailing matrix once per group instead of once per panel.
+  // The trailing update runs on the bf16 matrix cores (gemm_x3): the panel
+  // kernels write their factor rows below the diagonal block also as three
+  // bf16 planes of the group's panel P, which serves as both operands.
+  for (int64_t k = 0; k < n; k += kPGW) {
     for (int h = 0; h < kPanelGroup; ++h) {
       const int64_t kh = k + h * kNB;
       if (kh >= n) break;
       if (h > 0) {
+        // a 128-column product: 64 x 64 tiles on the fp32 matrix cores give
+        // the CUs enough tiles
         const int64_t wc = std::min<int64_t>(kNB, n - kh);
         const float* A = Hr + kh * n + k;  // rows kh .., the earlier panels' columns
         PhaseScope ph(kPhCholUpdate, st);
@@ -782,17 +801,16 @@ hipError_t prepare_launch(float* S, int64_t n, int64_t n_total, float damp, bool
       const int blocks = 1 + static_cast<int>(std::min<int64_t>((below + kChunk - 1) / kChunk, kMaxPanelWG - 1));
       {
         PhaseScope ph(kPhPanel, st);
-        panel_kernel<<<blocks, 256, 0, st>>>(Hr, n, kh, info, Dinv);
+        panel_kernel<<<blocks, 256, 0, st>>>(Hr, n, kh, info, Dinv, P, pplane, k);
       }
       GPTQ_TRY(hipGetLastError());
     }
-    const int64_t ke = std::min<int64_t>(n, k + kNB * kPanelGroup);
+    const int64_t ke = std::min<int64_t>(n, k + kPGW);
     const int64_t below = n - ke;
     if (below > 0) {
-      const float* P = Hr + ke * n + k;
+      const uint16_t* A = P + x3_offset(ke, 0, kPGW);
       PhaseScope ph(kPhCholUpdate, st);
-      GPTQ_TRY(gemm_f32(below, below, ke - k, -1.f, P, n, 0, P, n, 0, true, 1.f, Hr + ke * (n + 1), n, 0, 1, true,
-                        0, st));
+      GPTQ_TRY(gemm_x3(below, below, ke - k, -1.f, A, pplane, A, pplane, Hr + ke * (n + 1), n, st, kPGW, true));
     }
   }
   // triangular inverse by recursive doubling over the inverted diagonal blocks
