@@ -302,13 +302,15 @@ class LayerSolve:
 
 def update_gemm_flops(d_out, d_in, group_size, static_groups, group_launch=False):
     """Algorithmic flops of the trailing-update products the quantize stage
-    launches as separate products.  One sweep launch per group of 1024
-    columns (group_launch; layers whose rows fit one workgroup per CU, groups
-    inside a block): the products inside a group run in the sweep kernel and
-    the columns past each group take one product with all of its errors.
-    Otherwise blocks are swept in pairs, pairs in groups of four; a later pair
-    of a group is first brought up to date with the group's earlier pairs (a
-    product), the second block of a pair inside its sweep kernel."""
+    launches as separate products, as (fp32 products, three-part products).
+    Blocks are swept in pairs, pairs in groups of four (1024 columns) where
+    the groups allow; the columns past each group take one product with all
+    of the group's errors, on the bf16 matrix cores for groups of 1024
+    columns (fp32 otherwise).  One sweep launch per group (group_launch;
+    layers whose rows fit one workgroup per CU) runs the products inside a
+    group in the sweep kernel; otherwise a later pair of a group is first
+    brought up to date with the group's earlier pairs (an fp32 product), the
+    second block of a pair inside its sweep kernel."""
     B = 128
     g = group_size if group_size > 0 else 0
     preset = static_groups or g == 0
@@ -317,17 +319,20 @@ def update_gemm_flops(d_out, d_in, group_size, static_groups, group_launch=False
     grouped = pair and (preset or g <= 2 * B or g % (2 * B * 4) == 0)
     NU = 4 if grouped else 1
     GW = NU * SB
-    f = 0.0
+    f32, x3 = 0.0, 0.0
     for g0 in range(0, d_in, GW):
         for u in range(1, NU):
             j0 = g0 + u * SB
             if j0 >= d_in or group_launch:
                 break
-            f += 2.0 * d_out * min(SB, d_in - j0) * (j0 - g0)
+            f32 += 2.0 * d_out * min(SB, d_in - j0) * (j0 - g0)
         rest = d_in - g0 - GW
         if rest > 0:
-            f += 2.0 * d_out * rest * GW
-    return f
+            if GW == 1024:
+                x3 += 2.0 * d_out * rest * GW
+            else:
+                f32 += 2.0 * d_out * rest * GW
+    return f32, x3
 
 
 def cross_block_flops(d_out, d_in):
@@ -351,7 +356,8 @@ def kernel_metrics(layer, ph):
     n_blocks = -(-d_in // 128)
     group_launch = 0 < sw_n < n_blocks
     b_sweep = float(d_out) * d_in * (9 + 8.0 / G)
-    f_up = update_gemm_flops(d_out, d_in, layer.group_size, layer.static_groups, group_launch)
+    f_f32, f_x3 = update_gemm_flops(d_out, d_in, layer.group_size, layer.static_groups, group_launch)
+    f_up = f_f32 + f_x3
     f_in = cross_block_flops(d_out, d_in) - f_up
     out = {"phases_ms": {k: round(v[0], 4) for k, v in ph.items()},
            "phases_launches": {k: v[1] for k, v in ph.items()}}
@@ -363,15 +369,18 @@ def kernel_metrics(layer, ph):
                         "in_kernel_TFLOP/s": f_in / (sw_ms * 1e-3) / 1e12}
     if up_ms > 0:
         tf = f_up / (up_ms * 1e-3) / 1e12
-        if group_launch:
-            # fp32 products on the bf16 matrix cores: each operand split into
-            # three bf16 parts, six part products a flop, so the ceiling is the
-            # bf16 dense peak over six (fp32-equivalent flops)
-            peak, how = PEAK_BF16_TFLOPS / 6.0, "bf16 matrix cores, three-part split, six products"
-        else:
-            peak, how = PEAK_FP32_TFLOPS, "fp32 matrix cores"
-        out["trailing_update"] = {"launches": up_n, "ms": up_ms, "flops": f_up, "TFLOP/s": tf, "on": how,
-                                  "peak_TFLOP/s": peak, "frac_peak": tf / peak}
+        # fp32 products on the bf16 matrix cores: each operand split into three
+        # bf16 parts, six part products a flop, so their ceiling is the bf16
+        # dense peak over six (fp32-equivalent flops); the rest on the fp32
+        # matrix cores.  The ceiling of the mix: its flops over the least time.
+        peak_x3 = PEAK_BF16_TFLOPS / 6.0
+        t_min = f_f32 / (PEAK_FP32_TFLOPS * 1e12) + f_x3 / (peak_x3 * 1e12)
+        peak = f_up / t_min / 1e12
+        how = ("bf16 matrix cores, three-part split, six products" if f_f32 == 0 else
+               "fp32 matrix cores" if f_x3 == 0 else
+               f"fp32 matrix cores ({f_f32 / f_up:.0%} of flops), bf16 three-part split (the rest)")
+        out["trailing_update"] = {"launches": up_n, "ms": up_ms, "flops": f_up, "flops_three_part": f_x3,
+                                  "TFLOP/s": tf, "on": how, "peak_TFLOP/s": peak, "frac_peak": tf / peak}
     return out
 
 

@@ -160,8 +160,8 @@ gptq_status gptq_prepare_hinv(float* S_to_H, int64_t d_in, int64_t n_total, cons
  *   row_loss_or_null optional [d_out] fp32: sum of err^2 over the row, which
  *                    equals (w - w_hat) H_d (w - w_hat)^T
  * Requires d_in % (32 / bits) == 0 (d_in % 32 == 0 for 3 bits).
- * gptq_workspace_size depends on cfg and on the current device (its CU
- * count picks the launch plan); it returns 0 for an invalid cfg or size.
+ * gptq_workspace_size depends on cfg (its group layout picks the launch
+ * plan's buffers); it returns 0 for an invalid cfg or size.
  */
 size_t gptq_workspace_size(int64_t d_out, int64_t d_in, const gptq_config* cfg);
 gptq_status gptq_quantize_layer(const void* W, int32_t wt, int64_t d_out, int64_t d_in,

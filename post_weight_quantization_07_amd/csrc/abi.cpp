@@ -107,8 +107,7 @@ gptq_status gptq_prepare_hinv(float* S_to_H, int64_t d_in, int64_t n_total, cons
 
 size_t gptq_workspace_size(int64_t d_out, int64_t d_in, const gptq_config* cfg) {
   if (!dim_ok(d_out) || !dim_ok(d_in) || gptq_config_validate(cfg) != GPTQ_OK) return 0;
-  const bool group = gptq::group_launch(d_out, cfg->group_size, cfg->static_groups != 0, device_cus());
-  return gptq::quant_layout(d_out, d_in, group).ws_bytes;
+  return gptq::quant_layout(d_out, d_in, gptq::quant_planes(cfg->group_size, cfg->static_groups != 0)).ws_bytes;
 }
 
 gptq_status gptq_quantize_layer(const void* W, int32_t wt, int64_t d_out, int64_t d_in, const float* U,
@@ -123,7 +122,7 @@ gptq_status gptq_quantize_layer(const void* W, int32_t wt, int64_t d_out, int64_
   if (!aligned16(U) || !aligned16(codes) || (Q_or_null && !aligned16(Q_or_null))) return GPTQ_ERR_INVALID_ARG;
   const int n_cu = device_cus();
   const gptq::QuantLayout lay =
-      gptq::quant_layout(d_out, d_in, gptq::group_launch(d_out, cfg->group_size, cfg->static_groups != 0, n_cu));
+      gptq::quant_layout(d_out, d_in, gptq::quant_planes(cfg->group_size, cfg->static_groups != 0));
   if (!ws || ws_bytes < lay.ws_bytes || !aligned256(ws)) return GPTQ_ERR_WORKSPACE;
   return from_hip(gptq::quantize_launch(W, wt == GPTQ_BF16, d_out, d_in, U, perm, cfg->bits, cfg->group_size,
                                         cfg->sym != 0, cfg->static_groups != 0, codes, scales, zeros, g_idx,

@@ -62,8 +62,9 @@ struct SweepParams {
   int preset;           // 1: scales/zeros of every column are already in the outputs
   int identity;         // perm is the identity
   int nblk;             // blocks per launch (group kernel)
-  uint16_t* Ea;         // group kernel: the group's errors as three bf16 planes (blocked panel layout)
+  uint16_t* Ea;         // or null: the group's errors as three bf16 planes (blocked panel layout)
   int64_t ea_plane;     // elements per plane
+  int ea_col;           // launch per block: the block's first column in the group's panel
 };
 
 GPTQ_DEV void group_params(float lo, float hi, const SweepParams& p, float& scale, float& zero) {
@@ -459,6 +460,18 @@ __global__ __launch_bounds__(256) void sweep_kernel(SweepParams p) {
   const float loss = row_sum16(finish_block(p, row, row_ok, t, p.Err + std::min<int64_t>(row, p.d_out - 1) * p.ld_err,
                                             v, dv, sc, rc, zlo, zhi, er));
   if (!row_ok) return;
+  if (p.Ea) {
+    // and as three bf16 planes, for the product past the group
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      uint16_t hh, mm, ll;
+      split3(er[k], hh, mm, ll);
+      const int64_t o = x3_offset(row, p.ea_col + t + 16 * k, 2 * kB * kUnitsPerGroup);
+      p.Ea[o] = hh;
+      p.Ea[p.ea_plane + o] = mm;
+      p.Ea[2 * p.ea_plane + o] = ll;
+    }
+  }
   if (p.row_loss && t == 0) p.row_loss[row] = (p.j0 == 0 ? 0.f : p.row_loss[row]) + loss;
 }
 
@@ -742,19 +755,26 @@ int grid_for(int64_t total) {
 
 }  // namespace
 
+bool quant_planes(int group_size, bool static_groups) {
+  const int group = group_size > 0 ? group_size : 0;
+  const bool preset = static_groups || group == 0;
+  const bool pair = preset || group <= kB || group % (2 * kB) == 0;
+  return pair && (preset || group <= 2 * kB || group % (2 * kB * kUnitsPerGroup) == 0);
+}
+
 bool group_launch(int64_t d_out, int group_size, bool static_groups, int n_cu) {
   const int group = group_size > 0 ? group_size : 0;
   const bool preset = static_groups || group == 0;
   return (preset || group <= kB) && (d_out + kRowsPerWG - 1) / kRowsPerWG <= n_cu;
 }
 
-QuantLayout quant_layout(int64_t d_out, int64_t d_in, bool group) {
+QuantLayout quant_layout(int64_t d_out, int64_t d_in, bool planes) {
   auto up = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
   QuantLayout L{};
   L.off_wp = 0;
   L.off_err = up(static_cast<size_t>(d_out) * d_in * sizeof(float));
   L.ws_bytes = L.off_err + up(static_cast<size_t>(d_out) * 2 * kB * kUnitsPerGroup * sizeof(float));
-  if (group) {
+  if (planes) {
     // the group's errors and the transposed rows of U past the group, three
     // bf16 planes each, for the product on the bf16 matrix cores
     L.off_ea = L.ws_bytes;
@@ -770,7 +790,7 @@ hipError_t quantize_launch(const void* W, bool w_bf16, int64_t d_out, int64_t d_
                            uint8_t* codes, float* scales, int32_t* zeros, int32_t* g_idx, float* Q,
                            float* row_loss, void* ws, hipStream_t st, bool identity, int n_cu) {
   const bool by_group = group_launch(d_out, group_size, static_groups, n_cu);
-  const QuantLayout lay = quant_layout(d_out, d_in, by_group);
+  const QuantLayout lay = quant_layout(d_out, d_in, quant_planes(group_size, static_groups));
   float* Wp = reinterpret_cast<float*>(static_cast<char*>(ws) + lay.off_wp);
   float* Err = reinterpret_cast<float*>(static_cast<char*>(ws) + lay.off_err);
   const int group = group_size > 0 ? group_size : 0;
@@ -878,6 +898,12 @@ hipError_t quantize_launch(const void* W, bool w_bf16, int64_t d_out, int64_t d_
   const int64_t GW = static_cast<int64_t>(NU) * SB;
   p.ld_err = static_cast<int>(GW);
   p.nblk = 1;
+  // groups of kGW columns: the product past each group on the bf16 matrix
+  // cores (the sweep kernels also write the errors as planes)
+  const bool planes = GW == kGW;
+  uint16_t* Bt = planes ? reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + lay.off_bt) : nullptr;
+  p.Ea = planes ? reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + lay.off_ea) : nullptr;
+  p.ea_plane = x3_plane_elems(d_out, kGW);
   for (int64_t g0 = 0; g0 < d_in; g0 += GW) {
     for (int u = 0; u < NU; ++u) {
       const int64_t j0 = g0 + static_cast<int64_t>(u) * SB;
@@ -900,6 +926,7 @@ hipError_t quantize_launch(const void* W, bool w_bf16, int64_t d_out, int64_t d_
         p.j0 = jb;
         p.ncols = ncols;
         p.Err = Err + u * SB + h * kB;
+        p.ea_col = u * SB + h * kB;
         PhaseScope ph(kPhSweep, st);
         switch (gs) {
           case 0: sweep_kernel<0><<<blocks, 256, 0, st>>>(p); break;
@@ -919,8 +946,14 @@ hipError_t quantize_launch(const void* W, bool w_bf16, int64_t d_out, int64_t d_
     const int64_t rest = d_in - g0 - GW;
     if (rest > 0) {
       PhaseScope ph(kPhUpdate, st);
-      e = gemm_f32(d_out, rest, GW, -1.f, Err, GW, 0, U + g0 * d_in + g0 + GW, d_in, 0, false, 1.f, Wp + g0 + GW,
-                   d_in, 0, 1, false, 0, st);
+      const int64_t c0 = g0 + GW;
+      if (planes) {
+        if ((e = split3_t(U + g0 * d_in + c0, d_in, kGW, rest, Bt, st)) != hipSuccess) return e;
+        e = gemm_x3(d_out, rest, kGW, -1.f, p.Ea, p.ea_plane, Bt, x3_plane_elems(rest, kGW), Wp + c0, d_in, st);
+      } else {
+        e = gemm_f32(d_out, rest, GW, -1.f, Err, GW, 0, U + g0 * d_in + c0, d_in, 0, false, 1.f, Wp + c0, d_in, 0, 1,
+                     false, 0, st);
+      }
       if (e != hipSuccess) return e;
     }
   }

@@ -98,10 +98,13 @@ def test_workspace_sizes(lib):
     assert lib.gptq_hessian_workspace_size(4096, 262144, 1) > 0
     assert lib.gptq_prepare_workspace_size(4096) >= 4096 * 4096 * 4
     assert lib.gptq_workspace_size(4096, 4096, ctypes.byref(_cfg())) >= 4096 * 4096 * 4
-    # one sweep launch per group (here: the default CU count without a device)
-    # adds the bf16 error and U planes; the size needs a valid config
+    # groups of 1024 columns add the bf16 error and U planes for the product
+    # past each group (a dynamic group of 384 columns sweeps block by block
+    # with no such groups); the size needs a valid config
     assert (lib.gptq_workspace_size(4096, 4096, ctypes.byref(_cfg(group_size=128)))
-            > lib.gptq_workspace_size(4096, 4096, ctypes.byref(_cfg(group_size=256))))
+            > lib.gptq_workspace_size(4096, 4096, ctypes.byref(_cfg(group_size=384))))
+    assert (lib.gptq_workspace_size(4096, 4096, ctypes.byref(_cfg(group_size=128)))
+            == lib.gptq_workspace_size(4096, 4096, ctypes.byref(_cfg(group_size=2048))))
     assert lib.gptq_workspace_size(4096, 4096, None) == 0
 
 

@@ -235,6 +235,7 @@ SWEEP_CASES = [  # d_out, d_in, bits, G, sym, desc_act, static, w dtype
     (40, 2560, 4, 32, True, True, False, "bf16"),     # one sweep launch per group, three groups
     (4100, 384, 4, 128, True, False, False, "bf16"),  # more rows than one workgroup per CU: a launch per block
     (4100, 288, 3, 64, False, True, True, "f32"),     # the same, static act-order groups, last block ragged
+    (4100, 1152, 4, 128, True, True, False, "bf16"),  # a launch per block, product past a 1024-column group
 ]
 
 
