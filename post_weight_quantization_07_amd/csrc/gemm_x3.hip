@@ -22,6 +22,10 @@
 // planes) moved to LDS by buffer_load ... lds through a ring of three slots,
 // two workgroups a CU (measured at 4096 x 3072 x 1024: 156 us against 194 us
 // for one workgroup with a six-slot ring and 163 us for three with two).
+// Each wave reads the next stage's operand fragments from LDS while its
+// products of the current stage run (two register sets, one fragment read
+// between two products): 4-5% faster on the large shapes.  A 256 x 128 tile
+// (eight waves, one workgroup a CU) was slower.
 #include "gptq_common.h"
 #include "gptq_internal.h"
 
@@ -40,7 +44,8 @@ constexpr int kSlots = 3;      // ring depth: two stages in flight; two workgrou
 constexpr int kPlaneStage = kT * kSK * 2;    // bytes of one plane of one operand stage (4 KB)
 constexpr int kSlotBytes = 6 * kPlaneStage;  // A and B, three planes each (24 KB)
 
-#define GPTQ_X3_VMCNT(n) (((n) & 15) | (((n) >> 4) << 14) | 0x0F70)
+// s_waitcnt immediate: vmcnt(n) and lgkmcnt(0)
+#define GPTQ_X3_VMLGK(n) (((n) & 15) | (((n) >> 4) << 14) | 0x0070)
 
 struct X3Params {
   const uint16_t* A;  // 3 planes of [M][K], blocked
@@ -142,17 +147,18 @@ __global__ __launch_bounds__(256, 2) void gemm_x3_kernel(X3Params p) {
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
   const int h = lane >> 5, l32 = lane & 31;
-  auto compute = [&](const uint8_t* d) {
-    bf16x8_t a[2][3], bb[2][3];
+  // fragments of one stage: a[i][plane], b[j][plane]
+  struct Frag { bf16x8_t a[2][3], b[2][3]; };
+  auto read = [&](Frag& f, const uint8_t* d) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int pl = 0; pl < 3; ++pl)
 #pragma unroll
-      for (int pl = 0; pl < 3; ++pl) {
-        a[i][pl] = x3_read(d + pl * kPlaneStage, wm * 64 + 32 * i + l32, h);
-        bb[i][pl] = x3_read(d + (3 + pl) * kPlaneStage, wn * 64 + 32 * i + l32, h);
+      for (int i = 0; i < 2; ++i) {
+        f.a[i][pl] = x3_read(d + pl * kPlaneStage, wm * 64 + 32 * i + l32, h);
+        f.b[i][pl] = x3_read(d + (3 + pl) * kPlaneStage, wn * 64 + 32 * i + l32, h);
       }
-    // the six part products, smallest first, each over the four
-    // independent accumulators in turn
+  };
+  auto mfma = [&](const Frag& f) {
     constexpr int PA[6] = {2, 1, 0, 1, 0, 0}, PB[6] = {0, 1, 2, 0, 1, 0};
 #pragma unroll
     for (int q = 0; q < 6; ++q)
@@ -160,27 +166,49 @@ __global__ __launch_bounds__(256, 2) void gemm_x3_kernel(X3Params p) {
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int jj = 0; jj < 2; ++jj)
-          acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i][PA[q]], bb[jj][PB[q]], acc[i][jj], 0, 0, 0);
+          acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i][PA[q]], f.b[jj][PB[q]], acc[i][jj], 0, 0, 0);
+  };
+  // the next stage's 12 fragment reads spread over this stage's 24 products
+  auto interleave = [&]() {
+#pragma unroll
+    for (int r = 0; r < 12; ++r) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
   };
 
-  const int nstage = static_cast<int>((p.K + kSK - 1) / kSK);
-  // stage x lives in slot x % kSlots; before computing it: its loads have
-  // landed (later stages may stay in flight), barrier (everyone is done with
-  // slot (x - 1) % kSlots), refill that slot with stage x + kSlots - 1
-  for (int st = 0; st < kSlots - 1 && st < nstage; ++st) issue(st);
-  for (int xs = 0; xs < nstage; ++xs) {
-    const int ahead = min(kSlots - 2, nstage - 1 - xs);  // stages issued after xs
-    switch (ahead) {
-      case 4: __builtin_amdgcn_s_waitcnt(GPTQ_X3_VMCNT(4 * kLoads)); break;
-      case 3: __builtin_amdgcn_s_waitcnt(GPTQ_X3_VMCNT(3 * kLoads)); break;
-      case 2: __builtin_amdgcn_s_waitcnt(GPTQ_X3_VMCNT(2 * kLoads)); break;
-      case 1: __builtin_amdgcn_s_waitcnt(GPTQ_X3_VMCNT(kLoads)); break;
-      default: __builtin_amdgcn_s_waitcnt(GPTQ_X3_VMCNT(0)); break;
+  // K is a multiple of 32, at least 64 (the host checks): an even number of
+  // stages, at least four
+  const int nstage = static_cast<int>(p.K / kSK);
+  // stage x lives in slot x % kSlots.  Stage y - 1 is computed from registers
+  // while stage y is read from LDS; before that read: stage y has landed
+  // (with stage y + 1 still in flight) and a barrier (every wave has read
+  // stage y - 1 and finished those reads, so its slot takes stage y - 1 +
+  // kSlots).
+  auto half = [&](int y, const Frag& fc, Frag& fr) {
+    if (y - 1 + kSlots < nstage) {
+      __builtin_amdgcn_s_waitcnt(GPTQ_X3_VMLGK(kLoads));
+      __builtin_amdgcn_s_barrier();
+      issue(y - 1 + kSlots);
+    } else {
+      __builtin_amdgcn_s_waitcnt(GPTQ_X3_VMLGK(0));
+      __builtin_amdgcn_s_barrier();
     }
-    __builtin_amdgcn_s_barrier();
-    if (xs + kSlots - 1 < nstage) issue(xs + kSlots - 1);
-    compute(ring + (xs % kSlots) * kSlotBytes);
+    read(fr, ring + (y % kSlots) * kSlotBytes);
+    mfma(fc);
+    interleave();
+  };
+  for (int st = 0; st < kSlots && st < nstage; ++st) issue(st);
+  Frag F0, F1;
+  __builtin_amdgcn_s_waitcnt(GPTQ_X3_VMLGK(2 * kLoads));  // stage 0 (two more stages issued after it)
+  __builtin_amdgcn_s_barrier();
+  read(F0, ring);
+  for (int xs = 0; xs + 2 < nstage; xs += 2) {
+    half(xs + 1, F0, F1);
+    half(xs + 2, F1, F0);
   }
+  half(nstage - 1, F0, F1);
+  mfma(F1);
 
   // C += alpha acc: accumulator element e of lane l in a 32 x 32 block is row
   // 8 (e / 4) + 4 (l / 32) + e % 4, column l % 32.  Every C value is loaded
@@ -242,6 +270,7 @@ __global__ __launch_bounds__(256) void split3_t_kernel(const float* src, int64_t
 hipError_t gemm_x3(int64_t M, int64_t N, int64_t K, float alpha, const uint16_t* A, int64_t sA, const uint16_t* Bt,
                    int64_t sB, float* C, int64_t ldc, hipStream_t stream, int64_t ldk, bool lower) {
   if (M <= 0 || N <= 0) return hipSuccess;
+  if (K % 32 != 0 || K < 64) return hipErrorInvalidValue;  // an even number of stages, at least four
   if (ldk <= 0) ldk = K;
   X3Params p{A, Bt, M, N, K, ldk, sA, sB, C, ldc, alpha, 0, 0, lower ? 1 : 0};
   p.tiles_m = static_cast<int>((M + kT - 1) / kT);
