@@ -25,7 +25,10 @@
 // Each wave reads the next stage's operand fragments from LDS while its
 // products of the current stage run (two register sets, one fragment read
 // between two products): 4-5% faster on the large shapes.  A 256 x 128 tile
-// (eight waves, one workgroup a CU) was slower.
+// (eight waves, one workgroup a CU) was slower.  Problems with fewer than 512
+// such tiles use 64 x 64 tiles (2 x 2 waves of 32 x 32, four workgroups a
+// CU): the Cholesky's 128-column products and its smaller trailing updates
+// run about twice as fast on them.
 #include "gptq_common.h"
 #include "gptq_internal.h"
 
@@ -41,8 +44,7 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 constexpr int kT = 128;        // output tile edge
 constexpr int kSK = 16;        // k per stage (one MFMA k-step)
 constexpr int kSlots = 3;      // ring depth: two stages in flight; two workgroups a CU
-constexpr int kPlaneStage = kT * kSK * 2;    // bytes of one plane of one operand stage (4 KB)
-constexpr int kSlotBytes = 6 * kPlaneStage;  // A and B, three planes each (24 KB)
+constexpr int kSmallBelow = 512;             // fewer 128-tiles than this: 64-tiles
 
 // s_waitcnt immediate: vmcnt(n) and lgkmcnt(0)
 #define GPTQ_X3_VMLGK(n) (((n) & 15) | (((n) >> 4) << 14) | 0x0070)
@@ -71,17 +73,17 @@ GPTQ_DEV __amdgpu_buffer_rsrc_t x3_rsrc(const uint16_t* base, int64_t bytes) {
 }
 
 // One plane of one operand stage: the 4 KB block of 128 rows x 16 k (32
-// bytes a row, two 16-byte chunks), four 1 KB pieces of 32 rows.  Physical
+// bytes a row, two 16-byte chunks) is four 1 KB pieces of 32 rows.  Physical
 // chunk p of row r in LDS holds logical chunk p ^ ((r >> 3) & 1): an MFMA
 // operand read (16 consecutive rows, one chunk each) then covers all 64
 // banks; the permutation stays inside each row's 32 bytes, so a piece is
-// still one contiguous 1 KB read.  Wave w moves piece w of each plane; rs
-// spans the tile's row block, st is the stage.
-GPTQ_DEV void x3_dma(__amdgpu_buffer_rsrc_t rs, uint8_t* dst, int st, int wave, int lane) {
-  const int r = 32 * wave + (lane >> 1);
+// still one contiguous 1 KB read.  rs spans the tile's 128-row block, st is
+// the stage, src the piece in the block, dst the piece's place in LDS.
+GPTQ_DEV void x3_dma(__amdgpu_buffer_rsrc_t rs, uint8_t* dst, int st, int src, int lane) {
+  const int r = 32 * src + (lane >> 1);
   const int c = (lane & 1) ^ ((r >> 3) & 1);
   const uint32_t voff = static_cast<uint32_t>((st * 2048 + r * 16 + 8 * c) * 2);
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(dst + wave * 1024), 16, voff, 0, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)dst, 16, voff, 0, 0, 0);
 }
 
 // the 8 bf16 of row r, k 8 h .. 8 h + 7 (h = lane >> 5) of a stage plane
@@ -90,8 +92,19 @@ GPTQ_DEV bf16x8_t x3_read(const uint8_t* plane, int r, int h) {
   return *reinterpret_cast<const bf16x8_t*>(plane + r * 32 + pc * 16);
 }
 
-__global__ __launch_bounds__(256, 2) void gemm_x3_kernel(X3Params p) {
-  __shared__ __attribute__((aligned(1024))) uint8_t ring[kSlots * kSlotBytes];
+// TS x TS output tile per 256-thread workgroup, 2 x 2 waves of TS/2 x TS/2.
+// TS = 128: each wave moves piece w of all six planes of a stage.  TS = 64
+// (problems with few 128-tiles): a tile is half a 128-row block; waves 0-1
+// move A's two pieces, waves 2-3 B's, three planes each.
+template <int TS>
+__global__ __launch_bounds__(256, TS == 128 ? 2 : 4) void gemm_x3_kernel(X3Params p) {
+  constexpr int kNI = TS / 64;                   // 32 x 32 blocks per wave and dimension
+  constexpr int kPlane = TS * kSK * 2;           // bytes of one plane of one operand stage
+  constexpr int kSlot = 6 * kPlane;              // A and B, three planes each
+  constexpr int kLoads = TS == 128 ? 6 : 3;      // DMA instructions per wave per stage
+  constexpr int kFr = 6 * kNI;                   // fragments per wave per stage
+  constexpr int kMf = 6 * kNI * kNI;             // products per wave per stage
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[kSlots * kSlot];
   // Workgroups go round-robin to the 8 XCDs (b % 8), each with its own L2:
   // the tile list is cut into 8 contiguous ranges, one per XCD, listed in
   // groups of 8 tile rows, column by column inside a group, so the tiles an
@@ -116,63 +129,79 @@ __global__ __launch_bounds__(256, 2) void gemm_x3_kernel(X3Params p) {
     tn = idx / rows;
     tm = 8 * g + idx % rows;
   }
-  const int64_t m0 = static_cast<int64_t>(tm) * kT, n0 = static_cast<int64_t>(tn) * kT;
+  const int64_t m0 = static_cast<int64_t>(tm) * TS, n0 = static_cast<int64_t>(tn) * TS;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
 
-  // a tile's row block: K / 16 blocks of 4 KB (rows past M or N are padding)
+  // the 128-row block of each operand that holds the tile (rows past M or N
+  // are padding), and the tile's first piece in it
+  const int64_t ma = m0 & ~int64_t{127}, na = n0 & ~int64_t{127};
   __amdgpu_buffer_rsrc_t ra[3], rb[3];
 #pragma unroll
   for (int pl = 0; pl < 3; ++pl) {
-    ra[pl] = x3_rsrc(p.A + pl * p.sA + m0 * p.ldk, kT * p.ldk * 2);
-    rb[pl] = x3_rsrc(p.B + pl * p.sB + n0 * p.ldk, kT * p.ldk * 2);
+    ra[pl] = x3_rsrc(p.A + pl * p.sA + ma * p.ldk, 128 * p.ldk * 2);
+    rb[pl] = x3_rsrc(p.B + pl * p.sB + na * p.ldk, 128 * p.ldk * 2);
   }
+  const int pa = static_cast<int>(m0 - ma) / 32, pb = static_cast<int>(n0 - na) / 32;
   auto issue = [&](int st) {
-    uint8_t* d = ring + (st % kSlots) * kSlotBytes;
+    uint8_t* d = ring + (st % kSlots) * kSlot;
+    if (TS == 128) {
 #pragma unroll
-    for (int pl = 0; pl < 3; ++pl) {
-      x3_dma(ra[pl], d + pl * kPlaneStage, st, wave, lane);
-      x3_dma(rb[pl], d + (3 + pl) * kPlaneStage, st, wave, lane);
+      for (int pl = 0; pl < 3; ++pl) {
+        x3_dma(ra[pl], d + pl * kPlane + wave * 1024, st, wave, lane);
+        x3_dma(rb[pl], d + (3 + pl) * kPlane + wave * 1024, st, wave, lane);
+      }
+    } else {
+      const int c = wave & 1;
+#pragma unroll
+      for (int pl = 0; pl < 3; ++pl) {
+        if (wave < 2)
+          x3_dma(ra[pl], d + pl * kPlane + c * 1024, st, pa + c, lane);
+        else
+          x3_dma(rb[pl], d + (3 + pl) * kPlane + c * 1024, st, pb + c, lane);
+      }
     }
   };
-  constexpr int kLoads = 6;  // DMA instructions per wave per stage
 
-  f32x16_t acc[2][2];
+  f32x16_t acc[kNI][kNI];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < kNI; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < kNI; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
   const int h = lane >> 5, l32 = lane & 31;
+  constexpr int kWT = TS / 2;  // wave tile edge
   // fragments of one stage: a[i][plane], b[j][plane]
-  struct Frag { bf16x8_t a[2][3], b[2][3]; };
+  struct Frag { bf16x8_t a[kNI][3], b[kNI][3]; };
   auto read = [&](Frag& f, const uint8_t* d) {
 #pragma unroll
     for (int pl = 0; pl < 3; ++pl)
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        f.a[i][pl] = x3_read(d + pl * kPlaneStage, wm * 64 + 32 * i + l32, h);
-        f.b[i][pl] = x3_read(d + (3 + pl) * kPlaneStage, wn * 64 + 32 * i + l32, h);
+      for (int i = 0; i < kNI; ++i) {
+        f.a[i][pl] = x3_read(d + pl * kPlane, wm * kWT + 32 * i + l32, h);
+        f.b[i][pl] = x3_read(d + (3 + pl) * kPlane, wn * kWT + 32 * i + l32, h);
       }
   };
   auto mfma = [&](const Frag& f) {
+    // the six part products, smallest first, each over the independent
+    // accumulators in turn
     constexpr int PA[6] = {2, 1, 0, 1, 0, 0}, PB[6] = {0, 1, 2, 0, 1, 0};
 #pragma unroll
     for (int q = 0; q < 6; ++q)
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < kNI; ++i)
 #pragma unroll
-        for (int jj = 0; jj < 2; ++jj)
+        for (int jj = 0; jj < kNI; ++jj)
           acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i][PA[q]], f.b[jj][PB[q]], acc[i][jj], 0, 0, 0);
   };
-  // the next stage's 12 fragment reads spread over this stage's 24 products
+  // the next stage's fragment reads spread over this stage's products
   auto interleave = [&]() {
 #pragma unroll
-    for (int r = 0; r < 12; ++r) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    for (int r = 0; r < kFr; ++r) {
+      __builtin_amdgcn_sched_group_barrier(0x008, kMf / kFr, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
   };
@@ -194,7 +223,7 @@ __global__ __launch_bounds__(256, 2) void gemm_x3_kernel(X3Params p) {
       __builtin_amdgcn_s_waitcnt(GPTQ_X3_VMLGK(0));
       __builtin_amdgcn_s_barrier();
     }
-    read(fr, ring + (y % kSlots) * kSlotBytes);
+    read(fr, ring + (y % kSlots) * kSlot);
     mfma(fc);
     interleave();
   };
@@ -213,26 +242,26 @@ __global__ __launch_bounds__(256, 2) void gemm_x3_kernel(X3Params p) {
   // C += alpha acc: accumulator element e of lane l in a 32 x 32 block is row
   // 8 (e / 4) + 4 (l / 32) + e % 4, column l % 32.  Every C value is loaded
   // before the first store, so the loads are in flight together.
-  float cv[2][2][16];
+  float cv[kNI][kNI][16];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < kNI; ++i)
 #pragma unroll
-    for (int jj = 0; jj < 2; ++jj) {
-      const int64_t n = n0 + wn * 64 + 32 * jj + l32;
+    for (int jj = 0; jj < kNI; ++jj) {
+      const int64_t n = n0 + wn * kWT + 32 * jj + l32;
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const int64_t m = m0 + wm * 64 + 32 * i + 8 * (e >> 2) + 4 * h + (e & 3);
+        const int64_t m = m0 + wm * kWT + 32 * i + 8 * (e >> 2) + 4 * h + (e & 3);
         cv[i][jj][e] = (m < p.M && n < p.N) ? p.C[m * p.ldc + n] : 0.f;
       }
     }
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < kNI; ++i)
 #pragma unroll
-    for (int jj = 0; jj < 2; ++jj) {
-      const int64_t n = n0 + wn * 64 + 32 * jj + l32;
+    for (int jj = 0; jj < kNI; ++jj) {
+      const int64_t n = n0 + wn * kWT + 32 * jj + l32;
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const int64_t m = m0 + wm * 64 + 32 * i + 8 * (e >> 2) + 4 * h + (e & 3);
+        const int64_t m = m0 + wm * kWT + 32 * i + 8 * (e >> 2) + 4 * h + (e & 3);
         if (m < p.M && n < p.N && !(p.lower && (m >> 6) < (n >> 6)))
           p.C[m * p.ldc + n] = fmaf(p.alpha, acc[i][jj][e], cv[i][jj][e]);
       }
@@ -273,10 +302,17 @@ hipError_t gemm_x3(int64_t M, int64_t N, int64_t K, float alpha, const uint16_t*
   if (K % 32 != 0 || K < 64) return hipErrorInvalidValue;  // an even number of stages, at least four
   if (ldk <= 0) ldk = K;
   X3Params p{A, Bt, M, N, K, ldk, sA, sB, C, ldc, alpha, 0, 0, lower ? 1 : 0};
-  p.tiles_m = static_cast<int>((M + kT - 1) / kT);
-  p.tiles_n = static_cast<int>((N + kT - 1) / kT);
-  const int tiles = lower ? p.tiles_m * (p.tiles_m + 1) / 2 : p.tiles_m * p.tiles_n;
-  gemm_x3_kernel<<<tiles, 256, 0, stream>>>(p);
+  auto tiles_of = [&](int ts) {
+    p.tiles_m = static_cast<int>((M + ts - 1) / ts);
+    p.tiles_n = static_cast<int>((N + ts - 1) / ts);
+    return lower ? p.tiles_m * (p.tiles_m + 1) / 2 : p.tiles_m * p.tiles_n;
+  };
+  // 128-tiles while they give every CU two workgroups; 64-tiles below that
+  if (tiles_of(kT) >= kSmallBelow) {
+    gemm_x3_kernel<kT><<<tiles_of(kT), 256, 0, stream>>>(p);
+  } else {
+    gemm_x3_kernel<64><<<tiles_of(64), 256, 0, stream>>>(p);
+  }
   return hipGetLastError();
 }
 

@@ -781,21 +781,20 @@ hipError_t prepare_launch(float* S, int64_t n, int64_t n_total, float damp, bool
   // group's columns (K = 128 kPanelGroup).  The same products as one update
   // per panel, summed in another order; the large lower-triangle update reads
   // and writes the trailing matrix once per group instead of once per panel.
-  // The trailing update runs on the bf16 matrix cores (gemm_x3): the panel
-  // kernels write their factor rows below the diagonal block also as three
-  // bf16 planes of the group's panel P, which serves as both operands.
+  // Both products run on the bf16 matrix cores (gemm_x3): the panel kernels
+  // write their factor rows below the diagonal block also as three bf16
+  // planes of the group's panel P, which serves as both operands.
   for (int64_t k = 0; k < n; k += kPGW) {
     for (int h = 0; h < kPanelGroup; ++h) {
       const int64_t kh = k + h * kNB;
       if (kh >= n) break;
       if (h > 0) {
-        // a 128-column product: 64 x 64 tiles on the fp32 matrix cores give
-        // the CUs enough tiles
+        // the panel's block column takes the group's earlier panels: rows
+        // kh .. of their columns, from the group's planes (K = 128 per panel)
         const int64_t wc = std::min<int64_t>(kNB, n - kh);
-        const float* A = Hr + kh * n + k;  // rows kh .., the earlier panels' columns
+        const uint16_t* A = P + x3_offset(kh, 0, kPGW);
         PhaseScope ph(kPhCholUpdate, st);
-        GPTQ_TRY(gemm_f32(n - kh, wc, kh - k, -1.f, A, n, 0, A, n, 0, true, 1.f, Hr + kh * (n + 1), n, 0, 1,
-                          false, 0, st));
+        GPTQ_TRY(gemm_x3(n - kh, wc, kh - k, -1.f, A, pplane, A, pplane, Hr + kh * (n + 1), n, st, kPGW, false));
       }
       const int64_t below = std::max<int64_t>(0, n - kh - kNB);
       const int blocks = 1 + static_cast<int>(std::min<int64_t>((below + kChunk - 1) / kChunk, kMaxPanelWG - 1));
