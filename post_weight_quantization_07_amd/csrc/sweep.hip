@@ -318,20 +318,23 @@ GPTQ_DEV void load_preset(const SweepParams& p, int64_t row, bool row_ok, int t,
 // codes q = qr + z and dequantized weights s qr to their original columns.
 // Returns this lane's part of the row's loss (sum of squared normalised
 // errors); er receives the errors.
-GPTQ_DEV float finish_block(const SweepParams& p, int64_t row, bool row_ok, int t, float* e, const float (&v)[8],
-                            const float (&dv)[8], const float (&sc)[8], const float (&rc)[8],
-                            const float (&zlo)[8], const float (&zhi)[8], float (&er)[8]) {
-  float qr[8], loss = 0.f;
+// Codes and errors of a swept block, decided again from the values their
+// columns were decided on (the same arithmetic as the steps); returns the
+// lane's share of the row loss.
+GPTQ_DEV float decide_block(const float (&v)[8], const float (&dv)[8], const float (&sc)[8], const float (&rc)[8],
+                            const float (&zlo)[8], const float (&zhi)[8], float (&qr)[8], float (&er)[8]) {
+  float loss = 0.f;
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
     decide(v[k], sc[k], rc[k], zlo[k], zhi[k], dv[k], qr[k], er[k]);
     loss = fmaf(er[k], er[k], loss);
   }
-  if (!row_ok) return loss;
-  if (e) {
-#pragma unroll
-    for (int k = 0; k < 8; ++k) e[t + 16 * k] = er[k];
-  }
+  return loss;
+}
+
+// codes and dequantized weights of a block, in the original column order
+GPTQ_DEV void store_codes(const SweepParams& p, int64_t row, int t, const float (&qr)[8], const float (&sc)[8],
+                          const float (&zlo)[8]) {
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
     const int c = t + 16 * k;
@@ -342,6 +345,19 @@ GPTQ_DEV float finish_block(const SweepParams& p, int64_t row, bool row_ok, int 
       if (p.Q) p.Q[row * p.d_in + oc] = sc[k] * qr[k];
     }
   }
+}
+
+GPTQ_DEV float finish_block(const SweepParams& p, int64_t row, bool row_ok, int t, float* e, const float (&v)[8],
+                            const float (&dv)[8], const float (&sc)[8], const float (&rc)[8],
+                            const float (&zlo)[8], const float (&zhi)[8], float (&er)[8]) {
+  float qr[8];
+  const float loss = decide_block(v, dv, sc, rc, zlo, zhi, qr, er);
+  if (!row_ok) return loss;
+  if (e) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) e[t + 16 * k] = er[k];
+  }
+  store_codes(p, row, t, qr, sc, zlo);
   return loss;
 }
 
@@ -662,14 +678,18 @@ __global__ __launch_bounds__(512) void sweep_group_kernel(SweepParams p) {
     sweep_all<GS>(pb, Ut, t, v, sc, rc, zlo, zhi, row, std::make_integer_sequence<int, kB>{});
 
     // errors to El (for the next blocks' bring-up; rows past the end keep
-    // finite zeros) and, split into three bf16 planes, to the group's panel
-    // for the product past the group
+    // finite zeros); the stores to memory wait until after the barrier,
+    // beside the producers' part of the next block's bring-up
     const int kb = kB * b;
-    float er[8];
-    loss += finish_block(pb, row, row_ok, t, nullptr, v, dv, sc, rc, zlo, zhi, er);
+    float er[8], qr[8];
+    loss += decide_block(v, dv, sc, rc, zlo, zhi, qr, er);
 #pragma unroll
     for (int k = 0; k < 8; ++k) El[el_index(rl, kb + t + 16 * k)] = er[k];
+    __syncthreads();  // B(b)
     if (row_ok) {
+      store_codes(pb, row, t, qr, sc, zlo);
+      // the errors as three bf16 planes of the group's panel, for the
+      // product past the group
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
         uint16_t hh, mm, ll;
@@ -680,7 +700,6 @@ __global__ __launch_bounds__(512) void sweep_group_kernel(SweepParams p) {
         p.Ea[2 * p.ea_plane + o] = ll;
       }
     }
-    __syncthreads();  // B(b)
   }
   loss = row_sum16(loss);
   if (row_ok && p.row_loss && t == 0) p.row_loss[row] = (g0 == 0 ? 0.f : p.row_loss[row]) + loss;
