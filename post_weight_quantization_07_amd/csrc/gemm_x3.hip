@@ -60,6 +60,10 @@ struct X3Params {
   float alpha;
   int tiles_m, tiles_n;
   int lower;          // only the tiles on or below the diagonal; nothing written above the 64-block diagonal
+  int tri;            // 0 dense; 1 B lower-triangular (a tile skips k below its first column); 2 A
+                      // lower-triangular (a tile skips k past its last row)
+  int beta0;          // C = alpha A B (C is not read)
+  int64_t bA, bB, bC; // batch strides (blockIdx.y) in elements
 };
 
 GPTQ_DEV __amdgpu_buffer_rsrc_t x3_rsrc(const uint16_t* base, int64_t bytes) {
@@ -110,13 +114,22 @@ __global__ __launch_bounds__(256, TS == 128 ? 2 : 4) void gemm_x3_kernel(X3Param
   // groups of 8 tile rows, column by column inside a group, so the tiles an
   // XCD runs at once share rows of A and columns of B.
   // Lower-tile problems list the tiles (i >= j) row by row.
+  // Triangular problems instead list the tiles heaviest first in plain
+  // dispatch order, so the round robin gives every XCD an equal share of
+  // heavy and light tiles.
   constexpr int kXcd = 8;
   const int b = blockIdx.x, G = p.lower ? p.tiles_m * (p.tiles_m + 1) / 2 : p.tiles_m * p.tiles_n;
   const int x = b % kXcd, xl = b / kXcd;
   const int base = G / kXcd, rem = G % kXcd;
   const int t = x * base + min(x, rem) + xl;
   int tm, tn;
-  if (p.lower) {
+  if (p.tri == 1) {  // k from the tile's first column: the first columns are heaviest
+    tn = b / p.tiles_m;
+    tm = b % p.tiles_m;
+  } else if (p.tri == 2) {  // k up to the tile's last row: the last rows are heaviest
+    tm = p.tiles_m - 1 - b / p.tiles_n;
+    tn = b % p.tiles_n;
+  } else if (p.lower) {
     int i = static_cast<int>((__builtin_sqrtf(8.f * t + 1.f) - 1.f) * 0.5f);
     while (i * (i + 1) / 2 > t) --i;
     while ((i + 1) * (i + 2) / 2 <= t) ++i;
@@ -130,6 +143,15 @@ __global__ __launch_bounds__(256, TS == 128 ? 2 : 4) void gemm_x3_kernel(X3Param
     tm = 8 * g + idx % rows;
   }
   const int64_t m0 = static_cast<int64_t>(tm) * TS, n0 = static_cast<int64_t>(tn) * TS;
+  const int64_t bz = blockIdx.y;
+  const uint16_t* Ab = p.A + bz * p.bA;
+  const uint16_t* Bb = p.B + bz * p.bB;
+  float* Cb = p.C + bz * p.bC;
+  // the tile's k range: a lower-triangular operand is zero past it (both
+  // ends are multiples of 64, so the stage count stays a multiple of four)
+  const int64_t k_lo = p.tri == 1 ? min(n0, p.K) : 0;
+  const int64_t k_hi = p.tri == 2 ? min(m0 + TS, p.K) : p.K;
+  const int kst0 = static_cast<int>(k_lo / kSK);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
@@ -140,12 +162,13 @@ __global__ __launch_bounds__(256, TS == 128 ? 2 : 4) void gemm_x3_kernel(X3Param
   __amdgpu_buffer_rsrc_t ra[3], rb[3];
 #pragma unroll
   for (int pl = 0; pl < 3; ++pl) {
-    ra[pl] = x3_rsrc(p.A + pl * p.sA + ma * p.ldk, 128 * p.ldk * 2);
-    rb[pl] = x3_rsrc(p.B + pl * p.sB + na * p.ldk, 128 * p.ldk * 2);
+    ra[pl] = x3_rsrc(Ab + pl * p.sA + ma * p.ldk, 128 * p.ldk * 2);
+    rb[pl] = x3_rsrc(Bb + pl * p.sB + na * p.ldk, 128 * p.ldk * 2);
   }
   const int pa = static_cast<int>(m0 - ma) / 32, pb = static_cast<int>(n0 - na) / 32;
-  auto issue = [&](int st) {
-    uint8_t* d = ring + (st % kSlots) * kSlot;
+  auto issue = [&](int xs) {  // stage xs of the tile's k range
+    uint8_t* d = ring + (xs % kSlots) * kSlot;
+    const int st = kst0 + xs;
     if (TS == 128) {
 #pragma unroll
       for (int pl = 0; pl < 3; ++pl) {
@@ -208,7 +231,7 @@ __global__ __launch_bounds__(256, TS == 128 ? 2 : 4) void gemm_x3_kernel(X3Param
 
   // K is a multiple of 32, at least 64 (the host checks): an even number of
   // stages, at least four
-  const int nstage = static_cast<int>(p.K / kSK);
+  const int nstage = static_cast<int>((k_hi - k_lo) / kSK);
   // stage x lives in slot x % kSlots.  Stage y - 1 is computed from registers
   // while stage y is read from LDS; before that read: stage y has landed
   // (with stage y + 1 still in flight) and a barrier (every wave has read
@@ -227,8 +250,9 @@ __global__ __launch_bounds__(256, TS == 128 ? 2 : 4) void gemm_x3_kernel(X3Param
     mfma(fc);
     interleave();
   };
-  for (int st = 0; st < kSlots && st < nstage; ++st) issue(st);
   Frag F0, F1;
+  if (nstage > 0) {
+  for (int st = 0; st < kSlots && st < nstage; ++st) issue(st);
   __builtin_amdgcn_s_waitcnt(GPTQ_X3_VMLGK(2 * kLoads));  // stage 0 (two more stages issued after it)
   __builtin_amdgcn_s_barrier();
   read(F0, ring);
@@ -238,6 +262,7 @@ __global__ __launch_bounds__(256, TS == 128 ? 2 : 4) void gemm_x3_kernel(X3Param
   }
   half(nstage - 1, F0, F1);
   mfma(F1);
+  }
 
   // C += alpha acc: accumulator element e of lane l in a 32 x 32 block is row
   // 8 (e / 4) + 4 (l / 32) + e % 4, column l % 32.  Every C value is loaded
@@ -251,7 +276,7 @@ __global__ __launch_bounds__(256, TS == 128 ? 2 : 4) void gemm_x3_kernel(X3Param
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int64_t m = m0 + wm * kWT + 32 * i + 8 * (e >> 2) + 4 * h + (e & 3);
-        cv[i][jj][e] = (m < p.M && n < p.N) ? p.C[m * p.ldc + n] : 0.f;
+        cv[i][jj][e] = (m < p.M && n < p.N && !p.beta0) ? Cb[m * p.ldc + n] : 0.f;
       }
     }
 #pragma unroll
@@ -263,7 +288,7 @@ __global__ __launch_bounds__(256, TS == 128 ? 2 : 4) void gemm_x3_kernel(X3Param
       for (int e = 0; e < 16; ++e) {
         const int64_t m = m0 + wm * kWT + 32 * i + 8 * (e >> 2) + 4 * h + (e & 3);
         if (m < p.M && n < p.N && !(p.lower && (m >> 6) < (n >> 6)))
-          p.C[m * p.ldc + n] = fmaf(p.alpha, acc[i][jj][e], cv[i][jj][e]);
+          Cb[m * p.ldc + n] = fmaf(p.alpha, acc[i][jj][e], cv[i][jj][e]);
       }
     }
 }
@@ -272,8 +297,10 @@ __global__ __launch_bounds__(256, TS == 128 ? 2 : 4) void gemm_x3_kernel(X3Param
 // plane pl = part pl of src[k][n] for k < K, n < N (src row-major, ld
 // elements); 64 x 64 tiles through LDS.  Padding rows n >= N are not written.
 __global__ __launch_bounds__(256) void split3_t_kernel(const float* src, int64_t ld, int64_t K, int64_t N,
-                                                       uint16_t* out, int64_t plane) {
+                                                       uint16_t* out, int64_t plane, int64_t bsrc, int64_t bout) {
   __shared__ float tile[64][65];
+  src += blockIdx.z * bsrc;
+  out += blockIdx.z * bout;
   const int64_t k0 = static_cast<int64_t>(blockIdx.y) * 64, nb = static_cast<int64_t>(blockIdx.x) * 64;
   const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
   for (int r = ty; r < 64; r += 4) {
@@ -294,32 +321,62 @@ __global__ __launch_bounds__(256) void split3_t_kernel(const float* src, int64_t
   }
 }
 
+// planes of a row-major block in the blocked layout: element (r, k) of
+// plane pl = part pl of src[r][k] for r < R, k < K (K a multiple of 16); a
+// 256-thread workgroup covers 4 rows x 64 k.  Padding rows are not written.
+__global__ __launch_bounds__(256) void split3_rows_kernel(const float* src, int64_t ld, int64_t R, int64_t K,
+                                                          uint16_t* out, int64_t plane, int64_t bsrc, int64_t bout) {
+  src += blockIdx.z * bsrc;
+  out += blockIdx.z * bout;
+  const int64_t r = static_cast<int64_t>(blockIdx.y) * 4 + (threadIdx.x >> 6);
+  const int64_t k = static_cast<int64_t>(blockIdx.x) * 64 + (threadIdx.x & 63);
+  if (r >= R || k >= K) return;
+  uint16_t hh, mm, ll;
+  split3(src[r * ld + k], hh, mm, ll);
+  const int64_t o = x3_offset(r, k, K);
+  out[o] = hh;
+  out[plane + o] = mm;
+  out[2 * plane + o] = ll;
+}
+
 }  // namespace
 
 hipError_t gemm_x3(int64_t M, int64_t N, int64_t K, float alpha, const uint16_t* A, int64_t sA, const uint16_t* Bt,
-                   int64_t sB, float* C, int64_t ldc, hipStream_t stream, int64_t ldk, bool lower) {
-  if (M <= 0 || N <= 0) return hipSuccess;
+                   int64_t sB, float* C, int64_t ldc, hipStream_t stream, int64_t ldk, bool lower, int tri, bool beta0,
+                   int batch, int64_t bA, int64_t bB, int64_t bC) {
+  if (M <= 0 || N <= 0 || batch <= 0) return hipSuccess;
   if (K % 32 != 0 || K < 64) return hipErrorInvalidValue;  // an even number of stages, at least four
+  if (tri != 0 && (lower || K % 64 != 0)) return hipErrorInvalidValue;
   if (ldk <= 0) ldk = K;
-  X3Params p{A, Bt, M, N, K, ldk, sA, sB, C, ldc, alpha, 0, 0, lower ? 1 : 0};
+  X3Params p{A, Bt, M, N, K, ldk, sA, sB, C, ldc, alpha, 0, 0, lower ? 1 : 0, tri, beta0 ? 1 : 0, bA, bB, bC};
   auto tiles_of = [&](int ts) {
     p.tiles_m = static_cast<int>((M + ts - 1) / ts);
     p.tiles_n = static_cast<int>((N + ts - 1) / ts);
     return lower ? p.tiles_m * (p.tiles_m + 1) / 2 : p.tiles_m * p.tiles_n;
   };
   // 128-tiles while they give every CU two workgroups; 64-tiles below that
-  if (tiles_of(kT) >= kSmallBelow) {
-    gemm_x3_kernel<kT><<<tiles_of(kT), 256, 0, stream>>>(p);
+  if (tiles_of(kT) * batch >= kSmallBelow) {
+    gemm_x3_kernel<kT><<<dim3(tiles_of(kT), batch), 256, 0, stream>>>(p);
   } else {
-    gemm_x3_kernel<64><<<tiles_of(64), 256, 0, stream>>>(p);
+    gemm_x3_kernel<64><<<dim3(tiles_of(64), batch), 256, 0, stream>>>(p);
   }
   return hipGetLastError();
 }
 
-hipError_t split3_t(const float* src, int64_t ld, int64_t K, int64_t N, uint16_t* out, hipStream_t stream) {
-  if (K <= 0 || N <= 0) return hipSuccess;
-  const dim3 grid(static_cast<unsigned>((N + 63) / 64), static_cast<unsigned>((K + 63) / 64));
-  split3_t_kernel<<<grid, 256, 0, stream>>>(src, ld, K, N, out, x3_plane_elems(N, K));
+hipError_t split3_t(const float* src, int64_t ld, int64_t K, int64_t N, uint16_t* out, hipStream_t stream, int batch,
+                    int64_t bsrc, int64_t bout) {
+  if (K <= 0 || N <= 0 || batch <= 0) return hipSuccess;
+  const dim3 grid(static_cast<unsigned>((N + 63) / 64), static_cast<unsigned>((K + 63) / 64), batch);
+  split3_t_kernel<<<grid, 256, 0, stream>>>(src, ld, K, N, out, x3_plane_elems(N, K), bsrc, bout);
+  return hipGetLastError();
+}
+
+hipError_t split3_rows(const float* src, int64_t ld, int64_t R, int64_t K, uint16_t* out, hipStream_t stream, int batch,
+                       int64_t bsrc, int64_t bout) {
+  if (R <= 0 || K <= 0 || batch <= 0) return hipSuccess;
+  if (K % 16 != 0) return hipErrorInvalidValue;
+  const dim3 grid(static_cast<unsigned>((K + 63) / 64), static_cast<unsigned>((R + 3) / 4), batch);
+  split3_rows_kernel<<<grid, 256, 0, stream>>>(src, ld, R, K, out, x3_plane_elems(R, K), bsrc, bout);
   return hipGetLastError();
 }
 

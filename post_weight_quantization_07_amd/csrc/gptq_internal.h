@@ -47,7 +47,7 @@ hipError_t hessian_launch(const HessPlan& plan, float* S, int64_t d_in, const vo
 constexpr int kPanel = 128;  // Cholesky panel / diagonal block width
 
 struct PrepLayout {
-  size_t off_hr, off_t, off_diag, off_dinv, off_lambda, off_p, ws_bytes;
+  size_t off_hr, off_t, off_diag, off_dinv, off_lambda, off_p, off_qa, off_qb, ws_bytes;
 };
 PrepLayout prepare_layout(int64_t d_in);
 hipError_t prepare_launch(float* S_to_H, int64_t d_in, int64_t n_total, float damp, bool desc_act,
@@ -83,9 +83,20 @@ __host__ __device__ inline int64_t x3_plane_elems(int64_t rows, int64_t K) { ret
 // ldk: width of the planes' layout when the product uses only their first K
 // columns (0: K).  lower: square C, only tiles on or below the diagonal, and
 // nothing written above the 64-block diagonal (the Cholesky update).
+// tri: 1 B lower-triangular (each tile skips k below its first column), 2 A
+// lower-triangular (each tile skips k past its last row); K a multiple of 64
+// and the zero parts of the 64- or 128-tiles on the diagonal stored as zeros.
+// beta0: C = alpha A B without reading C.  batch: blockIdx.y, with element
+// strides bA, bB (of the planes) and bC.
 hipError_t gemm_x3(int64_t M, int64_t N, int64_t K, float alpha, const uint16_t* A, int64_t sA, const uint16_t* Bt,
-                   int64_t sB, float* C, int64_t ldc, hipStream_t stream, int64_t ldk = 0, bool lower = false);
-hipError_t split3_t(const float* src, int64_t ld, int64_t K, int64_t N, uint16_t* out, hipStream_t stream);
+                   int64_t sB, float* C, int64_t ldc, hipStream_t stream, int64_t ldk = 0, bool lower = false,
+                   int tri = 0, bool beta0 = false, int batch = 1, int64_t bA = 0, int64_t bB = 0, int64_t bC = 0);
+hipError_t split3_t(const float* src, int64_t ld, int64_t K, int64_t N, uint16_t* out, hipStream_t stream,
+                    int batch = 1, int64_t bsrc = 0, int64_t bout = 0);
+// split3_rows writes the planes of a row-major block src[R][K] itself (no
+// transpose), plane stride x3_plane_elems(R, K).
+hipError_t split3_rows(const float* src, int64_t ld, int64_t R, int64_t K, uint16_t* out, hipStream_t stream,
+                       int batch = 1, int64_t bsrc = 0, int64_t bout = 0);
 
 // --------------------------------------------------------------- quantize --
 struct QuantLayout {

@@ -133,6 +133,10 @@ constexpr int kChunk = 32;      // panel rows solved per pass
 constexpr int kMaxPanelWG = 256;
 constexpr int kPanelGroup = 4;  // panels per trailing update of the Cholesky
 constexpr int kPGW = kNB * kPanelGroup;  // columns of a panel group
+// triangular-inverse levels at least this wide run on the three-part product
+// (narrower levels measured faster on the fp32 product, whose 64-tiles skip
+// more of the triangular operands' zeros)
+constexpr int64_t kTrtriX3 = 2048;
 using Blk = float (*)[kLP];
 constexpr int kTP = 68;        // row pitch of the 64x64 product buffer
 using TBlk = float (*)[kTP];
@@ -737,6 +741,23 @@ PrepLayout prepare_layout(int64_t d) {
   off += 256;
   L.off_p = off;  // a panel group's factor columns as three bf16 planes (blocked layout)
   off += up(3 * static_cast<size_t>(x3_plane_elems(d, kPGW)) * sizeof(uint16_t));
+  // the triangular inverse's levels on the bf16 matrix cores: both operands
+  // of a level's products as three bf16 planes, all of the level's groups
+  size_t qa = 0, qb = 0;
+  for (int64_t w = kNB; w < d; w *= 2) {
+    if (w < kTrtriX3) continue;
+    const int64_t full = d / (2 * w), cw = d - (full * 2 * w + w);
+    qa = std::max(qa, static_cast<size_t>(full * w * w));  // the full groups' L21, then C^-1
+    qb = std::max(qb, static_cast<size_t>(full * w * w));  // A^-1 transposed, then T transposed
+    if (cw > 0) {  // the ragged group
+      qa = std::max(qa, static_cast<size_t>(std::max(x3_plane_elems(cw, w), x3_plane_elems(cw, cw))));
+      qb = std::max(qb, static_cast<size_t>(std::max(x3_plane_elems(w, w), x3_plane_elems(w, cw))));
+    }
+  }
+  L.off_qa = off;
+  off += up(3 * qa * sizeof(uint16_t));
+  L.off_qb = off;
+  off += up(3 * qb * sizeof(uint16_t));
   L.ws_bytes = off;
   return L;
 }
@@ -758,6 +779,8 @@ hipError_t prepare_launch(float* S, int64_t n, int64_t n_total, float damp, bool
   float* lam = reinterpret_cast<float*>(w + lay.off_lambda);
   float* Dinv = reinterpret_cast<float*>(w + lay.off_dinv);
   uint16_t* P = reinterpret_cast<uint16_t*>(w + lay.off_p);
+  uint16_t* QA = reinterpret_cast<uint16_t*>(w + lay.off_qa);
+  uint16_t* QB = reinterpret_cast<uint16_t*>(w + lay.off_qb);
   const int64_t pplane = x3_plane_elems(n, kPGW);
   const int64_t nn = n * n;
 
@@ -826,10 +849,26 @@ hipError_t prepare_launch(float* S, int64_t n, int64_t n_total, float damp, bool
       const float* L21 = Hr + w_el * n;        // rows [w_el, 2 w_el), cols [0, w_el)
       const float* Ainv = Hr;
       const float* Cinv = Hr + w_el * (n + 1);
-      GPTQ_TRY(gemm_f32(w_el, w_el, w_el, 1.f, L21, n, gs, Ainv, n, gs, false, 0.f, T, w_el, w_el * w_el,
-                        static_cast<int>(groups_full), false, 1, st));
-      GPTQ_TRY(gemm_f32(w_el, w_el, w_el, -1.f, Cinv, n, gs, T, w_el, w_el * w_el, false, 0.f,
-                        Hr + w_el * n, n, gs, static_cast<int>(groups_full), false, 2, st));
+      const int gb = static_cast<int>(groups_full);
+      if (w_el >= kTrtriX3) {
+        // on the bf16 matrix cores: each operand split into three bf16
+        // planes first (A row by row, B transposed); the tiles skip the
+        // zero K range of the triangular operand as gemm_f32 does
+        const int64_t pe = w_el * w_el;  // elements of one plane (w_el a multiple of 128)
+        const int64_t be = 3 * pe;       // one group's three planes
+        GPTQ_TRY(split3_rows(L21, n, w_el, w_el, QA, st, gb, gs, be));
+        GPTQ_TRY(split3_t(Ainv, n, w_el, w_el, QB, st, gb, gs, be));
+        GPTQ_TRY(gemm_x3(w_el, w_el, w_el, 1.f, QA, pe, QB, pe, T, w_el, st, 0, false, 1, true, gb, be, be, pe));
+        GPTQ_TRY(split3_rows(Cinv, n, w_el, w_el, QA, st, gb, gs, be));
+        GPTQ_TRY(split3_t(T, w_el, w_el, w_el, QB, st, gb, pe, be));
+        GPTQ_TRY(gemm_x3(w_el, w_el, w_el, -1.f, QA, pe, QB, pe, Hr + w_el * n, n, st, 0, false, 2, true, gb, be, be,
+                         gs));
+      } else {
+        GPTQ_TRY(gemm_f32(w_el, w_el, w_el, 1.f, L21, n, gs, Ainv, n, gs, false, 0.f, T, w_el, w_el * w_el, gb,
+                          false, 1, st));
+        GPTQ_TRY(gemm_f32(w_el, w_el, w_el, -1.f, Cinv, n, gs, T, w_el, w_el * w_el, false, 0.f, Hr + w_el * n, n,
+                          gs, gb, false, 2, st));
+      }
     }
     // ragged last group: A is h blocks wide, C is what remains (< h blocks)
     const int64_t a0 = groups_full * 2 * w_el;
@@ -839,9 +878,23 @@ hipError_t prepare_launch(float* S, int64_t n, int64_t n_total, float damp, bool
       const float* L21 = Hr + c0 * n + a0;
       const float* Ainv = Hr + a0 * (n + 1);
       const float* Cinv = Hr + c0 * (n + 1);
-      GPTQ_TRY(gemm_f32(cw, w_el, w_el, 1.f, L21, n, 0, Ainv, n, 0, false, 0.f, T, w_el, 0, 1, false, 1, st));
-      GPTQ_TRY(gemm_f32(cw, w_el, cw, -1.f, Cinv, n, 0, T, w_el, 0, false, 0.f, Hr + c0 * n + a0, n, 0, 1, false,
-                        2, st));
+      if (w_el >= kTrtriX3) {
+        GPTQ_TRY(split3_rows(L21, n, cw, w_el, QA, st));
+        GPTQ_TRY(split3_t(Ainv, n, w_el, w_el, QB, st));
+        GPTQ_TRY(gemm_x3(cw, w_el, w_el, 1.f, QA, x3_plane_elems(cw, w_el), QB, x3_plane_elems(w_el, w_el), T, w_el,
+                         st, 0, false, 1, true));
+      } else {
+        GPTQ_TRY(gemm_f32(cw, w_el, w_el, 1.f, L21, n, 0, Ainv, n, 0, false, 0.f, T, w_el, 0, 1, false, 1, st));
+      }
+      if (w_el >= kTrtriX3 && cw % 64 == 0) {
+        GPTQ_TRY(split3_rows(Cinv, n, cw, cw, QA, st));
+        GPTQ_TRY(split3_t(T, w_el, cw, w_el, QB, st));
+        GPTQ_TRY(gemm_x3(cw, w_el, cw, -1.f, QA, x3_plane_elems(cw, cw), QB, x3_plane_elems(w_el, cw),
+                         Hr + c0 * n + a0, n, st, 0, false, 2, true));
+      } else {
+        GPTQ_TRY(gemm_f32(cw, w_el, cw, -1.f, Cinv, n, 0, T, w_el, 0, false, 0.f, Hr + c0 * n + a0, n, 0, 1, false,
+                          2, st));
+      }
     }
   }
   reverse_kernel<<<grid_for(nn), 256, 0, st>>>(Hr, n, U);
