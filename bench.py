@@ -391,8 +391,9 @@ def all_configs(args):
 
     import synth
     lines = ["| cfg | layer | d_out x d_in | N | x | bits/G | ms per solve | weight cols/s | accumulate "
-             "TFLOP/s (% peak) | prepare TFLOP/s (% fp32) | quantize: update TFLOP/s (% fp32), sweep GB/s "
-             "(% HBM) | sweep kernel: us per block, GB/s (% HBM) | update products: TFLOP/s (% of their peak) | pack GB/s |",
+             "TFLOP/s (% peak) | prepare TFLOP/s (% of fp32 peak) | quantize: update TFLOP/s (% of fp32 peak), sweep "
+             "GB/s (% HBM) | sweep kernel: us per block, GB/s (% HBM) | update products: TFLOP/s (% of their ceiling) "
+             "| pack GB/s |",
              "|---|---|---|---:|---|---|---:|---:|---:|---:|---:|---:|---:|---:|"]
     for c in (1, 2, 3, 4, 5):
         for layer in synth.config_layers(c):
@@ -411,8 +412,9 @@ def all_configs(args):
                 f"{m['prepare']['TFLOP/s']:.1f} ({100 * m['prepare']['frac']:.1f}%) | "
                 f"{m['quantize']['update TFLOP/s']:.1f} ({100 * m['quantize']['frac']:.1f}%), "
                 f"{m['quantize']['sweep GB/s']:.0f} ({100 * m['quantize']['sweep frac of HBM']:.1f}%) | "
-                f"{sw.get('us_per_block', 0):.1f}, {sw.get('GB/s', 0):.0f} ({100 * sw.get('frac_hbm', 0):.1f}%) | "
-                f"{up.get('TFLOP/s', 0):.1f} ({100 * up.get('frac_peak', 0):.1f}% of {up.get('peak_TFLOP/s', 0):.0f}) | "
+                f"{sw.get('us_per_block', 0):.1f}, {sw.get('GB/s', 0):.0f} ({100 * sw.get('frac_hbm', 0):.1f}%) | " +
+                (f"{up['TFLOP/s']:.1f} ({100 * up['frac_peak']:.1f}% of {up['peak_TFLOP/s']:.0f}) | " if up else
+                 "— | ") +
                 f"{m['pack']['GB/s']:.0f} |")
             del ls
             torch.cuda.empty_cache()
