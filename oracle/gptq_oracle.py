@@ -252,14 +252,26 @@ def quantize_layer(W: np.ndarray, U: np.ndarray, perm: np.ndarray, bits: int, gr
                    tie_tol: float = 0.0, record_v: bool = False, decision=np.float32) -> SweepResult:
     """GPTQ column sweep.
 
-    blocksize=None runs the plain form: after column i is quantized its
-    normalised error err_i = (w_i - q_i) / U[i, i] is subtracted, scaled by
-    U[i, j], from every later column j at once.  An integer blocksize runs the
-    lazy-batch form of the chapter's pseudocode: the update is applied inside
-    the block of `blocksize` columns immediately and to the columns after the
-    block with one matrix product once the block is done.  The two agree
-    exactly in real arithmetic when group_size divides the block or the block
-    divides group_size.
+    Definition ([ch5] 5.1.4 objective, 5.1.8 OBS closed form and its Cholesky
+    form): columns are fixed one at a time in sweep order; fixing column i to
+    its quantized value changes it by e_i = w_i - q_i, and the remaining
+    columns take the OBS compensation that keeps the layer objective minimal,
+    -e_i / [H_F^-1]_ii * (H_F^-1)_{i, j} over the not-yet-fixed set F.  With
+    H_p^-1 = U^T U (U upper), row i of U restricted to j >= i is
+    (H_F^-1)_{i, j} / sqrt([H_F^-1]_ii), so the compensation of column j is
+    err_i * U[i, j] with err_i = e_i / U[i, i].  blocksize=None runs exactly
+    that, one column after another (the "plain" form); `naive_obq` below
+    re-inverts H_F instead of using U, and the two are pinned equal.
+
+    An integer blocksize reorders the same sums (the lazy batches of [ch5]
+    5.1.8): the plain form is run on each block of `blocksize` columns alone,
+    and the compensations the block's columns owe every later column, err_i *
+    U[i, j] summed over the block, are applied at the block's end as one
+    matrix product.  Column j of a later block receives the same terms as in
+    the plain form, only summed in another order, so the two agree exactly in
+    real arithmetic when group_size divides the block or the block divides
+    group_size (a dynamic group's range must be read after every earlier
+    column's compensation has arrived); pinned equal as well.
 
     rows selects a subset of output rows (rows are independent given U).
 
@@ -329,31 +341,32 @@ def quantize_layer(W: np.ndarray, U: np.ndarray, perm: np.ndarray, bits: int, gr
         e = w - what
         return e / U[i, i]
 
-    if blocksize is None:
-        for i in range(d_in):
+    def plain(cur: np.ndarray, lo: int, hi: int, outer: Optional[np.ndarray] = None):
+        """The plain form over sweep columns [lo, hi), held in cur[:, 0 : hi -
+        lo]: fix each column and compensate the later columns of the range.
+        A dynamic group starting here takes its range from cur, or, for groups
+        wider than a block (they start where a block starts, so nothing in
+        their range has been touched yet), from `outer`, the whole running
+        matrix."""
+        for i in range(lo, hi):
+            c = i - lo
             if dynamic and i % G == 0:
-                dyn_params(i, Wp[:, i:i + G])
-            err = step(i, Wp, i)
+                wide = outer is not None and G > blocksize
+                dyn_params(i, outer[:, i:i + G] if wide else cur[:, c:c + G])
+            err = step(i, cur, c)
             Err[:, i] = err
-            Wp[:, i + 1:] -= np.outer(err, U[i, i + 1:])
+            cur[:, c + 1:] -= np.outer(err, U[i, i + 1:hi])
+
+    if blocksize is None:
+        plain(Wp, 0, d_in)
     else:
         B = blocksize
         for b0 in range(0, d_in, B):
             b1 = min(b0 + B, d_in)
             Wb = Wp[:, b0:b1].copy()
-            for i in range(b0, b1):
-                c = i - b0
-                if dynamic and i % G == 0:
-                    if G <= B:
-                        grp = Wb[:, c:c + G]
-                    else:   # group spans later blocks; Wb is untouched at a block start
-                        grp = Wp[:, i:i + G]
-                    dyn_params(i, grp)
-                err = step(i, Wb, c)
-                Err[:, i] = err
-                Wb[:, c + 1:] -= np.outer(err, U[i, i + 1:b1])
+            plain(Wb, b0, b1, outer=Wp)
             Wp[:, b0:b1] = Wb
-            if b1 < d_in:
+            if b1 < d_in:  # what the block's columns owe the later ones
                 Wp[:, b1:] -= Err[:, b0:b1] @ U[b0:b1, b1:]
 
     codes = np.empty_like(codes_p)
