@@ -138,6 +138,10 @@ gptq_status gptq_hessian_accumulate(float* S, int64_t d_in, const void* X, int32
  *       fp32); every trailing block past p is.  U is then undefined.  Read it
  *       after synchronising.
  * n_total must be > 0.
+ * Arithmetic: fp32 throughout.  The factorization's large products run on the
+ * bf16 matrix cores with each fp32 operand split exactly into three bf16
+ * parts (six part products, summed in fp32): the accuracy of an fp32 product,
+ * not its bit pattern.  U is deterministic for a given S and cfg.
  */
 size_t gptq_prepare_workspace_size(int64_t d_in);
 gptq_status gptq_prepare_hinv(float* S_to_H, int64_t d_in, int64_t n_total, const gptq_config* cfg,
@@ -160,6 +164,9 @@ gptq_status gptq_prepare_hinv(float* S_to_H, int64_t d_in, int64_t n_total, cons
  *   row_loss_or_null optional [d_out] fp32: sum of err^2 over the row, which
  *                    equals (w - w_hat) H_d (w - w_hat)^T
  * Requires d_in % (32 / bits) == 0 (d_in % 32 == 0 for 3 bits).
+ * The products that carry errors past each group of 1024 columns run as
+ * three-part bf16 products (fp32 accuracy, see gptq_prepare_hinv); the rest in
+ * fp32.  Outputs are deterministic for given inputs.
  * gptq_workspace_size depends on cfg (its group layout picks the launch
  * plan's buffers); it returns 0 for an invalid cfg or size.
  */
