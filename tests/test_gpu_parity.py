@@ -106,7 +106,8 @@ def _gpu_S(G, L):
 
 
 @pytest.mark.parametrize("desc_act", [False, True])
-@pytest.mark.parametrize("d_in,n,corr", [(64, 300, True), (200, 900, True), (384, 2000, False), (576, 3000, True)])
+@pytest.mark.parametrize("d_in,n,corr", [(64, 300, True), (200, 900, True), (384, 2000, False), (576, 3000, True),
+                                         (4128, 9000, True)])  # ragged last panel; a 4096-wide inverse level
 def test_prepare_parity(G, desc_act, d_in, n, corr):
     banner(f"prepare d_in={d_in} desc_act={desc_act}")
     L = synth.Layer("p", 8, d_in, n, "f32", "f32", False, True, cfg=8, layer_id=d_in, correlated=corr)
@@ -236,6 +237,7 @@ SWEEP_CASES = [  # d_out, d_in, bits, G, sym, desc_act, static, w dtype
     (4100, 384, 4, 128, True, False, False, "bf16"),  # more rows than one workgroup per CU: a launch per block
     (4100, 288, 3, 64, False, True, True, "f32"),     # the same, static act-order groups, last block ragged
     (4100, 1152, 4, 128, True, True, False, "bf16"),  # a launch per block, product past a 1024-column group
+    (40, 4128, 4, 32, False, True, False, "bf16"),    # four groups of 1024 columns and a ragged 32-column rest
 ]
 
 
