@@ -11,7 +11,10 @@
 // part product is exact in the fp32 accumulator.  The result has the accuracy
 // of an fp32 product (it is not bit-equal to one: the sums round in another
 // order).  It serves the GPTQ lazy-batch update W[:, j+B:] -= Err U[j:j+B,
-// j+B:] (GPTQ 实战 ch.5, section 5.1.8).
+// j+B:] and the products of the factor U = Cholesky(inverse(H)) (GPTQ 实战
+// ch.5, section 5.1.8): the Cholesky's updates and the widest levels of the
+// triangular inverse (batched, with the triangular operands' zero K range
+// skipped per tile).
 //
 // Operands are given as three planes of bf16 bit patterns in the blocked
 // panel layout (x3_offset): A over [M][K], B transposed over [N][K]; C fp32
