@@ -502,8 +502,19 @@ __global__ __launch_bounds__(NE * 64) void hessian_reduce_kernel(const float* __
   constexpr int64_t kElems = static_cast<int64_t>(TILE) * TILE;
   const int64_t off = static_cast<int64_t>((w * 16 * NE + (i * 4 + j) * NE + e) * 64 + lane) << 2;
   const float* src = partial + static_cast<int64_t>(t) * n_split * kElems + off;
+  // sixteen slices' loads in flight at a time (a plain loop waits for each
+  // load before the next), added in slice order
   f32x4_t sum = {0.f, 0.f, 0.f, 0.f};
-  for (int k = 0; k < n_split; ++k) sum += *reinterpret_cast<const f32x4_t*>(src + k * kElems);
+  for (int k = 0; k < n_split; k += 16) {
+    f32x4_t v[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u)
+      v[u] = (k + u < n_split) ? __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(src + (k + u) * kElems))
+                               : f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < 16; ++u)
+      if (k + u < n_split) sum += v[u];
+  }
   const int r0 = (NE == 4) ? 8 * e + 4 * (lane >> 5) : 4 * (lane >> 4);
   const int c = lane & (BS - 1);
 #pragma unroll
@@ -511,11 +522,21 @@ __global__ __launch_bounds__(NE * 64) void hessian_reduce_kernel(const float* __
   __syncthreads();
   const int row0 = I * TILE + (w >> 1) * (TILE / 2) + BS * i;
   const int col0 = J * TILE + (w & 1) * (TILE / 2) + BS * j;
-  for (int idx = tid; idx < BS * BS; idx += NE * 64) {
-    const int rr = idx / BS, cc = idx % BS;
-    if (row0 + rr < d && col0 + cc < d) S[static_cast<int64_t>(row0 + rr) * d + col0 + cc] += blk[rr][cc];
-    if (mirror && col0 + rr < d && row0 + cc < d)
-      S[static_cast<int64_t>(col0 + rr) * d + row0 + cc] += blk[cc][rr];
+  // all reads of S first, then the writes (each element of S is read and
+  // written by one thread only)
+  constexpr int NI = BS * BS / (NE * 64);
+  float vd[NI], vm[NI];
+#pragma unroll
+  for (int u = 0; u < NI; ++u) {
+    const int idx = tid + u * NE * 64, rr = idx / BS, cc = idx % BS;
+    vd[u] = (row0 + rr < d && col0 + cc < d) ? S[static_cast<int64_t>(row0 + rr) * d + col0 + cc] : 0.f;
+    vm[u] = (mirror && col0 + rr < d && row0 + cc < d) ? S[static_cast<int64_t>(col0 + rr) * d + row0 + cc] : 0.f;
+  }
+#pragma unroll
+  for (int u = 0; u < NI; ++u) {
+    const int idx = tid + u * NE * 64, rr = idx / BS, cc = idx % BS;
+    if (row0 + rr < d && col0 + cc < d) S[static_cast<int64_t>(row0 + rr) * d + col0 + cc] = vd[u] + blk[rr][cc];
+    if (mirror && col0 + rr < d && row0 + cc < d) S[static_cast<int64_t>(col0 + rr) * d + row0 + cc] = vm[u] + blk[cc][rr];
   }
 }
 
