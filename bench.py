@@ -147,6 +147,12 @@ def cpu_baseline(layer, W_host, args, x_chunks=None):
     }
 
 
+def fp32_planes(d_in, n_tokens):
+    """Whether the library accumulates an fp32 X of this shape as three bf16
+    planes on the bf16 matrix cores (its rule: N d^2 >= 4e9 and d <= 8192)."""
+    return d_in <= 8192 and float(n_tokens) * d_in * d_in >= 4e9
+
+
 def stage_metrics(layer, st):
     """Algorithmic rates of the four stages and their fraction of the bound
     that applies: MFMA peak (bf16 or fp32) for the contractions, HBM for the
@@ -158,7 +164,9 @@ def stage_metrics(layer, st):
     f_upd = float(d_out) * d_in * (d_in - 1)
     b_sweep = float(d_out) * d_in * (9 + 8.0 / G)
     b_pack = float(d_out) * d_in * (1 + layer.bits / 8.0)
-    peak_h = PEAK_BF16_TFLOPS if layer.x_dtype == "bf16" else PEAK_FP32_TFLOPS
+    # fp32 X on the plane path: six bf16 part products per fp32-equivalent flop
+    peak_h = (PEAK_BF16_TFLOPS if layer.x_dtype == "bf16" else
+              PEAK_BF16_TFLOPS / 6.0 if fp32_planes(d_in, N) else PEAK_FP32_TFLOPS)
 
     def rate(work, ms, scale):
         return work / (ms * 1e-3) / scale

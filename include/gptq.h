@@ -110,7 +110,16 @@ const char* gptq_status_string(int32_t status);
  *            ldx a multiple of 8 (bf16) or 4 (fp32).
  *   n_tokens >= 0; 0 leaves S unchanged.
  * Products are formed exactly (bf16) or in fp32 and summed in fp32.  The sum
- * is deterministic: a fixed token split and a fixed reduction order.
+ * is deterministic: a fixed token split and a fixed reduction order.  fp32 X
+ * with n_tokens * d_in^2 >= 4e9 and d_in <= 8192 runs on the bf16 matrix
+ * cores: each value is split exactly into three bf16 parts (x = hi + mid +
+ * lo), and S takes the part products above 2^-24 of the total (hi hi, hi mid,
+ * mid hi, hi lo, lo hi, mid mid), each formed exactly and summed in fp32, so
+ * the result keeps fp32-product accuracy (every entry below the diagonal is
+ * written as a copy of its mirror); smaller calls use the fp32 matrix cores.
+ * The workspace size
+ * depends on d_in, n_tokens and the dtype (the fp32 path on the bf16 matrix
+ * cores also holds the bf16 parts of up to 512 MiB of X at a time).
  */
 size_t gptq_hessian_workspace_size(int64_t d_in, int64_t n_tokens, int32_t xt);
 gptq_status gptq_hessian_accumulate(float* S, int64_t d_in, const void* X, int32_t xt,

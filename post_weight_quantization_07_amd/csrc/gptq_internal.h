@@ -38,6 +38,9 @@ struct HessPlan {
   int64_t split_len; // tokens per slice (multiple of stage_tokens)
   size_t partial_bytes;
   size_t ws_bytes;
+  bool planes;       // fp32 X as three bf16 planes on the bf16 matrix cores
+  int64_t chunk;     // planes: tokens split per pass
+  size_t planes_off; // planes: offset of the plane buffer in the workspace
 };
 HessPlan hessian_plan(int64_t d_in, int64_t n_tokens, bool bf16, int n_cu);
 hipError_t hessian_launch(const HessPlan& plan, float* S, int64_t d_in, const void* X, bool bf16,

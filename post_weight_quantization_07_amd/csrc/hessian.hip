@@ -18,6 +18,9 @@
 //   operands come out of the token-major LDS tile through ds_read_b64_tr_b16.
 // fp32 path: 128x128 tile, 4 waves of 64x64, v_mfma_f32_16x16x4_f32, LDS
 //   holds [token][channel] rows padded to 144 floats.
+// fp32 path on the bf16 matrix cores (large calls): X is split exactly into
+//   three bf16 planes, the bf16 kernel runs the tiles of the part products
+//   above 2^-24, and a reduction combines them (see the plane kernels below).
 #include "gptq_common.h"
 #include "gptq_internal.h"
 
@@ -42,6 +45,7 @@ struct HessParams {
   int32_t n_split;
   int64_t split_len;
   float* partial;
+  int32_t planes;  // 1: the tiles of the three-plane list below (fp32 X split into bf16 parts)
 };
 
 // Tiles of the upper triangle in "super-tile" order: 4x4 blocks of tiles
@@ -74,6 +78,39 @@ GPTQ_DEV void tile_coords(int pos, int nt, int& I, int& J) {
     }
   }
   I = J = 0;
+}
+
+// Row-major upper triangle of an nt x nt tile grid: u -> (i, j), i <= j.
+GPTQ_DEV void tri_coords(int u, int nt, int& i, int& j) {
+  i = 0;
+  while (u >= nt - i) {
+    u -= nt - i;
+    ++i;
+  }
+  j = i + u;
+}
+
+// fp32 X enters as three bf16 planes X = Xh + Xm + Xl (exact split), stored
+// side by side, each nt tiles wide.  X^T X is the sum of the part products
+// above 2^-24 of the total: Xh^T Xh + Xm^T Xm + (Xh^T Xm + Xh^T Xl) + their
+// transposes.  The tile list (I, J index 256-column blocks of the planes):
+//   [0, T)             Xh^T Xh, upper triangle (T = nt (nt + 1) / 2)
+//   [T, T + nt^2)       Xh^T Xm, every tile
+//   [T + nt^2, ...)     Xh^T Xl, every tile
+//   [T + 2 nt^2, ...)   Xm^T Xm, upper triangle
+GPTQ_DEV void plane_tile_coords(int t, int nt, int& I, int& J) {
+  const int T = nt * (nt + 1) / 2, Q = nt * nt;
+  if (t < T) {
+    tri_coords(t, nt, I, J);
+  } else if (t < T + 2 * Q) {
+    const int u = t - T, pl = u / Q, v = u % Q;
+    I = v / nt;
+    J = (1 + pl) * nt + v % nt;
+  } else {
+    tri_coords(t - T - 2 * Q, nt, I, J);
+    I += nt;
+    J += nt;
+  }
 }
 
 // Work item of workgroup b.  Workgroups are dispatched round-robin over the
@@ -231,7 +268,10 @@ __global__ __launch_bounds__(kThreads, 1) void hessian_bf16_pipe_kernel(HessPara
       sB3[kPOpBytes], sB4[kPOpBytes], sB5[kPOpBytes], sB6[kPOpBytes], sB7[kPOpBytes];
   int t, split, I, J;
   work_item(blockIdx.x, p.n_tiles, p.n_split, t, split);
-  tile_coords(t, p.nt, I, J);
+  if (p.planes)
+    plane_tile_coords(t, p.nt, I, J);
+  else
+    tile_coords(t, p.nt, I, J);
   const int64_t k0 = static_cast<int64_t>(split) * p.split_len;
   const int64_t k1 = min(p.n_tokens, k0 + p.split_len);
   const int tid = threadIdx.x, lane = tid & 63;
@@ -540,9 +580,160 @@ __global__ __launch_bounds__(NE * 64) void hessian_reduce_kernel(const float* __
   }
 }
 
+// ======================================================== fp32 X planes ====
+// X (fp32, [n, ldx]) -> X3 (bf16, [n, 3 dp]): part q of channel c at q dp + c
+// (hi, mid, lo of the exact split), zeros for d <= c < dp.  d is a multiple
+// of 4 and rows of X are 16-byte aligned.
+__global__ __launch_bounds__(256) void plane_split_kernel(const float* __restrict__ X, int64_t ldx, int64_t n, int d,
+                                                         int dp, uint16_t* __restrict__ X3) {
+  const int64_t q = dp / 4;
+  const int64_t total = n * q;
+  for (int64_t idx = blockIdx.x * 256ll + threadIdx.x; idx < total; idx += static_cast<int64_t>(gridDim.x) * 256) {
+    const int64_t t = idx / q;
+    const int c = static_cast<int>(idx % q) * 4;
+    f32x4_t v = {0.f, 0.f, 0.f, 0.f};
+    if (c < d) v = *reinterpret_cast<const f32x4_t*>(X + t * ldx + c);
+    uint16_t h[4], m[4], l[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) split3(v[e], h[e], m[e], l[e]);
+    uint16_t* row = X3 + t * 3 * static_cast<int64_t>(dp) + c;
+    typedef __attribute__((__vector_size__(4 * sizeof(uint16_t)))) uint16_t u16x4_t;
+    *reinterpret_cast<u16x4_t*>(row) = u16x4_t{h[0], h[1], h[2], h[3]};
+    *reinterpret_cast<u16x4_t*>(row + dp) = u16x4_t{m[0], m[1], m[2], m[3]};
+    *reinterpret_cast<u16x4_t*>(row + 2 * dp) = u16x4_t{l[0], l[1], l[2], l[3]};
+  }
+}
+
+// S += Xh^T Xh + Xm^T Xm + Xh^T Xm + (Xh^T Xm)^T + Xh^T Xl + (Xh^T Xl)^T from
+// the partial tiles of the plane list.  One workgroup per 32x32 block (rb, cb)
+// of an upper-triangle output tile (I, J) of S: the blocks at (rb, cb) of the
+// tiles Xh^T Xh (I, J), Xh^T Xm (I, J), Xh^T Xl (I, J), Xm^T Xm (I, J), plus
+// the transposes of the blocks at (cb, rb) of Xh^T Xm (J, I) and Xh^T Xl
+// (J, I), each summed over the slices in slice order.  On a diagonal tile
+// only blocks with rb <= cb run, and the mirror of every block above the
+// diagonal is written too, so every element of S is updated by one thread.
+__global__ __launch_bounds__(256) void plane_reduce_kernel(const float* __restrict__ partial, int n_split, int nt,
+                                                          int d, float* __restrict__ S) {
+  __shared__ float D[32][33], Tr[32][33];
+  const int t = blockIdx.x >> 6, b = blockIdx.x & 63;
+  int I, J;
+  tri_coords(t, nt, I, J);
+  const int rb = b >> 3, cb = b & 7;
+  if (I == J && rb > cb) return;
+  const int T = nt * (nt + 1) / 2, Q = nt * nt;
+  constexpr int64_t kElems = static_cast<int64_t>(kBTile) * kBTile;
+  const int tid = threadIdx.x, e = tid >> 6, lane = tid & 63;
+  // this thread's 4 floats of block (r, c) of a tile in register order
+  auto off = [&](int r, int c) -> int64_t {
+    const int w = 2 * (r >> 2) + (c >> 2), i = r & 3, j = c & 3;
+    return static_cast<int64_t>(((w * 64 + (i * 4 + j) * 4 + e) * 64 + lane) << 2);
+  };
+  const int64_t od = off(rb, cb), ot = off(cb, rb);
+  const float* src[6] = {partial + static_cast<int64_t>(t) * n_split * kElems + od,                      // hh (I, J)
+                         partial + static_cast<int64_t>(T + I * nt + J) * n_split * kElems + od,         // hm (I, J)
+                         partial + static_cast<int64_t>(T + Q + I * nt + J) * n_split * kElems + od,     // hl (I, J)
+                         partial + static_cast<int64_t>(T + 2 * Q + t) * n_split * kElems + od,          // mm (I, J)
+                         partial + static_cast<int64_t>(T + J * nt + I) * n_split * kElems + ot,         // hm (J, I)
+                         partial + static_cast<int64_t>(T + Q + J * nt + I) * n_split * kElems + ot};    // hl (J, I)
+  f32x4_t sum[6];
+#pragma unroll
+  for (int x = 0; x < 6; ++x) sum[x] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int k = 0; k < n_split; k += 4) {
+    f32x4_t v[4][6];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int x = 0; x < 6; ++x)
+        v[u][x] = (k + u < n_split)
+                      ? __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(src[x] + (k + u) * kElems))
+                      : f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int x = 0; x < 6; ++x)
+        if (k + u < n_split) sum[x] += v[u][x];
+  }
+  // the small parts first
+  const f32x4_t dsum = sum[0] + (sum[1] + (sum[2] + sum[3]));
+  const f32x4_t tsum = sum[4] + sum[5];
+  const int r0 = 8 * e + 4 * (lane >> 5), c = lane & 31;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    D[r0 + r][c] = dsum[r];
+    Tr[r0 + r][c] = tsum[r];
+  }
+  __syncthreads();
+  // a block on the diagonal of S takes its upper triangle and that
+  // triangle's mirror, so S stays exactly symmetric
+  const bool diag = (I == J) && (rb == cb);
+  const bool mirror = (I != J) || (rb < cb);
+  const int row0 = I * kBTile + 32 * rb, col0 = J * kBTile + 32 * cb;
+  float vd[4], vm[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int idx = tid + u * 256, rr = idx >> 5, cc = idx & 31;
+    const bool wd = row0 + rr < d && col0 + cc < d && (!diag || rr <= cc);
+    const bool wm = col0 + rr < d && row0 + cc < d && (mirror || (diag && cc < rr));
+    vd[u] = wd ? S[static_cast<int64_t>(row0 + rr) * d + col0 + cc] : 0.f;
+    vm[u] = wm ? S[static_cast<int64_t>(col0 + rr) * d + row0 + cc] : 0.f;
+  }
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int idx = tid + u * 256, rr = idx >> 5, cc = idx & 31;
+    const bool wd = row0 + rr < d && col0 + cc < d && (!diag || rr <= cc);
+    const bool wm = col0 + rr < d && row0 + cc < d && (mirror || (diag && cc < rr));
+    if (wd) S[static_cast<int64_t>(row0 + rr) * d + col0 + cc] = vd[u] + (D[rr][cc] + Tr[cc][rr]);
+    if (wm) S[static_cast<int64_t>(col0 + rr) * d + row0 + cc] = vm[u] + (D[cc][rr] + Tr[rr][cc]);
+  }
+}
+
 }  // namespace
 
+// fp32 X goes through the three-plane path when the product is large enough
+// to repay the split pass (N d^2 >= 4e9) and the planes' partial tiles stay
+// modest (d_in <= 8192); it runs X in passes of at most 512 MiB of planes.
+constexpr double kPlaneMinWork = 4e9;
+constexpr int64_t kPlaneMaxDim = 8192;
+constexpr int64_t kPlaneBufBytes = int64_t{512} << 20;
+
+static HessPlan plane_plan(int64_t d_in, int64_t n_tokens, int n_cu) {
+  HessPlan pl{};
+  pl.planes = true;
+  pl.tile = kBTile;
+  pl.stage_tokens = kPStage * kPSlots;
+  pl.nt = static_cast<int>((d_in + kBTile - 1) / kBTile);
+  const int64_t dp = static_cast<int64_t>(pl.nt) * kBTile;
+  pl.n_tiles = pl.nt * (pl.nt + 1) + 2 * pl.nt * pl.nt;
+  const int64_t per_token = 3 * dp * static_cast<int64_t>(sizeof(uint16_t));
+  const int64_t cap = std::max<int64_t>(pl.stage_tokens, (kPlaneBufBytes / per_token) / pl.stage_tokens * pl.stage_tokens);
+  pl.chunk = std::min<int64_t>(n_tokens, cap);
+  // slice count: time of the partial-tile rounds (about 3 us per tile and
+  // 128-token stage) plus the reduction's read of the partials (5 TB/s)
+  const int64_t slots = n_cu > 0 ? n_cu : 256;
+  const int64_t stages = (pl.chunk + pl.stage_tokens - 1) / pl.stage_tokens;
+  const double tile_bytes = static_cast<double>(kBTile) * kBTile * sizeof(float);
+  int best = 1;
+  double best_cost = 1e300;
+  for (int s = 1; s <= std::min<int64_t>(64, stages); ++s) {
+    const int64_t waves = (static_cast<int64_t>(pl.n_tiles) * s + slots - 1) / slots;
+    const int64_t per = (stages + s - 1) / s;
+    const double cost = 3.0 * waves * per + pl.n_tiles * s * tile_bytes / 5e6;
+    if (cost < best_cost) {
+      best_cost = cost;
+      best = s;
+    }
+  }
+  pl.split_len = ((stages + best - 1) / best) * pl.stage_tokens;
+  pl.n_split = static_cast<int>((pl.chunk + pl.split_len - 1) / pl.split_len);
+  pl.partial_bytes = static_cast<size_t>(pl.n_tiles) * pl.n_split * static_cast<size_t>(tile_bytes);
+  pl.planes_off = (pl.partial_bytes + 255) & ~static_cast<size_t>(255);
+  pl.ws_bytes = pl.planes_off + static_cast<size_t>(pl.chunk * per_token);
+  return pl;
+}
+
 HessPlan hessian_plan(int64_t d_in, int64_t n_tokens, bool bf16, int n_cu) {
+  if (!bf16 && d_in <= kPlaneMaxDim && static_cast<double>(n_tokens) * d_in * d_in >= kPlaneMinWork)
+    return plane_plan(d_in, n_tokens, n_cu);
   HessPlan pl{};
   pl.tile = bf16 ? kBTile : kFTile;
   pl.stage_tokens = bf16 ? kPStage * kPSlots : kFStage;
@@ -592,6 +783,35 @@ hipError_t hessian_launch(const HessPlan& pl, float* S, int64_t d_in, const void
   p.partial = static_cast<float*>(ws);
   const int blocks = pl.n_tiles * pl.n_split;
   const int d = static_cast<int>(d_in);
+  if (pl.planes) {
+    // fp32 X in passes: split a pass into bf16 planes, the plane tiles'
+    // partials, then their sum into S
+    const int dp = pl.nt * kBTile;
+    uint16_t* X3 = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + pl.planes_off);
+    p.X = X3;
+    p.ldx = 3 * static_cast<int64_t>(dp);
+    p.d_in = 3 * dp;
+    p.planes = 1;
+    for (int64_t c0 = 0; c0 < n_tokens; c0 += pl.chunk) {
+      const int64_t len = std::min<int64_t>(pl.chunk, n_tokens - c0);
+      p.n_tokens = len;
+      // a shorter last pass takes fewer slices, so no slice is empty
+      p.n_split = static_cast<int32_t>((len + pl.split_len - 1) / pl.split_len);
+      {
+        PhaseScope ph(kPhHessian, stream);
+        const int64_t work = len * (dp / 4);
+        const int grid = static_cast<int>(std::max<int64_t>(1, std::min<int64_t>((work + 255) / 256, 8192)));
+        plane_split_kernel<<<grid, 256, 0, stream>>>(static_cast<const float*>(X) + c0 * ldx, ldx, len, d, dp, X3);
+        hessian_bf16_pipe_kernel<<<pl.n_tiles * p.n_split, kThreads, 0, stream>>>(p);
+      }
+      PhaseScope ph(kPhHessReduce, stream);
+      const int out_tiles = pl.nt * (pl.nt + 1) / 2;
+      plane_reduce_kernel<<<out_tiles * 64, 256, 0, stream>>>(p.partial, p.n_split, pl.nt, d, S);
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+  }
   if (bf16) {
     {
       PhaseScope ph(kPhHessian, stream);

@@ -132,9 +132,10 @@ def test_zero_channels(G, desc_act):
 
 @pytest.mark.parametrize("desc_act", [False, True])
 @pytest.mark.parametrize("bad", ["nan", "inf"])
-def test_nonfinite_inputs(G, desc_act, bad):
-    banner(f"non-finite X ({bad}), desc_act={desc_act}")
-    d, n = 300, 700
+@pytest.mark.parametrize("n", [700, 50000])  # 50000 tokens: fp32 X on the three-plane path
+def test_nonfinite_inputs(G, desc_act, bad, n):
+    banner(f"non-finite X ({bad}), desc_act={desc_act}, n={n}")
+    d = 300
     L = synth.Layer("nf", 8, d, n, "f32", "f32", False, False, cfg=10, layer_id=5)
     X = synth.activations(L)
     X[17, 42] = np.nan if bad == "nan" else np.inf

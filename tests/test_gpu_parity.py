@@ -48,7 +48,10 @@ def test_pack_bit_exact(G, bits, d_out, d_in):
 # --------------------------------------------------------------- Hessian ----
 
 HESS_CASES = [("bf16", 8, 1), ("bf16", 264, 63), ("bf16", 264, 1000), ("bf16", 520, 4097), ("bf16", 768, 20000),
-              ("f32", 4, 3), ("f32", 132, 1000), ("f32", 260, 4097), ("f32", 516, 9000)]
+              ("f32", 4, 3), ("f32", 132, 1000), ("f32", 260, 4097), ("f32", 516, 9000),
+              # fp32 X on the three-plane path (calls with N d^2 >= 4e9): a ragged plane (300 of 512 columns),
+              # eight tiles a plane, and calls of 90000 and 180000 tokens split into passes of 87296
+              ("f32", 300, 150000), ("f32", 2048, 20000), ("f32", 1000, 270000)]
 
 
 @pytest.mark.parametrize("dtype,d_in,n", HESS_CASES)
@@ -94,6 +97,25 @@ def test_hessian_empty_and_strided(G):
     torch.cuda.synchronize()
     ref, _ = O.hessian_sum([X])
     assert rel_fro(S.cpu().numpy() - 3.0, ref) <= 1e-5
+
+
+def test_hessian_planes_strided(G):
+    banner("hessian fp32 X on the three-plane path, row stride 512")
+    d_in, n = 300, 60000
+    L = synth.Layer("h", 8, d_in, n, "f32", "f32", False, True, cfg=7, layer_id=3)
+    X = synth.activations(L)
+    big = torch.zeros((n, 512), dtype=torch.float32)
+    big[:, :d_in] = torch.from_numpy(X)
+    Xd = big.to(dev())[:, :d_in]
+    S = torch.zeros((d_in, d_in), dtype=torch.float32, device=dev())
+    G.gptq_hessian_accumulate(S, Xd)
+    torch.cuda.synchronize()
+    ref, _ = O.hessian_sum([X])
+    got = S.cpu().numpy()
+    dg = np.sqrt(np.outer(np.diag(ref), np.diag(ref)))
+    assert rel_fro(got, ref) <= 1e-5
+    assert float(np.max(np.abs(got - ref) / dg)) <= 1e-5
+    np.testing.assert_array_equal(got, got.T)
 
 
 # --------------------------------------------------------------- prepare ----
