@@ -120,14 +120,13 @@ gptq_status gptq_quantize_layer(const void* W, int32_t wt, int64_t d_out, int64_
   if (cfg->desc_act && !perm) return GPTQ_ERR_INVALID_ARG;
   if (!packable(d_in, cfg->bits)) return GPTQ_ERR_INVALID_ARG;
   if (!aligned16(U) || !aligned16(codes) || (Q_or_null && !aligned16(Q_or_null))) return GPTQ_ERR_INVALID_ARG;
-  const int n_cu = device_cus();
   const gptq::QuantLayout lay =
       gptq::quant_layout(d_out, d_in, gptq::quant_planes(cfg->group_size, cfg->static_groups != 0));
   if (!ws || ws_bytes < lay.ws_bytes || !aligned256(ws)) return GPTQ_ERR_WORKSPACE;
   return from_hip(gptq::quantize_launch(W, wt == GPTQ_BF16, d_out, d_in, U, perm, cfg->bits, cfg->group_size,
                                         cfg->sym != 0, cfg->static_groups != 0, codes, scales, zeros, g_idx,
                                         Q_or_null, row_loss_or_null, ws, static_cast<hipStream_t>(stream),
-                                        cfg->desc_act == 0, n_cu));
+                                        cfg->desc_act == 0));
 }
 
 gptq_status gptq_pack(const uint8_t* codes, int64_t d_out, int64_t d_in, int32_t bits, int32_t* qweight,

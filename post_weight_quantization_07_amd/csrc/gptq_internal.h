@@ -106,9 +106,9 @@ struct QuantLayout {
   size_t off_wp, off_err, ws_bytes;
   size_t off_ea, off_bt;  // one launch per group: error planes, transposed U planes
 };
-// one sweep launch per group of columns: layers whose rows fit one workgroup
-// per CU, with groups inside a block or parameters fixed before the sweep
-bool group_launch(int64_t d_out, int group_size, bool static_groups, int n_cu);
+// one sweep launch per group of columns: groups inside a block or parameters
+// fixed before the sweep
+bool group_launch(int group_size, bool static_groups);
 // groups of 1024 columns, whose products past the group run on the bf16
 // matrix cores (error and U planes in the workspace)
 bool quant_planes(int group_size, bool static_groups);
@@ -116,7 +116,7 @@ QuantLayout quant_layout(int64_t d_out, int64_t d_in, bool planes);
 hipError_t quantize_launch(const void* W, bool w_bf16, int64_t d_out, int64_t d_in, const float* U,
                            const int32_t* perm, int bits, int group_size, bool sym, bool static_groups,
                            uint8_t* codes, float* scales, int32_t* zeros, int32_t* g_idx, float* Q,
-                           float* row_loss, void* ws, hipStream_t stream, bool identity, int n_cu);
+                           float* row_loss, void* ws, hipStream_t stream, bool identity);
 
 // ------------------------------------------------------------------- pack --
 hipError_t pack_launch(const uint8_t* codes, int64_t d_out, int64_t d_in, int bits, int32_t* qweight,

@@ -35,6 +35,8 @@ def _group(cfg, reduce=None):
 CASES = [
     pytest.param(2, None, id="cfg2-qkv-768"),
     pytest.param(4, dict(d_out=384, d_in=512, n_tokens=8192), id="cfg4-qkv-b3g32-actorder-reduced"),
+    # 4800 stacked rows (300 workgroups of 16 rows, more than one per CU) against members of 1600
+    pytest.param(3, dict(d_out=1600, d_in=512, n_tokens=8192), id="cfg3-qkv-stack-4800-rows"),
 ]
 
 
