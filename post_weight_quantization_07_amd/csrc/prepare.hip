@@ -36,15 +36,15 @@ namespace {
 
 constexpr int kNB = kPanel;  // 128
 
+// The elementwise passes over n x n matrices go row by row (workgroups over
+// rows, threads over columns), so no thread divides a flat index.
 __global__ void finalize_kernel(float* S, int64_t n, float scale, float* diag) {
-  const int64_t total = n * n;
-  for (int64_t e = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; e < total;
-       e += static_cast<int64_t>(gridDim.x) * blockDim.x) {
-    const float v = S[e] * scale;
-    S[e] = v;
-    const int64_t r = e / n;
-    if (r * n + r == e) diag[r] = v;
-  }
+  for (int64_t r = blockIdx.x; r < n; r += gridDim.x)
+    for (int64_t c = threadIdx.x; c < n; c += blockDim.x) {
+      const float v = S[r * n + c] * scale;
+      S[r * n + c] = v;
+      if (c == r) diag[r] = v;
+    }
 }
 
 // lambda = damp * mean(diag): fixed-order tree over 1024 threads.  A diagonal
@@ -99,17 +99,16 @@ __global__ __launch_bounds__(256) void order_kernel(const float* diag, int64_t n
 __global__ void gather_kernel(const float* H, int64_t n, const int32_t* perm, const float* lambda,
                               float* Hr) {
   const float lam = lambda[0];
-  const int64_t total = n * n;
-  for (int64_t e = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; e < total;
-       e += static_cast<int64_t>(gridDim.x) * blockDim.x) {
-    const int64_t a = e / n, b = e - a * n;
-    float v = 0.f;
-    if (b <= a) {
-      const int64_t pa = perm[n - 1 - a], pb = perm[n - 1 - b];
-      v = H[pa * n + pb];
-      if (a == b) v += lam;
+  for (int64_t a = blockIdx.x; a < n; a += gridDim.x) {
+    const int64_t pa = perm[n - 1 - a];
+    for (int64_t b = threadIdx.x; b < n; b += blockDim.x) {
+      float v = 0.f;
+      if (b <= a) {
+        v = H[pa * n + perm[n - 1 - b]];
+        if (a == b) v += lam;
+      }
+      Hr[a * n + b] = v;
     }
-    Hr[e] = v;
   }
 }
 
@@ -711,13 +710,13 @@ __global__ void place_dinv_kernel(const float* Dinv, int64_t n, float* Hr) {
 }
 
 __global__ void reverse_kernel(const float* M, int64_t n, float* U) {
-  const int64_t total = n * n;
-  for (int64_t e = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; e < total;
-       e += static_cast<int64_t>(gridDim.x) * blockDim.x) {
-    const int64_t i = e / n, j = e - i * n;
-    U[e] = (j >= i) ? M[(n - 1 - i) * n + (n - 1 - j)] : 0.f;
-  }
+  for (int64_t i = blockIdx.x; i < n; i += gridDim.x)
+    for (int64_t j = threadIdx.x; j < n; j += blockDim.x)
+      U[i * n + j] = (j >= i) ? M[(n - 1 - i) * n + (n - 1 - j)] : 0.f;
 }
+
+// one workgroup per row, at most 8192
+int row_grid(int64_t n) { return static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(n, 8192))); }
 
 int grid_for(int64_t total) {
   return static_cast<int>(std::max<int64_t>(1, std::min<int64_t>((total + 255) / 256, 8192)));
@@ -782,17 +781,16 @@ hipError_t prepare_launch(float* S, int64_t n, int64_t n_total, float damp, bool
   uint16_t* QA = reinterpret_cast<uint16_t*>(w + lay.off_qa);
   uint16_t* QB = reinterpret_cast<uint16_t*>(w + lay.off_qb);
   const int64_t pplane = x3_plane_elems(n, kPGW);
-  const int64_t nn = n * n;
 
   {
     PhaseScope ph(kPhPrepElem, st);
-    finalize_kernel<<<grid_for(nn), 256, 0, st>>>(S, n, static_cast<float>(2.0 / static_cast<double>(n_total)), diag);
+    finalize_kernel<<<row_grid(n), 256, 0, st>>>(S, n, static_cast<float>(2.0 / static_cast<double>(n_total)), diag);
     GPTQ_TRY(hipGetLastError());
     lambda_kernel<<<1, 1024, 0, st>>>(diag, n, damp, lam, info);
     GPTQ_TRY(hipGetLastError());
     order_kernel<<<static_cast<int>((n + 255) / 256), 256, 0, st>>>(diag, n, desc_act ? 1 : 0, perm);
     GPTQ_TRY(hipGetLastError());
-    gather_kernel<<<grid_for(nn), 256, 0, st>>>(S, n, perm, lam, Hr);
+    gather_kernel<<<row_grid(n), 256, 0, st>>>(S, n, perm, lam, Hr);
     GPTQ_TRY(hipGetLastError());
   }
 
@@ -897,7 +895,7 @@ hipError_t prepare_launch(float* S, int64_t n, int64_t n_total, float damp, bool
       }
     }
   }
-  reverse_kernel<<<grid_for(nn), 256, 0, st>>>(Hr, n, U);
+  reverse_kernel<<<row_grid(n), 256, 0, st>>>(Hr, n, U);
   return hipGetLastError();  // the triangular inverse's phase closes after the reversal
 }
 

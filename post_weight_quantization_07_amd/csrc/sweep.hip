@@ -706,6 +706,31 @@ __global__ __launch_bounds__(512) void sweep_group_kernel(SweepParams p) {
 }
 
 // Wp[r][i] = W[r][perm[i]] in fp32.
+// Without act-order the working copy is W converted to fp32: eight values a
+// thread, 16-byte loads and stores (W 16-byte aligned).
+__global__ void convert_w_kernel(const void* W, int w_bf16, int64_t total, float* Wp) {
+  const int64_t n8 = total / 8;
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  const int64_t t0 = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x;
+  for (int64_t v = t0; v < n8; v += stride) {
+    f32x4_t a, b;
+    if (w_bf16) {
+      const u32x4_t q = reinterpret_cast<const u32x4_t*>(W)[v];
+      a = f32x4_t{__uint_as_float(q[0] << 16), __uint_as_float(q[0] & 0xFFFF0000u), __uint_as_float(q[1] << 16),
+                  __uint_as_float(q[1] & 0xFFFF0000u)};
+      b = f32x4_t{__uint_as_float(q[2] << 16), __uint_as_float(q[2] & 0xFFFF0000u), __uint_as_float(q[3] << 16),
+                  __uint_as_float(q[3] & 0xFFFF0000u)};
+    } else {
+      a = reinterpret_cast<const f32x4_t*>(W)[2 * v];
+      b = reinterpret_cast<const f32x4_t*>(W)[2 * v + 1];
+    }
+    reinterpret_cast<f32x4_t*>(Wp)[2 * v] = a;
+    reinterpret_cast<f32x4_t*>(Wp)[2 * v + 1] = b;
+  }
+  for (int64_t e = 8 * n8 + t0; e < total; e += stride)
+    Wp[e] = w_bf16 ? bf16_to_f32(static_cast<const uint16_t*>(W)[e]) : static_cast<const float*>(W)[e];
+}
+
 __global__ void gather_w_kernel(const void* W, int w_bf16, int64_t d_out, int64_t d_in, const int32_t* perm,
                                 int identity, float* Wp) {
   const int64_t total = d_out * d_in;
@@ -819,8 +844,11 @@ hipError_t quantize_launch(const void* W, bool w_bf16, int64_t d_out, int64_t d_
   hipError_t e;
   {
     PhaseScope ph(kPhQuantElem, st);
-    gather_w_kernel<<<grid_for(d_out * d_in), 256, 0, st>>>(W, w_bf16 ? 1 : 0, d_out, d_in, perm, identity ? 1 : 0,
-                                                            Wp);
+    if (identity && reinterpret_cast<uintptr_t>(W) % 16 == 0)
+      convert_w_kernel<<<grid_for((d_out * d_in + 7) / 8), 256, 0, st>>>(W, w_bf16 ? 1 : 0, d_out * d_in, Wp);
+    else
+      gather_w_kernel<<<grid_for(d_out * d_in), 256, 0, st>>>(W, w_bf16 ? 1 : 0, d_out, d_in, perm,
+                                                              identity ? 1 : 0, Wp);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (preset) {
       const int64_t pairs = static_cast<int64_t>(n_groups) * d_out;
