@@ -51,7 +51,9 @@ HESS_CASES = [("bf16", 8, 1), ("bf16", 264, 63), ("bf16", 264, 1000), ("bf16", 5
               ("f32", 4, 3), ("f32", 132, 1000), ("f32", 260, 4097), ("f32", 516, 9000),
               # fp32 X on the three-plane path (calls with N d^2 >= 4e9): a ragged plane (300 of 512 columns),
               # eight tiles a plane, and calls of 90000 and 180000 tokens split into passes of 87296
-              ("f32", 300, 150000), ("f32", 2048, 20000), ("f32", 1000, 270000)]
+              ("f32", 300, 150000), ("f32", 2048, 20000), ("f32", 1000, 270000),
+              # the widest plane width (calls of 60 and 119 tokens: one partly filled stage) and one just past it
+              ("f32", 8192, 180), ("f32", 8196, 180)]
 
 
 @pytest.mark.parametrize("dtype,d_in,n", HESS_CASES)
